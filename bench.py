@@ -1,0 +1,228 @@
+"""Benchmark of the compressor hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole path over one batch: for the default
+workload (ratio-4 prefill of 65536 tokens, hidden 4096) that is the 512-wide
+compressor (fp32 projection GEMM, fused pool + RMSNorm + fp4 cache codes) and
+the 128-wide indexer compressor (GEMM, pool + RMSNorm, bf16 latent), with the
+hidden states resident in HBM. Prints one JSON line.
+
+Kernel durations are measured with HIP events on the launch stream around
+repeated launches of each kernel alone (the same library calls with the other
+stages switched off through their arguments: no outputs = projection GEMM only;
+projections given = pooling only). The roofline object reports the dominant
+kernel (the 512-wide projection GEMM, fp32 matrix-core bound); `pool` reports
+the fused pooling kernel against HBM bandwidth.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compressed KV entries/sec + achieved HBM GB/s, ratio-4 prefill N=65536"
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "gemm": "kv_cache_compression_fp32_amd/csrc/gemm_f32.hip",
+    "pool": "kv_cache_compression_fp32_amd/csrc/pool.hip",
+}
+
+
+def source_sha(name: str) -> str:
+    with open(os.path.join(ROOT, KERNEL_SOURCES[name]), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic(name: str, launches_bytes: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if there is none or the kernel source changed since it was taken."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    entry = data.get(name)
+    if not entry or entry.get("source_sha") != source_sha(name):
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def pool_bytes(batch, seqlen, ratio, hd, quantize, latent):
+    """Algorithmic HBM bytes of one pooling launch: every projection value
+    read once (kv and score planes), outputs written once."""
+    proj = 2 * hd if ratio == 4 else hd
+    groups = seqlen // ratio
+    read = 2 * batch * groups * ratio * proj * 4
+    write = 0
+    if latent:
+        write += batch * groups * hd * 2
+    if quantize:
+        write += batch * groups * (hd // 2 + hd // 16)
+    return read + write
+
+
+def cpu_baseline(wl, W, seconds=10.0, max_tokens=16384):
+    """The oracle, as it stands, on the first tokens of the workload: doubles
+    the sample until it takes `seconds` (or reaches max_tokens)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    tokens = 512
+    while True:
+        x = np.stack([W.hidden_rows(wl, b, 0, tokens) for b in range(wl.batch)])
+        t0 = time.perf_counter()
+        entries = 0
+        for comp in wl.compressors:
+            w = W.weights(wl, comp)
+            cfg = oracle.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps)
+            out = oracle.prefill(cfg, oracle.Weights(w["wkv"], w["wgate"], w["ape"]), oracle.State(cfg, wl.batch),
+                                 x=x, quantize=comp.quantize)
+            entries = max(entries, out["latent"].shape[0] * out["latent"].shape[1])
+        dt = time.perf_counter() - t0
+        if dt >= seconds or tokens >= max_tokens:
+            break
+        tokens *= 2
+    return {"value": entries / dt, "unit": "entries/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {tokens} tokens of each of {wl.batch} batch rows through all "
+                      f"{len(wl.compressors)} compressor(s) of the workload ({entries} entries, {dt:.2f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_r4_n65536_fp4_idx128")
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_compression_fp32_amd.kvc as kvc
+    import kv_cache_compression_fp32_amd.workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kvc.lib()  # fails loudly if the HIP library is missing
+    wl = W.WORKLOADS[args.workload]
+    if wl.decode or wl.dim == 0:
+        print("bench.py times the prefill workloads with hidden states", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda"
+    print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
+    x = torch.from_numpy(W.hidden(wl)).to(dev)
+    torch.cuda.synchronize()
+
+    comps = []
+    for comp in wl.compressors:
+        cfg = kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps)
+        w = {k: torch.from_numpy(v).to(dev) for k, v in W.weights(wl, comp).items()}
+        wts = kvc.Weights(wkv=w["wkv"], wgate=w["wgate"], ape=w["ape"])
+        groups = wl.seqlen // comp.ratio
+        ws = torch.empty(kvc.kvc_prefill_workspace_floats(cfg, wl.batch, wl.seqlen), dtype=torch.float32,
+                         device=dev)
+        state = kvc.new_state(cfg, wl.batch)
+        out = kvc.new_outputs(cfg, wl.batch, groups, latent=not comp.quantize, fp4=comp.quantize)
+        comps.append((comp, cfg, wts, ws, state, out, groups))
+
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for comp, cfg, wts, ws, state, out, groups in comps:
+            kvc.compressor_prefill(cfg, wts, x, wl.batch, wl.seqlen, ws, state[0], state[1], out)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] timed steps", file=sys.stderr, flush=True)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    entries = comps[0][6] * wl.batch
+    value = entries / (ms_per_step / 1e3)
+
+    # ---- per-kernel durations, measured live with events on the launch stream
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    kernels = {}
+    print("[bench] kernel timing", file=sys.stderr, flush=True)
+    for idx, (comp, cfg, wts, ws, state, out, groups) in enumerate(comps):
+        tag = f"hd{comp.head_dim}"
+        gemm_ms = timed(lambda: kvc.compressor_prefill(cfg, wts, x, wl.batch, wl.seqlen, ws), args.kernel_reps)
+        # ws now holds this compressor's projections: pool them alone
+        pool_ms = timed(lambda: kvc.compressor_prefill(cfg, kvc.Weights(ape=wts.ape), None, wl.batch, wl.seqlen,
+                                                       ws, None, None, out), args.kernel_reps)
+        proj = 2 * comp.head_dim if comp.ratio == 4 else comp.head_dim
+        flops = 2.0 * wl.batch * wl.seqlen * wl.dim * 2 * proj
+        pbytes = pool_bytes(wl.batch, wl.seqlen, comp.ratio, comp.head_dim, comp.quantize, not comp.quantize)
+        kernels[f"gemm_{tag}"] = {"ms": gemm_ms, "tflops": flops / gemm_ms / 1e9, "flop": flops}
+        kernels[f"pool_{tag}"] = {"ms": pool_ms, "gbps": pbytes / pool_ms / 1e6, "bytes": pbytes}
+
+    main_tag = f"hd{wl.compressors[0].head_dim}"
+    g = kernels[f"gemm_{main_tag}"]
+    p = kernels[f"pool_{main_tag}"]
+    g_traffic = measured_traffic("gemm", None)
+    p_traffic = measured_traffic("pool", None)
+    roofline = {"bound": "mfma", "achieved": round(g["tflops"], 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(g["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": g_traffic,
+                "kernel": "gemm_f32_kernel<128,128,64,64>", "per_launch": g["flop"], "avg_ms": round(g["ms"], 4)}
+    pool = {"bound": "hbm", "achieved": round(p["gbps"], 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(p["gbps"] / PEAK_HBM_GBPS, 4), "traffic": p_traffic,
+            "kernel": "pool_small_kernel<512,4,true>", "per_launch": p["bytes"], "avg_ms": round(p["ms"], 4)}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "entries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "seqlen": wl.seqlen, "dim": wl.dim,
+                   "compressors": [{"ratio": c.ratio, "head_dim": c.head_dim, "fp4": c.quantize}
+                                   for c in wl.compressors],
+                   "entries_per_step": entries},
+        "hbm_gbps": pool["achieved"],
+        "roofline": roofline,
+        "pool": pool,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, W)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

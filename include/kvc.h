@@ -1,0 +1,203 @@
+/*
+ * kvc.h - C ABI of libkvc.so, the MI355X (gfx950) compressor of the
+ * DeepSeek-V4.1 compressed-attention KV cache.
+ *
+ * The compressor turns hidden states x [batch, seqlen, dim] into compressed
+ * KV entries, one per `ratio` tokens:
+ *   1. kv = x . wkv^T and score = x . wgate^T, f32 weights [proj, dim]
+ *      ("Module compress", Functions, linear_f32; "DeepSeek V4.1 . Pool token
+ *      pairs", Compressor listing, forward).
+ *   2. score += ape[t mod ratio], a positional bias on the gate logits
+ *      ("Compressed Sparse Attention . ratio m = 4", Per-channel gated
+ *      pooling).
+ *   3. Groups of `ratio` tokens. At ratio 4 the groups overlap: each token's
+ *      projections hold two branches of head_dim (A = columns [0, hd),
+ *      B = [hd, 2 hd)), and entry j pools 8 candidates, the previous block's
+ *      branch B then the current block's branch A; entry 0's previous branch is
+ *      padding (kv 0, score -inf) ("Compressed Sparse Attention . ratio m = 4",
+ *      Why one output uses eight candidates; Tensor-shape walkthrough).
+ *   4. Per-feature softmax over the candidates' logits, weighted sum of their
+ *      kv values, all in f32 ("DeepSeek V4.1 . Pool token pairs", pooling
+ *      formula).
+ *   5. Rounding to bf16 and RMSNorm, output rounded to bf16 ("Module
+ *      compress", Precision paragraph; Compressor listing, forward).
+ *   6. Optionally the cache form of the latent: e2m1 codes with e4m3 scales
+ *      per block of 16, and its bf16 dequantisation ("Module compress",
+ *      Functions, fp4_quant_e4m3_inplace and to_e2m1_rne).
+ * The trailing seqlen mod ratio tokens wait in a caller-owned state, and a
+ * decode step emits one entry per completed group (Compressor listing,
+ * forward, decode branch; "Compressed Sparse Attention . ratio m = 4", Prefill
+ * and decode use the same rule).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers unless marked "host". Arrays are
+ *     dense and row-major in the index order given. The caller allocates and
+ *     owns all memory; the library allocates no device memory and keeps no
+ *     state between calls. Calls on different streams that do not share
+ *     buffers may run concurrently.
+ *   - bf16 values are passed as their uint16_t bit patterns, e4m3fn scales
+ *     and e2m1 codes as bytes.
+ *   - Arguments are checked on the host before anything is enqueued; on an
+ *     error nothing is enqueued and a negative KVC_E* code is returned.
+ *     On success the work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     null stream) and KVC_OK is returned; results are ready when the stream
+ *     is synchronised. Device faults surface at that synchronisation.
+ *   - "No output yet" (a prefill shorter than ratio, a decode step that does
+ *     not complete a group) is not an error: *n_groups / *emitted report it.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *kvc_stream; /* a hipStream_t */
+
+#define KVC_OK 0
+#define KVC_EINVAL (-1)       /* a required pointer is NULL, or a size is out of range */
+#define KVC_EUNSUPPORTED (-2) /* a valid configuration this library does not implement */
+#define KVC_ESPACE (-3)       /* a caller-provided buffer is too small */
+#define KVC_EHIP (-4)         /* the HIP runtime rejected a launch */
+
+/* Compressor configuration.
+ *   ratio    : 2, 4 or 128 (4 is the overlapped two-branch variant).
+ *   head_dim : latent width hd, 128 or 512.
+ *   dim      : hidden width of x, a positive multiple of 32 (ignored when x is
+ *              NULL).
+ *   eps      : RMSNorm epsilon (finite, >= 0).
+ * proj = 2 * head_dim at ratio 4, head_dim otherwise: the width of each
+ * projection plane. */
+typedef struct kvc_config {
+    int32_t ratio;
+    int32_t head_dim;
+    int64_t dim;
+    float eps;
+} kvc_config;
+
+/* Weights (device, f32).
+ *   wkv, wgate : [proj][dim]; required whenever x is not NULL.
+ *   ape        : [ratio][proj] positional bias of the gate logits, or NULL
+ *                (no bias).
+ *   norm_w     : [head_dim] RMSNorm weight, or NULL (all ones). */
+typedef struct kvc_weights {
+    const float *wkv;
+    const float *wgate;
+    const float *ape;
+    const float *norm_w;
+} kvc_weights;
+
+/* Outputs (device). Each is written iff its pointer is not NULL; G is the
+ * number of entries of the call (groups for a prefill, 1 for an emitting
+ * decode step).
+ *   latent  : [batch][G][head_dim] bf16, the RMSNorm output.
+ *   pooled  : [batch][G][head_dim] f32, the pooled value before rounding.
+ *   codes   : [batch][G][head_dim / 2] e2m1 codes of the latent, two per
+ *             byte, element 2k in the low nibble, sign in bit 3 of a nibble.
+ *   scales  : [batch][G][head_dim / 16] e4m3fn scale of each block of 16.
+ *   dequant : [batch][G][head_dim] bf16, codes times scales. */
+typedef struct kvc_outputs {
+    uint16_t *latent;
+    float *pooled;
+    uint8_t *codes;
+    uint8_t *scales;
+    uint16_t *dequant;
+} kvc_outputs;
+
+/* proj for `cfg`, or a negative KVC_E* code if cfg is invalid. */
+int64_t kvc_proj_width(const kvc_config *cfg);
+
+/* Rows of each state plane: 2 * ratio at ratio 4, ratio otherwise; or a
+ * negative KVC_E* code. */
+int64_t kvc_state_rows(const kvc_config *cfg);
+
+/* f32 elements of the workspace compressor_prefill needs:
+ * 2 * batch * seqlen * proj; or a negative KVC_E* code. */
+int64_t kvc_prefill_workspace_floats(const kvc_config *cfg, int64_t batch, int64_t seqlen);
+
+/* f32 elements of the workspace compressor_decode_step needs (split
+ * projection partial sums); at least 2 * batch * proj; or a negative code. */
+int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch);
+
+/* Compressor forward at start_pos == 0 (prefill) over `seqlen` tokens of
+ * `batch` rows ("DeepSeek V4.1 . Pool token pairs", Compressor listing,
+ * forward, prefill branch; the overlap of "Compressed Sparse Attention .
+ * ratio m = 4").
+ *   x            : [batch][seqlen][dim] f32, or NULL. NULL means the caller
+ *                  has put the projections (without bias) in `workspace`:
+ *                  the kv plane [batch][seqlen][proj] followed by the score
+ *                  plane [batch][seqlen][proj]; no weights are read then
+ *                  except ape and norm_w.
+ *   batch        : >= 1.   seqlen : >= 0.
+ *   workspace    : f32, >= kvc_prefill_workspace_floats() elements; receives
+ *                  the two projection planes when x is not NULL.
+ *   kv_state,
+ *   score_state  : [state_batch][kvc_state_rows()][proj] f32 each, or both
+ *                  NULL (nothing carried). Rows of batch row b are written as
+ *                  the decode continuation needs them: non-overlapped, rows
+ *                  [0, seqlen mod ratio) get the trailing tokens; at ratio 4,
+ *                  rows [0, 4) get the last complete block (kv 0 / score -inf
+ *                  when there is none) and rows [4, 4 + seqlen mod 4) the
+ *                  trailing tokens. Scores are stored with the bias added.
+ *   state_batch  : capacity of the state planes in batch rows (>= batch).
+ *   out          : outputs with G = seqlen / ratio (host struct; may be NULL
+ *                  to compute only projections and state).
+ *   n_groups     : host, optional; receives seqlen / ratio (0: no entry).
+ * Errors: KVC_EINVAL, KVC_EUNSUPPORTED, KVC_ESPACE, KVC_EHIP. */
+int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const float *x, int64_t batch,
+                       int64_t seqlen, float *workspace, int64_t workspace_floats, float *kv_state,
+                       float *score_state, int64_t state_batch, const kvc_outputs *out,
+                       int64_t *n_groups, kvc_stream stream);
+
+/* One decode step: one token per batch row at position start_pos
+ * (Compressor listing, forward, decode branch). The token fills slot
+ * start_pos mod ratio of the state; when (start_pos + 1) mod ratio == 0 the
+ * group is pooled and one entry per batch row is written to `out` (G = 1);
+ * at ratio 4 the current block then becomes the previous one. start_pos == 0
+ * is a prefill of one token, which resets the carried block.
+ *   x            : [batch][dim] f32 (one token per row), or NULL: then the
+ *                  caller has put the token's projections (without bias) in
+ *                  workspace[0 : 2 * batch * proj] as the kv rows
+ *                  [batch][proj] followed by the score rows [batch][proj].
+ *   start_pos    : >= 0, the token's position in its sequence.
+ *   workspace    : f32, >= kvc_decode_workspace_floats() elements.
+ *   kv_state,
+ *   score_state  : required, as for compressor_prefill, holding the carry
+ *                  of the previous calls of this sequence.
+ *   emitted      : host, optional; receives 1 if entries were written, else 0.
+ * Errors: as compressor_prefill. */
+int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const float *x, int64_t batch,
+                           int64_t start_pos, float *workspace, int64_t workspace_floats,
+                           float *kv_state, float *score_state, int64_t state_batch,
+                           const kvc_outputs *out, int32_t *emitted, kvc_stream stream);
+
+/* The latent's fp4 round trip ("Module compress", Functions,
+ * fp4_quant_e4m3_inplace; to_e2m1_rne; Constants, LATENT_BLOCK) on
+ * [rows][width] bf16 values, per block of 16 consecutive values of a row:
+ * amax floored at 6 * 2^-9; scale = e4m3fn(amax / 6), round to nearest even,
+ * the division an IEEE f32 one; codes = e2m1(value / scale), nearest, ties to
+ * the even code, saturating at 6, sign kept (also for values rounding to 0);
+ * dequant = e2m1 value * scale (exact in bf16).
+ *   in     : [rows][width] bf16.   rows >= 0, width > 0 and width % 16 == 0.
+ *   codes  : [rows][width / 2] bytes (layout as kvc_outputs.codes), or NULL.
+ *   scales : [rows][width / 16] e4m3fn bytes, or NULL.
+ *   out    : [rows][width] bf16 dequantised values, or NULL; may equal `in`
+ *            (in place). Other overlaps are not allowed.
+ * Errors: KVC_EINVAL, KVC_EHIP. */
+int latent_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *codes,
+                     uint8_t *scales, uint16_t *out, kvc_stream stream);
+
+/* A static description of a KVC_* code. */
+const char *kvc_strerror(int code);
+
+/* Library version string. */
+const char *kvc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

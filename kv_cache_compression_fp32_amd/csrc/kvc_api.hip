@@ -1,0 +1,317 @@
+// C ABI of libkvc.so (declared in include/kvc.h): argument checks and the
+// launch sequence of each entry point. Everything runs in this library's
+// kernels on the caller's stream; nothing is allocated and nothing is kept
+// between calls.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kvc.h"
+#include "kvc_launch.h"
+
+namespace {
+
+constexpr int64_t kAlign = 16;  // bytes; every device pointer is accessed in 16-byte vectors
+
+bool aligned(const void *p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
+
+int check_config(const kvc_config *cfg) {
+  if (!cfg) return KVC_EINVAL;
+  if (!(cfg->eps >= 0.0f) || !isfinite(cfg->eps)) return KVC_EINVAL;
+  if (cfg->ratio != 2 && cfg->ratio != 4 && cfg->ratio != 128) return KVC_EUNSUPPORTED;
+  if (cfg->head_dim != 128 && cfg->head_dim != 512) return KVC_EUNSUPPORTED;
+  return KVC_OK;
+}
+
+bool overlapped(const kvc_config *cfg) { return cfg->ratio == 4; }
+int64_t proj_of(const kvc_config *cfg) { return overlapped(cfg) ? 2 * (int64_t)cfg->head_dim : cfg->head_dim; }
+int64_t rows_of(const kvc_config *cfg) { return overlapped(cfg) ? 2 * (int64_t)cfg->ratio : cfg->ratio; }
+
+int check_projection_inputs(const kvc_config *cfg, const kvc_weights *w) {
+  if (!w || !w->wkv || !w->wgate) return KVC_EINVAL;
+  if (cfg->dim <= 0) return KVC_EINVAL;
+  if (cfg->dim % 32 != 0) return KVC_EUNSUPPORTED;
+  if (!aligned(w->wkv) || !aligned(w->wgate)) return KVC_EINVAL;
+  return KVC_OK;
+}
+
+int check_outputs(const kvc_outputs *out) {
+  if (!out) return KVC_OK;
+  if (!aligned(out->latent) || !aligned(out->pooled) || !aligned(out->dequant)) return KVC_EINVAL;
+  // codes rows are head_dim / 2 bytes: 64 or 256, each lane stores up to 4
+  if (out->codes && (reinterpret_cast<uintptr_t>(out->codes) % 4) != 0) return KVC_EINVAL;
+  return KVC_OK;
+}
+
+bool wants_entries(const kvc_outputs *out) {
+  return out && (out->latent || out->pooled || out->codes || out->scales || out->dequant);
+}
+
+// Decode splits the K range so that about 512 workgroups cover the batch's
+// projection; the split count divides the number of 32-wide k tiles.
+int32_t decode_splits(const kvc_config *cfg, int64_t batch) {
+  const int64_t m_tiles = (batch + 63) / 64;
+  const int64_t n_tiles = 2 * proj_of(cfg) / 64;
+  const int64_t k_tiles = cfg->dim / 32;
+  int64_t want = 512 / (m_tiles * n_tiles);
+  int32_t s = 1;
+  while (2 * s <= want && k_tiles % (2 * s) == 0) s *= 2;
+  return s;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_EHIP; }
+
+kvc::PoolArgs pool_args(const kvc_config *cfg, const kvc_weights *w, const kvc_outputs *out) {
+  kvc::PoolArgs p{};
+  p.ape = w ? w->ape : nullptr;
+  p.norm_w = w ? w->norm_w : nullptr;
+  p.eps = cfg->eps;
+  p.latent = out->latent;
+  p.pooled = out->pooled;
+  p.codes = out->codes;
+  p.scales = out->scales;
+  p.deq = out->dequant;
+  return p;
+}
+
+// Entries per wavefront run: about 2048 wavefronts in total (8 per CU), at
+// most 16 entries per run, so that the re-read of a run's first previous
+// block stays a small fraction of its traffic.
+int32_t entries_per_wave(int64_t batch, int64_t groups) {
+  const int64_t total = batch * groups;
+  int64_t e = (total + 2047) / 2048;
+  if (e < 1) e = 1;
+  if (e > 16) e = 16;
+  return (int32_t)e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t kvc_proj_width(const kvc_config *cfg) {
+  const int rc = check_config(cfg);
+  return rc ? rc : proj_of(cfg);
+}
+
+int64_t kvc_state_rows(const kvc_config *cfg) {
+  const int rc = check_config(cfg);
+  return rc ? rc : rows_of(cfg);
+}
+
+int64_t kvc_prefill_workspace_floats(const kvc_config *cfg, int64_t batch, int64_t seqlen) {
+  const int rc = check_config(cfg);
+  if (rc) return rc;
+  if (batch < 1 || seqlen < 0) return KVC_EINVAL;
+  return 2 * batch * seqlen * proj_of(cfg);
+}
+
+int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch) {
+  const int rc = check_config(cfg);
+  if (rc) return rc;
+  if (batch < 1) return KVC_EINVAL;
+  const int32_t splits = cfg->dim > 0 && cfg->dim % 32 == 0 ? decode_splits(cfg, batch) : 1;
+  return (int64_t)splits * 2 * batch * proj_of(cfg);
+}
+
+int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const float *x, int64_t batch,
+                       int64_t seqlen, float *workspace, int64_t workspace_floats, float *kv_state,
+                       float *score_state, int64_t state_batch, const kvc_outputs *out, int64_t *n_groups,
+                       kvc_stream stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (batch < 1 || seqlen < 0) return KVC_EINVAL;
+  if (x) {
+    if ((rc = check_projection_inputs(cfg, w))) return rc;
+    if (!aligned(x)) return KVC_EINVAL;
+  }
+  if (w && (!aligned(w->ape) || !aligned(w->norm_w))) return KVC_EINVAL;
+  const int64_t proj = proj_of(cfg);
+  const int64_t need = 2 * batch * seqlen * proj;
+  if (need > 0 && !workspace) return KVC_EINVAL;
+  if (workspace_floats < need) return KVC_ESPACE;
+  if (!aligned(workspace)) return KVC_EINVAL;
+  if ((kv_state == nullptr) != (score_state == nullptr)) return KVC_EINVAL;
+  if (kv_state && (state_batch < batch || !aligned(kv_state) || !aligned(score_state))) return KVC_EINVAL;
+  if ((rc = check_outputs(out))) return rc;
+
+  const int64_t groups = seqlen / cfg->ratio;
+  if (n_groups) *n_groups = groups;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t m = batch * seqlen;
+  float *kv_plane = workspace;
+  float *sc_plane = workspace ? workspace + m * proj : nullptr;
+
+  if (x && m > 0) {
+    kvc::GemmArgs g{};
+    g.a = x;
+    g.b0 = w->wkv;
+    g.b1 = w->wgate;
+    g.c0 = kv_plane;
+    g.c1 = sc_plane;
+    g.lda = cfg->dim;
+    g.ldb = cfg->dim;
+    g.ldc = proj;
+    g.m = m;
+    g.n_half = proj;
+    g.k = cfg->dim;
+    g.splits = 1;
+    g.c_split_stride = 0;
+    if ((rc = hip_status(kvc::launch_gemm(g, kvc::GemmShape::kPrefill, s)))) return rc;
+  }
+  if (groups > 0 && wants_entries(out)) {
+    kvc::PoolArgs p = pool_args(cfg, w, out);
+    p.kv = kv_plane;
+    p.sc = sc_plane;
+    p.row_stride = proj;
+    p.batch_stride = seqlen * proj;
+    p.batch = batch;
+    p.groups = groups;
+    p.first_entry = 0;
+    p.entries_per_wave = entries_per_wave(batch, groups);
+    p.out_batch_stride = groups;
+    if ((rc = hip_status(kvc::launch_pool(p, cfg->ratio, cfg->head_dim, s)))) return rc;
+  }
+  if (kv_state) {
+    kvc::StateStoreArgs st{};
+    st.kv = kv_plane;
+    st.sc = sc_plane;
+    st.ape = w ? w->ape : nullptr;
+    st.kv_state = kv_state;
+    st.sc_state = score_state;
+    st.batch = batch;
+    st.seqlen = seqlen;
+    st.proj = proj;
+    st.state_rows = rows_of(cfg);
+    st.ratio = cfg->ratio;
+    st.overlap = overlapped(cfg);
+    if ((rc = hip_status(kvc::launch_state_store(st, s)))) return rc;
+  }
+  return KVC_OK;
+}
+
+int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const float *x, int64_t batch,
+                           int64_t start_pos, float *workspace, int64_t workspace_floats, float *kv_state,
+                           float *score_state, int64_t state_batch, const kvc_outputs *out, int32_t *emitted,
+                           kvc_stream stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (batch < 1 || start_pos < 0) return KVC_EINVAL;
+  if (x) {
+    if ((rc = check_projection_inputs(cfg, w))) return rc;
+    if (!aligned(x)) return KVC_EINVAL;
+  }
+  if (w && (!aligned(w->ape) || !aligned(w->norm_w))) return KVC_EINVAL;
+  if (!workspace || !aligned(workspace)) return KVC_EINVAL;
+  const int64_t proj = proj_of(cfg);
+  const int32_t splits = x ? decode_splits(cfg, batch) : 1;
+  if (workspace_floats < (int64_t)splits * 2 * batch * proj) return KVC_ESPACE;
+  if (!kv_state || !score_state || state_batch < batch || !aligned(kv_state) || !aligned(score_state))
+    return KVC_EINVAL;
+  if ((rc = check_outputs(out))) return rc;
+
+  const int r = cfg->ratio;
+  const bool emit = start_pos > 0 && (start_pos + 1) % r == 0;
+  if (emitted) *emitted = emit ? 1 : 0;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  if (x) {
+    kvc::GemmArgs g{};
+    g.a = x;
+    g.b0 = w->wkv;
+    g.b1 = w->wgate;
+    g.c0 = workspace;
+    g.c1 = workspace + batch * proj;
+    g.lda = cfg->dim;
+    g.ldb = cfg->dim;
+    g.ldc = proj;
+    g.m = batch;
+    g.n_half = proj;
+    g.k = cfg->dim;
+    g.splits = splits;
+    g.c_split_stride = 2 * batch * proj;
+    if ((rc = hip_status(kvc::launch_gemm(g, kvc::GemmShape::kDecode, s)))) return rc;
+  }
+  const int slot = (int)(start_pos % r);
+  kvc::IngestArgs in{};
+  in.part = workspace;
+  in.splits = splits;
+  in.ape = w ? w->ape : nullptr;
+  in.kv_state = kv_state;
+  in.sc_state = score_state;
+  in.batch = batch;
+  in.proj = proj;
+  in.state_rows = rows_of(cfg);
+  in.slot = slot;
+  in.state_row = overlapped(cfg) ? r + slot : slot;
+  in.ratio = r;
+  in.reset_prev = (start_pos == 0 && overlapped(cfg)) ? 1 : 0;
+  if ((rc = hip_status(kvc::launch_decode_ingest(in, s)))) return rc;
+
+  if (emit && wants_entries(out)) {
+    kvc::PoolArgs p = pool_args(cfg, w, out);
+    p.ape = nullptr;  // the state already holds biased scores
+    p.kv = kv_state;
+    p.sc = score_state;
+    p.row_stride = proj;
+    p.batch_stride = rows_of(cfg) * proj;
+    p.batch = batch;
+    p.groups = 1;
+    p.first_entry = overlapped(cfg) ? 1 : 0;
+    p.entries_per_wave = 1;
+    p.out_batch_stride = 1;
+    if (overlapped(cfg)) {
+      p.shift_kv = kv_state;
+      p.shift_sc = score_state;
+    }
+    if ((rc = hip_status(kvc::launch_pool(p, r, cfg->head_dim, s)))) return rc;
+  } else if (emit && overlapped(cfg)) {
+    // no outputs requested: the carry must still move to the previous rows
+    kvc::PoolArgs p{};
+    p.kv = kv_state;
+    p.sc = score_state;
+    p.row_stride = proj;
+    p.batch_stride = rows_of(cfg) * proj;
+    p.batch = batch;
+    p.groups = 1;
+    p.first_entry = 1;
+    p.entries_per_wave = 1;
+    p.eps = cfg->eps;
+    p.out_batch_stride = 1;
+    p.shift_kv = kv_state;
+    p.shift_sc = score_state;
+    if ((rc = hip_status(kvc::launch_pool(p, r, cfg->head_dim, s)))) return rc;
+  }
+  return KVC_OK;
+}
+
+int latent_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *codes, uint8_t *scales,
+                     uint16_t *out, kvc_stream stream) {
+  if (rows < 0 || width <= 0 || width % 16 != 0) return KVC_EINVAL;
+  if (rows > 0 && !in) return KVC_EINVAL;
+  if (!aligned(in) || !aligned(out) || (codes && reinterpret_cast<uintptr_t>(codes) % 4 != 0))
+    return KVC_EINVAL;
+  if (out && out != in) {
+    // overlapping but distinct buffers would race
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(in), a1 = a0 + rows * width * 2;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(out), b1 = b0 + rows * width * 2;
+    if (a0 < b1 && b0 < a1) return KVC_EINVAL;
+  }
+  return hip_status(kvc::launch_fp4_quant(in, rows, width, codes, scales, out,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+const char *kvc_strerror(int code) {
+  switch (code) {
+    case KVC_OK: return "ok";
+    case KVC_EINVAL: return "invalid argument (null pointer, size out of range or misaligned pointer)";
+    case KVC_EUNSUPPORTED: return "unsupported configuration";
+    case KVC_ESPACE: return "buffer too small";
+    case KVC_EHIP: return "HIP launch failed";
+    default: return "unknown error code";
+  }
+}
+
+const char *kvc_version(void) { return "kvc 0.1.0 gfx950"; }
+
+}  // extern "C"

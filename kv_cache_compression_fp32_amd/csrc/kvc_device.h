@@ -1,0 +1,105 @@
+// Device helpers of the compressor kernels (gfx950, wave64).
+//
+// Number formats: bf16 (round to nearest even), OCP e4m3fn scales and OCP
+// e2m1 codes of the latent's fp4 round trip ("Module compress", Functions,
+// fp4_quant_e4m3_inplace and to_e2m1_rne). Every rounding decision below is
+// exact: scalings by powers of two, exact products and compares, and v_rndne.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+// amax floor of the fp4 round trip: 6 * 2^-9
+constexpr float kAmaxFloor = 0.01171875f;
+
+__device__ __forceinline__ uint32_t as_u32(float f) { return __float_as_uint(f); }
+__device__ __forceinline__ float as_f32(uint32_t u) { return __uint_as_float(u); }
+
+// bf16 bits of f, round to nearest, ties to even; overflow goes to infinity.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = as_u32(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_val(uint32_t b) { return as_f32(b << 16); }
+
+// e4m3fn code of q >= 0 (finite): nearest value, ties to even, saturating at
+// 448. Below 2^-6 the values are multiples of 2^-9; above, 3 mantissa bits.
+__device__ __forceinline__ uint32_t e4m3fn_rne(float q) {
+  if (q >= 448.0f) return 0x7eu;
+  if (q < 0.015625f) return (uint32_t)__builtin_rintf(q * 512.0f);  // 0..8; 8 is 2^-6
+  const uint32_t u = as_u32(q);
+  const int e = (int)(u >> 23) - 127;                             // -6 .. 8
+  const float frac = as_f32((u & 0x007fffffu) | 0x3f800000u);     // [1, 2)
+  const uint32_t m = (uint32_t)__builtin_rintf((frac - 1.0f) * 8.0f);  // 0..8
+  const uint32_t code = ((uint32_t)(e + 7) << 3) + m;             // m == 8 carries
+  return code > 0x7eu ? 0x7eu : code;
+}
+
+// value of an e4m3fn code (0x00..0x7e)
+__device__ __forceinline__ float e4m3fn_val(uint32_t c) {
+  const uint32_t e = c >> 3, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;
+  return as_f32(((e + 120u) << 23) | (m << 20));
+}
+
+// e2m1 code (sign in bit 3) of y / s by exact compares: |y| against the
+// midpoints of the grid {0, .5, 1, 1.5, 2, 3, 4, 6} times s. The products are
+// exact (s has at most 4 significant bits, the midpoints 3). A value on a
+// midpoint goes to the even code: upward at 0.75, 1.75, 3.5, downward at
+// 0.25, 1.25, 2.5, 5.
+__device__ __forceinline__ uint32_t e2m1_rne(float y, float s) {
+  const float a = __builtin_fabsf(y);
+  uint32_t c = (a > 0.25f * s) + (a >= 0.75f * s) + (a > 1.25f * s) + (a >= 1.75f * s) +
+               (a > 2.5f * s) + (a >= 3.5f * s) + (a > 5.0f * s);
+  return c | ((as_u32(y) >> 31) << 3);
+}
+
+__device__ __forceinline__ float e2m1_val(uint32_t c) {
+  // 0, .5, 1, 1.5, 2, 3, 4, 6 as (1 + m/2) * 2^(e-1), subnormal at e = 0
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  float v = (e == 0) ? 0.5f * (float)m : (1.0f + 0.5f * (float)m) * (float)(1u << (e - 1));
+  return (c & 8u) ? -v : v;
+}
+
+// Sum over all 64 lanes; every lane receives the same bits (each butterfly
+// step adds the same two operands in both lanes of a pair).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// fp4 round trip of VEC consecutive bf16 values held by each lane, 16 / VEC
+// neighbouring lanes forming one block of 16. `y` holds the bf16 values as
+// f32. Returns through references: the packed codes of this lane (VEC / 2
+// bytes, element 2k in the low nibble), the block's scale byte, and the bf16
+// bits of the dequantised values.
+template <int VEC>
+__device__ __forceinline__ void fp4_block(const float (&y)[VEC], uint32_t &packed, uint32_t &scale_code,
+                                          uint32_t (&deq)[VEC]) {
+  static_assert(VEC >= 2 && VEC <= 8 && 16 % VEC == 0, "VEC must divide 16 and fit 32 code bits");
+  float amax = 0.0f;
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) amax = __builtin_fmaxf(amax, __builtin_fabsf(y[v]));
+#pragma unroll
+  for (int o = 1; o < 16 / VEC; o <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, o, kWave));
+  const float a = __builtin_fmaxf(amax, kAmaxFloor);
+  const float q = a / 6.0f;  // IEEE division (HIP's default for '/')
+  scale_code = e4m3fn_rne(q);
+  const float s = e4m3fn_val(scale_code);
+  packed = 0;
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    const uint32_t c = e2m1_rne(y[v], s);
+    packed |= c << (4 * v);
+    deq[v] = as_u32(e2m1_val(c) * s) >> 16;  // exact: at most 6 significant bits
+  }
+}
+
+}  // namespace kvc

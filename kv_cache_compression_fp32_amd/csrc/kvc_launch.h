@@ -1,0 +1,79 @@
+// Internal launchers of libkvc.so's kernels. Host code only; not part of the
+// C ABI. Each launcher enqueues on `stream` and returns the hipError_t of the
+// launch. Shapes are checked by the C-ABI layer before any launcher is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+// C_h[m][n] = sum_k A[m][k] * B_h[n][k] for the two halves h = 0, 1 of the
+// output columns (kv with wkv, score with wgate), f32 in and out, fp32 MFMA.
+// The K range is cut into `splits` equal parts; split s writes its partial
+// sums at C_h + s * c_split_stride.
+struct GemmArgs {
+  const float *a;       // [m][k], row stride lda
+  const float *b0, *b1; // [n_half][k] each, row stride ldb
+  float *c0, *c1;       // [m][n_half] each, row stride ldc
+  int64_t lda, ldb, ldc;
+  int64_t m, n_half, k;
+  int32_t splits;
+  int64_t c_split_stride;
+};
+
+enum class GemmShape { kPrefill, kDecode };
+// Rows/columns of one workgroup's output tile for a shape.
+int gemm_tile_m(GemmShape s);
+int gemm_tile_n(GemmShape s);
+hipError_t launch_gemm(const GemmArgs &g, GemmShape shape, hipStream_t stream);
+
+// Pools `groups` entries of each batch row from kv/score planes holding a
+// sequence of token rows (see the pool kernels for the candidate layout).
+struct PoolArgs {
+  const float *kv, *sc;       // planes: row t of batch b at b * batch_stride + t * row_stride
+  int64_t row_stride, batch_stride;
+  int64_t batch, groups;
+  int64_t first_entry;        // entry index of output 0 inside the sequence
+  int32_t entries_per_wave;
+  const float *ape;           // [ratio][row_stride] bias added to score rows, or null
+  const float *norm_w;        // [head_dim] or null
+  float eps;
+  uint16_t *latent;
+  float *pooled;
+  uint8_t *codes, *scales;
+  uint16_t *deq;
+  int64_t out_batch_stride;   // entries per batch row in the outputs
+  float *shift_kv, *shift_sc; // ratio 4: move the last block's rows to the previous rows, or null
+};
+hipError_t launch_pool(const PoolArgs &p, int ratio, int head_dim, hipStream_t stream);
+
+// Writes the carry of a prefill into the state planes (ratio 4: last complete
+// block or padding, then the trailing tokens; other ratios: trailing tokens).
+struct StateStoreArgs {
+  const float *kv, *sc;  // projection planes [batch][seqlen][proj]
+  const float *ape;      // [ratio][proj] or null
+  float *kv_state, *sc_state;
+  int64_t batch, seqlen, proj, state_rows;
+  int32_t ratio, overlap;
+};
+hipError_t launch_state_store(const StateStoreArgs &s, hipStream_t stream);
+
+// Decode: sums the split partial projections of one token per batch row, adds
+// the bias row of the slot and writes the state row; optionally resets the
+// previous-block rows (ratio 4 at position 0).
+struct IngestArgs {
+  const float *part;      // [splits][2][batch][proj]
+  int32_t splits;
+  const float *ape;       // [ratio][proj] or null
+  float *kv_state, *sc_state;
+  int64_t batch, proj, state_rows;
+  int32_t slot, state_row, ratio, reset_prev;
+};
+hipError_t launch_decode_ingest(const IngestArgs &g, hipStream_t stream);
+
+// Standalone fp4 round trip of bf16 rows.
+hipError_t launch_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *codes,
+                            uint8_t *scales, uint16_t *out, hipStream_t stream);
+
+}  // namespace kvc

@@ -1,0 +1,491 @@
+// Fused pooling kernels of the compressor (gfx950): positional bias, the
+// candidate window, per-feature softmax pooling, bf16 rounding, RMSNorm and
+// the fp4 round trip of each compressed entry, plus the state hand-off kernels
+// and the standalone fp4 quantiser.
+//
+// Pooling: "DeepSeek V4.1 . Pool token pairs", pooling formula and Compressor
+// listing (forward). Overlap at ratio 4: "Compressed Sparse Attention . ratio
+// m = 4", Why one output uses eight candidates. Precision: "Module compress",
+// Precision paragraph. fp4: "Module compress", Functions,
+// fp4_quant_e4m3_inplace / to_e2m1_rne.
+//
+// Memory-bound work: every kernel streams f32 projection rows with 16-byte
+// (or 8-byte) coalesced loads, one wavefront per 64 x VEC features, and keeps
+// all per-entry arithmetic in registers.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kvc_device.h"
+#include "kvc_launch.h"
+
+namespace kvc {
+namespace {
+
+// Round-robin dispatch puts consecutive workgroups on different XCDs; remap
+// so that each XCD works on one contiguous range of the sequence, keeping
+// neighbouring entries (which share a block of rows at ratio 4) in one L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t id, uint32_t n) {
+  const uint32_t q = n / 8, r = n % 8, x = id % 8, local = id / 8;
+  return (x < r) ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_vec(const float *p, float (&d)[VEC]) {
+  if constexpr (VEC % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < VEC / 4; ++q) {
+      const float4 t = *reinterpret_cast<const float4 *>(p + 4 * q);
+      d[4 * q] = t.x; d[4 * q + 1] = t.y; d[4 * q + 2] = t.z; d[4 * q + 3] = t.w;
+    }
+  } else {
+    static_assert(VEC == 2, "VEC must be 2 or a multiple of 4");
+    const float2 t = *reinterpret_cast<const float2 *>(p);
+    d[0] = t.x; d[1] = t.y;
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void store_vec(float *p, const float (&d)[VEC]) {
+  if constexpr (VEC % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < VEC / 4; ++q)
+      *reinterpret_cast<float4 *>(p + 4 * q) = make_float4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
+  } else {
+    *reinterpret_cast<float2 *>(p) = make_float2(d[0], d[1]);
+  }
+}
+
+// VEC bf16 patterns (low 16 bits of each word) as one store
+template <int VEC>
+__device__ __forceinline__ void store_bf16(uint16_t *p, const uint32_t (&b)[VEC]) {
+  if constexpr (VEC == 8) {
+    *reinterpret_cast<uint4 *>(p) = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16),
+                                               b[4] | (b[5] << 16), b[6] | (b[7] << 16));
+  } else if constexpr (VEC == 4) {
+    *reinterpret_cast<uint2 *>(p) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+  } else {
+    static_assert(VEC == 2, "VEC must be 2, 4 or 8");
+    *reinterpret_cast<uint32_t *>(p) = b[0] | (b[1] << 16);
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void store_codes(uint8_t *p, uint32_t packed) {
+  if constexpr (VEC == 8) *reinterpret_cast<uint32_t *>(p) = packed;
+  else if constexpr (VEC == 4) *reinterpret_cast<uint16_t *>(p) = (uint16_t)packed;
+  else *p = (uint8_t)packed;
+}
+
+// Softmax-weighted sum over NC candidates for each of VEC features, f32.
+// Candidates with logit -inf get weight exactly 0 (exp2(-inf) = 0).
+template <int NC, int VEC>
+__device__ __forceinline__ void softmax_pool(const float (&k)[NC][VEC], const float (&s)[NC][VEC],
+                                             float (&out)[VEC]) {
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    float m = s[0][v];
+#pragma unroll
+    for (int i = 1; i < NC; ++i) m = __builtin_fmaxf(m, s[i][v]);
+    float den = 0.0f, num = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const float e = __builtin_amdgcn_exp2f((s[i][v] - m) * kLog2e);
+      den += e;
+      num = __builtin_fmaf(e, k[i][v], num);
+    }
+    out[v] = num / den;
+  }
+}
+
+// Per-entry epilogue of one wavefront holding VEC = HD / 64 pooled features
+// per lane: optional f32 store, bf16 round, RMSNorm over the entry (wave
+// reduction), bf16 latent, fp4 codes / scales / dequantised values.
+template <int HD, int VEC>
+__device__ __forceinline__ void finish_entry(const float (&p)[VEC], const PoolArgs &a, int64_t out_row,
+                                             int lane) {
+  const int f0 = lane * VEC;
+  if (a.pooled) store_vec<VEC>(a.pooled + out_row * HD + f0, p);
+  float u[VEC];
+  float ss = 0.0f;
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    u[v] = bf16_val(bf16_rne(p[v]));
+    ss = __builtin_fmaf(u[v], u[v], ss);
+  }
+  ss = wave_sum(ss);
+  const float r = __builtin_amdgcn_rsqf(ss * (1.0f / HD) + a.eps);
+  float y[VEC];
+  uint32_t yb[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    float t = u[v] * r;
+    if (a.norm_w) t *= a.norm_w[f0 + v];
+    yb[v] = bf16_rne(t);
+    y[v] = bf16_val(yb[v]);
+  }
+  if (a.latent) store_bf16<VEC>(a.latent + out_row * HD + f0, yb);
+  if (a.codes || a.scales || a.deq) {
+    uint32_t packed, scode, deq[VEC];
+    fp4_block<VEC>(y, packed, scode, deq);
+    if (a.codes) store_codes<VEC>(a.codes + out_row * (HD / 2) + f0 / 2, packed);
+    if (a.scales && (f0 % 16) == 0) a.scales[out_row * (HD / 16) + f0 / 16] = (uint8_t)scode;
+    if (a.deq) store_bf16<VEC>(a.deq + out_row * HD + f0, deq);
+  }
+}
+
+// Small groups (ratio 2, ratio 4 overlapped). One wavefront walks a run of
+// consecutive entries of one batch row; lane l owns features [l*VEC, l*VEC+VEC).
+// Ratio 4: entry j pools rows 4(j-1)..4j-1 of branch B (columns [HD, 2HD))
+// then rows 4j..4j+3 of branch A (columns [0, HD)); branch B of the current
+// block stays in registers for the next entry. Entry 0's previous branch is
+// kv 0 / score -inf.
+template <int HD, int R, bool OV>
+__global__ __launch_bounds__(256) void pool_small_kernel(PoolArgs a) {
+  constexpr int VEC = HD / kWave;
+  constexpr int NC = OV ? 2 * R : R;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
+  const int64_t runs = (a.groups + a.entries_per_wave - 1) / a.entries_per_wave;
+  const int64_t b = wave / runs;
+  if (b >= a.batch) return;
+  const int64_t run = wave - b * runs;
+  const int64_t e_begin = run * a.entries_per_wave;
+  const int64_t e_end = min(e_begin + (int64_t)a.entries_per_wave, a.groups);
+  const float *KV = a.kv + b * a.batch_stride;
+  const float *SC = a.sc + b * a.batch_stride;
+  const int f0 = lane * VEC;
+
+  float prev_k[R][VEC], prev_s[R][VEC];  // previous block, branch B (OV)
+  float cur_k[R][VEC], cur_s[R][VEC];    // current block, branch A (or the only branch)
+  float nb_k[R][VEC], nb_s[R][VEC];      // current block, branch B (OV)
+
+  if constexpr (OV) {
+    const int64_t j = a.first_entry + e_begin;
+    if (j == 0) {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) { prev_k[i][v] = 0.0f; prev_s[i][v] = -INFINITY; }
+    } else {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int64_t row = (int64_t)R * (j - 1) + i;
+        load_vec<VEC>(KV + row * a.row_stride + HD + f0, prev_k[i]);
+        load_vec<VEC>(SC + row * a.row_stride + HD + f0, prev_s[i]);
+        if (a.ape) {
+          float bias[VEC];
+          load_vec<VEC>(a.ape + (int64_t)i * a.row_stride + HD + f0, bias);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) prev_s[i][v] += bias[v];
+        }
+      }
+    }
+  }
+
+  for (int64_t e = e_begin; e < e_end; ++e) {
+    const int64_t j = a.first_entry + e;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int64_t row = (int64_t)R * j + i;
+      load_vec<VEC>(KV + row * a.row_stride + f0, cur_k[i]);
+      load_vec<VEC>(SC + row * a.row_stride + f0, cur_s[i]);
+      if constexpr (OV) {
+        load_vec<VEC>(KV + row * a.row_stride + HD + f0, nb_k[i]);
+        load_vec<VEC>(SC + row * a.row_stride + HD + f0, nb_s[i]);
+      }
+    }
+    if (a.ape) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        float bias[VEC];
+        load_vec<VEC>(a.ape + (int64_t)i * a.row_stride + f0, bias);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) cur_s[i][v] += bias[v];
+        if constexpr (OV) {
+          load_vec<VEC>(a.ape + (int64_t)i * a.row_stride + HD + f0, bias);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) nb_s[i][v] += bias[v];
+        }
+      }
+    }
+    float ck[NC][VEC], cs[NC][VEC];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        if constexpr (OV) {
+          ck[i][v] = prev_k[i][v]; cs[i][v] = prev_s[i][v];
+          ck[R + i][v] = cur_k[i][v]; cs[R + i][v] = cur_s[i][v];
+        } else {
+          ck[i][v] = cur_k[i][v]; cs[i][v] = cur_s[i][v];
+        }
+      }
+    float p[VEC];
+    softmax_pool<NC, VEC>(ck, cs, p);
+    finish_entry<HD, VEC>(p, a, b * a.out_batch_stride + e, lane);
+    if constexpr (OV) {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) { prev_k[i][v] = nb_k[i][v]; prev_s[i][v] = nb_s[i][v]; }
+    }
+  }
+
+  if constexpr (OV) {
+    // decode: the block just pooled becomes the previous block. This lane
+    // only overwrites the features it alone has read.
+    if (a.shift_kv && e_end > e_begin) {
+      float *SK = a.shift_kv + b * a.batch_stride;
+      float *SS = a.shift_sc + b * a.batch_stride;
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        store_vec<VEC>(SK + (int64_t)i * a.row_stride + f0, cur_k[i]);
+        store_vec<VEC>(SS + (int64_t)i * a.row_stride + f0, cur_s[i]);
+        store_vec<VEC>(SK + (int64_t)i * a.row_stride + HD + f0, nb_k[i]);
+        store_vec<VEC>(SS + (int64_t)i * a.row_stride + HD + f0, nb_s[i]);
+      }
+    }
+  }
+}
+
+// Long groups (ratio 128). One workgroup of 512 threads per entry: thread t
+// owns 4 features (fg = t % (HD/4)) and every RL-th row of the group
+// (rl = t / (HD/4)), keeping a running max / sum / weighted sum per feature
+// over chunks of CH rows. The RL partial states are merged in LDS by the
+// first wavefront, which then runs the per-entry epilogue.
+template <int HD, int R>
+__global__ __launch_bounds__(512) void pool_long_kernel(PoolArgs a) {
+  constexpr int FG = HD / 4;        // feature groups of 4
+  constexpr int RL = 512 / FG;      // row lanes
+  constexpr int ROWS = R / RL;      // rows per row lane
+  constexpr int CH = 8;             // rows per chunk
+  static_assert(ROWS % CH == 0, "rows per row lane must be a multiple of the chunk");
+  constexpr int VEC = HD / kWave;   // features per lane in the epilogue
+  __shared__ float s_m[RL][HD], s_l[RL][HD], s_acc[RL][HD];
+
+  const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t b = id / a.groups;
+  const int64_t e = id - b * a.groups;
+  const int64_t j = a.first_entry + e;
+  const int t = threadIdx.x;
+  const int fg = t % FG, rl = t / FG;
+  const float *KV = a.kv + b * a.batch_stride + (int64_t)R * j * a.row_stride + 4 * fg;
+  const float *SC = a.sc + b * a.batch_stride + (int64_t)R * j * a.row_stride + 4 * fg;
+
+  float m[4], l[4], acc[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) { m[v] = -INFINITY; l[v] = 0.0f; acc[v] = 0.0f; }
+  for (int c = 0; c < ROWS / CH; ++c) {
+    float k[CH][4], s[CH][4];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int row = (c * CH + i) * RL + rl;
+      load_vec<4>(KV + (int64_t)row * a.row_stride, k[i]);
+      load_vec<4>(SC + (int64_t)row * a.row_stride, s[i]);
+    }
+    if (a.ape) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int row = (c * CH + i) * RL + rl;
+        float bias[4];
+        load_vec<4>(a.ape + (int64_t)row * a.row_stride + 4 * fg, bias);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s[i][v] += bias[v];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float cm = m[v];
+#pragma unroll
+      for (int i = 0; i < CH; ++i) cm = __builtin_fmaxf(cm, s[i][v]);
+      const float scale = __builtin_amdgcn_exp2f((m[v] - cm) * kLog2e);  // m = -inf -> 0
+      float sl = 0.0f, sa = 0.0f;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const float ex = __builtin_amdgcn_exp2f((s[i][v] - cm) * kLog2e);
+        sl += ex;
+        sa = __builtin_fmaf(ex, k[i][v], sa);
+      }
+      l[v] = __builtin_fmaf(l[v], scale, sl);
+      acc[v] = __builtin_fmaf(acc[v], scale, sa);
+      m[v] = cm;
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    s_m[rl][4 * fg + v] = m[v];
+    s_l[rl][4 * fg + v] = l[v];
+    s_acc[rl][4 * fg + v] = acc[v];
+  }
+  __syncthreads();
+  if (t >= kWave) return;
+  const int lane = t;
+  float p[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    const int f = lane * VEC + v;
+    float mm = s_m[0][f];
+#pragma unroll
+    for (int r = 1; r < RL; ++r) mm = __builtin_fmaxf(mm, s_m[r][f]);
+    float den = 0.0f, num = 0.0f;
+#pragma unroll
+    for (int r = 0; r < RL; ++r) {
+      const float w = __builtin_amdgcn_exp2f((s_m[r][f] - mm) * kLog2e);
+      den = __builtin_fmaf(s_l[r][f], w, den);
+      num = __builtin_fmaf(s_acc[r][f], w, num);
+    }
+    p[v] = num / den;
+  }
+  finish_entry<HD, VEC>(p, a, b * a.out_batch_stride + e, lane);
+}
+
+__global__ __launch_bounds__(256) void state_store_kernel(StateStoreArgs s) {
+  const int64_t c4 = s.proj / 4;
+  const int64_t total = s.batch * s.state_rows * c4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int64_t c = (idx % c4) * 4;
+  const int64_t row = (idx / c4) % s.state_rows;
+  const int64_t b = idx / (c4 * s.state_rows);
+  const int64_t n = s.seqlen / s.ratio, rem = s.seqlen - n * s.ratio;
+  int64_t tok = -1;  // source token, or -1 for padding
+  if (s.overlap) {
+    if (row < s.ratio) {
+      if (n > 0) tok = (n - 1) * s.ratio + row;
+    } else {
+      if (row - s.ratio >= rem) return;  // not part of the carry
+      tok = n * s.ratio + (row - s.ratio);
+    }
+  } else {
+    if (row >= rem) return;
+    tok = n * s.ratio + row;
+  }
+  float4 k, g;
+  if (tok < 0) {
+    k = make_float4(0.f, 0.f, 0.f, 0.f);
+    g = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  } else {
+    const int64_t src = (b * s.seqlen + tok) * s.proj + c;
+    k = *reinterpret_cast<const float4 *>(s.kv + src);
+    g = *reinterpret_cast<const float4 *>(s.sc + src);
+    if (s.ape) {
+      const float4 bias = *reinterpret_cast<const float4 *>(s.ape + (tok % s.ratio) * s.proj + c);
+      g.x += bias.x; g.y += bias.y; g.z += bias.z; g.w += bias.w;
+    }
+  }
+  const int64_t dst = (b * s.state_rows + row) * s.proj + c;
+  *reinterpret_cast<float4 *>(s.kv_state + dst) = k;
+  *reinterpret_cast<float4 *>(s.sc_state + dst) = g;
+}
+
+__global__ __launch_bounds__(256) void decode_ingest_kernel(IngestArgs g) {
+  const int64_t c4 = g.proj / 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= g.batch * c4) return;
+  const int64_t b = idx / c4, c = (idx - b * c4) * 4;
+  const int64_t plane = g.batch * g.proj;
+  float4 k = make_float4(0.f, 0.f, 0.f, 0.f), s = k;
+  for (int sp = 0; sp < g.splits; ++sp) {  // fixed order: deterministic sums
+    const float4 pk = *reinterpret_cast<const float4 *>(g.part + (2 * sp) * plane + b * g.proj + c);
+    const float4 ps = *reinterpret_cast<const float4 *>(g.part + (2 * sp + 1) * plane + b * g.proj + c);
+    if (sp == 0) { k = pk; s = ps; }
+    else {
+      k.x += pk.x; k.y += pk.y; k.z += pk.z; k.w += pk.w;
+      s.x += ps.x; s.y += ps.y; s.z += ps.z; s.w += ps.w;
+    }
+  }
+  if (g.ape) {
+    const float4 bias = *reinterpret_cast<const float4 *>(g.ape + (int64_t)g.slot * g.proj + c);
+    s.x += bias.x; s.y += bias.y; s.z += bias.z; s.w += bias.w;
+  }
+  float *KS = g.kv_state + b * g.state_rows * g.proj;
+  float *SS = g.sc_state + b * g.state_rows * g.proj;
+  *reinterpret_cast<float4 *>(KS + (int64_t)g.state_row * g.proj + c) = k;
+  *reinterpret_cast<float4 *>(SS + (int64_t)g.state_row * g.proj + c) = s;
+  if (g.reset_prev) {
+    for (int i = 0; i < g.ratio; ++i) {
+      *reinterpret_cast<float4 *>(KS + (int64_t)i * g.proj + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4 *>(SS + (int64_t)i * g.proj + c) =
+          make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+  }
+}
+
+// Standalone fp4 round trip: each thread owns 8 consecutive values (16 bytes),
+// two neighbouring lanes one block of 16. The value count is a multiple of 16,
+// so both lanes of a block are always in range together.
+__global__ __launch_bounds__(256) void fp4_quant_kernel(const uint16_t *in, int64_t n8, uint8_t *codes,
+                                                        uint8_t *scales, uint16_t *out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const uint4 raw = *reinterpret_cast<const uint4 *>(in + 8 * i);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float y[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    y[2 * q] = bf16_val(w[q] & 0xffffu);
+    y[2 * q + 1] = bf16_val(w[q] >> 16);
+  }
+  uint32_t packed, scode, deq[8];
+  fp4_block<8>(y, packed, scode, deq);
+  if (codes) *reinterpret_cast<uint32_t *>(codes + 4 * i) = packed;
+  if (scales && (i & 1) == 0) scales[i / 2] = (uint8_t)scode;
+  if (out) store_bf16<8>(out + 8 * i, deq);
+}
+
+template <int HD, int R, bool OV>
+hipError_t launch_small(const PoolArgs &p, hipStream_t stream) {
+  const int64_t runs = (p.groups + p.entries_per_wave - 1) / p.entries_per_wave;
+  const int64_t waves = p.batch * runs;
+  const int64_t blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL((pool_small_kernel<HD, R, OV>), dim3((uint32_t)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int HD>
+hipError_t launch_long(const PoolArgs &p, hipStream_t stream) {
+  const int64_t blocks = p.batch * p.groups;
+  hipLaunchKernelGGL((pool_long_kernel<HD, 128>), dim3((uint32_t)blocks), dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pool(const PoolArgs &p, int ratio, int head_dim, hipStream_t stream) {
+  if (p.batch <= 0 || p.groups <= 0) return hipSuccess;
+  switch (ratio * 10000 + head_dim) {
+    case 2 * 10000 + 512: return launch_small<512, 2, false>(p, stream);
+    case 2 * 10000 + 128: return launch_small<128, 2, false>(p, stream);
+    case 4 * 10000 + 512: return launch_small<512, 4, true>(p, stream);
+    case 4 * 10000 + 128: return launch_small<128, 4, true>(p, stream);
+    case 128 * 10000 + 512: return launch_long<512>(p, stream);
+    case 128 * 10000 + 128: return launch_long<128>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_state_store(const StateStoreArgs &s, hipStream_t stream) {
+  const int64_t total = s.batch * s.state_rows * (s.proj / 4);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(state_store_kernel, dim3((uint32_t)((total + 255) / 256)), dim3(256), 0, stream, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_ingest(const IngestArgs &g, hipStream_t stream) {
+  const int64_t total = g.batch * (g.proj / 4);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_ingest_kernel, dim3((uint32_t)((total + 255) / 256)), dim3(256), 0, stream, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *codes, uint8_t *scales,
+                            uint16_t *out, hipStream_t stream) {
+  const int64_t n8 = rows * width / 8;
+  if (n8 == 0) return hipSuccess;
+  hipLaunchKernelGGL(fp4_quant_kernel, dim3((uint32_t)((n8 + 255) / 256)), dim3(256), 0, stream, in, n8, codes,
+                     scales, out);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,250 @@
+"""Python binding of libkvc.so (include/kvc.h).
+
+Argument marshalling only: the functions below take torch tensors, check their
+device, dtype and contiguity, and pass raw device pointers, sizes and the
+current HIP stream to the C entry points of the same names. Every step of the
+compressor runs in the library's HIP kernels; nothing here computes.
+
+The library is loaded on first use. torch is imported first so that libkvc.so
+binds to the HIP runtime torch has already loaded (both carry the soname
+libamdhip64.so.7) and device pointers and streams are shared.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvc.so")
+
+KVC_OK, KVC_EINVAL, KVC_EUNSUPPORTED, KVC_ESPACE, KVC_EHIP = 0, -1, -2, -3, -4
+
+_lib = None
+
+
+class KvcError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("ratio", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dim", ctypes.c_int64), ("eps", ctypes.c_float)]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("wkv", ctypes.c_void_p), ("wgate", ctypes.c_void_p),
+                ("ape", ctypes.c_void_p), ("norm_w", ctypes.c_void_p)]
+
+
+class _Outputs(ctypes.Structure):
+    _fields_ = [("latent", ctypes.c_void_p), ("pooled", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("dequant", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SIGNATURES = {
+    "kvc_proj_width": (_I64, [ctypes.POINTER(_Config)]),
+    "kvc_state_rows": (_I64, [ctypes.POINTER(_Config)]),
+    "kvc_prefill_workspace_floats": (_I64, [ctypes.POINTER(_Config), _I64, _I64]),
+    "kvc_decode_workspace_floats": (_I64, [ctypes.POINTER(_Config), _I64]),
+    "compressor_prefill": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), _P, _I64, _I64,
+                                          _P, _I64, _P, _P, _I64, ctypes.POINTER(_Outputs),
+                                          ctypes.POINTER(_I64), _P]),
+    "compressor_decode_step": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), _P, _I64, _I64,
+                                              _P, _I64, _P, _P, _I64, ctypes.POINTER(_Outputs),
+                                              ctypes.POINTER(ctypes.c_int32), _P]),
+    "latent_fp4_quant": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
+    "kvc_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "kvc_version": (ctypes.c_char_p, []),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkvc.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m kv_cache_compression_fp32_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().kvc_strerror(code).decode()
+
+
+def version() -> str:
+    return lib().kvc_version().decode()
+
+
+# ----------------------------------------------------------------- config
+@dataclass(frozen=True)
+class Config:
+    ratio: int
+    head_dim: int
+    dim: int = 0
+    eps: float = 1e-6
+
+    def c(self) -> _Config:
+        return _Config(self.ratio, self.head_dim, self.dim, self.eps)
+
+
+def kvc_proj_width(cfg: Config) -> int:
+    return _check(lib().kvc_proj_width(ctypes.byref(cfg.c())), "kvc_proj_width")
+
+
+def kvc_state_rows(cfg: Config) -> int:
+    return _check(lib().kvc_state_rows(ctypes.byref(cfg.c())), "kvc_state_rows")
+
+
+def kvc_prefill_workspace_floats(cfg: Config, batch: int, seqlen: int) -> int:
+    return _check(lib().kvc_prefill_workspace_floats(ctypes.byref(cfg.c()), batch, seqlen),
+                  "kvc_prefill_workspace_floats")
+
+
+def kvc_decode_workspace_floats(cfg: Config, batch: int) -> int:
+    return _check(lib().kvc_decode_workspace_floats(ctypes.byref(cfg.c()), batch),
+                  "kvc_decode_workspace_floats")
+
+
+def _check(rc: int, what: str) -> int:
+    if rc < 0:
+        raise KvcError(rc, what)
+    return rc
+
+
+# ----------------------------------------------------------------- marshalling
+def _ptr(t, dtype=None, name="tensor") -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream or None
+
+
+@dataclass
+class Weights:
+    wkv: torch.Tensor | None = None
+    wgate: torch.Tensor | None = None
+    ape: torch.Tensor | None = None
+    norm_w: torch.Tensor | None = None
+
+    def c(self) -> _Weights:
+        return _Weights(_ptr(self.wkv, torch.float32, "wkv"), _ptr(self.wgate, torch.float32, "wgate"),
+                        _ptr(self.ape, torch.float32, "ape"), _ptr(self.norm_w, torch.float32, "norm_w"))
+
+
+@dataclass
+class Outputs:
+    latent: torch.Tensor | None = None   # bf16 (or int16 bit patterns)
+    pooled: torch.Tensor | None = None   # float32
+    codes: torch.Tensor | None = None    # uint8
+    scales: torch.Tensor | None = None   # uint8
+    dequant: torch.Tensor | None = None  # bf16
+
+    def c(self) -> _Outputs:
+        def bf(t, n):
+            if t is None:
+                return None
+            if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+                raise TypeError(f"{n} must be bf16")
+            return _ptr(t, None, n)
+        return _Outputs(bf(self.latent, "latent"), _ptr(self.pooled, torch.float32, "pooled"),
+                        _ptr(self.codes, torch.uint8, "codes"), _ptr(self.scales, torch.uint8, "scales"),
+                        bf(self.dequant, "dequant"))
+
+
+def compressor_prefill(cfg: Config, w: Weights, x: torch.Tensor | None, batch: int, seqlen: int,
+                       workspace: torch.Tensor, kv_state: torch.Tensor | None = None,
+                       score_state: torch.Tensor | None = None, out: Outputs | None = None,
+                       stream=None) -> int:
+    """Enqueue a prefill; returns the number of groups (seqlen // ratio)."""
+    n = ctypes.c_int64(0)
+    state_batch = kv_state.shape[0] if kv_state is not None else 0
+    rc = lib().compressor_prefill(
+        ctypes.byref(cfg.c()), ctypes.byref(w.c()), _ptr(x, torch.float32, "x"), batch, seqlen,
+        _ptr(workspace, torch.float32, "workspace"), workspace.numel(),
+        _ptr(kv_state, torch.float32, "kv_state"), _ptr(score_state, torch.float32, "score_state"),
+        state_batch, ctypes.byref(out.c()) if out is not None else None, ctypes.byref(n), _stream(stream))
+    _check(rc, "compressor_prefill")
+    return n.value
+
+
+def compressor_decode_step(cfg: Config, w: Weights, x: torch.Tensor | None, batch: int, start_pos: int,
+                           workspace: torch.Tensor, kv_state: torch.Tensor, score_state: torch.Tensor,
+                           out: Outputs | None = None, stream=None) -> bool:
+    """Enqueue one decode step; returns True if entries were written."""
+    e = ctypes.c_int32(0)
+    rc = lib().compressor_decode_step(
+        ctypes.byref(cfg.c()), ctypes.byref(w.c()), _ptr(x, torch.float32, "x"), batch, start_pos,
+        _ptr(workspace, torch.float32, "workspace"), workspace.numel(),
+        _ptr(kv_state, torch.float32, "kv_state"), _ptr(score_state, torch.float32, "score_state"),
+        kv_state.shape[0], ctypes.byref(out.c()) if out is not None else None, ctypes.byref(e),
+        _stream(stream))
+    _check(rc, "compressor_decode_step")
+    return bool(e.value)
+
+
+def latent_fp4_quant(inp: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                     out: torch.Tensor | None = None, stream=None) -> None:
+    """Enqueue the fp4 round trip of [rows, width] bf16 values."""
+    if inp.dim() != 2:
+        raise ValueError("inp must be [rows, width]")
+    if inp.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("inp must be bf16")
+    if out is not None and out.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("out must be bf16")
+    rows, width = inp.shape
+    rc = lib().latent_fp4_quant(_ptr(inp, None, "inp"), rows, width, _ptr(codes, torch.uint8, "codes"),
+                                _ptr(scales, torch.uint8, "scales"), _ptr(out, None, "out"), _stream(stream))
+    _check(rc, "latent_fp4_quant")
+
+
+# ----------------------------------------------------------------- convenience
+def new_state(cfg: Config, batch: int, device="cuda") -> tuple[torch.Tensor, torch.Tensor]:
+    """kv_state / score_state planes initialised as the model does (kv 0,
+    score -inf)."""
+    rows, proj = kvc_state_rows(cfg), kvc_proj_width(cfg)
+    kv = torch.zeros((batch, rows, proj), dtype=torch.float32, device=device)
+    sc = torch.full((batch, rows, proj), float("-inf"), dtype=torch.float32, device=device)
+    return kv, sc
+
+
+def new_outputs(cfg: Config, batch: int, groups: int, latent=True, pooled=False, fp4=False,
+                dequant=False, device="cuda") -> Outputs:
+    hd = cfg.head_dim
+    o = Outputs()
+    if latent:
+        o.latent = torch.empty((batch, groups, hd), dtype=torch.bfloat16, device=device)
+    if pooled:
+        o.pooled = torch.empty((batch, groups, hd), dtype=torch.float32, device=device)
+    if fp4:
+        o.codes = torch.empty((batch, groups, hd // 2), dtype=torch.uint8, device=device)
+        o.scales = torch.empty((batch, groups, hd // 16), dtype=torch.uint8, device=device)
+    if dequant:
+        o.dequant = torch.empty((batch, groups, hd), dtype=torch.bfloat16, device=device)
+    return o

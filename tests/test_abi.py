@@ -1,0 +1,137 @@
+"""The C ABI on the CPU: libkvc.so loads, exports every function include/kvc.h
+declares, and its host-side logic (sizes, argument checks) answers without
+touching a GPU. No call here enqueues work."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import kv_cache_compression_fp32_amd.kvc as kvc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \t\*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("compressor_prefill", "compressor_decode_step", "latent_fp4_quant"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kvc.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", kvc.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(line.split()[-1] for line in out.stdout.splitlines() if line.strip())
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_version_and_strerror():
+    assert "gfx950" in kvc.version()
+    for code in (0, -1, -2, -3, -4):
+        assert kvc.strerror(code)
+    assert "unknown" in kvc.strerror(-99)
+
+
+@pytest.mark.parametrize("ratio,hd,proj,rows", [(2, 512, 512, 2), (4, 512, 1024, 8), (4, 128, 256, 8),
+                                                (128, 512, 512, 128), (128, 128, 128, 128)])
+def test_sizes(ratio, hd, proj, rows):
+    cfg = kvc.Config(ratio, hd, 4096)
+    assert kvc.kvc_proj_width(cfg) == proj
+    assert kvc.kvc_state_rows(cfg) == rows
+    assert kvc.kvc_prefill_workspace_floats(cfg, 3, 100) == 2 * 3 * 100 * proj
+    ws = kvc.kvc_decode_workspace_floats(cfg, 64)
+    assert ws >= 2 * 64 * proj and ws % (2 * 64 * proj) == 0
+
+
+def test_decode_workspace_of_the_b64_ratio4_step():
+    # 64 rows, 2 x 1024 columns, k = 4096: 32 column tiles of 64, split in 16
+    cfg = kvc.Config(4, 512, 4096)
+    assert kvc.kvc_decode_workspace_floats(cfg, 64) == 16 * 2 * 64 * 1024
+
+
+@pytest.mark.parametrize("cfg,code", [
+    (kvc.Config(3, 512, 4096), kvc.KVC_EUNSUPPORTED),
+    (kvc.Config(1, 512, 4096), kvc.KVC_EUNSUPPORTED),
+    (kvc.Config(4, 256, 4096), kvc.KVC_EUNSUPPORTED),
+    (kvc.Config(4, 512, 4096, eps=-1.0), kvc.KVC_EINVAL),
+    (kvc.Config(4, 512, 4096, eps=float("nan")), kvc.KVC_EINVAL),
+])
+def test_invalid_configs(cfg, code):
+    with pytest.raises(kvc.KvcError) as err:
+        kvc.kvc_proj_width(cfg)
+    assert err.value.code == code
+
+
+def _prefill_raw(cfg, **kw):
+    lib = kvc.lib()
+    args = dict(w=None, x=None, batch=1, seqlen=8, ws=None, ws_n=0, kv=None, sc=None, sb=0, out=None)
+    args.update(kw)
+    n = ctypes.c_int64(-7)
+    w = args["w"]
+    rc = lib.compressor_prefill(ctypes.byref(cfg.c()), ctypes.byref(w) if w is not None else None,
+                                args["x"], args["batch"], args["seqlen"], args["ws"], args["ws_n"],
+                                args["kv"], args["sc"], args["sb"], args["out"], ctypes.byref(n), None)
+    return rc, n.value
+
+
+def test_prefill_argument_errors_return_before_enqueueing():
+    cfg = kvc.Config(4, 512, 4096)
+    fake = 0x100000  # never dereferenced: every case below fails its host checks
+    assert _prefill_raw(kvc.Config(3, 512, 4096))[0] == kvc.KVC_EUNSUPPORTED
+    assert _prefill_raw(cfg, batch=0)[0] == kvc.KVC_EINVAL
+    assert _prefill_raw(cfg, seqlen=-1)[0] == kvc.KVC_EINVAL
+    # projections given (x NULL) but no workspace
+    assert _prefill_raw(cfg, seqlen=8)[0] == kvc.KVC_EINVAL
+    # workspace too small
+    assert _prefill_raw(cfg, seqlen=8, ws=fake, ws_n=10)[0] == kvc.KVC_ESPACE
+    # x given without weights
+    assert _prefill_raw(cfg, x=fake, ws=fake, ws_n=1 << 30)[0] == kvc.KVC_EINVAL
+    # x given with a hidden width that is not a multiple of 32
+    w = kvc._Weights(fake, fake, None, None)
+    assert _prefill_raw(kvc.Config(4, 512, 100), x=fake, w=w, ws=fake, ws_n=1 << 30)[0] == kvc.KVC_EUNSUPPORTED
+    # misaligned pointer
+    assert _prefill_raw(cfg, x=fake + 4, w=w, ws=fake, ws_n=1 << 30)[0] == kvc.KVC_EINVAL
+    # one state plane without the other, or a state smaller than the batch
+    assert _prefill_raw(cfg, ws=fake, ws_n=1 << 30, kv=fake)[0] == kvc.KVC_EINVAL
+    assert _prefill_raw(cfg, batch=2, ws=fake, ws_n=1 << 30, kv=fake, sc=fake, sb=1)[0] == kvc.KVC_EINVAL
+
+
+def test_decode_argument_errors_return_before_enqueueing():
+    lib = kvc.lib()
+    cfg = kvc.Config(4, 512, 4096)
+    fake = 0x100000
+    e = ctypes.c_int32(-1)
+
+    def call(**kw):
+        a = dict(x=None, batch=1, pos=5, ws=fake, ws_n=1 << 30, kv=fake, sc=fake, sb=1)
+        a.update(kw)
+        return lib.compressor_decode_step(ctypes.byref(cfg.c()), None, a["x"], a["batch"], a["pos"], a["ws"],
+                                          a["ws_n"], a["kv"], a["sc"], a["sb"], None, ctypes.byref(e), None)
+    assert call(pos=-1) == kvc.KVC_EINVAL
+    assert call(kv=None) == kvc.KVC_EINVAL
+    assert call(ws=None) == kvc.KVC_EINVAL
+    assert call(ws_n=2 * 1024 - 1) == kvc.KVC_ESPACE
+    assert call(batch=2, sb=1) == kvc.KVC_EINVAL
+
+
+def test_fp4_argument_errors():
+    lib = kvc.lib()
+    fake = 0x100000
+    assert lib.latent_fp4_quant(fake, 4, 24, None, None, None, None) == kvc.KVC_EINVAL   # width % 16
+    assert lib.latent_fp4_quant(fake, -1, 32, None, None, None, None) == kvc.KVC_EINVAL
+    assert lib.latent_fp4_quant(None, 4, 32, None, None, None, None) == kvc.KVC_EINVAL
+    # partially overlapping input and output
+    assert lib.latent_fp4_quant(fake, 4, 32, None, None, fake + 64, None) == kvc.KVC_EINVAL
+    # nothing to do: no launch
+    assert lib.latent_fp4_quant(None, 0, 32, None, None, None, None) == kvc.KVC_OK

@@ -1,0 +1,173 @@
+"""GPU parity at the five workload sizes, in the launch configuration the
+benchmark times. Where the oracle cannot compute everything in seconds, it
+computes sampled entries one by one from the token rows they depend on."""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_fp32_amd.kvc as kvc
+import kv_cache_compression_fp32_amd.workloads as W
+import oracle
+from gpu_util import dev, note, oracle_cfg, oracle_weights, outputs_to_host, prefill, weights
+from parity import check_fp4, check_latent, check_pooled
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kvc.lib()
+
+
+def _cfg(wl, comp):
+    return kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps)
+
+
+def _sample_entries(groups, n=24, seed=0):
+    rng = np.random.default_rng(seed)
+    fixed = {0, 1, 2, groups // 2, groups - 2, groups - 1}
+    rand = set(rng.choice(groups, size=min(n, groups), replace=False).tolist())
+    return sorted(e for e in fixed | rand if 0 <= e < groups)
+
+
+def _oracle_entry(wl, comp, w, b, j):
+    """One entry from only the token rows it depends on: ratio 4 needs the
+    previous block too (the slice then starts at a multiple of 4, so the bias
+    rows line up), other ratios only the group itself."""
+    cfg = oracle.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps)
+    r = comp.ratio
+    if r == 4 and j > 0:
+        t0, idx = r * (j - 1), 1
+    else:
+        t0, idx = r * j, 0
+    x = W.hidden_rows(wl, b, t0, r * j + r)[None]
+    out = oracle.prefill(cfg, oracle_weights(w), oracle.State(cfg, 1), x=x, quantize=comp.quantize)
+    return {k: v[0, idx] for k, v in out.items()}
+
+
+def _check_sampled(wl, comp, w, got, entries, batch_rows):
+    ref = {}
+    for b in batch_rows:
+        for j in entries:
+            e = _oracle_entry(wl, comp, w, b, j)
+            for k, v in e.items():
+                ref.setdefault(k, []).append(v)
+    ref = {k: np.stack(v) for k, v in ref.items()}
+    sel = lambda a: np.stack([a[b, j] for b in batch_rows for j in entries])  # noqa: E731
+    check_pooled(sel(got["pooled"]), ref["pooled"])
+    check_latent(sel(got["latent"]), sel(got["pooled"]), ref["latent"], ref["pooled"], eps=wl.eps)
+    if comp.quantize:
+        check_fp4(sel(got["codes"]), sel(got["scales"]), sel(got["latent"]), ref["codes"], ref["scales"],
+                  ref["latent"], sel(got["dequant"]))
+
+
+def test_pair_pool_r2_full():
+    wl = W.WORKLOADS["pair_pool_r2"]
+    comp = wl.compressors[0]
+    note(f"{wl.name}")
+    kc, gc = W.given_projections(wl)
+    cfg = _cfg(wl, comp)
+    g = prefill(cfg, {}, wl.batch, wl.seqlen, kv=kc, sc=gc, fp4=False)
+    ref = oracle.prefill(oracle_cfg(cfg), oracle.Weights(), oracle.State(oracle_cfg(cfg), wl.batch), kv=kc,
+                         score=gc)
+    assert g["latent"].shape == (1, 32, 512)
+    check_pooled(g["pooled"], ref["pooled"])
+    check_latent(g["latent"], g["pooled"], ref["latent"], ref["pooled"], eps=wl.eps)
+
+
+def test_prefill_r4_n4096_full_oracle():
+    wl = W.WORKLOADS["prefill_r4_n4096"]
+    comp = wl.compressors[0]
+    note(f"{wl.name}")
+    w = W.weights(wl, comp)
+    x = W.hidden(wl)
+    cfg = _cfg(wl, comp)
+    g = prefill(cfg, w, wl.batch, wl.seqlen, x=x, fp4=True)
+    ref = oracle.prefill(oracle_cfg(cfg), oracle_weights(w), oracle.State(oracle_cfg(cfg), wl.batch), x=x,
+                         quantize=True)
+    assert g["n_groups"] == 1024
+    check_pooled(g["pooled"], ref["pooled"])
+    flips, total = check_latent(g["latent"], g["pooled"], ref["latent"], ref["pooled"], eps=wl.eps)
+    note(f"entries with a pooled bf16 flip: {flips} of {total}")
+    check_fp4(g["codes"], g["scales"], g["latent"], ref["codes"], ref["scales"], ref["latent"], g["dequant"])
+
+
+@pytest.mark.parametrize("seqlen", [16384, 16384 + 37])
+def test_prefill_r128_sampled(seqlen):
+    wl = W.scaled(W.WORKLOADS["prefill_r128_b2_n16384"], seqlen=seqlen)
+    comp = wl.compressors[0]
+    note(f"{wl.name} seqlen={seqlen}")
+    w = W.weights(wl, comp)
+    cfg = _cfg(wl, comp)
+    g = prefill(cfg, w, wl.batch, wl.seqlen, x_dev=dev(W.hidden(wl)), fp4=True)
+    groups = seqlen // 128
+    assert g["n_groups"] == groups
+    _check_sampled(wl, comp, w, g, _sample_entries(groups, 12), range(wl.batch))
+    # the carried tail: rows [0, seqlen mod 128) are the last tokens' projections
+    rem = seqlen % 128
+    if rem:
+        ocfg = oracle.Config(128, 512, wl.dim, wl.eps)
+        for b in range(wl.batch):
+            xt = W.hidden_rows(wl, b, groups * 128, seqlen)
+            kv = oracle.project(xt, w["wkv"])
+            sc = oracle.add_bias(oracle.project(xt, w["wgate"])[None], w["ape"], np.arange(rem), 128)[0]
+            check_pooled(g["state_kv"][b, :rem], kv, "state kv")
+            check_pooled(g["state_sc"][b, :rem], sc, "state score")
+        del ocfg
+    assert np.all(g["state_kv"][:, rem:] == 0) and np.all(np.isneginf(g["state_sc"][:, rem:]))
+
+
+def test_decode_r4_b64_s512_equals_prefill():
+    wl = W.WORKLOADS["decode_r4_b64_s512"]
+    comp = wl.compressors[0]
+    note(f"{wl.name}")
+    w = W.weights(wl, comp)
+    cfg = _cfg(wl, comp)
+    x = W.hidden(wl)
+    xd = dev(x)
+    full = prefill(cfg, w, wl.batch, wl.seqlen, x_dev=xd, fp4=True)
+    wts = weights(w)
+    ws = torch.empty(kvc.kvc_decode_workspace_floats(cfg, wl.batch), dtype=torch.float32, device="cuda")
+    state = kvc.new_state(cfg, wl.batch)
+    outs = []
+    for p in range(wl.seqlen):
+        out = kvc.new_outputs(cfg, wl.batch, 1, latent=True, pooled=True, fp4=True, dequant=True)
+        e = kvc.compressor_decode_step(cfg, wts, xd[:, p].contiguous(), wl.batch, p, ws, state[0], state[1], out)
+        assert e == (p > 0 and (p + 1) % 4 == 0)
+        if e:
+            outs.append(out)
+    torch.cuda.synchronize()
+    assert len(outs) == 128
+    hs = [outputs_to_host(o) for o in outs]
+    dec = {k: np.concatenate([h[k] for h in hs], axis=1) for k in hs[0]}
+    # decode and prefill project with different GEMM tilings: equal within
+    # the f32 tolerance, the latents within 1 bf16 ulp
+    check_pooled(dec["pooled"], full["pooled"], "decode vs prefill")
+    check_latent(dec["latent"], dec["pooled"], full["latent"], full["pooled"], eps=wl.eps)
+    # and sampled rows against the oracle
+    ocfg = oracle_cfg(cfg)
+    for b in (0, 37, 63):
+        ref = oracle.prefill(ocfg, oracle_weights(w), oracle.State(ocfg, 1), x=x[b:b + 1], quantize=True)
+        check_pooled(dec["pooled"][b:b + 1], ref["pooled"])
+        check_latent(dec["latent"][b:b + 1], dec["pooled"][b:b + 1], ref["latent"], ref["pooled"], eps=wl.eps)
+        check_fp4(dec["codes"][b], dec["scales"][b], dec["latent"][b], ref["codes"][0], ref["scales"][0],
+                  ref["latent"][0], dec["dequant"][b])
+
+
+def test_prefill_r4_n65536_fp4_idx128_sampled():
+    wl = W.WORKLOADS["prefill_r4_n65536_fp4_idx128"]
+    note(f"{wl.name}")
+    xd = dev(W.hidden(wl))
+    for comp in wl.compressors:
+        w = W.weights(wl, comp)
+        cfg = _cfg(wl, comp)
+        note(f"  compressor ratio={comp.ratio} hd={comp.head_dim} fp4={comp.quantize}")
+        g = prefill(cfg, w, wl.batch, wl.seqlen, x_dev=xd, fp4=True)
+        assert g["n_groups"] == 16384
+        _check_sampled(wl, comp, w, g, _sample_entries(16384, 40), [0])
+        if comp.quantize:
+            # every entry: the fp4 codes of the GPU's latent, bit-exact
+            check_fp4(g["codes"], g["scales"], g["latent"], gpu_dequant=g["dequant"])
+        del g

@@ -1,0 +1,278 @@
+"""GPU parity of the HIP path against the CPU oracle on seeded inputs, at sizes
+the oracle finishes in seconds that span several tiles and a ragged tail."""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_fp32_amd.kvc as kvc
+import oracle
+from gpu_util import dev, host_bf16, note, oracle_cfg, oracle_weights, prefill
+from parity import check_fp4, check_latent, check_pooled
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kvc.lib()
+
+
+def test_single_hip_runtime_is_mapped():
+    maps = open("/proc/self/maps").read()
+    paths = set(line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line)
+    assert len(paths) == 1, paths
+
+
+# ---------------------------------------------------------------- fp4 quantiser
+def _fp4_gpu(vals_bits: np.ndarray, width: int, inplace=False):
+    rows = vals_bits.size // width
+    inp = torch.from_numpy(vals_bits.view(np.int16).reshape(rows, width).copy()).cuda()
+    codes = torch.empty((rows, width // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, width // 16), dtype=torch.uint8, device="cuda")
+    out = inp if inplace else torch.empty_like(inp)
+    kvc.latent_fp4_quant(inp, codes, scales, out)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy(), host_bf16(out)
+
+
+def test_fp4_quant_every_finite_bf16_value():
+    note("fp4 every finite bf16, sorted blocks")
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    pats = pats[np.isfinite(oracle.bf16_from_bits(pats))]
+    assert pats.size % 64 == 0
+    codes, scales, deq = _fp4_gpu(pats, 64)
+    rc, rs, rd = oracle.fp4_quant_e4m3(oracle.bf16_from_bits(pats).reshape(-1, 64))
+    assert np.array_equal(codes, rc)
+    assert np.array_equal(scales, rs)
+    assert np.array_equal(deq.view(np.uint32), rd.view(np.uint32))
+
+
+@pytest.mark.parametrize("inplace", [False, True])
+def test_fp4_quant_shuffled_blocks(inplace):
+    note(f"fp4 shuffled inplace={inplace}")
+    rng = np.random.default_rng(11)
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    pats = pats[np.isfinite(oracle.bf16_from_bits(pats))]
+    pats = np.concatenate([rng.permutation(pats), np.zeros(256, dtype=np.uint16)])
+    # plus rows of latent-like values of every scale
+    lat = oracle.bf16_bits((rng.standard_normal((300, 512)) * np.exp2(rng.integers(-20, 8, (300, 1)))).astype(np.float32))
+    allp = np.concatenate([pats, lat.reshape(-1)])
+    codes, scales, deq = _fp4_gpu(allp, 512, inplace)
+    rc, rs, rd = oracle.fp4_quant_e4m3(oracle.bf16_from_bits(allp).reshape(-1, 512))
+    assert np.array_equal(codes, rc)
+    assert np.array_equal(scales, rs)
+    assert np.array_equal(deq.view(np.uint32), rd.view(np.uint32))
+
+
+def test_fp4_quant_ragged_and_empty():
+    note("fp4 ragged/empty")
+    rng = np.random.default_rng(12)
+    for rows, width in ((1, 16), (3, 48), (7, 128), (0, 512)):
+        y = oracle.bf16_bits(rng.standard_normal((rows, width)).astype(np.float32)).reshape(-1)
+        if rows == 0:
+            kvc.latent_fp4_quant(torch.empty((0, width), dtype=torch.int16, device="cuda"))
+            continue
+        codes, scales, deq = _fp4_gpu(y, width)
+        rc, rs, rd = oracle.fp4_quant_e4m3(oracle.bf16_from_bits(y).reshape(rows, width))
+        assert np.array_equal(codes, rc) and np.array_equal(scales, rs)
+        assert np.array_equal(deq, rd)
+
+
+# ---------------------------------------------------------------- pooling from given projections
+POOL_CASES = [
+    # ratio, head_dim, batch, seqlen, bias, norm weight
+    (2, 512, 1, 64, False, False),
+    (2, 128, 3, 77, True, True),
+    (4, 512, 2, 4 * 37 + 3, True, False),
+    (4, 512, 1, 4, True, True),
+    (4, 128, 3, 4 * 50 + 1, True, False),
+    (4, 512, 2, 3, True, False),         # shorter than the ratio: no entry, carry only
+    (128, 512, 2, 128 * 3 + 37, True, False),
+    (128, 128, 1, 128 * 2, True, True),
+]
+
+
+@pytest.mark.parametrize("ratio,hd,batch,seqlen,bias,normw", POOL_CASES)
+def test_pool_given_projections(ratio, hd, batch, seqlen, bias, normw):
+    note(f"pool ratio={ratio} hd={hd} batch={batch} seqlen={seqlen}")
+    rng = np.random.default_rng(ratio * 1000 + hd + seqlen)
+    cfg = kvc.Config(ratio, hd, 0)
+    proj = kvc.kvc_proj_width(cfg)
+    kv = rng.standard_normal((batch, seqlen, proj), dtype=np.float32)
+    sc = (rng.standard_normal((batch, seqlen, proj), dtype=np.float32) * np.float32(2.0))
+    w = {}
+    if bias:
+        w["ape"] = (rng.standard_normal((ratio, proj), dtype=np.float32) * np.float32(0.1))
+    if normw:
+        w["norm_w"] = rng.uniform(0.5, 1.5, hd).astype(np.float32)
+    g = prefill(cfg, w, batch, seqlen, kv=kv, sc=sc)
+    st = oracle.State(oracle_cfg(cfg), batch)
+    ref = oracle.prefill(oracle_cfg(cfg), oracle_weights(w), st, kv=kv, score=sc, quantize=True)
+    assert g["n_groups"] == seqlen // ratio
+    if ref is None:
+        assert seqlen < ratio
+    else:
+        check_pooled(g["pooled"], ref["pooled"])
+        check_latent(g["latent"], g["pooled"], ref["latent"], ref["pooled"], w.get("norm_w"), cfg.eps)
+        check_fp4(g["codes"], g["scales"], g["latent"], ref["codes"], ref["scales"], ref["latent"], g["dequant"])
+    # the carry is a copy of projection rows plus the bias: bit-exact
+    assert np.array_equal(g["state_kv"], st.kv)
+    assert np.array_equal(g["state_sc"], st.score)
+
+
+# ---------------------------------------------------------------- projection GEMM
+GEMM_CASES = [
+    # ratio, head_dim, dim, batch, seqlen
+    (4, 128, 256, 2, 300),
+    (128, 512, 512, 1, 256 + 128 + 5),
+    (2, 512, 128, 3, 61),
+    (4, 512, 4096, 1, 130),
+]
+
+
+@pytest.mark.parametrize("ratio,hd,dim,batch,seqlen", GEMM_CASES)
+def test_projection_gemm_and_full_prefill(ratio, hd, dim, batch, seqlen):
+    note(f"gemm+prefill ratio={ratio} hd={hd} dim={dim} batch={batch} seqlen={seqlen}")
+    rng = np.random.default_rng(dim + seqlen)
+    cfg = kvc.Config(ratio, hd, dim)
+    proj = kvc.kvc_proj_width(cfg)
+    x = rng.standard_normal((batch, seqlen, dim), dtype=np.float32)
+    w = {"wkv": rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.02),
+         "wgate": rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.02),
+         "ape": rng.standard_normal((ratio, proj), dtype=np.float32) * np.float32(0.1)}
+    g = prefill(cfg, w, batch, seqlen, x=x)
+    # projections: inside the worst-case bound of any f32 summation order,
+    # dim * 2^-24 * sum |x| |w|, and 1e-5 of each row's largest value
+    for name, wname in (("proj_kv", "wkv"), ("proj_sc", "wgate")):
+        ref = oracle.project(x.reshape(-1, dim), w[wname]).reshape(batch, seqlen, proj)
+        absdot = (np.abs(x.reshape(-1, dim)).astype(np.float64) @ np.abs(w[wname]).astype(np.float64).T)
+        bound = dim * 2.0 ** -24 * absdot.reshape(batch, seqlen, proj) + 1e-30
+        err = np.abs(g[name].astype(np.float64) - ref)
+        assert np.all(err <= bound), f"{name}: {np.sum(err > bound)} beyond the bound"
+        check_pooled(g[name], ref, name)
+    st = oracle.State(oracle_cfg(cfg), batch)
+    ref = oracle.prefill(oracle_cfg(cfg), oracle_weights(w), st, x=x, quantize=True)
+    check_pooled(g["pooled"], ref["pooled"])
+    check_latent(g["latent"], g["pooled"], ref["latent"], ref["pooled"])
+    check_fp4(g["codes"], g["scales"], g["latent"], ref["codes"], ref["scales"], ref["latent"], g["dequant"])
+    # the carried rows are projections (+ bias): same tolerance as the projections
+    fin = np.isfinite(st.score)
+    assert np.array_equal(np.isfinite(g["state_sc"]), fin)
+    check_pooled(np.where(fin, g["state_sc"], 0), np.where(fin, st.score, 0), "state score")
+    check_pooled(g["state_kv"], st.kv, "state kv")
+
+
+# ---------------------------------------------------------------- decode
+def _decode_gpu(cfg, w, batch, xs=None, kvs=None, scs=None, start=0, state=None, fp4=True):
+    """Run decode steps for positions start..; xs [batch, steps, dim] or the
+    projections kvs/scs [batch, steps, proj]. Returns the emitted entries
+    concatenated along the entry axis, and the final state."""
+    proj = kvc.kvc_proj_width(cfg)
+    steps = (xs if xs is not None else kvs).shape[1]
+    ws = torch.empty(kvc.kvc_decode_workspace_floats(cfg, batch), dtype=torch.float32, device="cuda")
+    if state is None:
+        state = kvc.new_state(cfg, batch)
+    xd = dev(xs) if xs is not None else None
+    kvd, scd = (dev(kvs), dev(scs)) if kvs is not None else (None, None)
+    emitted = []
+    for i in range(steps):
+        p = start + i
+        out = kvc.new_outputs(cfg, batch, 1, latent=True, pooled=True, fp4=fp4, dequant=fp4)
+        if xd is None:
+            ws[:batch * proj] = kvd[:, i].reshape(-1)
+            ws[batch * proj:2 * batch * proj] = scd[:, i].reshape(-1)
+            xi = None
+        else:
+            xi = xd[:, i].contiguous()
+        e = kvc.compressor_decode_step(cfg, w, xi, batch, p, ws, state[0], state[1], out)
+        assert e == (p > 0 and (p + 1) % cfg.ratio == 0)
+        if e:
+            emitted.append(out)
+    torch.cuda.synchronize()
+    from gpu_util import outputs_to_host
+    res = [outputs_to_host(o) for o in emitted]
+    cat = {k: np.concatenate([r[k] for r in res], axis=1) for k in res[0]} if res else {}
+    cat["state_kv"] = state[0].cpu().numpy()
+    cat["state_sc"] = state[1].cpu().numpy()
+    return cat
+
+
+def _live_rows(ratio, seqlen):
+    rem = seqlen % ratio
+    if ratio == 4:
+        return list(range(ratio)) + [ratio + i for i in range(rem)]
+    return list(range(rem))
+
+
+@pytest.mark.parametrize("ratio,hd,batch,steps", [(4, 512, 3, 40), (4, 128, 2, 33), (2, 512, 2, 21),
+                                                  (128, 512, 2, 256 + 9)])
+def test_decode_equals_prefill_bitwise_given_projections(ratio, hd, batch, steps):
+    note(f"decode==prefill bitwise ratio={ratio} hd={hd}")
+    from gpu_util import weights
+    rng = np.random.default_rng(ratio + steps)
+    cfg = kvc.Config(ratio, hd, 0)
+    proj = kvc.kvc_proj_width(cfg)
+    kv = rng.standard_normal((batch, steps, proj), dtype=np.float32)
+    sc = rng.standard_normal((batch, steps, proj), dtype=np.float32) * np.float32(2)
+    w = {"ape": rng.standard_normal((ratio, proj), dtype=np.float32) * np.float32(0.1)}
+    full = prefill(cfg, w, batch, steps, kv=kv, sc=sc)
+    dec = _decode_gpu(cfg, weights(w), batch, kvs=kv, scs=sc)
+    for k in ("pooled", "latent", "codes", "scales", "dequant"):
+        assert np.array_equal(dec[k].view(np.uint8), full[k].view(np.uint8)), k
+    # the rows a continuation reads next (other rows hold dead values)
+    live = _live_rows(ratio, steps)
+    assert np.array_equal(dec["state_kv"][:, live], full["state_kv"][:, live])
+    assert np.array_equal(dec["state_sc"][:, live], full["state_sc"][:, live])
+    # and the oracle agrees with both
+    ref = oracle.prefill(oracle_cfg(cfg), oracle_weights(w), oracle.State(oracle_cfg(cfg), batch), kv=kv,
+                         score=sc, quantize=True)
+    check_pooled(dec["pooled"], ref["pooled"])
+
+
+@pytest.mark.parametrize("ratio", [2, 4, 128])
+def test_prefill_then_decode_continuation(ratio):
+    note(f"continuation ratio={ratio}")
+    from gpu_util import weights
+    rng = np.random.default_rng(77 + ratio)
+    hd, batch = 128, 2
+    cfg = kvc.Config(ratio, hd, 0)
+    proj = kvc.kvc_proj_width(cfg)
+    n = 3 * ratio + 1
+    kv = rng.standard_normal((batch, n, proj), dtype=np.float32)
+    sc = rng.standard_normal((batch, n, proj), dtype=np.float32)
+    w = {"ape": rng.standard_normal((ratio, proj), dtype=np.float32) * np.float32(0.1)}
+    full = prefill(cfg, w, batch, n, kv=kv, sc=sc)
+    splits = sorted(set([1, 2, ratio - 1, ratio, ratio + 1, 2 * ratio + 3, n - 1, n]) - {0})
+    for n0 in splits:
+        state = kvc.new_state(cfg, batch)
+        state[0].fill_(5.0)  # stale values of an earlier sequence must not leak
+        state[1].fill_(3.0)
+        first = prefill(cfg, w, batch, n0, kv=kv[:, :n0], sc=sc[:, :n0], state=state)
+        rest = _decode_gpu(cfg, weights(w), batch, kvs=kv[:, n0:], scs=sc[:, n0:], start=n0, state=state)
+        parts = [p for p in (first.get("latent"), rest.get("latent")) if p is not None]
+        got = np.concatenate(parts, axis=1)
+        assert np.array_equal(got.view(np.uint32), full["latent"].view(np.uint32)), n0
+
+
+def test_decode_with_projection_matches_oracle():
+    note("decode with x, ratio 4, batch 64, dim 4096, 16 steps")
+    from gpu_util import weights
+    rng = np.random.default_rng(5)
+    cfg = kvc.Config(4, 512, 4096)
+    proj = 1024
+    batch, steps = 64, 16
+    x = rng.standard_normal((batch, steps, 4096), dtype=np.float32)
+    w = {"wkv": rng.standard_normal((proj, 4096), dtype=np.float32) * np.float32(0.02),
+         "wgate": rng.standard_normal((proj, 4096), dtype=np.float32) * np.float32(0.02),
+         "ape": rng.standard_normal((4, proj), dtype=np.float32) * np.float32(0.1)}
+    dec = _decode_gpu(cfg, weights(w), batch, xs=x)
+    ref = oracle.prefill(oracle_cfg(cfg), oracle_weights(w), oracle.State(oracle_cfg(cfg), batch), x=x,
+                         quantize=True)
+    check_pooled(dec["pooled"], ref["pooled"])
+    check_latent(dec["latent"], dec["pooled"], ref["latent"], ref["pooled"])
+    check_fp4(dec["codes"], dec["scales"], dec["latent"], ref["codes"], ref["scales"], ref["latent"], dec["dequant"])
+    # and the GPU prefill over the same tokens
+    full = prefill(cfg, w, batch, steps, x=x)
+    check_pooled(dec["pooled"], full["pooled"], "decode vs prefill")
