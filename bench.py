@@ -44,7 +44,7 @@ def source_sha(name: str) -> str:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
-def measured_traffic(name: str, launches_bytes: float):
+def measured_traffic(name: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None if there is none or the kernel source changed since it was taken."""
     try:
@@ -71,9 +71,9 @@ def pool_bytes(batch, seqlen, ratio, hd, quantize, latent):
     return read + write
 
 
-def cpu_baseline(wl, W, seconds=10.0, max_tokens=16384):
+def cpu_baseline(wl, W, seconds=10.0):
     """The oracle, as it stands, on the first tokens of the workload: doubles
-    the sample until it takes `seconds` (or reaches max_tokens)."""
+    the sample until it takes `seconds` or covers the whole sequence."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -92,9 +92,9 @@ def cpu_baseline(wl, W, seconds=10.0, max_tokens=16384):
                                  x=x, quantize=comp.quantize)
             entries = max(entries, out["latent"].shape[0] * out["latent"].shape[1])
         dt = time.perf_counter() - t0
-        if dt >= seconds or tokens >= max_tokens:
+        if dt >= seconds or tokens >= wl.seqlen:
             break
-        tokens *= 2
+        tokens = min(2 * tokens, wl.seqlen)
     return {"value": entries / dt, "unit": "entries/s", "cores": threads, "kind": "oracle",
             "sample": f"first {tokens} tokens of each of {wl.batch} batch rows through all "
                       f"{len(wl.compressors)} compressor(s) of the workload ({entries} entries, {dt:.2f} s)"}
@@ -195,8 +195,8 @@ def main():
     main_tag = f"hd{wl.compressors[0].head_dim}"
     g = kernels[f"gemm_{main_tag}"]
     p = kernels[f"pool_{main_tag}"]
-    g_traffic = measured_traffic("gemm", None)
-    p_traffic = measured_traffic("pool", None)
+    g_traffic = measured_traffic("gemm")
+    p_traffic = measured_traffic("pool")
     roofline = {"bound": "mfma", "achieved": round(g["tflops"], 2), "peak": PEAK_FP32_MFMA_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(g["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": g_traffic,
                 "kernel": "gemm_f32_kernel<128,128,64,64>", "per_launch": g["flop"], "avg_ms": round(g["ms"], 4)}

@@ -5,12 +5,12 @@
                 nearly zero are judged against the entry's scale).
   latent bf16 : within 1 bf16 ulp of the oracle, the ulp taken at
                 max(|ref|, 2^-8 * max |ref| of the entry), wherever the GPU's
-                pooled values round to the same bf16 values as the oracle's.
+                pooled value rounds to the same bf16 value as the oracle's.
                 An f32 pooled value within the f32 tolerance of a bf16
-                rounding midpoint may round the other way on the GPU; for
-                those entries the GPU latent must instead be within 1 ulp of
-                the oracle's RMSNorm applied to the GPU's own pooled values,
-                and such entries must be rare.
+                rounding midpoint may round the other way on the GPU (a
+                "flip", explained by that tolerance); there the latent is
+                within 2 ulps. Everywhere, the GPU latent is within 1 ulp of
+                the oracle's RMSNorm applied to the GPU's own pooled values.
   fp4         : codes and scales bit-exact against the oracle's fp4 round trip
                 of the GPU's own bf16 latent (the decision is taken on the
                 same input on both sides), and bit-exact against the oracle's
@@ -39,33 +39,49 @@ def check_pooled(gpu: np.ndarray, ref: np.ndarray, what="pooled"):
     scale = np.abs(ref).max(axis=1, keepdims=True)
     err = np.abs(gpu - ref).max(axis=1, keepdims=True)
     bad = err > POOLED_RTOL * scale
-    assert not bad.any(), f"{what}: {bad.sum()} entries beyond {POOLED_RTOL} relative, worst {(err / scale).max():.3e}"
-    return float((err / scale).max())
+    rel = np.where(scale > 0, err / np.where(scale > 0, scale, 1), 0)
+    assert not bad.any(), f"{what}: {bad.sum()} entries beyond {POOLED_RTOL} relative, worst {rel.max():.3e}"
+    return float(rel.max())
 
 
-def check_latent(gpu_latent, gpu_pooled, ref_latent, ref_pooled, norm_w=None, eps=1e-6,
-                 max_flip_fraction=0.05):
-    """Returns (entries with a pooled bf16 flip, total entries)."""
+def check_latent(gpu_latent, gpu_pooled, ref_latent, ref_pooled, norm_w=None, eps=1e-6):
+    """Returns (elements whose pooled value rounds to another bf16, total).
+
+    Per element, with u = bf16(pooled):
+      - where the GPU's u equals the oracle's, the latent is within 1 bf16 ulp;
+      - where it differs (a "flip"), the oracle's f32 pooled value must lie
+        within the pooled tolerance of the bf16 midpoint between the two u
+        values, and the latent is within 2 ulps (one from u, one from the
+        final rounding);
+      - everywhere, the latent is within 1 ulp of the oracle's RMSNorm of the
+        GPU's own pooled values.
+    """
     hd = gpu_latent.shape[-1]
     gl = gpu_latent.reshape(-1, hd).astype(np.float64)
     rl = ref_latent.reshape(-1, hd).astype(np.float64)
     gp = gpu_pooled.reshape(-1, hd)
     rp = ref_pooled.reshape(-1, hd)
-    same_u = np.all(oracle.bf16_round(gp) == oracle.bf16_round(rp), axis=1)
+    ug = oracle.bf16_round(gp).astype(np.float64)
+    ur = oracle.bf16_round(rp).astype(np.float64)
+    flip = ug != ur
+    if flip.any():
+        scale = np.abs(rp.astype(np.float64)).max(axis=1, keepdims=True) * np.ones_like(ug)
+        mid = (ug + ur) / 2
+        near = np.abs(rp.astype(np.float64) - mid) <= POOLED_RTOL * scale
+        assert np.all(near[flip]), f"{np.sum(flip & ~near)} bf16 flips not explained by the pooled tolerance"
     floor = 2.0 ** -8 * np.abs(rl).max(axis=1, keepdims=True)
     ulp = bf16_ulp(np.maximum(np.abs(rl), floor))
+    allowed = np.where(flip, 2.0, 1.0) * ulp
     err = np.abs(gl - rl)
-    bad = (err > ulp) & same_u[:, None]
-    assert not bad.any(), f"latent: {bad.sum()} values beyond 1 bf16 ulp in {bad.any(axis=1).sum()} entries"
-    # every entry: the GPU's norm step on its own pooled values
+    bad = err > allowed
+    assert not bad.any(), f"latent: {bad.sum()} values beyond the ulp bound in {bad.any(axis=1).sum()} entries"
+    # every element: the GPU's norm step on its own pooled values
     own = oracle.rms_norm_bf16(gp, norm_w, eps).astype(np.float64)
     floor2 = 2.0 ** -8 * np.abs(own).max(axis=1, keepdims=True)
     ulp2 = bf16_ulp(np.maximum(np.abs(own), floor2))
     bad2 = np.abs(gl - own) > ulp2
     assert not bad2.any(), f"latent vs norm of own pooled: {bad2.sum()} values beyond 1 ulp"
-    flips = int((~same_u).sum())
-    assert flips <= max(1, max_flip_fraction * len(same_u)), f"{flips} of {len(same_u)} entries with bf16 flips"
-    return flips, len(same_u)
+    return int(flip.sum()), flip.size
 
 
 def check_fp4(gpu_codes, gpu_scales, gpu_latent, ref_codes=None, ref_scales=None, ref_latent=None,
