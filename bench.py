@@ -183,8 +183,9 @@ def main():
     for idx, (comp, cfg, wts, ws, state, out, groups) in enumerate(comps):
         tag = f"hd{comp.head_dim}"
         gemm_ms = timed(lambda: kvc.compressor_prefill(cfg, wts, x, wl.batch, wl.seqlen, ws), args.kernel_reps)
-        # ws now holds this compressor's projections: pool them alone
-        pool_ms = timed(lambda: kvc.compressor_prefill(cfg, kvc.Weights(ape=wts.ape), None, wl.batch, wl.seqlen,
+        # ws now holds this compressor's projections, the bias already in the
+        # score plane: pool them alone, exactly as the step's pooling launch
+        pool_ms = timed(lambda: kvc.compressor_prefill(cfg, kvc.Weights(), None, wl.batch, wl.seqlen,
                                                        ws, None, None, out), args.kernel_reps)
         proj = 2 * comp.head_dim if comp.ratio == 4 else comp.head_dim
         flops = 2.0 * wl.batch * wl.seqlen * wl.dim * 2 * proj
@@ -199,7 +200,7 @@ def main():
     p_traffic = measured_traffic("pool")
     roofline = {"bound": "mfma", "achieved": round(g["tflops"], 2), "peak": PEAK_FP32_MFMA_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(g["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": g_traffic,
-                "kernel": "gemm_f32_kernel<128,128,64,64>", "per_launch": g["flop"], "avg_ms": round(g["ms"], 4)}
+                "kernel": "gemm_f32_kernel (512-wide projection)", "per_launch": g["flop"], "avg_ms": round(g["ms"], 4)}
     pool = {"bound": "hbm", "achieved": round(p["gbps"], 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(p["gbps"] / PEAK_HBM_GBPS, 4), "traffic": p_traffic,
             "kernel": "pool_small_kernel<512,4,true>", "per_launch": p["bytes"], "avg_ms": round(p["ms"], 4)}

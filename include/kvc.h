@@ -133,7 +133,8 @@ int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch);
  *                  except ape and norm_w.
  *   batch        : >= 1.   seqlen : >= 0.
  *   workspace    : f32, >= kvc_prefill_workspace_floats() elements; receives
- *                  the two projection planes when x is not NULL.
+ *                  the two projection planes when x is not NULL (the score
+ *                  plane then with the positional bias added).
  *   kv_state,
  *   score_state  : [state_batch][kvc_state_rows()][proj] f32 each, or both
  *                  NULL (nothing carried). Rows of batch row b are written as

@@ -74,12 +74,11 @@ kvc::PoolArgs pool_args(const kvc_config *cfg, const kvc_weights *w, const kvc_o
   return p;
 }
 
-// Entries per wavefront run: about 2048 wavefronts in total (8 per CU), at
-// most 16 entries per run, so that the re-read of a run's first previous
-// block stays a small fraction of its traffic.
+// Entries per wavefront run: one entry per wavefront up to 16384 entries
+// (many short wavefronts keep the most loads in flight), then longer runs.
 int32_t entries_per_wave(int64_t batch, int64_t groups) {
   const int64_t total = batch * groups;
-  int64_t e = (total + 2047) / 2048;
+  int64_t e = (total + 16383) / 16384;
   if (e < 1) e = 1;
   if (e > 16) e = 16;
   return (int32_t)e;
@@ -157,10 +156,17 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const float 
     g.k = cfg->dim;
     g.splits = 1;
     g.c_split_stride = 0;
+    // the positional bias joins the gate logits in the GEMM epilogue
+    g.bias1 = w->ape;
+    g.bias_seqlen = seqlen;
+    g.bias_ratio = cfg->ratio;
     if ((rc = hip_status(kvc::launch_gemm(g, kvc::GemmShape::kPrefill, s)))) return rc;
   }
+  // projections the caller put in the workspace carry no bias yet
+  const float *ape_after = x ? nullptr : (w ? w->ape : nullptr);
   if (groups > 0 && wants_entries(out)) {
     kvc::PoolArgs p = pool_args(cfg, w, out);
+    p.ape = ape_after;
     p.kv = kv_plane;
     p.sc = sc_plane;
     p.row_stride = proj;
@@ -176,7 +182,7 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const float 
     kvc::StateStoreArgs st{};
     st.kv = kv_plane;
     st.sc = sc_plane;
-    st.ape = w ? w->ape : nullptr;
+    st.ape = ape_after;
     st.kv_state = kv_state;
     st.sc_state = score_state;
     st.batch = batch;

@@ -12,6 +12,9 @@ namespace kvc {
 // output columns (kv with wkv, score with wgate), f32 in and out, fp32 MFMA.
 // The K range is cut into `splits` equal parts; split s writes its partial
 // sums at C_h + s * c_split_stride.
+// Optionally the second half gets a positional bias row added to each output
+// row (one f32 addition): row r of C_1 adds bias1[((r mod bias_seqlen) mod
+// bias_ratio) * ldc + n] (the gate logits' bias of token r mod seqlen).
 struct GemmArgs {
   const float *a;       // [m][k], row stride lda
   const float *b0, *b1; // [n_half][k] each, row stride ldb
@@ -20,12 +23,14 @@ struct GemmArgs {
   int64_t m, n_half, k;
   int32_t splits;
   int64_t c_split_stride;
+  const float *bias1;   // [bias_ratio][ldc] or null (splits must be 1)
+  int64_t bias_seqlen;
+  int32_t bias_ratio;
 };
 
+// Prefill tiles need n_half % 128 == 0 and k % 32 == 0; decode tiles need
+// n_half % 64 == 0 and k % (32 * splits) == 0.
 enum class GemmShape { kPrefill, kDecode };
-// Rows/columns of one workgroup's output tile for a shape.
-int gemm_tile_m(GemmShape s);
-int gemm_tile_n(GemmShape s);
 hipError_t launch_gemm(const GemmArgs &g, GemmShape shape, hipStream_t stream);
 
 // Pools `groups` entries of each batch row from kv/score planes holding a

@@ -30,51 +30,59 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t id, uint32_t n) {
   return (x < r) ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
 }
 
-template <int VEC>
-__device__ __forceinline__ void load_vec(const float *p, float (&d)[VEC]) {
-  if constexpr (VEC % 4 == 0) {
-#pragma unroll
-    for (int q = 0; q < VEC / 4; ++q) {
-      const float4 t = *reinterpret_cast<const float4 *>(p + 4 * q);
-      d[4 * q] = t.x; d[4 * q + 1] = t.y; d[4 * q + 2] = t.z; d[4 * q + 3] = t.w;
-    }
+// Lane layout of one entry's HD features across a wavefront: chunks of QV
+// consecutive features (one 4*QV-byte access each), H = HD / (64*QV) chunks
+// per lane; chunk h of lane l holds features h*64*QV + l*QV + [0, QV). Every
+// load instruction of a wavefront then covers one contiguous span of 64*QV
+// floats, and a block of 16 features (one fp4 scale) spans 16/QV lanes.
+template <int HD>
+struct Lanes {
+  static constexpr int VEC = HD / kWave;
+  static constexpr int QV = VEC >= 4 ? 4 : VEC;
+  static constexpr int H = VEC / QV;
+  static_assert(QV == 2 || QV == 4, "head_dim must be 128 or a multiple of 256");
+  __device__ static int feature(int lane, int h) { return h * kWave * QV + lane * QV; }
+};
+
+template <int QV>
+__device__ __forceinline__ void load_q(const float *p, float *d) {
+  if constexpr (QV == 4) {
+    const float4 t = *reinterpret_cast<const float4 *>(p);
+    d[0] = t.x; d[1] = t.y; d[2] = t.z; d[3] = t.w;
   } else {
-    static_assert(VEC == 2, "VEC must be 2 or a multiple of 4");
+    static_assert(QV == 2, "QV must be 2 or 4");
     const float2 t = *reinterpret_cast<const float2 *>(p);
     d[0] = t.x; d[1] = t.y;
   }
 }
 
-template <int VEC>
-__device__ __forceinline__ void store_vec(float *p, const float (&d)[VEC]) {
-  if constexpr (VEC % 4 == 0) {
+template <int QV>
+__device__ __forceinline__ void store_q(float *p, const float *d) {
+  if constexpr (QV == 4) *reinterpret_cast<float4 *>(p) = make_float4(d[0], d[1], d[2], d[3]);
+  else *reinterpret_cast<float2 *>(p) = make_float2(d[0], d[1]);
+}
+
+// QV bf16 patterns (low 16 bits of each word) as one store
+template <int QV>
+__device__ __forceinline__ void store_bf16_q(uint16_t *p, const uint32_t *b) {
+  if constexpr (QV == 4) *reinterpret_cast<uint2 *>(p) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+  else *reinterpret_cast<uint32_t *>(p) = b[0] | (b[1] << 16);
+}
+
+// One token row's VEC features of this lane (layout Lanes<HD>), `base` at
+// the row's first feature.
+template <int HD>
+__device__ __forceinline__ void load_row(const float *base, int lane, float (&d)[HD / kWave]) {
+  using L = Lanes<HD>;
 #pragma unroll
-    for (int q = 0; q < VEC / 4; ++q)
-      *reinterpret_cast<float4 *>(p + 4 * q) = make_float4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
-  } else {
-    *reinterpret_cast<float2 *>(p) = make_float2(d[0], d[1]);
-  }
+  for (int h = 0; h < L::H; ++h) load_q<L::QV>(base + L::feature(lane, h), d + h * L::QV);
 }
 
-// VEC bf16 patterns (low 16 bits of each word) as one store
-template <int VEC>
-__device__ __forceinline__ void store_bf16(uint16_t *p, const uint32_t (&b)[VEC]) {
-  if constexpr (VEC == 8) {
-    *reinterpret_cast<uint4 *>(p) = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16),
-                                               b[4] | (b[5] << 16), b[6] | (b[7] << 16));
-  } else if constexpr (VEC == 4) {
-    *reinterpret_cast<uint2 *>(p) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
-  } else {
-    static_assert(VEC == 2, "VEC must be 2, 4 or 8");
-    *reinterpret_cast<uint32_t *>(p) = b[0] | (b[1] << 16);
-  }
-}
-
-template <int VEC>
-__device__ __forceinline__ void store_codes(uint8_t *p, uint32_t packed) {
-  if constexpr (VEC == 8) *reinterpret_cast<uint32_t *>(p) = packed;
-  else if constexpr (VEC == 4) *reinterpret_cast<uint16_t *>(p) = (uint16_t)packed;
-  else *p = (uint8_t)packed;
+template <int HD>
+__device__ __forceinline__ void store_row(float *base, int lane, const float (&d)[HD / kWave]) {
+  using L = Lanes<HD>;
+#pragma unroll
+  for (int h = 0; h < L::H; ++h) store_q<L::QV>(base + L::feature(lane, h), d + h * L::QV);
 }
 
 // Softmax-weighted sum over NC candidates for each of VEC features, f32.
@@ -94,18 +102,19 @@ __device__ __forceinline__ void softmax_pool(const float (&k)[NC][VEC], const fl
       den += e;
       num = __builtin_fmaf(e, k[i][v], num);
     }
-    out[v] = num / den;
+    out[v] = num * __builtin_amdgcn_rcpf(den);  // den in [1, NC]: v_rcp_f32 is within 1 ulp
   }
 }
 
-// Per-entry epilogue of one wavefront holding VEC = HD / 64 pooled features
-// per lane: optional f32 store, bf16 round, RMSNorm over the entry (wave
-// reduction), bf16 latent, fp4 codes / scales / dequantised values.
-template <int HD, int VEC>
-__device__ __forceinline__ void finish_entry(const float (&p)[VEC], const PoolArgs &a, int64_t out_row,
+// Per-entry epilogue of one wavefront holding the entry's pooled features
+// (layout Lanes<HD>): optional f32 store, bf16 round, RMSNorm over the entry
+// (wave reduction), bf16 latent, fp4 codes / scales / dequantised values.
+template <int HD>
+__device__ __forceinline__ void finish_entry(const float (&p)[HD / kWave], const PoolArgs &a, int64_t out_row,
                                              int lane) {
-  const int f0 = lane * VEC;
-  if (a.pooled) store_vec<VEC>(a.pooled + out_row * HD + f0, p);
+  using L = Lanes<HD>;
+  constexpr int VEC = L::VEC, QV = L::QV;
+  if (a.pooled) store_row<HD>(a.pooled + out_row * HD, lane, p);
   float u[VEC];
   float ss = 0.0f;
 #pragma unroll
@@ -118,28 +127,46 @@ __device__ __forceinline__ void finish_entry(const float (&p)[VEC], const PoolAr
   float y[VEC];
   uint32_t yb[VEC];
 #pragma unroll
-  for (int v = 0; v < VEC; ++v) {
-    float t = u[v] * r;
-    if (a.norm_w) t *= a.norm_w[f0 + v];
-    yb[v] = bf16_rne(t);
-    y[v] = bf16_val(yb[v]);
+  for (int h = 0; h < L::H; ++h)
+#pragma unroll
+    for (int q = 0; q < QV; ++q) {
+      const int v = h * QV + q;
+      float t = u[v] * r;
+      if (a.norm_w) t *= a.norm_w[L::feature(lane, h) + q];
+      yb[v] = bf16_rne(t);
+      y[v] = bf16_val(yb[v]);
+    }
+  if (a.latent) {
+#pragma unroll
+    for (int h = 0; h < L::H; ++h) store_bf16_q<QV>(a.latent + out_row * HD + L::feature(lane, h), yb + h * QV);
   }
-  if (a.latent) store_bf16<VEC>(a.latent + out_row * HD + f0, yb);
   if (a.codes || a.scales || a.deq) {
-    uint32_t packed, scode, deq[VEC];
-    fp4_block<VEC>(y, packed, scode, deq);
-    if (a.codes) store_codes<VEC>(a.codes + out_row * (HD / 2) + f0 / 2, packed);
-    if (a.scales && (f0 % 16) == 0) a.scales[out_row * (HD / 16) + f0 / 16] = (uint8_t)scode;
-    if (a.deq) store_bf16<VEC>(a.deq + out_row * HD + f0, deq);
+#pragma unroll
+    for (int h = 0; h < L::H; ++h) {
+      const int f = L::feature(lane, h);
+      float yq[QV];
+#pragma unroll
+      for (int q = 0; q < QV; ++q) yq[q] = y[h * QV + q];
+      uint32_t packed, scode, deq[QV];
+      fp4_block<QV>(yq, packed, scode, deq);
+      if (a.codes) {
+        uint8_t *c = a.codes + out_row * (HD / 2) + f / 2;
+        if constexpr (QV == 4) *reinterpret_cast<uint16_t *>(c) = (uint16_t)packed;
+        else *c = (uint8_t)packed;
+      }
+      if (a.scales && (f % 16) == 0) a.scales[out_row * (HD / 16) + f / 16] = (uint8_t)scode;
+      if (a.deq) store_bf16_q<QV>(a.deq + out_row * HD + f, deq);
+    }
   }
 }
 
 // Small groups (ratio 2, ratio 4 overlapped). One wavefront walks a run of
-// consecutive entries of one batch row; lane l owns features [l*VEC, l*VEC+VEC).
+// consecutive entries of one batch row (features laid out as Lanes<HD>).
 // Ratio 4: entry j pools rows 4(j-1)..4j-1 of branch B (columns [HD, 2HD))
-// then rows 4j..4j+3 of branch A (columns [0, HD)); branch B of the current
-// block stays in registers for the next entry. Entry 0's previous branch is
-// kv 0 / score -inf.
+// then rows 4j..4j+3 of branch A (columns [0, HD)); entry 0's previous branch
+// is kv 0 / score -inf. Each entry loads exactly its own candidates, so every
+// projection value is read once over the whole launch and nothing is carried
+// in registers from one entry to the next.
 template <int HD, int R, bool OV>
 __global__ __launch_bounds__(256) void pool_small_kernel(PoolArgs a) {
   constexpr int VEC = HD / kWave;
@@ -154,96 +181,69 @@ __global__ __launch_bounds__(256) void pool_small_kernel(PoolArgs a) {
   const int64_t e_end = min(e_begin + (int64_t)a.entries_per_wave, a.groups);
   const float *KV = a.kv + b * a.batch_stride;
   const float *SC = a.sc + b * a.batch_stride;
-  const int f0 = lane * VEC;
-
-  float prev_k[R][VEC], prev_s[R][VEC];  // previous block, branch B (OV)
-  float cur_k[R][VEC], cur_s[R][VEC];    // current block, branch A (or the only branch)
-  float nb_k[R][VEC], nb_s[R][VEC];      // current block, branch B (OV)
-
-  if constexpr (OV) {
-    const int64_t j = a.first_entry + e_begin;
-    if (j == 0) {
-#pragma unroll
-      for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) { prev_k[i][v] = 0.0f; prev_s[i][v] = -INFINITY; }
-    } else {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const int64_t row = (int64_t)R * (j - 1) + i;
-        load_vec<VEC>(KV + row * a.row_stride + HD + f0, prev_k[i]);
-        load_vec<VEC>(SC + row * a.row_stride + HD + f0, prev_s[i]);
-        if (a.ape) {
-          float bias[VEC];
-          load_vec<VEC>(a.ape + (int64_t)i * a.row_stride + HD + f0, bias);
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) prev_s[i][v] += bias[v];
-        }
-      }
-    }
-  }
 
   for (int64_t e = e_begin; e < e_end; ++e) {
     const int64_t j = a.first_entry + e;
+    // candidates in pooling order: [previous block's branch B,] current rows
+    float ck[NC][VEC], cs[NC][VEC];
+    constexpr int C0 = OV ? R : 0;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int64_t row = (int64_t)R * j + i;
-      load_vec<VEC>(KV + row * a.row_stride + f0, cur_k[i]);
-      load_vec<VEC>(SC + row * a.row_stride + f0, cur_s[i]);
-      if constexpr (OV) {
-        load_vec<VEC>(KV + row * a.row_stride + HD + f0, nb_k[i]);
-        load_vec<VEC>(SC + row * a.row_stride + HD + f0, nb_s[i]);
+      load_row<HD>(KV + row * a.row_stride, lane, ck[C0 + i]);
+      load_row<HD>(SC + row * a.row_stride, lane, cs[C0 + i]);
+    }
+    if constexpr (OV) {
+      if (j > 0) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const int64_t row = (int64_t)R * (j - 1) + i;
+          load_row<HD>(KV + row * a.row_stride + HD, lane, ck[i]);
+          load_row<HD>(SC + row * a.row_stride + HD, lane, cs[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) { ck[i][v] = 0.0f; cs[i][v] = -INFINITY; }
       }
     }
     if (a.ape) {
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         float bias[VEC];
-        load_vec<VEC>(a.ape + (int64_t)i * a.row_stride + f0, bias);
+        load_row<HD>(a.ape + (int64_t)i * a.row_stride, lane, bias);
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) cur_s[i][v] += bias[v];
+        for (int v = 0; v < VEC; ++v) cs[C0 + i][v] += bias[v];
         if constexpr (OV) {
-          load_vec<VEC>(a.ape + (int64_t)i * a.row_stride + HD + f0, bias);
+          load_row<HD>(a.ape + (int64_t)i * a.row_stride + HD, lane, bias);
 #pragma unroll
-          for (int v = 0; v < VEC; ++v) nb_s[i][v] += bias[v];
+          for (int v = 0; v < VEC; ++v) cs[i][v] += bias[v];  // -inf padding stays -inf
         }
       }
     }
-    float ck[NC][VEC], cs[NC][VEC];
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        if constexpr (OV) {
-          ck[i][v] = prev_k[i][v]; cs[i][v] = prev_s[i][v];
-          ck[R + i][v] = cur_k[i][v]; cs[R + i][v] = cur_s[i][v];
-        } else {
-          ck[i][v] = cur_k[i][v]; cs[i][v] = cur_s[i][v];
-        }
-      }
     float p[VEC];
     softmax_pool<NC, VEC>(ck, cs, p);
-    finish_entry<HD, VEC>(p, a, b * a.out_batch_stride + e, lane);
-    if constexpr (OV) {
-#pragma unroll
-      for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) { prev_k[i][v] = nb_k[i][v]; prev_s[i][v] = nb_s[i][v]; }
-    }
-  }
+    finish_entry<HD>(p, a, b * a.out_batch_stride + e, lane);
 
-  if constexpr (OV) {
-    // decode: the block just pooled becomes the previous block. This lane
-    // only overwrites the features it alone has read.
-    if (a.shift_kv && e_end > e_begin) {
-      float *SK = a.shift_kv + b * a.batch_stride;
-      float *SS = a.shift_sc + b * a.batch_stride;
+    if constexpr (OV) {
+      // decode: the block just pooled becomes the previous block. This lane
+      // only touches the features it alone reads.
+      if (a.shift_kv) {
+        float *SK = a.shift_kv + b * a.batch_stride;
+        float *SS = a.shift_sc + b * a.batch_stride;
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        store_vec<VEC>(SK + (int64_t)i * a.row_stride + f0, cur_k[i]);
-        store_vec<VEC>(SS + (int64_t)i * a.row_stride + f0, cur_s[i]);
-        store_vec<VEC>(SK + (int64_t)i * a.row_stride + HD + f0, nb_k[i]);
-        store_vec<VEC>(SS + (int64_t)i * a.row_stride + HD + f0, nb_s[i]);
+        for (int i = 0; i < R; ++i) {
+          const int64_t row = (int64_t)R * j + i;
+          float bk[VEC], bs[VEC];
+          load_row<HD>(KV + row * a.row_stride + HD, lane, bk);
+          load_row<HD>(SC + row * a.row_stride + HD, lane, bs);
+          const int64_t dst = (int64_t)R * (j - 1) + i;
+          store_row<HD>(SK + dst * a.row_stride, lane, ck[C0 + i]);
+          store_row<HD>(SS + dst * a.row_stride, lane, cs[C0 + i]);
+          store_row<HD>(SK + dst * a.row_stride + HD, lane, bk);
+          store_row<HD>(SS + dst * a.row_stride + HD, lane, bs);
+        }
       }
     }
   }
@@ -262,6 +262,7 @@ __global__ __launch_bounds__(512) void pool_long_kernel(PoolArgs a) {
   constexpr int CH = 8;             // rows per chunk
   static_assert(ROWS % CH == 0, "rows per row lane must be a multiple of the chunk");
   constexpr int VEC = HD / kWave;   // features per lane in the epilogue
+  using L = Lanes<HD>;
   __shared__ float s_m[RL][HD], s_l[RL][HD], s_acc[RL][HD];
 
   const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
@@ -281,15 +282,15 @@ __global__ __launch_bounds__(512) void pool_long_kernel(PoolArgs a) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int row = (c * CH + i) * RL + rl;
-      load_vec<4>(KV + (int64_t)row * a.row_stride, k[i]);
-      load_vec<4>(SC + (int64_t)row * a.row_stride, s[i]);
+      load_q<4>(KV + (int64_t)row * a.row_stride, k[i]);
+      load_q<4>(SC + (int64_t)row * a.row_stride, s[i]);
     }
     if (a.ape) {
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         const int row = (c * CH + i) * RL + rl;
         float bias[4];
-        load_vec<4>(a.ape + (int64_t)row * a.row_stride + 4 * fg, bias);
+        load_q<4>(a.ape + (int64_t)row * a.row_stride + 4 * fg, bias);
 #pragma unroll
         for (int v = 0; v < 4; ++v) s[i][v] += bias[v];
       }
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(512) void pool_long_kernel(PoolArgs a) {
   float p[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) {
-    const int f = lane * VEC + v;
+    const int f = L::feature(lane, v / L::QV) + v % L::QV;
     float mm = s_m[0][f];
 #pragma unroll
     for (int r = 1; r < RL; ++r) mm = __builtin_fmaxf(mm, s_m[r][f]);
@@ -335,9 +336,9 @@ __global__ __launch_bounds__(512) void pool_long_kernel(PoolArgs a) {
       den = __builtin_fmaf(s_l[r][f], w, den);
       num = __builtin_fmaf(s_acc[r][f], w, num);
     }
-    p[v] = num / den;
+    p[v] = num * __builtin_amdgcn_rcpf(den);
   }
-  finish_entry<HD, VEC>(p, a, b * a.out_batch_stride + e, lane);
+  finish_entry<HD>(p, a, b * a.out_batch_stride + e, lane);
 }
 
 __global__ __launch_bounds__(256) void state_store_kernel(StateStoreArgs s) {
@@ -431,7 +432,10 @@ __global__ __launch_bounds__(256) void fp4_quant_kernel(const uint16_t *in, int6
   fp4_block<8>(y, packed, scode, deq);
   if (codes) *reinterpret_cast<uint32_t *>(codes + 4 * i) = packed;
   if (scales && (i & 1) == 0) scales[i / 2] = (uint8_t)scode;
-  if (out) store_bf16<8>(out + 8 * i, deq);
+  if (out) {
+    store_bf16_q<4>(out + 8 * i, deq);
+    store_bf16_q<4>(out + 8 * i + 4, deq + 4);
+  }
 }
 
 template <int HD, int R, bool OV>

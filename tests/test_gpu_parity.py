@@ -129,6 +129,8 @@ GEMM_CASES = [
     (128, 512, 512, 1, 256 + 128 + 5),
     (2, 512, 128, 3, 61),
     (4, 512, 4096, 1, 130),
+    (4, 512, 64, 1, 16384 + 37),   # 256 x 256 tiles, ragged last row tile
+    (4, 512, 64, 1, 4096 + 37),    # 256 x 128 tiles, ragged last row tile
 ]
 
 
@@ -144,11 +146,14 @@ def test_projection_gemm_and_full_prefill(ratio, hd, dim, batch, seqlen):
          "ape": rng.standard_normal((ratio, proj), dtype=np.float32) * np.float32(0.1)}
     g = prefill(cfg, w, batch, seqlen, x=x)
     # projections: inside the worst-case bound of any f32 summation order,
-    # dim * 2^-24 * sum |x| |w|, and 1e-5 of each row's largest value
+    # dim * 2^-24 * sum |x| |w| (plus one rounding of the bias addition on the
+    # score plane), and 1e-5 of each row's largest value
     for name, wname in (("proj_kv", "wkv"), ("proj_sc", "wgate")):
         ref = oracle.project(x.reshape(-1, dim), w[wname]).reshape(batch, seqlen, proj)
+        if name == "proj_sc":  # the workspace's score plane carries the positional bias
+            ref = oracle.add_bias(ref, w["ape"], np.arange(seqlen), ratio)
         absdot = (np.abs(x.reshape(-1, dim)).astype(np.float64) @ np.abs(w[wname]).astype(np.float64).T)
-        bound = dim * 2.0 ** -24 * absdot.reshape(batch, seqlen, proj) + 1e-30
+        bound = dim * 2.0 ** -24 * absdot.reshape(batch, seqlen, proj) + np.spacing(np.abs(ref)) + 1e-30
         err = np.abs(g[name].astype(np.float64) - ref)
         assert np.all(err <= bound), f"{name}: {np.sum(err > bound)} beyond the bound"
         check_pooled(g[name], ref, name)
