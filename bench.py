@@ -33,15 +33,20 @@ METRIC = "compressed KV entries/sec + achieved HBM GB/s, ratio-4 prefill N=65536
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# the sources each counted kernel is built from (the traffic figures turn
+# null as soon as any of them changes)
 KERNEL_SOURCES = {
-    "gemm": "kv_cache_compression_fp32_amd/csrc/gemm_f32.hip",
-    "pool": "kv_cache_compression_fp32_amd/csrc/pool.hip",
+    "gemm": ["kv_cache_compression_fp32_amd/csrc/gemm_f32_kernel.h", "kv_cache_compression_fp32_amd/csrc/gemm_f32.hip"],
+    "pool": ["kv_cache_compression_fp32_amd/csrc/pool.hip", "kv_cache_compression_fp32_amd/csrc/kvc_device.h"],
 }
 
 
 def source_sha(name: str) -> str:
-    with open(os.path.join(ROOT, KERNEL_SOURCES[name]), "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[name]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(name: str):
@@ -100,6 +105,121 @@ def cpu_baseline(wl, W, seconds=10.0):
                       f"{len(wl.compressors)} compressor(s) of the workload ({entries} entries, {dt:.2f} s)"}
 
 
+def _timed(torch, stream, fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def _rounded(d):
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+
+
+def run_prefill(wl, steps, warmup, reps, torch, kvc, W):
+    """Time whole prefill steps of `wl`, then each kernel alone."""
+    dev = "cuda"
+    print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
+    x = torch.from_numpy(W.hidden(wl)).to(dev)
+    torch.cuda.synchronize()
+    comps = []
+    for comp in wl.compressors:
+        cfg = kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps)
+        w = {k: torch.from_numpy(v).to(dev) for k, v in W.weights(wl, comp).items()}
+        wts = kvc.Weights(wkv=w["wkv"], wgate=w["wgate"], ape=w["ape"])
+        groups = wl.seqlen // comp.ratio
+        ws = torch.empty(kvc.kvc_prefill_workspace_floats(cfg, wl.batch, wl.seqlen), dtype=torch.float32,
+                         device=dev)
+        state = kvc.new_state(cfg, wl.batch)
+        out = kvc.new_outputs(cfg, wl.batch, groups, latent=not comp.quantize, fp4=comp.quantize)
+        comps.append((comp, cfg, wts, ws, state, out, groups))
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for comp, cfg, wts, ws, state, out, groups in comps:
+            kvc.compressor_prefill(cfg, wts, x, wl.batch, wl.seqlen, ws, state[0], state[1], out)
+
+    print(f"[bench] {wl.name}: warmup + {steps} timed steps", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = _timed(torch, stream, step, steps)
+    entries = comps[0][6] * wl.batch
+
+    kernels = {}
+    for comp, cfg, wts, ws, state, out, groups in comps:
+        tag = f"hd{comp.head_dim}"
+        gemm_ms = _timed(torch, stream, lambda: kvc.compressor_prefill(cfg, wts, x, wl.batch, wl.seqlen, ws), reps)
+        # ws now holds this compressor's projections, the bias already in the
+        # score plane: pool them alone, exactly as the step's pooling launch
+        pool_ms = _timed(torch, stream, lambda: kvc.compressor_prefill(cfg, kvc.Weights(), None, wl.batch,
+                                                                       wl.seqlen, ws, None, None, out), reps)
+        proj = 2 * comp.head_dim if comp.ratio == 4 else comp.head_dim
+        flops = 2.0 * wl.batch * wl.seqlen * wl.dim * 2 * proj
+        pbytes = pool_bytes(wl.batch, wl.seqlen, comp.ratio, comp.head_dim, comp.quantize, not comp.quantize)
+        kernels[f"gemm_{tag}"] = {"ms": gemm_ms, "tflops": flops / gemm_ms / 1e9, "flop": flops}
+        kernels[f"pool_{tag}"] = {"ms": pool_ms, "gbps": pbytes / pool_ms / 1e6, "bytes": pbytes}
+    del comps, x
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms_per_step, "entries_per_step": entries,
+            "entries_per_s": entries / (ms_per_step / 1e3), "kernels": kernels}
+
+
+def run_decode(wl, passes, torch, kvc, W):
+    """Time whole decode passes (every row streams all its tokens from
+    start_pos 0, one decode step per token), captured once in a HIP graph so
+    that host launch overhead is not measured."""
+    dev = "cuda"
+    comp = wl.compressors[0]
+    cfg = kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps)
+    print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
+    x = torch.from_numpy(W.hidden(wl)).to(dev).transpose(0, 1).contiguous()  # [steps, batch, dim]
+    w = {k: torch.from_numpy(v).to(dev) for k, v in W.weights(wl, comp).items()}
+    wts = kvc.Weights(wkv=w["wkv"], wgate=w["wgate"], ape=w["ape"])
+    ws = torch.empty(kvc.kvc_decode_workspace_floats(cfg, wl.batch), dtype=torch.float32, device=dev)
+    state = kvc.new_state(cfg, wl.batch)
+    groups = wl.seqlen // comp.ratio
+    lat = torch.empty((groups, wl.batch, comp.head_dim), dtype=torch.bfloat16, device=dev)
+    outs = [kvc.Outputs(latent=lat[e]) for e in range(groups)]
+
+    def one_pass():
+        e = 0
+        for p in range(wl.seqlen):
+            emits = p > 0 and (p + 1) % comp.ratio == 0
+            kvc.compressor_decode_step(cfg, wts, x[p], wl.batch, p, ws, state[0], state[1],
+                                       outs[e] if emits else None)
+            e += emits
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one_pass()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_pass()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    print(f"[bench] {wl.name}: {passes} timed graph replays", file=sys.stderr, flush=True)
+    ms = _timed(torch, stream, graph.replay, passes)
+    eager_ms = _timed(torch, stream, one_pass, 1)
+    proj = 2 * comp.head_dim if comp.ratio == 4 else comp.head_dim
+    flop_step = 2.0 * wl.batch * wl.dim * 2 * proj
+    entries = wl.batch * groups
+    del graph, x, outs, lat
+    torch.cuda.empty_cache()
+    return {"ms_per_pass": ms, "entries_per_pass": entries, "entries_per_s": entries / (ms / 1e3),
+            "us_per_step": ms * 1e3 / wl.seqlen, "tflops": flop_step * wl.seqlen / ms / 1e9,
+            "eager_ms_per_pass": eager_ms}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +228,9 @@ def main():
     ap.add_argument("--workload", default="prefill_r4_n65536_fp4_idx128")
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one plain copy kernel (read + write) of this many MiB")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
@@ -124,101 +247,51 @@ def main():
     kvc.lib()  # fails loudly if the HIP library is missing
     wl = W.WORKLOADS[args.workload]
     if wl.decode or wl.dim == 0:
-        print("bench.py times the prefill workloads with hidden states", file=sys.stderr)
+        print("bench.py's headline is a prefill workload with hidden states", file=sys.stderr)
         sys.exit(2)
-    dev = "cuda"
-    print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
-    x = torch.from_numpy(W.hidden(wl)).to(dev)
-    torch.cuda.synchronize()
-
-    comps = []
-    for comp in wl.compressors:
-        cfg = kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps)
-        w = {k: torch.from_numpy(v).to(dev) for k, v in W.weights(wl, comp).items()}
-        wts = kvc.Weights(wkv=w["wkv"], wgate=w["wgate"], ape=w["ape"])
-        groups = wl.seqlen // comp.ratio
-        ws = torch.empty(kvc.kvc_prefill_workspace_floats(cfg, wl.batch, wl.seqlen), dtype=torch.float32,
-                         device=dev)
-        state = kvc.new_state(cfg, wl.batch)
-        out = kvc.new_outputs(cfg, wl.batch, groups, latent=not comp.quantize, fp4=comp.quantize)
-        comps.append((comp, cfg, wts, ws, state, out, groups))
-
-    stream = torch.cuda.current_stream()
-
-    def step():
-        for comp, cfg, wts, ws, state, out, groups in comps:
-            kvc.compressor_prefill(cfg, wts, x, wl.batch, wl.seqlen, ws, state[0], state[1], out)
-
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    print("[bench] timed steps", file=sys.stderr, flush=True)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for _ in range(args.steps):
-        step()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    entries = comps[0][6] * wl.batch
-    value = entries / (ms_per_step / 1e3)
-
-    # ---- per-kernel durations, measured live with events on the launch stream
-    def timed(fn, reps):
-        fn()
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)  # reads n * 4 bytes, writes n * 4 bytes
         torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+        del src, dst
+        torch.cuda.empty_cache()
 
-    kernels = {}
-    print("[bench] kernel timing", file=sys.stderr, flush=True)
-    for idx, (comp, cfg, wts, ws, state, out, groups) in enumerate(comps):
-        tag = f"hd{comp.head_dim}"
-        gemm_ms = timed(lambda: kvc.compressor_prefill(cfg, wts, x, wl.batch, wl.seqlen, ws), args.kernel_reps)
-        # ws now holds this compressor's projections, the bias already in the
-        # score plane: pool them alone, exactly as the step's pooling launch
-        pool_ms = timed(lambda: kvc.compressor_prefill(cfg, kvc.Weights(), None, wl.batch, wl.seqlen,
-                                                       ws, None, None, out), args.kernel_reps)
-        proj = 2 * comp.head_dim if comp.ratio == 4 else comp.head_dim
-        flops = 2.0 * wl.batch * wl.seqlen * wl.dim * 2 * proj
-        pbytes = pool_bytes(wl.batch, wl.seqlen, comp.ratio, comp.head_dim, comp.quantize, not comp.quantize)
-        kernels[f"gemm_{tag}"] = {"ms": gemm_ms, "tflops": flops / gemm_ms / 1e9, "flop": flops}
-        kernels[f"pool_{tag}"] = {"ms": pool_ms, "gbps": pbytes / pool_ms / 1e6, "bytes": pbytes}
-
+    head = run_prefill(wl, args.steps, args.warmup, args.kernel_reps, torch, kvc, W)
+    kernels = head["kernels"]
     main_tag = f"hd{wl.compressors[0].head_dim}"
     g = kernels[f"gemm_{main_tag}"]
     p = kernels[f"pool_{main_tag}"]
-    g_traffic = measured_traffic("gemm")
-    p_traffic = measured_traffic("pool")
     roofline = {"bound": "mfma", "achieved": round(g["tflops"], 2), "peak": PEAK_FP32_MFMA_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(g["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": g_traffic,
-                "kernel": "gemm_f32_kernel (512-wide projection)", "per_launch": g["flop"], "avg_ms": round(g["ms"], 4)}
+                "unit": "TFLOP/s", "frac": round(g["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4),
+                "traffic": measured_traffic("gemm"), "kernel": "gemm_f32_kernel (512-wide projection)",
+                "per_launch": g["flop"], "avg_ms": round(g["ms"], 4)}
     pool = {"bound": "hbm", "achieved": round(p["gbps"], 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": round(p["gbps"] / PEAK_HBM_GBPS, 4), "traffic": p_traffic,
+            "frac": round(p["gbps"] / PEAK_HBM_GBPS, 4), "traffic": measured_traffic("pool"),
             "kernel": "pool_small_kernel<512,4,true>", "per_launch": p["bytes"], "avg_ms": round(p["ms"], 4)}
-
     result = {
-        "metric": METRIC, "value": round(value, 1), "unit": "entries/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "metric": METRIC, "value": round(head["entries_per_s"], 1), "unit": "entries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "seqlen": wl.seqlen, "dim": wl.dim,
                    "compressors": [{"ratio": c.ratio, "head_dim": c.head_dim, "fp4": c.quantize}
                                    for c in wl.compressors],
-                   "entries_per_step": entries},
+                   "entries_per_step": head["entries_per_step"]},
         "hbm_gbps": pool["achieved"],
         "roofline": roofline,
         "pool": pool,
-        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                    for k, v in kernels.items()},
+        "kernels": {k: _rounded(v) for k, v in kernels.items()},
     }
+    if not args.no_extras:
+        extras = {}
+        for name in ("prefill_r4_n4096", "prefill_r128_b2_n16384"):
+            r = run_prefill(W.WORKLOADS[name], 5, 2, 5, torch, kvc, W)
+            extras[name] = {"ms_per_step": round(r["ms_per_step"], 4), "entries_per_s": round(r["entries_per_s"], 1),
+                            "kernels": {k: _rounded(v) for k, v in r["kernels"].items()}}
+        d = run_decode(W.WORKLOADS["decode_r4_b64_s512"], 5, torch, kvc, W)
+        extras["decode_r4_b64_s512"] = _rounded(d)
+        result["workloads"] = extras
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, W)
