@@ -47,15 +47,15 @@ bool wants_entries(const kvc_outputs *out) {
   return out && (out->latent || out->pooled || out->codes || out->scales || out->dequant);
 }
 
-// Decode splits the K range so that about 512 workgroups cover the batch's
-// projection; the split count divides the number of 32-wide k tiles.
+// Decode splits the K range over workgroups so that about 256 of them (one
+// per CU) share the batch's projection: 32 columns x 64 rows per workgroup,
+// at most 16 splits.
 int32_t decode_splits(const kvc_config *cfg, int64_t batch) {
   const int64_t m_tiles = (batch + 63) / 64;
-  const int64_t n_tiles = 2 * proj_of(cfg) / 64;
-  const int64_t k_tiles = cfg->dim / 32;
-  int64_t want = 512 / (m_tiles * n_tiles);
+  const int64_t n_tiles = 2 * proj_of(cfg) / 32;
+  const int64_t want = 256 / (m_tiles * n_tiles);
   int32_t s = 1;
-  while (2 * s <= want && k_tiles % (2 * s) == 0) s *= 2;
+  while (2 * s <= want && s < 16) s *= 2;
   return s;
 }
 
@@ -252,40 +252,34 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const fl
   in.state_row = overlapped(cfg) ? r + slot : slot;
   in.ratio = r;
   in.reset_prev = (start_pos == 0 && overlapped(cfg)) ? 1 : 0;
-  if ((rc = hip_status(kvc::launch_decode_ingest(in, s)))) return rc;
 
-  if (emit && wants_entries(out)) {
-    kvc::PoolArgs p = pool_args(cfg, w, out);
-    p.ape = nullptr;  // the state already holds biased scores
-    p.kv = kv_state;
-    p.sc = score_state;
-    p.row_stride = proj;
-    p.batch_stride = rows_of(cfg) * proj;
-    p.batch = batch;
-    p.groups = 1;
-    p.first_entry = overlapped(cfg) ? 1 : 0;
-    p.entries_per_wave = 1;
-    p.out_batch_stride = 1;
-    if (overlapped(cfg)) {
-      p.shift_kv = kv_state;
-      p.shift_sc = score_state;
-    }
-    if ((rc = hip_status(kvc::launch_pool(p, r, cfg->head_dim, s)))) return rc;
-  } else if (emit && overlapped(cfg)) {
-    // no outputs requested: the carry must still move to the previous rows
-    kvc::PoolArgs p{};
-    p.kv = kv_state;
-    p.sc = score_state;
-    p.row_stride = proj;
-    p.batch_stride = rows_of(cfg) * proj;
-    p.batch = batch;
-    p.groups = 1;
-    p.first_entry = 1;
-    p.entries_per_wave = 1;
-    p.eps = cfg->eps;
-    p.out_batch_stride = 1;
+  // the pooled entry of a completed group, over the state planes (whose
+  // scores already hold the bias); at ratio 4 the block then shifts even
+  // when no output is requested
+  const bool pool_now = emit && (wants_entries(out) || overlapped(cfg));
+  kvc::PoolArgs p = out ? pool_args(cfg, w, out) : kvc::PoolArgs{};
+  p.ape = nullptr;
+  p.norm_w = w ? w->norm_w : nullptr;
+  p.eps = cfg->eps;
+  p.kv = kv_state;
+  p.sc = score_state;
+  p.row_stride = proj;
+  p.batch_stride = rows_of(cfg) * proj;
+  p.batch = batch;
+  p.groups = 1;
+  p.first_entry = overlapped(cfg) ? 1 : 0;
+  p.entries_per_wave = 1;
+  p.out_batch_stride = 1;
+  if (overlapped(cfg)) {
     p.shift_kv = kv_state;
     p.shift_sc = score_state;
+  }
+  if (pool_now && r != 128) {
+    // ingest and pool in one launch
+    return hip_status(kvc::launch_decode_finish(in, &p, cfg->head_dim, s));
+  }
+  if ((rc = hip_status(kvc::launch_decode_finish(in, nullptr, cfg->head_dim, s)))) return rc;
+  if (pool_now && wants_entries(out)) {
     if ((rc = hip_status(kvc::launch_pool(p, r, cfg->head_dim, s)))) return rc;
   }
   return KVC_OK;

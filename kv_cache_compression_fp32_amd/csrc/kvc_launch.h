@@ -28,8 +28,8 @@ struct GemmArgs {
   int32_t bias_ratio;
 };
 
-// Prefill tiles need n_half % 128 == 0 and k % 32 == 0; decode tiles need
-// n_half % 64 == 0 and k % (32 * splits) == 0.
+// Prefill tiles need n_half % 128 == 0 and k % 32 == 0; decode needs
+// n_half % 32 == 0 and k % 16 == 0 (any split count; no bias).
 enum class GemmShape { kPrefill, kDecode };
 hipError_t launch_gemm(const GemmArgs &g, GemmShape shape, hipStream_t stream);
 
@@ -64,9 +64,11 @@ struct StateStoreArgs {
 };
 hipError_t launch_state_store(const StateStoreArgs &s, hipStream_t stream);
 
-// Decode: sums the split partial projections of one token per batch row, adds
-// the bias row of the slot and writes the state row; optionally resets the
-// previous-block rows (ratio 4 at position 0).
+// Decode: sums the split partial projections of one token per batch row in a
+// fixed order, adds the bias row of the slot and writes the state row;
+// optionally resets the previous-block rows (ratio 4 at position 0). With
+// `pool` (ratios 2 and 4 only), the same launch then pools the state window of
+// each batch row (PoolArgs over the state planes, entry 0 of each row).
 struct IngestArgs {
   const float *part;      // [splits][2][batch][proj]
   int32_t splits;
@@ -75,7 +77,7 @@ struct IngestArgs {
   int64_t batch, proj, state_rows;
   int32_t slot, state_row, ratio, reset_prev;
 };
-hipError_t launch_decode_ingest(const IngestArgs &g, hipStream_t stream);
+hipError_t launch_decode_finish(const IngestArgs &g, const PoolArgs *pool, int head_dim, hipStream_t stream);
 
 // Standalone fp4 round trip of bf16 rows.
 hipError_t launch_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *codes,

@@ -160,17 +160,88 @@ __device__ __forceinline__ void finish_entry(const float (&p)[HD / kWave], const
   }
 }
 
-// Small groups (ratio 2, ratio 4 overlapped). One wavefront walks a run of
-// consecutive entries of one batch row (features laid out as Lanes<HD>).
-// Ratio 4: entry j pools rows 4(j-1)..4j-1 of branch B (columns [HD, 2HD))
-// then rows 4j..4j+3 of branch A (columns [0, HD)); entry 0's previous branch
-// is kv 0 / score -inf. Each entry loads exactly its own candidates, so every
-// projection value is read once over the whole launch and nothing is carried
-// in registers from one entry to the next.
+// One entry of a small group (ratio 2, ratio 4 overlapped) by one wavefront
+// (features laid out as Lanes<HD>), from kv/score planes holding the token
+// rows of batch row b. Ratio 4: entry j pools rows 4(j-1)..4j-1 of branch B
+// (columns [HD, 2HD)) then rows 4j..4j+3 of branch A (columns [0, HD));
+// entry 0's previous branch is kv 0 / score -inf. The entry loads exactly its
+// own candidates. With shift_kv set (decode), the block just pooled is then
+// copied to the previous-block rows; the lane only touches features it alone
+// reads.
 template <int HD, int R, bool OV>
-__global__ __launch_bounds__(256) void pool_small_kernel(PoolArgs a) {
+__device__ __forceinline__ void small_entry(const PoolArgs &a, int64_t b, int64_t e, int lane) {
   constexpr int VEC = HD / kWave;
   constexpr int NC = OV ? 2 * R : R;
+  constexpr int C0 = OV ? R : 0;
+  const float *KV = a.kv + b * a.batch_stride;
+  const float *SC = a.sc + b * a.batch_stride;
+  const int64_t j = a.first_entry + e;
+  // candidates in pooling order: [previous block's branch B,] current rows
+  float ck[NC][VEC], cs[NC][VEC];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int64_t row = (int64_t)R * j + i;
+    load_row<HD>(KV + row * a.row_stride, lane, ck[C0 + i]);
+    load_row<HD>(SC + row * a.row_stride, lane, cs[C0 + i]);
+  }
+  if constexpr (OV) {
+    if (j > 0) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int64_t row = (int64_t)R * (j - 1) + i;
+        load_row<HD>(KV + row * a.row_stride + HD, lane, ck[i]);
+        load_row<HD>(SC + row * a.row_stride + HD, lane, cs[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) { ck[i][v] = 0.0f; cs[i][v] = -INFINITY; }
+    }
+  }
+  if (a.ape) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      float bias[VEC];
+      load_row<HD>(a.ape + (int64_t)i * a.row_stride, lane, bias);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) cs[C0 + i][v] += bias[v];
+      if constexpr (OV) {
+        load_row<HD>(a.ape + (int64_t)i * a.row_stride + HD, lane, bias);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) cs[i][v] += bias[v];  // -inf padding stays -inf
+      }
+    }
+  }
+  float p[VEC];
+  softmax_pool<NC, VEC>(ck, cs, p);
+  finish_entry<HD>(p, a, b * a.out_batch_stride + e, lane);
+
+  if constexpr (OV) {
+    if (a.shift_kv) {
+      float *SK = a.shift_kv + b * a.batch_stride;
+      float *SS = a.shift_sc + b * a.batch_stride;
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int64_t row = (int64_t)R * j + i;
+        float bk[VEC], bs[VEC];
+        load_row<HD>(KV + row * a.row_stride + HD, lane, bk);
+        load_row<HD>(SC + row * a.row_stride + HD, lane, bs);
+        const int64_t dst = (int64_t)R * (j - 1) + i;
+        store_row<HD>(SK + dst * a.row_stride, lane, ck[C0 + i]);
+        store_row<HD>(SS + dst * a.row_stride, lane, cs[C0 + i]);
+        store_row<HD>(SK + dst * a.row_stride + HD, lane, bk);
+        store_row<HD>(SS + dst * a.row_stride + HD, lane, bs);
+      }
+    }
+  }
+}
+
+// Small groups (ratio 2, ratio 4 overlapped): one wavefront walks a run of
+// consecutive entries of one batch row. Every projection value is read once
+// over the whole launch and nothing is carried from one entry to the next.
+template <int HD, int R, bool OV>
+__global__ __launch_bounds__(256) void pool_small_kernel(PoolArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
   const int64_t runs = (a.groups + a.entries_per_wave - 1) / a.entries_per_wave;
@@ -179,74 +250,7 @@ __global__ __launch_bounds__(256) void pool_small_kernel(PoolArgs a) {
   const int64_t run = wave - b * runs;
   const int64_t e_begin = run * a.entries_per_wave;
   const int64_t e_end = min(e_begin + (int64_t)a.entries_per_wave, a.groups);
-  const float *KV = a.kv + b * a.batch_stride;
-  const float *SC = a.sc + b * a.batch_stride;
-
-  for (int64_t e = e_begin; e < e_end; ++e) {
-    const int64_t j = a.first_entry + e;
-    // candidates in pooling order: [previous block's branch B,] current rows
-    float ck[NC][VEC], cs[NC][VEC];
-    constexpr int C0 = OV ? R : 0;
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int64_t row = (int64_t)R * j + i;
-      load_row<HD>(KV + row * a.row_stride, lane, ck[C0 + i]);
-      load_row<HD>(SC + row * a.row_stride, lane, cs[C0 + i]);
-    }
-    if constexpr (OV) {
-      if (j > 0) {
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const int64_t row = (int64_t)R * (j - 1) + i;
-          load_row<HD>(KV + row * a.row_stride + HD, lane, ck[i]);
-          load_row<HD>(SC + row * a.row_stride + HD, lane, cs[i]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < R; ++i)
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) { ck[i][v] = 0.0f; cs[i][v] = -INFINITY; }
-      }
-    }
-    if (a.ape) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        float bias[VEC];
-        load_row<HD>(a.ape + (int64_t)i * a.row_stride, lane, bias);
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) cs[C0 + i][v] += bias[v];
-        if constexpr (OV) {
-          load_row<HD>(a.ape + (int64_t)i * a.row_stride + HD, lane, bias);
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) cs[i][v] += bias[v];  // -inf padding stays -inf
-        }
-      }
-    }
-    float p[VEC];
-    softmax_pool<NC, VEC>(ck, cs, p);
-    finish_entry<HD>(p, a, b * a.out_batch_stride + e, lane);
-
-    if constexpr (OV) {
-      // decode: the block just pooled becomes the previous block. This lane
-      // only touches the features it alone reads.
-      if (a.shift_kv) {
-        float *SK = a.shift_kv + b * a.batch_stride;
-        float *SS = a.shift_sc + b * a.batch_stride;
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const int64_t row = (int64_t)R * j + i;
-          float bk[VEC], bs[VEC];
-          load_row<HD>(KV + row * a.row_stride + HD, lane, bk);
-          load_row<HD>(SC + row * a.row_stride + HD, lane, bs);
-          const int64_t dst = (int64_t)R * (j - 1) + i;
-          store_row<HD>(SK + dst * a.row_stride, lane, ck[C0 + i]);
-          store_row<HD>(SS + dst * a.row_stride, lane, cs[C0 + i]);
-          store_row<HD>(SK + dst * a.row_stride + HD, lane, bk);
-          store_row<HD>(SS + dst * a.row_stride + HD, lane, bs);
-        }
-      }
-    }
-  }
+  for (int64_t e = e_begin; e < e_end; ++e) small_entry<HD, R, OV>(a, b, e, lane);
 }
 
 // Long groups (ratio 128). One workgroup of 512 threads per entry: thread t
@@ -380,36 +384,45 @@ __global__ __launch_bounds__(256) void state_store_kernel(StateStoreArgs s) {
   *reinterpret_cast<float4 *>(s.sc_state + dst) = g;
 }
 
-__global__ __launch_bounds__(256) void decode_ingest_kernel(IngestArgs g) {
-  const int64_t c4 = g.proj / 4;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= g.batch * c4) return;
-  const int64_t b = idx / c4, c = (idx - b * c4) * 4;
+// Decode step after the projection: one workgroup per batch row sums the
+// split partial projections of the row's token in a fixed order, adds the
+// slot's bias row and writes the state row (ratio 4 at position 0 also resets
+// the previous-block rows). On a step that completes a group of a small
+// ratio, the first wavefront then pools the state window with the same entry
+// code as the prefill kernel (so decode and prefill compute identical entries
+// from identical projections) and, at ratio 4, shifts the block.
+template <int HD, int R, bool OV, bool POOL>
+__global__ __launch_bounds__(256) void decode_finish_kernel(IngestArgs g, PoolArgs a) {
+  const int64_t b = blockIdx.x;
   const int64_t plane = g.batch * g.proj;
-  float4 k = make_float4(0.f, 0.f, 0.f, 0.f), s = k;
-  for (int sp = 0; sp < g.splits; ++sp) {  // fixed order: deterministic sums
-    const float4 pk = *reinterpret_cast<const float4 *>(g.part + (2 * sp) * plane + b * g.proj + c);
-    const float4 ps = *reinterpret_cast<const float4 *>(g.part + (2 * sp + 1) * plane + b * g.proj + c);
-    if (sp == 0) { k = pk; s = ps; }
-    else {
+  float *KS = g.kv_state + b * g.state_rows * g.proj;
+  float *SS = g.sc_state + b * g.state_rows * g.proj;
+  for (int64_t c = 4 * (int64_t)threadIdx.x; c < g.proj; c += 4 * (int64_t)blockDim.x) {
+    float4 k = *reinterpret_cast<const float4 *>(g.part + b * g.proj + c);
+    float4 s = *reinterpret_cast<const float4 *>(g.part + plane + b * g.proj + c);
+    for (int sp = 1; sp < g.splits; ++sp) {  // fixed order: deterministic sums
+      const float4 pk = *reinterpret_cast<const float4 *>(g.part + (2 * sp) * plane + b * g.proj + c);
+      const float4 ps = *reinterpret_cast<const float4 *>(g.part + (2 * sp + 1) * plane + b * g.proj + c);
       k.x += pk.x; k.y += pk.y; k.z += pk.z; k.w += pk.w;
       s.x += ps.x; s.y += ps.y; s.z += ps.z; s.w += ps.w;
     }
-  }
-  if (g.ape) {
-    const float4 bias = *reinterpret_cast<const float4 *>(g.ape + (int64_t)g.slot * g.proj + c);
-    s.x += bias.x; s.y += bias.y; s.z += bias.z; s.w += bias.w;
-  }
-  float *KS = g.kv_state + b * g.state_rows * g.proj;
-  float *SS = g.sc_state + b * g.state_rows * g.proj;
-  *reinterpret_cast<float4 *>(KS + (int64_t)g.state_row * g.proj + c) = k;
-  *reinterpret_cast<float4 *>(SS + (int64_t)g.state_row * g.proj + c) = s;
-  if (g.reset_prev) {
-    for (int i = 0; i < g.ratio; ++i) {
-      *reinterpret_cast<float4 *>(KS + (int64_t)i * g.proj + c) = make_float4(0.f, 0.f, 0.f, 0.f);
-      *reinterpret_cast<float4 *>(SS + (int64_t)i * g.proj + c) =
-          make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    if (g.ape) {
+      const float4 bias = *reinterpret_cast<const float4 *>(g.ape + (int64_t)g.slot * g.proj + c);
+      s.x += bias.x; s.y += bias.y; s.z += bias.z; s.w += bias.w;
     }
+    *reinterpret_cast<float4 *>(KS + (int64_t)g.state_row * g.proj + c) = k;
+    *reinterpret_cast<float4 *>(SS + (int64_t)g.state_row * g.proj + c) = s;
+    if (g.reset_prev) {
+      for (int i = 0; i < g.ratio; ++i) {
+        *reinterpret_cast<float4 *>(KS + (int64_t)i * g.proj + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4 *>(SS + (int64_t)i * g.proj + c) =
+            make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      }
+    }
+  }
+  if constexpr (POOL) {
+    __syncthreads();  // the state row written above is visible to the whole workgroup
+    if (threadIdx.x < kWave) small_entry<HD, R, OV>(a, b, 0, threadIdx.x);
   }
 }
 
@@ -476,10 +489,24 @@ hipError_t launch_state_store(const StateStoreArgs &s, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode_ingest(const IngestArgs &g, hipStream_t stream) {
-  const int64_t total = g.batch * (g.proj / 4);
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_ingest_kernel, dim3((uint32_t)((total + 255) / 256)), dim3(256), 0, stream, g);
+hipError_t launch_decode_finish(const IngestArgs &g, const PoolArgs *pool, int head_dim, hipStream_t stream) {
+  if (g.batch <= 0) return hipSuccess;
+  const dim3 grid((uint32_t)g.batch), block(256);
+  if (!pool) {
+    hipLaunchKernelGGL((decode_finish_kernel<512, 4, true, false>), grid, block, 0, stream, g, PoolArgs{});
+    return hipGetLastError();
+  }
+  switch (g.ratio * 10000 + head_dim) {
+    case 2 * 10000 + 512:
+      hipLaunchKernelGGL((decode_finish_kernel<512, 2, false, true>), grid, block, 0, stream, g, *pool); break;
+    case 2 * 10000 + 128:
+      hipLaunchKernelGGL((decode_finish_kernel<128, 2, false, true>), grid, block, 0, stream, g, *pool); break;
+    case 4 * 10000 + 512:
+      hipLaunchKernelGGL((decode_finish_kernel<512, 4, true, true>), grid, block, 0, stream, g, *pool); break;
+    case 4 * 10000 + 128:
+      hipLaunchKernelGGL((decode_finish_kernel<128, 4, true, true>), grid, block, 0, stream, g, *pool); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

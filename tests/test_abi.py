@@ -55,9 +55,12 @@ def test_sizes(ratio, hd, proj, rows):
 
 
 def test_decode_workspace_of_the_b64_ratio4_step():
-    # 64 rows, 2 x 1024 columns, k = 4096: 32 column tiles of 64, split in 16
+    # 64 rows, 2 x 1024 columns: 64 column tiles of 32, k split in 4 so that
+    # 256 workgroups (one per CU) share the step
     cfg = kvc.Config(4, 512, 4096)
-    assert kvc.kvc_decode_workspace_floats(cfg, 64) == 16 * 2 * 64 * 1024
+    assert kvc.kvc_decode_workspace_floats(cfg, 64) == 4 * 2 * 64 * 1024
+    # a narrower projection splits k further, at most 16 ways
+    assert kvc.kvc_decode_workspace_floats(kvc.Config(4, 128, 4096), 64) == 16 * 2 * 64 * 256
 
 
 @pytest.mark.parametrize("cfg,code", [
