@@ -62,7 +62,7 @@ def measured_traffic(name: str):
     return entry.get("bytes_per_launch")
 
 
-def pool_bytes(batch, seqlen, ratio, hd, quantize, latent):
+def pool_bytes(batch, seqlen, ratio, hd, quantize, latent, block=16):
     """Algorithmic HBM bytes of one pooling launch: every projection value
     read once (kv and score planes), outputs written once."""
     proj = 2 * hd if ratio == 4 else hd
@@ -72,7 +72,7 @@ def pool_bytes(batch, seqlen, ratio, hd, quantize, latent):
     if latent:
         write += batch * groups * hd * 2
     if quantize:
-        write += batch * groups * (hd // 2 + hd // 16)
+        write += batch * groups * (hd // 2 + hd // block)
     return read + write
 
 
@@ -165,6 +165,16 @@ def run_prefill(wl, steps, warmup, reps, torch, kvc, W):
         pbytes = pool_bytes(wl.batch, wl.seqlen, comp.ratio, comp.head_dim, comp.quantize, not comp.quantize)
         kernels[f"gemm_{tag}"] = {"ms": gemm_ms, "tflops": flops / gemm_ms / 1e9, "flop": flops}
         kernels[f"pool_{tag}"] = {"ms": pool_ms, "gbps": pbytes / pool_ms / 1e6, "bytes": pbytes}
+        if comp.head_dim == 128 and not comp.quantize:
+            # the same pooling with the index keys' fp4 form (power-of-two
+            # scales, blocks of 32) fused in place of the bf16 latent
+            cfg8 = kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps, fp4_format=kvc.KVC_FP4_E8M0_B32)
+            out8 = kvc.new_outputs(cfg8, wl.batch, groups, latent=False, fp4=True)
+            ms8 = _timed(torch, stream, lambda: kvc.compressor_prefill(cfg8, kvc.Weights(), None, wl.batch,
+                                                                       wl.seqlen, ws, None, None, out8), reps)
+            b8 = pool_bytes(wl.batch, wl.seqlen, comp.ratio, comp.head_dim, True, False, block=32)
+            kernels[f"pool_{tag}_e8m0"] = {"ms": ms8, "gbps": b8 / ms8 / 1e6, "bytes": b8}
+            del out8
     del comps, x
     torch.cuda.empty_cache()
     return {"ms_per_step": ms_per_step, "entries_per_step": entries,
@@ -218,6 +228,26 @@ def run_decode(wl, passes, torch, kvc, W):
     return {"ms_per_pass": ms, "entries_per_pass": entries, "entries_per_s": entries / (ms / 1e3),
             "us_per_step": ms * 1e3 / wl.seqlen, "tflops": flop_step * wl.seqlen / ms / 1e9,
             "eager_ms_per_pass": eager_ms}
+
+
+def run_fp4_quant(rows, width, reps, torch, kvc):
+    """Time the standalone fp4 round trips over rows x width bf16 values
+    (codes, scales and the dequantised copy written)."""
+    g = torch.Generator(device="cuda").manual_seed(7)
+    inp = torch.randn((rows, width), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(inp)
+    res = {}
+    for name, fn, blk in (("latent_e4m3_b16", kvc.latent_fp4_quant, 16),
+                          ("indexer_e8m0_b32", kvc.indexer_fp4_quant, 32)):
+        codes = torch.empty((rows, width // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((rows, width // blk), dtype=torch.uint8, device="cuda")
+        ms = _timed(torch, torch.cuda.current_stream(), lambda: fn(inp, codes, scales, out), reps)
+        nbytes = rows * width * (2 + 0.5 + 2) + rows * (width // blk)
+        res[name] = {"rows": rows, "width": width, "ms": round(ms, 4), "gbps": round(nbytes / ms / 1e6, 1),
+                     "bytes": int(nbytes)}
+    del inp, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -291,6 +321,7 @@ def main():
                             "kernels": {k: _rounded(v) for k, v in r["kernels"].items()}}
         d = run_decode(W.WORKLOADS["decode_r4_b64_s512"], 5, torch, kvc, W)
         extras["decode_r4_b64_s512"] = _rounded(d)
+        extras["fp4_quant_262144x512"] = run_fp4_quant(262144, 512, 10, torch, kvc)
         result["workloads"] = extras
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -63,12 +63,20 @@ typedef struct ihipStream_t *kvc_stream; /* a hipStream_t */
 #define KVC_ESPACE (-3)       /* a caller-provided buffer is too small */
 #define KVC_EHIP (-4)         /* the HIP runtime rejected a launch */
 
+/* fp4 forms of a compressed entry (kvc_config.fp4_format) */
+#define KVC_FP4_E4M3_B16 0 /* the KV latent's form: e4m3fn scale per block of 16 */
+#define KVC_FP4_E8M0_B32 1 /* the indexer's form: power-of-two (e8m0) scale per block of 32 */
+
 /* Compressor configuration.
- *   ratio    : 2, 4 or 128 (4 is the overlapped two-branch variant).
- *   head_dim : latent width hd, 128 or 512.
- *   dim      : hidden width of x, a positive multiple of 32 (ignored when x is
- *              NULL).
- *   eps      : RMSNorm epsilon (finite, >= 0).
+ *   ratio      : 2, 4 or 128 (4 is the overlapped two-branch variant).
+ *   head_dim   : latent width hd, 128 or 512.
+ *   dim        : hidden width of x, a positive multiple of 32 (ignored when x
+ *                is NULL).
+ *   eps        : RMSNorm epsilon (finite, >= 0).
+ *   fp4_format : form of kvc_outputs.codes / scales: KVC_FP4_E4M3_B16 (the
+ *                KV latent's, "Module compress", Functions,
+ *                fp4_quant_e4m3_inplace) or KVC_FP4_E8M0_B32 (the indexer's,
+ *                fp4_quant_e8m0_inplace; Precision paragraph: block 32).
  * proj = 2 * head_dim at ratio 4, head_dim otherwise: the width of each
  * projection plane. */
 typedef struct kvc_config {
@@ -76,6 +84,7 @@ typedef struct kvc_config {
     int32_t head_dim;
     int64_t dim;
     float eps;
+    int32_t fp4_format;
 } kvc_config;
 
 /* Weights (device, f32).
@@ -97,7 +106,9 @@ typedef struct kvc_weights {
  *   pooled  : [batch][G][head_dim] f32, the pooled value before rounding.
  *   codes   : [batch][G][head_dim / 2] e2m1 codes of the latent, two per
  *             byte, element 2k in the low nibble, sign in bit 3 of a nibble.
- *   scales  : [batch][G][head_dim / 16] e4m3fn scale of each block of 16.
+ *   scales  : [batch][G][head_dim / 16] e4m3fn scale of each block of 16, or
+ *             with KVC_FP4_E8M0_B32 [batch][G][head_dim / 32] e8m0 scale
+ *             bytes (2^(byte - 127)) of each block of 32.
  *   dequant : [batch][G][head_dim] bf16, codes times scales. */
 typedef struct kvc_outputs {
     uint16_t *latent;
@@ -190,6 +201,21 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const fl
  * Errors: KVC_EINVAL, KVC_EHIP. */
 int latent_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *codes,
                      uint8_t *scales, uint16_t *out, kvc_stream stream);
+
+/* The indexer's fp4 round trip ("Module compress", Functions,
+ * fp4_quant_e8m0_inplace; Constants, FP4_BLOCK; Precision paragraph: the
+ * indexer's q and k use power-of-two scales in blocks of 32) on [rows][width]
+ * bf16 values, per block of 32 consecutive values of a row: amax floored at
+ * 6 * 2^-126; scale = 2^e with e the smallest integer such that 2^e >= amax / 6
+ * (an IEEE f32 division); codes = e2m1(value / scale), nearest, ties to the
+ * even code, sign kept; dequant = e2m1 value * scale (exact in bf16).
+ *   in     : [rows][width] bf16.   rows >= 0, width > 0 and width % 32 == 0.
+ *   codes  : [rows][width / 2] bytes (layout as kvc_outputs.codes), or NULL.
+ *   scales : [rows][width / 32] e8m0 bytes (e + 127), or NULL.
+ *   out    : [rows][width] bf16 dequantised values, or NULL; may equal `in`.
+ * Errors: KVC_EINVAL, KVC_EHIP. */
+int indexer_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *codes,
+                      uint8_t *scales, uint16_t *out, kvc_stream stream);
 
 /* A static description of a KVC_* code. */
 const char *kvc_strerror(int code);

@@ -18,6 +18,7 @@ bool aligned(const void *p) { return p == nullptr || (reinterpret_cast<uintptr_t
 int check_config(const kvc_config *cfg) {
   if (!cfg) return KVC_EINVAL;
   if (!(cfg->eps >= 0.0f) || !isfinite(cfg->eps)) return KVC_EINVAL;
+  if (cfg->fp4_format != KVC_FP4_E4M3_B16 && cfg->fp4_format != KVC_FP4_E8M0_B32) return KVC_EINVAL;
   if (cfg->ratio != 2 && cfg->ratio != 4 && cfg->ratio != 128) return KVC_EUNSUPPORTED;
   if (cfg->head_dim != 128 && cfg->head_dim != 512) return KVC_EUNSUPPORTED;
   return KVC_OK;
@@ -71,6 +72,7 @@ kvc::PoolArgs pool_args(const kvc_config *cfg, const kvc_weights *w, const kvc_o
   p.codes = out->codes;
   p.scales = out->scales;
   p.deq = out->dequant;
+  p.e8m0 = cfg->fp4_format == KVC_FP4_E8M0_B32;
   return p;
 }
 
@@ -285,9 +287,10 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const fl
   return KVC_OK;
 }
 
-int latent_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *codes, uint8_t *scales,
-                     uint16_t *out, kvc_stream stream) {
-  if (rows < 0 || width <= 0 || width % 16 != 0) return KVC_EINVAL;
+namespace {
+int fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *codes, uint8_t *scales, uint16_t *out,
+              int block, kvc_stream stream) {
+  if (rows < 0 || width <= 0 || width % block != 0) return KVC_EINVAL;
   if (rows > 0 && !in) return KVC_EINVAL;
   if (!aligned(in) || !aligned(out) || (codes && reinterpret_cast<uintptr_t>(codes) % 4 != 0))
     return KVC_EINVAL;
@@ -297,8 +300,19 @@ int latent_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *c
     const uintptr_t b0 = reinterpret_cast<uintptr_t>(out), b1 = b0 + rows * width * 2;
     if (a0 < b1 && b0 < a1) return KVC_EINVAL;
   }
-  return hip_status(kvc::launch_fp4_quant(in, rows, width, codes, scales, out,
+  return hip_status(kvc::launch_fp4_quant(in, rows, width, codes, scales, out, block == 32,
                                           reinterpret_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int latent_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *codes, uint8_t *scales,
+                     uint16_t *out, kvc_stream stream) {
+  return fp4_quant(in, rows, width, codes, scales, out, 16, stream);
+}
+
+int indexer_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *codes, uint8_t *scales,
+                      uint16_t *out, kvc_stream stream) {
+  return fp4_quant(in, rows, width, codes, scales, out, 32, stream);
 }
 
 const char *kvc_strerror(int code) {

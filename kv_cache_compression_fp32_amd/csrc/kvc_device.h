@@ -13,8 +13,10 @@ namespace kvc {
 
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
-// amax floor of the fp4 round trip: 6 * 2^-9
+// amax floor of the latent's fp4 round trip: 6 * 2^-9
 constexpr float kAmaxFloor = 0.01171875f;
+// amax floor of the power-of-two-scaled fp4 round trip: 6 * 2^-126
+constexpr float kAmaxFloorE8m0 = 7.052966e-38f;
 
 __device__ __forceinline__ uint32_t as_u32(float f) { return __float_as_uint(f); }
 __device__ __forceinline__ float as_f32(uint32_t u) { return __uint_as_float(u); }
@@ -99,6 +101,45 @@ __device__ __forceinline__ void fp4_block(const float (&y)[VEC], uint32_t &packe
     const uint32_t c = e2m1_rne(y[v], s);
     packed |= c << (4 * v);
     deq[v] = as_u32(e2m1_val(c) * s) >> 16;  // exact: at most 6 significant bits
+  }
+}
+
+// e2m1 code (sign in bit 3) of t = |y| / scale already scaled exactly (the
+// scale a power of two): compares against the grid midpoints, a value on a
+// midpoint going to the even code.
+__device__ __forceinline__ uint32_t e2m1_code_scaled(float t, uint32_t sign) {
+  uint32_t c = (t > 0.25f) + (t >= 0.75f) + (t > 1.25f) + (t >= 1.75f) + (t > 2.5f) + (t >= 3.5f) + (t > 5.0f);
+  return c | (sign << 3);
+}
+
+// fp4 round trip with power-of-two scales (the indexer's form, "Module
+// compress", Functions, fp4_quant_e8m0_inplace) of VEC consecutive bf16
+// values per lane, 32 / VEC neighbouring lanes forming one block of 32:
+// amax floored at 6 * 2^-126, scale = 2^e with e the power-of-two ceiling
+// exponent of amax / 6 (an IEEE f32 division), codes of y / scale, dequant =
+// code value * scale. Scaling by 2^e is done with ldexp, which is exact here.
+// Returns the packed codes (element 2k in the low nibble), the e8m0 scale byte
+// (e + 127) and the bf16 bits of the dequantised values.
+template <int VEC>
+__device__ __forceinline__ void fp4_block_e8m0(const float (&y)[VEC], uint32_t &packed, uint32_t &scale_code,
+                                               uint32_t (&deq)[VEC]) {
+  static_assert(VEC >= 2 && VEC <= 8 && 32 % VEC == 0, "VEC must divide 32 and fit 32 code bits");
+  float amax = 0.0f;
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) amax = __builtin_fmaxf(amax, __builtin_fabsf(y[v]));
+#pragma unroll
+  for (int o = 1; o < 32 / VEC; o <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, o, kWave));
+  const float q = __builtin_fmaxf(amax, kAmaxFloorE8m0) / 6.0f;  // normal, >= 2^-126
+  const uint32_t qb = as_u32(q);
+  const int e = (int)(qb >> 23) - 127 + ((qb & 0x007fffffu) != 0u);
+  scale_code = (uint32_t)(e + 127);
+  packed = 0;
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    const float t = __builtin_ldexpf(__builtin_fabsf(y[v]), -e);
+    const uint32_t c = e2m1_code_scaled(t, as_u32(y[v]) >> 31);
+    packed |= c << (4 * v);
+    deq[v] = as_u32(__builtin_ldexpf(e2m1_val(c), e)) >> 16;
   }
 }
 

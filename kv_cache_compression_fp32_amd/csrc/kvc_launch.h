@@ -48,6 +48,7 @@ struct PoolArgs {
   float *pooled;
   uint8_t *codes, *scales;
   uint16_t *deq;
+  int32_t e8m0;               // codes/scales in the power-of-two, block-32 form
   int64_t out_batch_stride;   // entries per batch row in the outputs
   float *shift_kv, *shift_sc; // ratio 4: move the last block's rows to the previous rows, or null
 };
@@ -79,8 +80,9 @@ struct IngestArgs {
 };
 hipError_t launch_decode_finish(const IngestArgs &g, const PoolArgs *pool, int head_dim, hipStream_t stream);
 
-// Standalone fp4 round trip of bf16 rows.
+// Standalone fp4 round trip of bf16 rows: e4m3 scales per block of 16, or
+// (e8m0 set) power-of-two scales per block of 32.
 hipError_t launch_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *codes,
-                            uint8_t *scales, uint16_t *out, hipStream_t stream);
+                            uint8_t *scales, uint16_t *out, int e8m0, hipStream_t stream);
 
 }  // namespace kvc

@@ -148,13 +148,15 @@ __device__ __forceinline__ void finish_entry(const float (&p)[HD / kWave], const
 #pragma unroll
       for (int q = 0; q < QV; ++q) yq[q] = y[h * QV + q];
       uint32_t packed, scode, deq[QV];
-      fp4_block<QV>(yq, packed, scode, deq);
+      const int blk = a.e8m0 ? 32 : 16;
+      if (a.e8m0) fp4_block_e8m0<QV>(yq, packed, scode, deq);
+      else fp4_block<QV>(yq, packed, scode, deq);
       if (a.codes) {
         uint8_t *c = a.codes + out_row * (HD / 2) + f / 2;
         if constexpr (QV == 4) *reinterpret_cast<uint16_t *>(c) = (uint16_t)packed;
         else *c = (uint8_t)packed;
       }
-      if (a.scales && (f % 16) == 0) a.scales[out_row * (HD / 16) + f / 16] = (uint8_t)scode;
+      if (a.scales && (f % blk) == 0) a.scales[out_row * (HD / blk) + f / blk] = (uint8_t)scode;
       if (a.deq) store_bf16_q<QV>(a.deq + out_row * HD + f, deq);
     }
   }
@@ -426,9 +428,11 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(IngestArgs g, PoolAr
   }
 }
 
-// Standalone fp4 round trip: each thread owns 8 consecutive values (16 bytes),
-// two neighbouring lanes one block of 16. The value count is a multiple of 16,
-// so both lanes of a block are always in range together.
+// Standalone fp4 round trip: each thread owns 8 consecutive values (16 bytes);
+// two neighbouring lanes form a block of 16 (e4m3 scales), four a block of 32
+// (power-of-two scales). The value count is a multiple of the block, so all
+// lanes of a block are in range together.
+template <bool E8M0>
 __global__ __launch_bounds__(256) void fp4_quant_kernel(const uint16_t *in, int64_t n8, uint8_t *codes,
                                                         uint8_t *scales, uint16_t *out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -442,9 +446,11 @@ __global__ __launch_bounds__(256) void fp4_quant_kernel(const uint16_t *in, int6
     y[2 * q + 1] = bf16_val(w[q] >> 16);
   }
   uint32_t packed, scode, deq[8];
-  fp4_block<8>(y, packed, scode, deq);
+  if constexpr (E8M0) fp4_block_e8m0<8>(y, packed, scode, deq);
+  else fp4_block<8>(y, packed, scode, deq);
   if (codes) *reinterpret_cast<uint32_t *>(codes + 4 * i) = packed;
-  if (scales && (i & 1) == 0) scales[i / 2] = (uint8_t)scode;
+  constexpr int per = E8M0 ? 4 : 2;  // threads per block
+  if (scales && (i % per) == 0) scales[i / per] = (uint8_t)scode;
   if (out) {
     store_bf16_q<4>(out + 8 * i, deq);
     store_bf16_q<4>(out + 8 * i + 4, deq + 4);
@@ -511,11 +517,12 @@ hipError_t launch_decode_finish(const IngestArgs &g, const PoolArgs *pool, int h
 }
 
 hipError_t launch_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *codes, uint8_t *scales,
-                            uint16_t *out, hipStream_t stream) {
+                            uint16_t *out, int e8m0, hipStream_t stream) {
   const int64_t n8 = rows * width / 8;
   if (n8 == 0) return hipSuccess;
-  hipLaunchKernelGGL(fp4_quant_kernel, dim3((uint32_t)((n8 + 255) / 256)), dim3(256), 0, stream, in, n8, codes,
-                     scales, out);
+  const dim3 grid((uint32_t)((n8 + 255) / 256)), block(256);
+  if (e8m0) hipLaunchKernelGGL(fp4_quant_kernel<true>, grid, block, 0, stream, in, n8, codes, scales, out);
+  else hipLaunchKernelGGL(fp4_quant_kernel<false>, grid, block, 0, stream, in, n8, codes, scales, out);
   return hipGetLastError();
 }
 

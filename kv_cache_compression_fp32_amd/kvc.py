@@ -21,6 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvc.so")
 
 KVC_OK, KVC_EINVAL, KVC_EUNSUPPORTED, KVC_ESPACE, KVC_EHIP = 0, -1, -2, -3, -4
+KVC_FP4_E4M3_B16, KVC_FP4_E8M0_B32 = 0, 1
 
 _lib = None
 
@@ -33,7 +34,7 @@ class KvcError(RuntimeError):
 
 class _Config(ctypes.Structure):
     _fields_ = [("ratio", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("dim", ctypes.c_int64), ("eps", ctypes.c_float)]
+                ("dim", ctypes.c_int64), ("eps", ctypes.c_float), ("fp4_format", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
@@ -61,6 +62,7 @@ _SIGNATURES = {
                                               _P, _I64, _P, _P, _I64, ctypes.POINTER(_Outputs),
                                               ctypes.POINTER(ctypes.c_int32), _P]),
     "latent_fp4_quant": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
+    "indexer_fp4_quant": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
     "kvc_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "kvc_version": (ctypes.c_char_p, []),
 }
@@ -96,9 +98,14 @@ class Config:
     head_dim: int
     dim: int = 0
     eps: float = 1e-6
+    fp4_format: int = KVC_FP4_E4M3_B16
+
+    @property
+    def fp4_block(self) -> int:
+        return 32 if self.fp4_format == KVC_FP4_E8M0_B32 else 16
 
     def c(self) -> _Config:
-        return _Config(self.ratio, self.head_dim, self.dim, self.eps)
+        return _Config(self.ratio, self.head_dim, self.dim, self.eps, self.fp4_format)
 
 
 def kvc_proj_width(cfg: Config) -> int:
@@ -209,9 +216,7 @@ def compressor_decode_step(cfg: Config, w: Weights, x: torch.Tensor | None, batc
     return bool(e.value)
 
 
-def latent_fp4_quant(inp: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
-                     out: torch.Tensor | None = None, stream=None) -> None:
-    """Enqueue the fp4 round trip of [rows, width] bf16 values."""
+def _fp4_quant(fn, name, inp, codes, scales, out, stream):
     if inp.dim() != 2:
         raise ValueError("inp must be [rows, width]")
     if inp.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
@@ -219,9 +224,23 @@ def latent_fp4_quant(inp: torch.Tensor, codes: torch.Tensor | None = None, scale
     if out is not None and out.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
         raise TypeError("out must be bf16")
     rows, width = inp.shape
-    rc = lib().latent_fp4_quant(_ptr(inp, None, "inp"), rows, width, _ptr(codes, torch.uint8, "codes"),
-                                _ptr(scales, torch.uint8, "scales"), _ptr(out, None, "out"), _stream(stream))
-    _check(rc, "latent_fp4_quant")
+    rc = fn(_ptr(inp, None, "inp"), rows, width, _ptr(codes, torch.uint8, "codes"),
+            _ptr(scales, torch.uint8, "scales"), _ptr(out, None, "out"), _stream(stream))
+    _check(rc, name)
+
+
+def latent_fp4_quant(inp: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                     out: torch.Tensor | None = None, stream=None) -> None:
+    """Enqueue the latent's fp4 round trip (e4m3 scales, blocks of 16) of
+    [rows, width] bf16 values."""
+    _fp4_quant(lib().latent_fp4_quant, "latent_fp4_quant", inp, codes, scales, out, stream)
+
+
+def indexer_fp4_quant(inp: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None, stream=None) -> None:
+    """Enqueue the indexer's fp4 round trip (power-of-two scales, blocks of
+    32) of [rows, width] bf16 values."""
+    _fp4_quant(lib().indexer_fp4_quant, "indexer_fp4_quant", inp, codes, scales, out, stream)
 
 
 # ----------------------------------------------------------------- convenience
@@ -244,7 +263,7 @@ def new_outputs(cfg: Config, batch: int, groups: int, latent=True, pooled=False,
         o.pooled = torch.empty((batch, groups, hd), dtype=torch.float32, device=device)
     if fp4:
         o.codes = torch.empty((batch, groups, hd // 2), dtype=torch.uint8, device=device)
-        o.scales = torch.empty((batch, groups, hd // 16), dtype=torch.uint8, device=device)
+        o.scales = torch.empty((batch, groups, hd // cfg.fp4_block), dtype=torch.uint8, device=device)
     if dequant:
         o.dequant = torch.empty((batch, groups, hd), dtype=torch.bfloat16, device=device)
     return o

@@ -44,7 +44,9 @@ What it computes, step by step, in the pages' order:
    none) in the previous rows and the trailing tokens in the first current
    rows.
 7. Cache quantisation. Optionally the latent goes through the e4m3-scaled
-   block-16 fp4 round trip of formats.fp4_quant_e4m3.
+   block-16 fp4 round trip of formats.fp4_quant_e4m3 (the KV latent's form),
+   or the power-of-two-scaled block-32 one of formats.fp4_quant_e8m0 (the
+   indexer's form).
 
 Pins (tests/test_oracle_compressor.py): shape traces (16 tokens -> 4 entries,
 32 candidate slots at ratio 4), softmax weights summing to one, the convex hull
@@ -63,7 +65,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .formats import bf16_round, fp4_quant_e4m3
+from .formats import bf16_round, fp4_quant_e4m3, fp4_quant_e8m0
 
 
 @dataclass(frozen=True)
@@ -72,6 +74,7 @@ class Config:
     head_dim: int       # latent width hd
     dim: int = 0        # hidden width of x (0 when projections are given)
     eps: float = 1e-6   # RMSNorm epsilon
+    fp4: str = "e4m3"   # fp4 form of the output: "e4m3" (block 16) or "e8m0" (block 32)
 
     @property
     def overlap(self) -> bool:
@@ -194,10 +197,11 @@ def _finish(cfg: Config, w: Weights, pooled: np.ndarray, quantize: bool) -> dict
     out = {"pooled": pooled, "latent": latent}
     if quantize:
         flat = latent.reshape(-1, cfg.head_dim)
-        codes, scales, deq = fp4_quant_e4m3(flat)
+        quant, block = (fp4_quant_e8m0, 32) if cfg.fp4 == "e8m0" else (fp4_quant_e4m3, 16)
+        codes, scales, deq = quant(flat)
         lead = latent.shape[:-1]
         out["codes"] = codes.reshape(lead + (cfg.head_dim // 2,))
-        out["scales"] = scales.reshape(lead + (cfg.head_dim // 16,))
+        out["scales"] = scales.reshape(lead + (cfg.head_dim // block,))
         out["dequant"] = deq.reshape(latent.shape)
     return out
 

@@ -38,6 +38,14 @@ import numpy as np
 # Constants, LATENT_BLOCK).
 LATENT_BLOCK = 16
 
+# Values per power-of-two scale in the indexer's fp4 round trip ("Module
+# compress", Constants, FP4_BLOCK; Precision paragraph: block 32).
+FP4_BLOCK = 32
+
+# The amax floor of fp4_quant_e8m0_inplace: 6 * 2^-126, so that amax / 6 is
+# at least the smallest normal power of two.
+E8M0_AMAX_FLOOR = 6.0 * 2.0 ** -126
+
 # The amax floor of fp4_quant_e4m3_inplace: 6 * 2^-9, so that amax / 6 is at
 # least the smallest e4m3fn subnormal and the scale never flushes to zero.
 AMAX_FLOOR = 6.0 * 2.0 ** -9
@@ -234,7 +242,11 @@ def fp4_quant_e4m3(y, block: int = LATENT_BLOCK):
     # so its float64 value decides the same code as the exact quotient.
     v = blocks / scale[:, :, None]
     codes = e2m1_encode(v)
-    deq = bf16_round((e2m1_decode(codes) * scale[:, :, None]).astype(np.float32))
+    # A block whose largest magnitude lies above 3.5 * 2^126 takes scale 2^126
+    # and code 4: the decoded 2^128 lies past the f32 and bf16 range and becomes
+    # inf, as round-to-nearest does on overflow.
+    with np.errstate(over="ignore"):
+        deq = bf16_round((e2m1_decode(codes) * scale[:, :, None]).astype(np.float32))
     codes = codes.reshape(rows, width)
     packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
     return packed, scale_code.astype(np.uint8), deq.reshape(rows, width)
@@ -247,3 +259,48 @@ def fp4_unpack(packed: np.ndarray) -> np.ndarray:
     out[..., 0::2] = packed & 0xF
     out[..., 1::2] = packed >> 4
     return out
+
+
+# --------------------------------------------------------------------------
+# the indexer's fp4 round trip (power-of-two scales)
+# --------------------------------------------------------------------------
+def pow2_ceil_exponent(q) -> np.ndarray:
+    """The smallest integer e with 2^e >= q, for finite q > 0 (exact: from
+    the float64 value's frexp, q = m * 2^x with 0.5 <= m < 1)."""
+    q = np.asarray(q, dtype=np.float64)
+    if np.any(~(q > 0)) or np.any(~np.isfinite(q)):
+        raise ValueError("pow2_ceil_exponent takes finite positive values")
+    m, x = np.frexp(q)
+    return np.where(m == 0.5, x - 1, x).astype(np.int64)
+
+
+def fp4_quant_e8m0(y, block: int = FP4_BLOCK):
+    """fp4_quant_e8m0_inplace on rows of bf16 values.
+
+    Per block of `block` consecutive values of a row:
+      a     = max(max |y|, 6 * 2^-126)
+      scale = 2^e, e the power-of-two ceiling exponent of round_f32(a / 6)
+      code  = e2m1(y / scale)
+      deq   = bf16(e2m1_value(code) * scale)
+    The scale byte is the e8m0 pattern e + 127. Returns (codes [rows,
+    width/2] u8, low nibble first; scales [rows, width/block] u8; deq [rows,
+    width] float32 holding bf16 values).
+    """
+    y = np.asarray(y, dtype=np.float32)
+    if y.ndim != 2 or y.shape[1] % block:
+        raise ValueError("y must be [rows, width] with width a multiple of the block")
+    rows, width = y.shape
+    blocks = y.reshape(rows, width // block, block).astype(np.float64)
+    amax = np.maximum(np.abs(blocks).max(axis=2), E8M0_AMAX_FLOOR)
+    quotient = (amax.astype(np.float32) / np.float32(6.0)).astype(np.float32)
+    e = pow2_ceil_exponent(quotient)
+    scale = np.exp2(e.astype(np.float64))
+    codes = e2m1_encode(blocks / scale[:, :, None])  # exact quotients
+    # A block whose largest magnitude lies above 3.5 * 2^126 takes scale 2^126
+    # and code 4: the decoded 2^128 lies past the f32 and bf16 range and becomes
+    # inf, as round-to-nearest does on overflow.
+    with np.errstate(over="ignore"):
+        deq = bf16_round((e2m1_decode(codes) * scale[:, :, None]).astype(np.float32))
+    codes = codes.reshape(rows, width)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (e + 127).astype(np.uint8), deq.reshape(rows, width)

@@ -23,7 +23,10 @@ def bf16(v: float) -> float:
         return v
     m, e = math.frexp(v)          # v = m * 2^e, 0.5 <= |m| < 1
     q = round(m * 256.0)          # 8 significant bits, half to even
-    return math.ldexp(q, e - 8)
+    r = math.ldexp(q, e - 8)
+    if abs(r) >= 2.0 ** 128:      # past the largest finite bf16: overflow
+        return math.copysign(math.inf, v)
+    return r
 
 
 def dot(a, b) -> float:
@@ -170,3 +173,25 @@ class BruteCompressor:
             self.sc[:r] = [list(v) for v in self.sc[r:]]
             return res
         return self._emit(self.kv, self.sc)
+
+
+def pow2_ceil(q: float) -> int:
+    """Smallest integer e with 2^e >= q (exact, Fraction comparisons)."""
+    fq = Fraction(q)
+    e = 0
+    while Fraction(2) ** e < fq:
+        e += 1
+    while Fraction(2) ** (e - 1) >= fq:
+        e -= 1
+    return e
+
+
+def fp4_block_e8m0(y: list[float]):
+    """Power-of-two-scaled fp4 round trip of one block (any length):
+    (codes, scale byte, deq)."""
+    a = max(max(abs(v) for v in y), 6.0 * 2.0 ** -126)
+    e = pow2_ceil(f32(a / 6.0))
+    s = 2.0 ** e
+    codes = [e2m1(v, s) for v in y]
+    deq = [bf16(math.copysign(_E2M1[c & 7] * s, -1.0 if c & 8 else 1.0)) for c in codes]
+    return codes, e + 127, deq

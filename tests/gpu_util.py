@@ -72,7 +72,8 @@ def prefill(cfg: kvc.Config, w: dict, batch: int, seqlen: int, x=None, kv=None, 
 
 
 def oracle_cfg(cfg: kvc.Config) -> oracle.Config:
-    return oracle.Config(ratio=cfg.ratio, head_dim=cfg.head_dim, dim=cfg.dim, eps=cfg.eps)
+    return oracle.Config(ratio=cfg.ratio, head_dim=cfg.head_dim, dim=cfg.dim, eps=cfg.eps,
+                         fp4="e8m0" if cfg.fp4_format == kvc.KVC_FP4_E8M0_B32 else "e4m3")
 
 
 def oracle_weights(w: dict) -> oracle.Weights:

@@ -11,7 +11,7 @@
                 "flip", explained by that tolerance); there the latent is
                 within 2 ulps. Everywhere, the GPU latent is within 1 ulp of
                 the oracle's RMSNorm applied to the GPU's own pooled values.
-  fp4         : codes and scales bit-exact against the oracle's fp4 round trip
+  fp4         : (either form) codes and scales bit-exact against the oracle's fp4 round trip
                 of the GPU's own bf16 latent (the decision is taken on the
                 same input on both sides), and bit-exact against the oracle's
                 end-to-end result on every block whose latent is bitwise equal.
@@ -85,22 +85,23 @@ def check_latent(gpu_latent, gpu_pooled, ref_latent, ref_pooled, norm_w=None, ep
 
 
 def check_fp4(gpu_codes, gpu_scales, gpu_latent, ref_codes=None, ref_scales=None, ref_latent=None,
-              gpu_dequant=None):
+              gpu_dequant=None, e8m0=False):
     hd = gpu_latent.shape[-1]
+    blk = 32 if e8m0 else 16
     lat = gpu_latent.reshape(-1, hd).astype(np.float32)
-    codes, scales, deq = oracle.fp4_quant_e4m3(lat)
+    codes, scales, deq = (oracle.fp4_quant_e8m0 if e8m0 else oracle.fp4_quant_e4m3)(lat)
     gc = gpu_codes.reshape(-1, hd // 2)
-    gs = gpu_scales.reshape(-1, hd // 16)
+    gs = gpu_scales.reshape(-1, hd // blk)
     assert np.array_equal(gc, codes), f"codes: {np.sum(gc != codes)} bytes differ"
     assert np.array_equal(gs, scales), f"scales: {np.sum(gs != scales)} differ"
     if gpu_dequant is not None:
         gd = gpu_dequant.reshape(-1, hd).astype(np.float32)
         assert np.array_equal(gd.view(np.uint32), deq.view(np.uint32))
     if ref_codes is not None:
-        rl = ref_latent.reshape(-1, hd // 16, 16)
-        same_block = np.all(lat.reshape(-1, hd // 16, 16) == rl, axis=2)
-        rc = ref_codes.reshape(-1, hd // 16, 8)
-        assert np.array_equal(gc.reshape(-1, hd // 16, 8)[same_block], rc[same_block])
-        assert np.array_equal(gs[same_block], ref_scales.reshape(-1, hd // 16)[same_block])
+        rl = ref_latent.reshape(-1, hd // blk, blk)
+        same_block = np.all(lat.reshape(-1, hd // blk, blk) == rl, axis=2)
+        rc = ref_codes.reshape(-1, hd // blk, blk // 2)
+        assert np.array_equal(gc.reshape(-1, hd // blk, blk // 2)[same_block], rc[same_block])
+        assert np.array_equal(gs[same_block], ref_scales.reshape(-1, hd // blk)[same_block])
         return int((~same_block).sum()), same_block.size
     return 0, 0

@@ -138,3 +138,12 @@ def test_fp4_argument_errors():
     assert lib.latent_fp4_quant(fake, 4, 32, None, None, fake + 64, None) == kvc.KVC_EINVAL
     # nothing to do: no launch
     assert lib.latent_fp4_quant(None, 0, 32, None, None, None, None) == kvc.KVC_OK
+    # the indexer's form works on blocks of 32
+    assert lib.indexer_fp4_quant(fake, 4, 48, None, None, None, None) == kvc.KVC_EINVAL
+    assert lib.indexer_fp4_quant(None, 0, 64, None, None, None, None) == kvc.KVC_OK
+
+
+def test_fp4_format_is_checked():
+    with pytest.raises(kvc.KvcError):
+        kvc.kvc_proj_width(kvc.Config(4, 512, 4096, fp4_format=7))
+    assert kvc.kvc_proj_width(kvc.Config(4, 512, 4096, fp4_format=kvc.KVC_FP4_E8M0_B32)) == 1024

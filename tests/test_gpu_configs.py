@@ -32,35 +32,35 @@ def _sample_entries(groups, n=24, seed=0):
     return sorted(e for e in fixed | rand if 0 <= e < groups)
 
 
-def _oracle_entry(wl, comp, w, b, j):
+def _oracle_entry(wl, comp, w, b, j, fp4="e4m3"):
     """One entry from only the token rows it depends on: ratio 4 needs the
     previous block too (the slice then starts at a multiple of 4, so the bias
     rows line up), other ratios only the group itself."""
-    cfg = oracle.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps)
+    cfg = oracle.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps, fp4=fp4)
     r = comp.ratio
     if r == 4 and j > 0:
         t0, idx = r * (j - 1), 1
     else:
         t0, idx = r * j, 0
     x = W.hidden_rows(wl, b, t0, r * j + r)[None]
-    out = oracle.prefill(cfg, oracle_weights(w), oracle.State(cfg, 1), x=x, quantize=comp.quantize)
+    out = oracle.prefill(cfg, oracle_weights(w), oracle.State(cfg, 1), x=x, quantize=comp.quantize or fp4 == "e8m0")
     return {k: v[0, idx] for k, v in out.items()}
 
 
-def _check_sampled(wl, comp, w, got, entries, batch_rows):
+def _check_sampled(wl, comp, w, got, entries, batch_rows, fp4="e4m3"):
     ref = {}
     for b in batch_rows:
         for j in entries:
-            e = _oracle_entry(wl, comp, w, b, j)
+            e = _oracle_entry(wl, comp, w, b, j, fp4)
             for k, v in e.items():
                 ref.setdefault(k, []).append(v)
     ref = {k: np.stack(v) for k, v in ref.items()}
     sel = lambda a: np.stack([a[b, j] for b in batch_rows for j in entries])  # noqa: E731
     check_pooled(sel(got["pooled"]), ref["pooled"])
     check_latent(sel(got["latent"]), sel(got["pooled"]), ref["latent"], ref["pooled"], eps=wl.eps)
-    if comp.quantize:
+    if comp.quantize or fp4 == "e8m0":
         check_fp4(sel(got["codes"]), sel(got["scales"]), sel(got["latent"]), ref["codes"], ref["scales"],
-                  ref["latent"], sel(got["dequant"]))
+                  ref["latent"], sel(got["dequant"]), e8m0=fp4 == "e8m0")
 
 
 def test_pair_pool_r2_full():
@@ -171,3 +171,19 @@ def test_prefill_r4_n65536_fp4_idx128_sampled():
             # every entry: the fp4 codes of the GPU's latent, bit-exact
             check_fp4(g["codes"], g["scales"], g["latent"], gpu_dequant=g["dequant"])
         del g
+
+
+def test_prefill_r4_n65536_index_keys_power_of_two_fp4_sampled():
+    # the 128-wide indexer compressor of the long workload with its keys in
+    # the indexer's fp4 form (power-of-two scales, blocks of 32), fused
+    wl = W.WORKLOADS["prefill_r4_n65536_fp4_idx128"]
+    comp = wl.compressors[1]
+    assert comp.head_dim == 128
+    note(f"{wl.name} indexer keys e8m0")
+    xd = dev(W.hidden(wl))
+    w = W.weights(wl, comp)
+    cfg = kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps, fp4_format=kvc.KVC_FP4_E8M0_B32)
+    g = prefill(cfg, w, wl.batch, wl.seqlen, x_dev=xd, fp4=True)
+    assert g["scales"].shape == (1, 16384, 4)
+    _check_sampled(wl, comp, w, g, _sample_entries(16384, 40, seed=1), [0], fp4="e8m0")
+    check_fp4(g["codes"], g["scales"], g["latent"], gpu_dequant=g["dequant"], e8m0=True)

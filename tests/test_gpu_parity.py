@@ -26,13 +26,13 @@ def test_single_hip_runtime_is_mapped():
 
 
 # ---------------------------------------------------------------- fp4 quantiser
-def _fp4_gpu(vals_bits: np.ndarray, width: int, inplace=False):
+def _fp4_gpu(vals_bits: np.ndarray, width: int, inplace=False, e8m0=False):
     rows = vals_bits.size // width
     inp = torch.from_numpy(vals_bits.view(np.int16).reshape(rows, width).copy()).cuda()
     codes = torch.empty((rows, width // 2), dtype=torch.uint8, device="cuda")
-    scales = torch.empty((rows, width // 16), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, width // (32 if e8m0 else 16)), dtype=torch.uint8, device="cuda")
     out = inp if inplace else torch.empty_like(inp)
-    kvc.latent_fp4_quant(inp, codes, scales, out)
+    (kvc.indexer_fp4_quant if e8m0 else kvc.latent_fp4_quant)(inp, codes, scales, out)
     torch.cuda.synchronize()
     return codes.cpu().numpy(), scales.cpu().numpy(), host_bf16(out)
 
@@ -78,6 +78,40 @@ def test_fp4_quant_ragged_and_empty():
         rc, rs, rd = oracle.fp4_quant_e4m3(oracle.bf16_from_bits(y).reshape(rows, width))
         assert np.array_equal(codes, rc) and np.array_equal(scales, rs)
         assert np.array_equal(deq, rd)
+
+
+@pytest.mark.parametrize("inplace", [False, True])
+def test_indexer_fp4_quant_every_finite_bf16_value(inplace):
+    note(f"e8m0 fp4 every finite bf16 inplace={inplace}")
+    rng = np.random.default_rng(13)
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    pats = pats[np.isfinite(oracle.bf16_from_bits(pats))]
+    for arr in (pats, rng.permutation(pats)):
+        codes, scales, deq = _fp4_gpu(arr, 64, inplace, e8m0=True)
+        rc, rs, rd = oracle.fp4_quant_e8m0(oracle.bf16_from_bits(arr).reshape(-1, 64))
+        assert np.array_equal(codes, rc)
+        assert np.array_equal(scales, rs)
+        assert np.array_equal(deq.view(np.uint32), rd.view(np.uint32))
+
+
+@pytest.mark.parametrize("ratio,hd,batch,seqlen", [(4, 128, 2, 4 * 33 + 2), (4, 512, 1, 64), (128, 128, 1, 256),
+                                                   (2, 512, 2, 40)])
+def test_pool_with_power_of_two_fp4(ratio, hd, batch, seqlen):
+    note(f"pool e8m0 ratio={ratio} hd={hd}")
+    rng = np.random.default_rng(ratio + hd + seqlen)
+    cfg = kvc.Config(ratio, hd, 0, fp4_format=kvc.KVC_FP4_E8M0_B32)
+    proj = kvc.kvc_proj_width(cfg)
+    kv = rng.standard_normal((batch, seqlen, proj), dtype=np.float32)
+    sc = rng.standard_normal((batch, seqlen, proj), dtype=np.float32) * np.float32(2)
+    w = {"ape": rng.standard_normal((ratio, proj), dtype=np.float32) * np.float32(0.1)}
+    g = prefill(cfg, w, batch, seqlen, kv=kv, sc=sc)
+    ref = oracle.prefill(oracle_cfg(cfg), oracle_weights(w), oracle.State(oracle_cfg(cfg), batch), kv=kv,
+                         score=sc, quantize=True)
+    assert g["scales"].shape[-1] == hd // 32
+    check_pooled(g["pooled"], ref["pooled"])
+    check_latent(g["latent"], g["pooled"], ref["latent"], ref["pooled"])
+    check_fp4(g["codes"], g["scales"], g["latent"], ref["codes"], ref["scales"], ref["latent"], g["dequant"],
+              e8m0=True)
 
 
 # ---------------------------------------------------------------- pooling from given projections

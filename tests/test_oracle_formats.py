@@ -247,3 +247,83 @@ def test_fp4_dequant_is_exact_in_bf16():
     s = F.E4M3FN_VALUES[None, 1:]
     prod = (g * s).astype(np.float32)
     assert np.array_equal(F.bf16_round(prod), prod)
+
+
+# ---------------------------------------------------------------- e8m0 fp4 round trip
+def test_pow2_ceil_exponent_matches_brute():
+    rng = np.random.default_rng(6)
+    q = np.concatenate([np.exp2(rng.uniform(-126, 126, 500)),
+                        np.exp2(np.arange(-126, 127, dtype=np.float64)),
+                        np.nextafter(np.exp2(np.arange(-100, 100, 7, dtype=np.float64)), np.inf),
+                        np.nextafter(np.exp2(np.arange(-100, 100, 7, dtype=np.float64)), 0)])
+    ours = F.pow2_ceil_exponent(q)
+    ref = [brute.pow2_ceil(float(v)) for v in q]
+    assert list(ours) == ref
+    with pytest.raises(ValueError):
+        F.pow2_ceil_exponent(np.array([0.0]))
+
+
+def test_fp4_e8m0_special_cases():
+    # zero block: scale 2^-126 (byte 1), codes 0
+    codes, scales, deq = F.fp4_quant_e8m0(np.zeros((1, 64), dtype=np.float32))
+    assert np.all(scales == 1) and np.all(codes == 0) and np.all(deq == 0)
+    # amax exactly 6 * 2^k: scale 2^k, grid values come back exactly
+    rng = np.random.default_rng(7)
+    for k in (-20, -3, 0, 5, 40):
+        mags = rng.choice(F.E2M1_VALUES, size=32)
+        mags[7] = 6.0
+        y = (mags * rng.choice([-1.0, 1.0], 32) * 2.0 ** k).astype(np.float32)[None]
+        codes, scales, deq = F.fp4_quant_e8m0(y)
+        assert scales[0, 0] == k + 127
+        assert np.array_equal(deq, y)
+    # amax just above 6 * 2^k: the next power of two
+    y = np.zeros((1, 32), dtype=np.float32)
+    y[0, 0] = F.bf16_round(np.array([6.0 * 1.0078125], dtype=np.float32))[0]
+    _, scales, _ = F.fp4_quant_e8m0(y)
+    assert scales[0, 0] == 1 + 127
+
+
+def test_fp4_e8m0_bounds():
+    rng = np.random.default_rng(8)
+    y = F.bf16_round((rng.standard_normal((64, 128)) * np.exp2(rng.integers(-30, 30, (64, 1)))).astype(np.float32))
+    codes, scales, deq = F.fp4_quant_e8m0(y)
+    s = np.exp2(scales.astype(np.float64) - 127).repeat(32, axis=1)
+    amax = np.maximum(np.abs(y.reshape(64, 4, 32)).max(axis=2), F.E8M0_AMAX_FLOOR).repeat(32, axis=1)
+    # the power-of-two ceiling: amax / 6 <= scale < amax / 3
+    assert np.all(s >= amax / 6) and np.all(s < amax / 3)
+    # no saturation: |y / scale| <= 6, so the error is at most half the
+    # widest grid gap (4 -> 6), one scale unit
+    assert np.all(np.abs(deq.astype(np.float64) - y) <= s)
+
+
+def test_fp4_e8m0_matches_brute_fraction_implementation():
+    rng = np.random.default_rng(9)
+    y = F.bf16_round((rng.standard_normal((6, 64)) * np.exp2(rng.integers(-40, 20, (6, 1)))).astype(np.float32))
+    y[2, :32] = 0.0
+    y[3, 32:] = -0.0
+    codes, scales, deq = F.fp4_quant_e8m0(y)
+    unpacked = F.fp4_unpack(codes)
+    for r in range(6):
+        for b in range(2):
+            blk = [float(v) for v in y[r, 32 * b:32 * b + 32]]
+            bc, bs, bd = brute.fp4_block_e8m0(blk)
+            assert list(unpacked[r, 32 * b:32 * b + 32]) == bc
+            assert scales[r, b] == bs
+            assert [float(v) for v in deq[r, 32 * b:32 * b + 32]] == bd
+
+
+def test_fp4_e8m0_top_of_the_bf16_range():
+    # the largest finite bf16 value: amax / 6 lies in (2^125, 2^126], scale
+    # 2^126 (byte 253); |y| / 2^126 ~ 3.98 takes code 4, whose value 2^128 is
+    # past the bf16 range, so the dequantised value is inf; 2.98e38 (code 3,
+    # value 3 * 2^126) still comes back finite
+    top = np.float32(F.bf16_from_bits(np.array([0x7F7F], dtype=np.uint16))[0])
+    y = np.zeros((1, 32), dtype=np.float32)
+    y[0, 0], y[0, 1], y[0, 2] = top, -top, F.bf16_round(np.array([2.9e38], dtype=np.float32))[0]
+    codes, scales, deq = F.fp4_quant_e8m0(y)
+    assert scales[0, 0] == 253
+    assert deq[0, 0] == np.inf and deq[0, 1] == -np.inf
+    assert deq[0, 2] == np.float32(3.0 * 2.0 ** 126)
+    bc, bs, bd = brute.fp4_block_e8m0([float(v) for v in y[0]])
+    assert list(F.fp4_unpack(codes)[0]) == bc and bs == 253
+    assert [float(v) for v in deq[0]] == bd
