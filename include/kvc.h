@@ -70,8 +70,8 @@ typedef struct ihipStream_t *kvc_stream; /* a hipStream_t */
 /* Compressor configuration.
  *   ratio      : 2, 4 or 128 (4 is the overlapped two-branch variant).
  *   head_dim   : latent width hd, 128 or 512.
- *   dim        : hidden width of x, a positive multiple of 32 (ignored when x
- *                is NULL).
+ *   dim        : hidden width of x, a positive multiple of 32 and at most
+ *                2^20 (KVC_EUNSUPPORTED otherwise; ignored when x is NULL).
  *   eps        : RMSNorm epsilon (finite, >= 0).
  *   fp4_format : form of kvc_outputs.codes / scales: KVC_FP4_E4M3_B16 (the
  *                KV latent's, "Module compress", Functions,

@@ -1,21 +1,18 @@
-// fp32 matrix-core GEMM kernel template of the compressor's projections
-// (gfx950, wave64). Included by gemm_f32.hip, which picks the instances.
+// fp32 matrix-core GEMM kernels of the compressor's projections (gfx950,
+// wave64). Included by gemm_f32.hip, which picks the instances.
 //
 // C_h[m][n] = sum_k A[m][k] * B_h[n][k] for the two column halves h of the
 // output (kv with wkv, score with wgate): "Module compress", Functions,
 // linear_f32 (w is [out_dim, in_dim]); "DeepSeek V4.1 . Pool token pairs",
 // Compressor listing, forward.
 //
-// Matrix-core layouts used (lane l of a wavefront):
-//   v_mfma_f32_16x16x4_f32: A[l % 16][k-slot l / 16], B[k-slot l / 16][l % 16];
-//     accumulator r holds D[4 (l / 16) + r][l % 16].
-//   v_mfma_f32_32x32x2_f32: A[l % 32][k-slot l / 32], B[k-slot l / 32][l % 32];
-//     accumulator r holds D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
-// LDS holds each k tile as [k / 4][row][4] floats (plus one padding row per
-// k-group so the 16-byte stores of 8 neighbouring threads hit distinct banks).
-// One ds_read_b128 gives a lane 4 consecutive k of its row; MFMA t of a chunk
-// takes element t, so k-slot q of MFMA t holds k = chunk_base + 4 q + t for
-// both operands and every k is covered once.
+// Matrix-core layout used (lane l of a wavefront), v_mfma_f32_16x16x4_f32:
+//   A[l % 16][k-slot l / 16], B[k-slot l / 16][l % 16]; accumulator r holds
+//   D[4 (l / 16) + r][l % 16].
+// One ds_read_b128 gives a lane 4 consecutive k of its row; MFMA t of a 16-k
+// chunk takes element t, so k-slot q of MFMA t holds k = chunk_base + 4 q + t
+// for both operands and every k is covered once, in the same order for every
+// output element.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,182 +24,63 @@ namespace kvc {
 namespace gemm {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
-typedef float f16v __attribute__((ext_vector_type(16)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t id, uint32_t n) {
   const uint32_t q = n / 8, r = n % 8, x = id % 8, local = id / 8;
   return (x < r) ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
 }
 
-constexpr int kBK = 32;       // k per LDS tile
-constexpr int kKG = kBK / 4;  // k-groups of 4 per tile
+// Buffer load of 16 bytes per lane straight into LDS: lane l's bytes land at
+// M0 + 16 l, M0 being the (wavefront-uniform) LDS address passed here.
+__device__ void buffer_load_lds(i32x4 rsrc, lds_u32 *lds, int32_t size, int32_t voffset, int32_t soffset,
+                                int32_t offset, int32_t aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
-// MFMA shape traits. KS = k-slots per MFMA (lanes split into KS groups);
-// a chunk covers 4 * KS k (one b128 read per fragment, 4 MFMAs).
-template <bool BIG> struct Mfma;
-template <> struct Mfma<false> {
-  static constexpr int D = 16, KS = 4, ACC = 4;
-  typedef f4 acc_t;
-  __device__ static acc_t run(float a, float b, acc_t c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
-  __device__ static int row(int lane, int r) { return 4 * (lane >> 4) + r; }
-};
-template <> struct Mfma<true> {
-  static constexpr int D = 32, KS = 2, ACC = 16;
-  typedef f16v acc_t;
-  __device__ static acc_t run(float a, float b, acc_t c) { return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0); }
-  __device__ static int row(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-};
-
-// BM x BN workgroup tile, WM x WN per wavefront, NW wavefronts.
-template <int BM, int BN, int WM, int WN, int NW, bool BIG, int MINW>
-__global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
-  using M = Mfma<BIG>;
-  constexpr int NT = NW * 64;
-  constexpr int WAVES_N = BN / WN;
-  static_assert((BM / WM) * (BN / WN) == NW, "wavefront grid must cover the tile");
-  constexpr int FM = WM / M::D, FN = WN / M::D;
-  constexpr int CH = 4 * M::KS;                  // k per chunk
-  constexpr int NCH = kBK / CH;                  // chunks per tile
-  constexpr int AL = BM * kKG / NT, BL = BN * kKG / NT;
-  static_assert(AL >= 1 && BL >= 1 && BM * kKG % NT == 0 && BN * kKG % NT == 0, "tile/thread mismatch");
-  constexpr int AP = BM + 1, BP = BN + 1;
-  __shared__ f4 As[2][kKG][AP];
-  __shared__ f4 Bs[2][kKG][BP];
-
-  const int64_t m_tiles = (g.m + BM - 1) / BM;
-  const int64_t n_tiles = 2 * g.n_half / BN;
-  const uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t mt = tile / n_tiles, nt = tile - mt * n_tiles;
-  if (mt >= m_tiles) return;
-  const int64_t m0 = mt * BM;
-  const int64_t n_glob = nt * BN;
-  const bool second = n_glob >= g.n_half;
-  const int64_t n0 = second ? n_glob - g.n_half : n_glob;
-  const float *__restrict__ B = second ? g.b1 : g.b0;
-  float *__restrict__ C = (second ? g.c1 : g.c0) + (int64_t)blockIdx.y * g.c_split_stride;
-  const int64_t k_len = g.k / g.splits;
-  const int64_t k_begin = (int64_t)blockIdx.y * k_len;
-  const int kt_count = (int)(k_len / kBK);
-
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-
-  // global -> register prefetch: load u of thread t covers row (t + NT u) / kKG,
-  // k-group (t + NT u) % kKG; eight threads read one 128-byte row segment
-  const float *a_src[AL];
-  const float *b_src[BL];
-#pragma unroll
-  for (int u = 0; u < AL; ++u) {
-    const int li = t + NT * u, r = li / kKG, q = li % kKG;
-    int64_t row = m0 + r;
-    if (row >= g.m) row = g.m - 1;  // ragged last tile: read a valid row, never store it
-    a_src[u] = g.a + row * g.lda + k_begin + 4 * q;
-  }
-#pragma unroll
-  for (int u = 0; u < BL; ++u) {
-    const int li = t + NT * u, r = li / kKG, q = li % kKG;
-    b_src[u] = B + (n0 + r) * g.ldb + k_begin + 4 * q;
-  }
-  f4 ra[AL], rb[BL];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int u = 0; u < AL; ++u) ra[u] = *reinterpret_cast<const f4 *>(a_src[u] + kt * kBK);
-#pragma unroll
-    for (int u = 0; u < BL; ++u) rb[u] = *reinterpret_cast<const f4 *>(b_src[u] + kt * kBK);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < AL; ++u) {
-      const int li = t + NT * u;
-      As[buf][li % kKG][li / kKG] = ra[u];
-    }
-#pragma unroll
-    for (int u = 0; u < BL; ++u) {
-      const int li = t + NT * u;
-      Bs[buf][li % kKG][li / kKG] = rb[u];
-    }
-  };
-
-  typename M::acc_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = typename M::acc_t{};
-
-  const int row_in = lane % M::D, slot = lane / M::D;
-  // fragments of two chunks: the next chunk's reads are issued before the
-  // current chunk's MFMAs
-  f4 fa[2][FM], fb[2][FN];
-  auto fload = [&](int buf, int c, int s) {
-    const int q = c * M::KS + slot;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) fa[s][i] = As[buf][q][wm * WM + M::D * i + row_in];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) fb[s][j] = Bs[buf][q][wn * WN + M::D * j + row_in];
-  };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < kt_count; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < kt_count) gload(kt + 1);
-    fload(buf, 0, 0);
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      if (c + 1 < NCH) fload(buf, c + 1, (c + 1) & 1);
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = M::run(fa[c & 1][i][s], fb[c & 1][j][s], acc[i][j]);
-    }
-    if (kt + 1 < kt_count) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  const float *bias = second ? g.bias1 : nullptr;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int r = 0; r < M::ACC; ++r) {
-      const int64_t row = m0 + wm * WM + M::D * i + M::row(lane, r);
-      if (row < g.m) {
-        float *crow = C + row * g.ldc + n0 + wn * WN + row_in;
-        if (bias) {
-          const float *brow = bias + ((row % g.bias_seqlen) % g.bias_ratio) * g.ldc + n0 + wn * WN + row_in;
-#pragma unroll
-          for (int j = 0; j < FN; ++j) crow[M::D * j] = acc[i][j][r] + brow[M::D * j];
-        } else {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) crow[M::D * j] = acc[i][j][r];
-        }
-      }
-    }
+// Raw buffer resource (stride 0, 32-bit elements) over num_bytes from base.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = (int32_t)(uint32_t)a;
+  r.y = (int32_t)((uint32_t)(a >> 32) & 0xffffu);
+  r.z = (int32_t)num_bytes;
+  r.w = 0x00020000;
+  return r;
 }
 
-// Single-LDS-buffer variant with a deeper k tile: BK k per tile (16 k-groups
-// at BK = 64), so sixteen neighbouring threads load one 256-byte row segment
-// and their 16-byte LDS stores land on 16 distinct bank groups (row pitch of
-// BM + 1 k-groups). The next tile is prefetched into registers while the
-// current one is multiplied; two barriers per tile (reads done, stores done),
-// covered by the second workgroup on the CU. Fragments of the next 16-k chunk
-// are read from LDS before the current chunk's MFMAs.
-template <int BM, int BN, int WM, int WN, int NW, int BK, int MINW>
-__global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_sb_kernel(GemmArgs g) {
-  using M = Mfma<false>;
-  constexpr int NT = NW * 64;
-  constexpr int KG = BK / 4;
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+constexpr int kBK = 32;  // k per LDS stage
+
+// Prefill projection: BM x BN workgroup tile, WM x WN per wavefront, NW
+// wavefronts, two LDS stages of 32 k each. Tiles are loaded with buffer loads
+// that write LDS directly (no registers, no LDS store instructions); each load
+// instruction of a wavefront fills 1 KiB of LDS: 8 rows of 32 k. LDS holds a
+// stage as [rows][32] floats with the 16-byte k-group q of row r at group
+// position q ^ (r & 7), so the fragment reads of 8 neighbouring rows hit 8
+// distinct bank groups.
+// Per tile: the fragments of the first 16-k chunk are read, the second chunk's
+// reads are issued behind the first chunk's MFMAs, the next tile's loads go
+// out after the tile's last LDS read (to the other stage, which every
+// wavefront finished reading before the last barrier), then wait + barrier.
+// With DEFER, the tile's last k-slice of MFMAs (operands already in
+// registers) runs after the barrier, behind the next tile's first LDS reads.
+// Rows of a ragged last row tile are clamped to the last row of A (loaded,
+// never stored).
+template <int BM, int BN, int WM, int WN, int NW, int MINW, bool DEFER>
+__global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
+  constexpr int BK = kBK, G = BK / 4;
   constexpr int WAVES_N = BN / WN;
   static_assert((BM / WM) * (BN / WN) == NW, "wavefront grid must cover the tile");
+  static_assert(G == 8, "the k-group swizzle assumes 8 groups per row");
   constexpr int FM = WM / 16, FN = WN / 16;
   constexpr int NCH = BK / 16;
-  constexpr int AL = BM * KG / NT, BL = BN * KG / NT;
-  static_assert(AL >= 1 && BL >= 1 && BM * KG % NT == 0 && BN * KG % NT == 0, "tile/thread mismatch");
-  constexpr int AP = BM + 1, BP = BN + 1;
-  __shared__ f4 As[KG][AP];
-  __shared__ f4 Bs[KG][BP];
+  constexpr int LAST = (NCH - 1) & 1;  // fragment slot of a tile's last chunk
+  constexpr int A_INS = BM * BK / 256 / NW, B_INS = BN * BK / 256 / NW;  // 1 KiB loads per wavefront
+  static_assert(A_INS >= 1 && B_INS >= 1 && BM * BK % (256 * NW) == 0 && BN * BK % (256 * NW) == 0,
+                "tile/wavefront mismatch");
+  __shared__ __attribute__((aligned(16))) float As[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) float Bs[2][BN * BK];
 
   const int64_t m_tiles = (g.m + BM - 1) / BM;
   const int64_t n_tiles = 2 * g.n_half / BN;
@@ -221,38 +99,33 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_sb_kernel(GemmArgs g) 
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const float *a_src[AL];
-  const float *b_src[BL];
+
+  // Load u of this wavefront fills LDS bytes [1 KiB (wave INS + u), +1 KiB):
+  // lane l -> row 8 (wave INS + u) + l / 8, group position l % 8, which holds
+  // k-group lq = (l % 8) ^ ((l / 8) & 7). Buffer resources start at the
+  // tile's first row; the k offset is wavefront-uniform.
+  const int64_t a_rows = (g.m - m0 < BM) ? (g.m - m0) : BM;
+  const i32x4 a_rsrc = make_rsrc(g.a + m0 * g.lda, (uint32_t)(a_rows * g.lda * 4));
+  const i32x4 b_rsrc = make_rsrc(B + n0 * g.ldb, (uint32_t)(BN * g.ldb * 4));
+  const int lr = lane / G, lq = (lane % G) ^ (lr & 7);
+  uint32_t a_voff[A_INS];
 #pragma unroll
-  for (int u = 0; u < AL; ++u) {
-    const int li = t + NT * u, r = li / KG, q = li % KG;
-    int64_t row = m0 + r;
-    if (row >= g.m) row = g.m - 1;  // ragged last tile: read a valid row, never store it
-    a_src[u] = g.a + row * g.lda + k_begin + 4 * q;
+  for (int u = 0; u < A_INS; ++u) {
+    int64_t r = 8 * (wave * A_INS + u) + lr;
+    if (r >= a_rows) r = a_rows - 1;  // ragged last tile: read a valid row, never store it
+    a_voff[u] = (uint32_t)((r * g.lda + 4 * lq) * 4);
   }
+  const uint32_t b_voff = (uint32_t)(((8 * wave * B_INS + lr) * g.ldb + 4 * lq) * 4);
+  auto issue = [&](int kt, int st) {
+    const uint32_t koff = (uint32_t)((k_begin + (int64_t)kt * BK) * 4);
 #pragma unroll
-  for (int u = 0; u < BL; ++u) {
-    const int li = t + NT * u, r = li / KG, q = li % KG;
-    b_src[u] = B + (n0 + r) * g.ldb + k_begin + 4 * q;
-  }
-  f4 ra[AL], rb[BL];
-  auto gload = [&](int kt) {
+    for (int u = 0; u < A_INS; ++u)
+      buffer_load_lds(a_rsrc, (lds_u32 *)(&As[st][256 * (wave * A_INS + u)]), 16, (int32_t)a_voff[u],
+                      (int32_t)koff, 0, 0);
 #pragma unroll
-    for (int u = 0; u < AL; ++u) ra[u] = *reinterpret_cast<const f4 *>(a_src[u] + kt * BK);
-#pragma unroll
-    for (int u = 0; u < BL; ++u) rb[u] = *reinterpret_cast<const f4 *>(b_src[u] + kt * BK);
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int u = 0; u < AL; ++u) {
-      const int li = t + NT * u;
-      As[li % KG][li / KG] = ra[u];
-    }
-#pragma unroll
-    for (int u = 0; u < BL; ++u) {
-      const int li = t + NT * u;
-      Bs[li % KG][li / KG] = rb[u];
-    }
+    for (int u = 0; u < B_INS; ++u)
+      buffer_load_lds(b_rsrc, (lds_u32 *)(&Bs[st][256 * (wave * B_INS + u)]), 16, (int32_t)b_voff,
+                      (int32_t)(koff + (uint32_t)(8 * u * g.ldb * 4)), 0, 0);
   };
 
   f4 acc[FM][FN];
@@ -263,44 +136,60 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_sb_kernel(GemmArgs g) 
 
   const int row_in = lane & 15, slot = lane >> 4;
   f4 fa[2][FM], fb[2][FN];
-  auto fload = [&](int c, int sl) {
+  auto fload = [&](int st, int c, int sl) {
     const int q = c * 4 + slot;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) fa[sl][i] = As[q][wm * WM + 16 * i + row_in];
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WM + 16 * i + row_in;
+      fa[sl][i] = *reinterpret_cast<const f4 *>(&As[st][r * BK + 4 * (q ^ (r & 7))]);
+    }
 #pragma unroll
-    for (int j = 0; j < FN; ++j) fb[sl][j] = Bs[q][wn * WN + 16 * j + row_in];
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * WN + 16 * j + row_in;
+      fb[sl][j] = *reinterpret_cast<const f4 *>(&Bs[st][r * BK + 4 * (q ^ (r & 7))]);
+    }
+  };
+  auto mfma_slice = [&](int sl, int s) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[sl][i][s], fb[sl][j][s], acc[i][j], 0, 0, 0);
   };
 
-  gload(0);
-  lstore();
+  issue(0, 0);
+  wait_vm0();
   __syncthreads();
-  fload(0, 0);
   for (int kt = 0; kt < kt_count; ++kt) {
-    if (kt + 1 < kt_count) gload(kt + 1);
+    const int st = kt & 1;
+    fload(st, 0, 0);
+    if (DEFER && kt > 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_slice(LAST, 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      if (c + 1 < NCH) fload(c + 1, (c + 1) & 1);
+      if (c + 1 < NCH) fload(st, c + 1, (c + 1) & 1);
+      // unconditional, so the loop body stays one block: the last iteration
+      // reloads its own tile into the idle stage, which is never read
+      if (c == NCH - 1) issue(kt + 1 < kt_count ? kt + 1 : kt, st ^ 1);
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = M::run(fa[c & 1][i][s], fb[c & 1][j][s], acc[i][j]);
+        if (!(DEFER && c == NCH - 1 && s == 3)) mfma_slice(c & 1, s);
     }
-    __syncthreads();  // every wavefront is done reading this tile
-    if (kt + 1 < kt_count) {
-      lstore();
-      __syncthreads();  // the next tile is in LDS
-      fload(0, 0);
-    }
+    __builtin_amdgcn_sched_barrier(0);  // the tile's MFMAs stay ahead of the wait
+    wait_vm0();                         // this wavefront's loads of the next tile landed
+    __syncthreads();                    // everyone's landed; everyone is done reading this stage
   }
+  if (DEFER) mfma_slice(LAST, 3);
 
   const float *bias = second ? g.bias1 : nullptr;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t row = m0 + wm * WM + 16 * i + M::row(lane, r);
+      const int64_t row = m0 + wm * WM + 16 * i + 4 * slot + r;
       if (row < g.m) {
         float *crow = C + row * g.ldc + n0 + wn * WN + row_in;
         if (bias) {
@@ -313,18 +202,6 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_sb_kernel(GemmArgs g) 
         }
       }
     }
-}
-
-template <int BM, int BN, int WM, int WN, int NW, int BK, int MINW>
-hipError_t launch_sb(const GemmArgs &g, hipStream_t stream) {
-  if (g.n_half % BN != 0 || g.splits < 1 || g.k % (BK * g.splits) != 0 || (g.bias1 && g.splits != 1) ||
-      (g.bias1 && (g.bias_seqlen < 1 || g.bias_ratio < 1)))
-    return hipErrorInvalidValue;
-  const int64_t m_tiles = (g.m + BM - 1) / BM;
-  const int64_t n_tiles = 2 * g.n_half / BN;
-  hipLaunchKernelGGL((gemm_f32_sb_kernel<BM, BN, WM, WN, NW, BK, MINW>),
-                     dim3((uint32_t)(m_tiles * n_tiles), (uint32_t)g.splits), dim3(NW * 64), 0, stream, g);
-  return hipGetLastError();
 }
 
 // Decode projection (M = batch rows, 64 per row tile in blockIdx.z): 32
@@ -432,15 +309,17 @@ inline hipError_t launch_decode_gemm(const GemmArgs &g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int NW, bool BIG, int MINW>
+template <int BM, int BN, int WM, int WN, int NW, int MINW, bool DEFER>
 hipError_t launch_tiled(const GemmArgs &g, hipStream_t stream) {
-  // every column tile must lie inside one half, every split cover whole k tiles
+  // every column tile inside one half, every split whole k tiles, and a
+  // tile's rows addressable by a 32-bit buffer offset
   if (g.n_half % BN != 0 || g.splits < 1 || g.k % (kBK * g.splits) != 0 || (g.bias1 && g.splits != 1) ||
-      (g.bias1 && (g.bias_seqlen < 1 || g.bias_ratio < 1)))
+      (g.bias1 && (g.bias_seqlen < 1 || g.bias_ratio < 1)) || g.lda < g.k || g.ldb < g.k ||
+      (int64_t)BM * g.lda * 4 > INT32_MAX || (int64_t)BN * g.ldb * 4 > INT32_MAX)
     return hipErrorInvalidValue;
   const int64_t m_tiles = (g.m + BM - 1) / BM;
   const int64_t n_tiles = 2 * g.n_half / BN;
-  hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, WM, WN, NW, BIG, MINW>),
+  hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, WM, WN, NW, MINW, DEFER>),
                      dim3((uint32_t)(m_tiles * n_tiles), (uint32_t)g.splits), dim3(NW * 64), 0, stream, g);
   return hipGetLastError();
 }

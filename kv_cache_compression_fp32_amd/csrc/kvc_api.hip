@@ -12,6 +12,9 @@
 namespace {
 
 constexpr int64_t kAlign = 16;  // bytes; every device pointer is accessed in 16-byte vectors
+// hidden width limit: a 256-row tile of x (or of a weight) must be addressable
+// with 32-bit byte offsets by the projection kernel's buffer loads
+constexpr int64_t kMaxDim = int64_t(1) << 20;
 
 bool aligned(const void *p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
 
@@ -31,7 +34,7 @@ int64_t rows_of(const kvc_config *cfg) { return overlapped(cfg) ? 2 * (int64_t)c
 int check_projection_inputs(const kvc_config *cfg, const kvc_weights *w) {
   if (!w || !w->wkv || !w->wgate) return KVC_EINVAL;
   if (cfg->dim <= 0) return KVC_EINVAL;
-  if (cfg->dim % 32 != 0) return KVC_EUNSUPPORTED;
+  if (cfg->dim % 32 != 0 || cfg->dim > kMaxDim) return KVC_EUNSUPPORTED;
   if (!aligned(w->wkv) || !aligned(w->wgate)) return KVC_EINVAL;
   return KVC_OK;
 }

@@ -103,6 +103,9 @@ def test_prefill_argument_errors_return_before_enqueueing():
     # x given with a hidden width that is not a multiple of 32
     w = kvc._Weights(fake, fake, None, None)
     assert _prefill_raw(kvc.Config(4, 512, 100), x=fake, w=w, ws=fake, ws_n=1 << 30)[0] == kvc.KVC_EUNSUPPORTED
+    # or one too wide for 32-bit tile offsets
+    assert _prefill_raw(kvc.Config(4, 512, (1 << 20) + 32), x=fake, w=w, ws=fake,
+                        ws_n=1 << 40)[0] == kvc.KVC_EUNSUPPORTED
     # misaligned pointer
     assert _prefill_raw(cfg, x=fake + 4, w=w, ws=fake, ws_n=1 << 30)[0] == kvc.KVC_EINVAL
     # one state plane without the other, or a state smaller than the batch
