@@ -47,6 +47,14 @@ What it computes, step by step, in the pages' order:
    block-16 fp4 round trip of formats.fp4_quant_e4m3 (the KV latent's form),
    or the power-of-two-scaled block-32 one of formats.fp4_quant_e8m0 (the
    indexer's form).
+8. Ratio 1 (plain_projection). No gate, no pooling, no state: every token is
+   one entry, latent = RMSNorm(wkv(x)) in the checkpoint's bf16 (Compressor
+   listing, __init__ and the ratio-1 branch of forward; "Module compress",
+   CompressorWeights: wkv holds bf16 values at ratio 1). Reading: x and wkv
+   hold bf16 values; the linear sums the exact products and rounds once to f32
+   (the accumulator of a bf16 matrix product), which is rounded to bf16 (the
+   linear's output dtype) and normalised as in step 5. "pooled" holds the f32
+   projection.
 
 Pins (tests/test_oracle_compressor.py): shape traces (16 tokens -> 4 entries,
 32 candidate slots at ratio 4), softmax weights summing to one, the convex hull
@@ -70,7 +78,7 @@ from .formats import bf16_round, fp4_quant_e4m3, fp4_quant_e8m0
 
 @dataclass(frozen=True)
 class Config:
-    ratio: int          # compress ratio: 2, 4 (overlapped) or 128
+    ratio: int          # compress ratio: 1 (plain projection), 2, 4 (overlapped) or 128
     head_dim: int       # latent width hd
     dim: int = 0        # hidden width of x (0 when projections are given)
     eps: float = 1e-6   # RMSNorm epsilon
@@ -279,3 +287,19 @@ def decode_step(cfg: Config, w: Weights, state: State, start_pos: int, x=None,
         state.kv[:batch, :r] = state.kv[:batch, r:]
         state.score[:batch, :r] = state.score[:batch, r:]
     return _finish(cfg, w, pooled, quantize)
+
+
+def plain_projection(cfg: Config, w: Weights, x: np.ndarray, quantize: bool = False) -> dict:
+    """The ratio-1 compressor over [..., dim] x (bf16 values in float32
+    arrays) with wkv [hd, dim] (bf16 values): every token gives one entry.
+    Returns pooled (the f32 projection), latent and, with quantize, codes /
+    scales / dequant, each with x's leading shape."""
+    if cfg.ratio != 1:
+        raise ValueError("plain_projection is the ratio-1 compressor")
+    x = np.asarray(x, dtype=np.float32)
+    wkv = np.asarray(w.wkv, dtype=np.float32)
+    if not (np.array_equal(bf16_round(x), x) and np.array_equal(bf16_round(wkv), wkv)):
+        raise ValueError("x and wkv must hold bf16 values at ratio 1")
+    if wkv.shape != (cfg.head_dim, x.shape[-1]):
+        raise ValueError("wkv must be [head_dim, dim]")
+    return _finish(cfg, w, project(x, wkv), quantize)

@@ -195,3 +195,13 @@ def fp4_block_e8m0(y: list[float]):
     codes = [e2m1(v, s) for v in y]
     deq = [bf16(math.copysign(_E2M1[c & 7] * s, -1.0 if c & 8 else 1.0)) for c in codes]
     return codes, e + 127, deq
+
+
+def plain_projection(xs, wkv, eps=1e-6):
+    """Ratio-1 compressor over a list of token vectors (bf16 values): for each
+    token, (f32 projection, latent) with an exactly rounded dot product."""
+    out = []
+    for x in xs:
+        p = [f32(dot(x, w)) for w in wkv]
+        out.append((p, rmsnorm(p, eps)))
+    return out

@@ -274,3 +274,64 @@ def test_fp4_output_of_prefill_matches_standalone_quant():
     assert np.array_equal(out["codes"].reshape(-1, 32), codes)
     assert np.array_equal(out["scales"].reshape(-1, 4), scales)
     assert np.array_equal(out["dequant"].reshape(-1, 64), deq)
+
+
+# ---------------------------------------------------------------- ratio 1
+def _bf16_rand(rng, shape, std):
+    return oracle.bf16_round((rng.standard_normal(shape) * std).astype(np.float32))
+
+
+def test_plain_projection_matches_pure_python():
+    rng = np.random.default_rng(41)
+    hd, dim, n = 16, 24, 5
+    x = _bf16_rand(rng, (n, dim), 1.0)
+    wkv = _bf16_rand(rng, (hd, dim), 0.2)
+    cfg = Config(ratio=1, head_dim=hd, dim=dim)
+    out = oracle.plain_projection(cfg, Weights(wkv=wkv), x)
+    ref = brute.plain_projection([[float(v) for v in row] for row in x], [[float(v) for v in row] for row in wkv])
+    for t in range(n):
+        assert [float(v) for v in out["pooled"][t]] == ref[t][0]
+        assert [float(v) for v in out["latent"][t]] == ref[t][1]
+
+
+def test_plain_projection_one_hot_token_reads_a_weight_column():
+    rng = np.random.default_rng(42)
+    hd, dim = 32, 64
+    wkv = _bf16_rand(rng, (hd, dim), 0.02)
+    x = np.zeros((3, dim), dtype=np.float32)
+    for t, i in enumerate((0, 17, 63)):
+        x[t, i] = 1.0
+    out = oracle.plain_projection(Config(ratio=1, head_dim=hd, dim=dim), Weights(wkv=wkv), x)
+    for t, i in enumerate((0, 17, 63)):
+        assert np.array_equal(out["pooled"][t], wkv[:, i])
+        # bf16 of a bf16 value is itself: the latent is the RMSNorm of the column
+        u = wkv[:, i].astype(np.float64)
+        ref = oracle.bf16_round(u / np.sqrt((u * u).mean() + 1e-6))
+        assert np.array_equal(out["latent"][t], ref)
+
+
+def test_plain_projection_scale_invariance_and_token_independence():
+    rng = np.random.default_rng(43)
+    hd, dim, n = 64, 128, 6
+    x = _bf16_rand(rng, (n, dim), 1.0)
+    wkv = _bf16_rand(rng, (hd, dim), 0.02)
+    cfg = Config(ratio=1, head_dim=hd, dim=dim, eps=0.0)
+    base = oracle.plain_projection(cfg, Weights(wkv=wkv), x)
+    # x * 2^k: exact in bf16, projections scale exactly, RMSNorm (eps 0) is unchanged
+    for k in (-5, 3):
+        scaled = oracle.plain_projection(cfg, Weights(wkv=wkv), x * np.float32(2.0 ** k))
+        assert np.array_equal(scaled["pooled"], base["pooled"] * np.float32(2.0 ** k))
+        assert np.array_equal(scaled["latent"], base["latent"])
+    # no state, no mixing: a permutation of the tokens permutes the entries
+    perm = rng.permutation(n)
+    moved = oracle.plain_projection(cfg, Weights(wkv=wkv), x[perm])
+    assert np.array_equal(moved["latent"], base["latent"][perm])
+
+
+def test_plain_projection_checks_its_inputs():
+    cfg = Config(ratio=1, head_dim=16, dim=8)
+    w = Weights(wkv=np.ones((16, 8), dtype=np.float32))
+    with pytest.raises(ValueError):
+        oracle.plain_projection(cfg, w, np.full((2, 8), 0.1, dtype=np.float32))  # not a bf16 value
+    with pytest.raises(ValueError):
+        oracle.plain_projection(Config(ratio=4, head_dim=16, dim=8), w, np.ones((2, 8), dtype=np.float32))
