@@ -32,11 +32,13 @@ sys.path.insert(0, ROOT)
 METRIC = "compressed KV entries/sec + achieved HBM GB/s, ratio-4 prefill N=65536"
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # the sources each counted kernel is built from (the traffic figures turn
 # null as soon as any of them changes)
 KERNEL_SOURCES = {
-    "gemm": ["kv_cache_compression_fp32_amd/csrc/gemm_f32_kernel.h", "kv_cache_compression_fp32_amd/csrc/gemm_f32.hip"],
+    "gemm": ["kv_cache_compression_fp32_amd/csrc/gemm_common.h", "kv_cache_compression_fp32_amd/csrc/gemm_f32_kernel.h",
+             "kv_cache_compression_fp32_amd/csrc/gemm_f32.hip"],
     "pool": ["kv_cache_compression_fp32_amd/csrc/pool.hip", "kv_cache_compression_fp32_amd/csrc/kvc_device.h"],
 }
 
@@ -230,6 +232,41 @@ def run_decode(wl, passes, torch, kvc, W):
             "eager_ms_per_pass": eager_ms}
 
 
+def run_ratio1(wl, steps, warmup, reps, torch, kvc, W):
+    """Time the ratio-1 compressor over the whole workload (every token one
+    entry), then its projection alone."""
+    comp = wl.compressors[0]
+    cfg = kvc.Config(1, comp.head_dim, wl.dim, wl.eps)
+    print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
+    tokens = wl.batch * wl.seqlen
+    x = torch.from_numpy(W.hidden(wl).reshape(tokens, wl.dim)).cuda().to(torch.bfloat16)
+    wkv = torch.from_numpy(W.weights(wl, comp)["wkv"]).cuda().to(torch.bfloat16)
+    ws = torch.empty(kvc.kvc_ratio1_workspace_floats(cfg, tokens), dtype=torch.float32, device="cuda")
+    out = kvc.new_outputs(cfg, 1, tokens, latent=not comp.quantize, fp4=comp.quantize)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kvc.compressor_ratio1_forward(cfg, wkv, x, tokens, ws, out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = _timed(torch, stream, step, steps)
+    gemm_ms = _timed(torch, stream, lambda: kvc.compressor_ratio1_forward(cfg, wkv, x, tokens, ws), reps)
+    flop = 2.0 * tokens * wl.dim * comp.head_dim
+    # the epilogue kernel reads the f32 projections and writes the outputs
+    hd = comp.head_dim
+    fin_bytes = tokens * hd * 4 + (tokens * (hd // 2 + hd // 16) if comp.quantize else tokens * hd * 2)
+    fin_ms = ms - gemm_ms
+    del x, ws, out
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(ms, 4), "entries_per_s": round(tokens / (ms / 1e3), 1),
+            "kernels": {"gemm_bf16": {"ms": round(gemm_ms, 4), "tflops": round(flop / gemm_ms / 1e9, 2),
+                                      "flop": flop, "frac_of_bf16_peak": round(flop / gemm_ms / 1e9 / PEAK_BF16_MFMA_TFLOPS, 4)},
+                        "rows_finish": {"ms": round(fin_ms, 4), "gbps": round(fin_bytes / fin_ms / 1e6, 1),
+                                        "bytes": fin_bytes, "note": "step minus projection"}}}
+
+
 def run_fp4_quant(rows, width, reps, torch, kvc):
     """Time the standalone fp4 round trips over rows x width bf16 values
     (codes, scales and the dequantised copy written)."""
@@ -322,6 +359,7 @@ def main():
         d = run_decode(W.WORKLOADS["decode_r4_b64_s512"], 5, torch, kvc, W)
         extras["decode_r4_b64_s512"] = _rounded(d)
         extras["fp4_quant_262144x512"] = run_fp4_quant(262144, 512, 10, torch, kvc)
+        extras["prefill_r1_n65536"] = run_ratio1(W.WORKLOADS["prefill_r1_n65536"], 10, 3, 10, torch, kvc, W)
         result["workloads"] = extras
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

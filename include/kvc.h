@@ -68,7 +68,8 @@ typedef struct ihipStream_t *kvc_stream; /* a hipStream_t */
 #define KVC_FP4_E8M0_B32 1 /* the indexer's form: power-of-two (e8m0) scale per block of 32 */
 
 /* Compressor configuration.
- *   ratio      : 2, 4 or 128 (4 is the overlapped two-branch variant).
+ *   ratio      : 2, 4 or 128 (4 is the overlapped two-branch variant); 1 for
+ *                compressor_ratio1_forward only.
  *   head_dim   : latent width hd, 128 or 512.
  *   dim        : hidden width of x, a positive multiple of 32 and at most
  *                2^20 (KVC_EUNSUPPORTED otherwise; ignored when x is NULL).
@@ -185,6 +186,31 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const fl
                            int64_t start_pos, float *workspace, int64_t workspace_floats,
                            float *kv_state, float *score_state, int64_t state_batch,
                            const kvc_outputs *out, int32_t *emitted, kvc_stream stream);
+
+/* f32 elements of the workspace compressor_ratio1_forward needs:
+ * tokens * head_dim; or a negative KVC_E* code (cfg->ratio must be 1). */
+int64_t kvc_ratio1_workspace_floats(const kvc_config *cfg, int64_t tokens);
+
+/* The ratio-1 compressor ("DeepSeek V4.1 . Pool token pairs", Compressor
+ * listing, __init__ and the ratio-1 branch of forward; "Module compress",
+ * CompressorWeights): no gate, no pooling and no state, every token is one
+ * entry: latent = RMSNorm(bf16(x . wkv^T)) with bf16 x and bf16 wkv, the
+ * products summed in f32. Prefill and decode are the same call.
+ *   cfg          : ratio 1 (any other ratio: KVC_EINVAL); head_dim 128 or
+ *                  512; dim a positive multiple of 64, at most 2^20.
+ *   wkv          : [head_dim][dim] bf16.
+ *   norm_w       : [head_dim] f32 RMSNorm weight, or NULL (all ones).
+ *   x            : [tokens][dim] bf16 (batch rows and positions flattened).
+ *   tokens       : >= 0 (0: nothing is enqueued).
+ *   workspace    : f32, >= kvc_ratio1_workspace_floats() elements; receives
+ *                  the f32 projections [tokens][head_dim].
+ *   out          : outputs with batch 1 and G = tokens; `pooled` receives the
+ *                  f32 projection (before the bf16 rounding). May be NULL to
+ *                  compute only the projections.
+ * Errors: KVC_EINVAL, KVC_EUNSUPPORTED, KVC_ESPACE, KVC_EHIP. */
+int compressor_ratio1_forward(const kvc_config *cfg, const uint16_t *wkv, const float *norm_w,
+                              const uint16_t *x, int64_t tokens, float *workspace,
+                              int64_t workspace_floats, const kvc_outputs *out, kvc_stream stream);
 
 /* The latent's fp4 round trip ("Module compress", Functions,
  * fp4_quant_e4m3_inplace; to_e2m1_rne; Constants, LATENT_BLOCK) on

@@ -18,13 +18,27 @@ constexpr int64_t kMaxDim = int64_t(1) << 20;
 
 bool aligned(const void *p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
 
-int check_config(const kvc_config *cfg) {
+int check_common(const kvc_config *cfg) {
   if (!cfg) return KVC_EINVAL;
   if (!(cfg->eps >= 0.0f) || !isfinite(cfg->eps)) return KVC_EINVAL;
   if (cfg->fp4_format != KVC_FP4_E4M3_B16 && cfg->fp4_format != KVC_FP4_E8M0_B32) return KVC_EINVAL;
-  if (cfg->ratio != 2 && cfg->ratio != 4 && cfg->ratio != 128) return KVC_EUNSUPPORTED;
   if (cfg->head_dim != 128 && cfg->head_dim != 512) return KVC_EUNSUPPORTED;
   return KVC_OK;
+}
+
+// the pooled compressor (ratio > 1)
+int check_config(const kvc_config *cfg) {
+  const int rc = check_common(cfg);
+  if (rc) return rc;
+  if (cfg->ratio != 2 && cfg->ratio != 4 && cfg->ratio != 128) return KVC_EUNSUPPORTED;
+  return KVC_OK;
+}
+
+// the ratio-1 compressor
+int check_ratio1(const kvc_config *cfg) {
+  const int rc = check_common(cfg);
+  if (rc) return rc;
+  return cfg->ratio == 1 ? KVC_OK : KVC_EINVAL;
 }
 
 bool overlapped(const kvc_config *cfg) { return cfg->ratio == 4; }
@@ -286,6 +300,54 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const fl
   if ((rc = hip_status(kvc::launch_decode_finish(in, nullptr, cfg->head_dim, s)))) return rc;
   if (pool_now && wants_entries(out)) {
     if ((rc = hip_status(kvc::launch_pool(p, r, cfg->head_dim, s)))) return rc;
+  }
+  return KVC_OK;
+}
+
+int64_t kvc_ratio1_workspace_floats(const kvc_config *cfg, int64_t tokens) {
+  const int rc = check_ratio1(cfg);
+  if (rc) return rc;
+  if (tokens < 0) return KVC_EINVAL;
+  return tokens * cfg->head_dim;
+}
+
+int compressor_ratio1_forward(const kvc_config *cfg, const uint16_t *wkv, const float *norm_w, const uint16_t *x,
+                              int64_t tokens, float *workspace, int64_t workspace_floats, const kvc_outputs *out,
+                              kvc_stream stream) {
+  int rc = check_ratio1(cfg);
+  if (rc) return rc;
+  if (tokens < 0) return KVC_EINVAL;
+  if (tokens == 0) return KVC_OK;
+  if (!x || !wkv || !workspace) return KVC_EINVAL;
+  if (cfg->dim <= 0) return KVC_EINVAL;
+  if (cfg->dim % 64 != 0 || cfg->dim > kMaxDim) return KVC_EUNSUPPORTED;
+  if (!aligned(x) || !aligned(wkv) || !aligned(norm_w) || !aligned(workspace)) return KVC_EINVAL;
+  const int64_t hd = cfg->head_dim;
+  if (workspace_floats < tokens * hd) return KVC_ESPACE;
+  if ((rc = check_outputs(out))) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  kvc::GemmBf16Args g{};
+  g.a = x;
+  g.b = wkv;
+  g.c = workspace;
+  g.lda = cfg->dim;
+  g.ldb = cfg->dim;
+  g.ldc = hd;
+  g.m = tokens;
+  g.n = hd;
+  g.k = cfg->dim;
+  if ((rc = hip_status(kvc::launch_gemm_bf16(g, s)))) return rc;
+  if (wants_entries(out)) {
+    kvc::PoolArgs p = pool_args(cfg, nullptr, out);
+    p.norm_w = norm_w;
+    p.kv = workspace;
+    p.row_stride = hd;
+    p.batch_stride = tokens * hd;
+    p.batch = 1;
+    p.groups = tokens;
+    p.out_batch_stride = tokens;
+    if ((rc = hip_status(kvc::launch_rows_finish(p, cfg->head_dim, s)))) return rc;
   }
   return KVC_OK;
 }

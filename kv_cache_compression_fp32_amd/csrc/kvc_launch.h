@@ -33,6 +33,17 @@ struct GemmArgs {
 enum class GemmShape { kPrefill, kDecode };
 hipError_t launch_gemm(const GemmArgs &g, GemmShape shape, hipStream_t stream);
 
+// Ratio-1 projection: C[m][n] = sum_k A[m][k] * B[n][k], bf16 A and B, f32
+// accumulation and output, bf16 MFMA. Needs k % 64 == 0 and n % 128 == 0.
+struct GemmBf16Args {
+  const uint16_t *a;  // [m][k] bf16, row stride lda
+  const uint16_t *b;  // [n][k] bf16, row stride ldb
+  float *c;           // [m][n] f32, row stride ldc
+  int64_t lda, ldb, ldc;
+  int64_t m, n, k;
+};
+hipError_t launch_gemm_bf16(const GemmBf16Args &g, hipStream_t stream);
+
 // Pools `groups` entries of each batch row from kv/score planes holding a
 // sequence of token rows (see the pool kernels for the candidate layout).
 struct PoolArgs {
@@ -53,6 +64,11 @@ struct PoolArgs {
   float *shift_kv, *shift_sc; // ratio 4: move the last block's rows to the previous rows, or null
 };
 hipError_t launch_pool(const PoolArgs &p, int ratio, int head_dim, hipStream_t stream);
+
+// Ratio 1: the per-entry epilogue (bf16 round, RMSNorm, outputs, fp4) of
+// `groups` rows of f32 projections, row e at kv + e * row_stride; one entry
+// per row (batch 1 in the PoolArgs; sc, ape and the shift are unused).
+hipError_t launch_rows_finish(const PoolArgs &p, int head_dim, hipStream_t stream);
 
 // Writes the carry of a prefill into the state planes (ratio 4: last complete
 // block or padding, then the trailing tokens; other ratios: trailing tokens).

@@ -255,6 +255,18 @@ __global__ __launch_bounds__(256) void pool_small_kernel(PoolArgs a) {
   for (int64_t e = e_begin; e < e_end; ++e) small_entry<HD, R, OV>(a, b, e, lane);
 }
 
+// Ratio 1: every row of f32 projections is one entry; one wavefront runs the
+// per-entry epilogue of one row (the same code as the pooled entries).
+template <int HD>
+__global__ __launch_bounds__(256) void rows_finish_kernel(PoolArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= a.groups) return;
+  float p[HD / kWave];
+  load_row<HD>(a.kv + e * a.row_stride, lane, p);
+  finish_entry<HD>(p, a, e, lane);
+}
+
 // Long groups (ratio 128). One workgroup of 512 threads per entry: thread t
 // owns 4 features (fg = t % (HD/4)) and every RL-th row of the group
 // (rl = t / (HD/4)), keeping a running max / sum / weighted sum per feature
@@ -486,6 +498,17 @@ hipError_t launch_pool(const PoolArgs &p, int ratio, int head_dim, hipStream_t s
     case 128 * 10000 + 128: return launch_long<128>(p, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_rows_finish(const PoolArgs &p, int head_dim, hipStream_t stream) {
+  if (p.groups <= 0) return hipSuccess;
+  const dim3 grid((uint32_t)((p.groups + 3) / 4)), block(256);
+  switch (head_dim) {
+    case 512: hipLaunchKernelGGL(rows_finish_kernel<512>, grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL(rows_finish_kernel<128>, grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_state_store(const StateStoreArgs &s, hipStream_t stream) {

@@ -61,6 +61,9 @@ _SIGNATURES = {
     "compressor_decode_step": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), _P, _I64, _I64,
                                               _P, _I64, _P, _P, _I64, ctypes.POINTER(_Outputs),
                                               ctypes.POINTER(ctypes.c_int32), _P]),
+    "kvc_ratio1_workspace_floats": (_I64, [ctypes.POINTER(_Config), _I64]),
+    "compressor_ratio1_forward": (ctypes.c_int, [ctypes.POINTER(_Config), _P, _P, _P, _I64, _P, _I64,
+                                                 ctypes.POINTER(_Outputs), _P]),
     "latent_fp4_quant": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
     "indexer_fp4_quant": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
     "kvc_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -124,6 +127,11 @@ def kvc_prefill_workspace_floats(cfg: Config, batch: int, seqlen: int) -> int:
 def kvc_decode_workspace_floats(cfg: Config, batch: int) -> int:
     return _check(lib().kvc_decode_workspace_floats(ctypes.byref(cfg.c()), batch),
                   "kvc_decode_workspace_floats")
+
+
+def kvc_ratio1_workspace_floats(cfg: Config, tokens: int) -> int:
+    return _check(lib().kvc_ratio1_workspace_floats(ctypes.byref(cfg.c()), tokens),
+                  "kvc_ratio1_workspace_floats")
 
 
 def _check(rc: int, what: str) -> int:
@@ -214,6 +222,24 @@ def compressor_decode_step(cfg: Config, w: Weights, x: torch.Tensor | None, batc
         _stream(stream))
     _check(rc, "compressor_decode_step")
     return bool(e.value)
+
+
+def _bf16_ptr(t, name):
+    if t is not None and t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must be bf16")
+    return _ptr(t, None, name)
+
+
+def compressor_ratio1_forward(cfg: Config, wkv: torch.Tensor, x: torch.Tensor, tokens: int,
+                              workspace: torch.Tensor, out: Outputs | None = None,
+                              norm_w: torch.Tensor | None = None, stream=None) -> None:
+    """Enqueue the ratio-1 compressor over `tokens` rows of bf16 x [tokens,
+    dim] with bf16 wkv [head_dim, dim]; every token is one entry."""
+    rc = lib().compressor_ratio1_forward(
+        ctypes.byref(cfg.c()), _bf16_ptr(wkv, "wkv"), _ptr(norm_w, torch.float32, "norm_w"), _bf16_ptr(x, "x"),
+        tokens, _ptr(workspace, torch.float32, "workspace"), workspace.numel(),
+        ctypes.byref(out.c()) if out is not None else None, _stream(stream))
+    _check(rc, "compressor_ratio1_forward")
 
 
 def _fp4_quant(fn, name, inp, codes, scales, out, stream):

@@ -12,6 +12,9 @@ compressor. Values are N(0, std) with std the standard deviation: hidden states
 N(0, 1), projection weights N(0, 0.02), positional bias N(0, 0.1); the
 projection-free pair-pooling case draws k^c ~ N(0, 1) and g^c ~ N(0, 2).
 
+The ratio-1 compressor (a plain bf16 projection) draws x and wkv the same
+way; its callers hand the library the bf16 roundings of those arrays.
+
 Every tensor is drawn in float32 by NumPy's PCG64 generator. Hidden states are
 drawn in blocks of BLOCK_TOKENS tokens, each block from its own seed
 (seed, stream, batch row, block index), so any token range of a long sequence
@@ -85,11 +88,14 @@ WORKLOADS = {
         "prefill_r4_n65536_fp4_idx128", batch=1, seqlen=65536, dim=4096,
         compressors=(Compressor(ratio=4, head_dim=512, quantize=True),
                      Compressor(ratio=4, head_dim=128, quantize=False, tag=_TAG_IDX))),
+    # ratio-1 compressor (bf16 projection + RMSNorm, fp4 cache form) over a long prefill
+    "prefill_r1_n65536": Workload("prefill_r1_n65536", batch=1, seqlen=65536, dim=4096,
+                                  compressors=(Compressor(ratio=1, head_dim=512, quantize=True),)),
 }
 
 # the order the workloads are listed in (smallest first)
 ORDER = ["pair_pool_r2", "prefill_r4_n4096", "prefill_r128_b2_n16384",
-         "decode_r4_b64_s512", "prefill_r4_n65536_fp4_idx128"]
+         "decode_r4_b64_s512", "prefill_r4_n65536_fp4_idx128", "prefill_r1_n65536"]
 
 
 def _normal(seed_words, shape, std) -> np.ndarray:
@@ -100,8 +106,11 @@ def _normal(seed_words, shape, std) -> np.ndarray:
 
 
 def weights(wl: Workload, comp: Compressor) -> dict:
-    """wkv, wgate [proj, dim] and ape [ratio, proj], float32."""
+    """wkv, wgate [proj, dim] and ape [ratio, proj], float32 (ratio 1: wkv
+    only)."""
     s = wl.seed
+    if comp.ratio == 1:
+        return {"wkv": _normal((s, _TAG_WKV + comp.tag), (comp.proj, wl.dim), comp.weight_std)}
     return {
         "wkv": _normal((s, _TAG_WKV + comp.tag), (comp.proj, wl.dim), comp.weight_std),
         "wgate": _normal((s, _TAG_WGATE + comp.tag), (comp.proj, wl.dim), comp.weight_std),

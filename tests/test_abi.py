@@ -150,3 +150,30 @@ def test_fp4_format_is_checked():
     with pytest.raises(kvc.KvcError):
         kvc.kvc_proj_width(kvc.Config(4, 512, 4096, fp4_format=7))
     assert kvc.kvc_proj_width(kvc.Config(4, 512, 4096, fp4_format=kvc.KVC_FP4_E8M0_B32)) == 1024
+
+
+def test_ratio1_argument_errors_return_before_enqueueing():
+    lib = kvc.lib()
+    fake = 0x100000
+
+    def call(cfg, **kw):
+        a = dict(wkv=fake, norm=None, x=fake, tokens=8, ws=fake, ws_n=1 << 30, out=None)
+        a.update(kw)
+        return lib.compressor_ratio1_forward(ctypes.byref(cfg.c()), a["wkv"], a["norm"], a["x"], a["tokens"],
+                                             a["ws"], a["ws_n"], a["out"], None)
+    ok = kvc.Config(1, 512, 4096)
+    assert kvc.kvc_ratio1_workspace_floats(ok, 10) == 5120
+    with pytest.raises(kvc.KvcError):
+        kvc.kvc_ratio1_workspace_floats(kvc.Config(4, 512, 4096), 10)   # the pooled compressor's config
+    assert call(kvc.Config(4, 512, 4096)) == kvc.KVC_EINVAL
+    assert call(kvc.Config(1, 256, 4096)) == kvc.KVC_EUNSUPPORTED
+    assert call(kvc.Config(1, 512, 4096 + 32)) == kvc.KVC_EUNSUPPORTED   # dim % 64
+    assert call(kvc.Config(1, 512, 0)) == kvc.KVC_EINVAL
+    assert call(ok, tokens=-1) == kvc.KVC_EINVAL
+    assert call(ok, x=None) == kvc.KVC_EINVAL
+    assert call(ok, wkv=None) == kvc.KVC_EINVAL
+    assert call(ok, ws_n=8 * 512 - 1) == kvc.KVC_ESPACE
+    assert call(ok, x=fake + 2) == kvc.KVC_EINVAL                          # misaligned
+    assert call(ok, tokens=0, x=None, wkv=None, ws=None) == kvc.KVC_OK     # nothing to do
+    # and the pooled entry points reject ratio 1
+    assert _prefill_raw(kvc.Config(1, 512, 4096))[0] == kvc.KVC_EUNSUPPORTED

@@ -187,3 +187,31 @@ def test_prefill_r4_n65536_index_keys_power_of_two_fp4_sampled():
     assert g["scales"].shape == (1, 16384, 4)
     _check_sampled(wl, comp, w, g, _sample_entries(16384, 40, seed=1), [0], fp4="e8m0")
     check_fp4(g["codes"], g["scales"], g["latent"], gpu_dequant=g["dequant"], e8m0=True)
+
+
+def test_prefill_r1_n65536_sampled():
+    # the ratio-1 compressor over the long sequence, in the benchmark's launch
+    # configuration; tokens are independent, so sampled rows are checked
+    wl = W.WORKLOADS["prefill_r1_n65536"]
+    comp = wl.compressors[0]
+    note(f"{wl.name}")
+    cfg = kvc.Config(1, comp.head_dim, wl.dim, wl.eps)
+    xt = torch.from_numpy(W.hidden(wl)[0]).cuda().to(torch.bfloat16)
+    wt = torch.from_numpy(W.weights(wl, comp)["wkv"]).cuda().to(torch.bfloat16)
+    tokens = wl.seqlen
+    ws = torch.empty(kvc.kvc_ratio1_workspace_floats(cfg, tokens), dtype=torch.float32, device="cuda")
+    out = kvc.new_outputs(cfg, 1, tokens, latent=True, pooled=True, fp4=True, dequant=True)
+    kvc.compressor_ratio1_forward(cfg, wt, xt, tokens, ws, out)
+    torch.cuda.synchronize()
+    rows = np.array(_sample_entries(tokens, 200, seed=3) + list(range(tokens - 256, tokens - 200)))
+    rows_t = torch.from_numpy(rows).cuda()
+    x = xt[rows_t].float().cpu().numpy()
+    wkv = wt.float().cpu().numpy()
+    g = outputs_to_host(kvc.Outputs(latent=out.latent[0][rows_t], pooled=out.pooled[0][rows_t],
+                                    codes=out.codes[0][rows_t], scales=out.scales[0][rows_t],
+                                    dequant=out.dequant[0][rows_t]))
+    ref = oracle.plain_projection(oracle.Config(ratio=1, head_dim=comp.head_dim, dim=wl.dim, eps=wl.eps),
+                                  oracle.Weights(wkv=wkv), x, quantize=True)
+    check_pooled(g["pooled"], ref["pooled"], "projection")
+    check_latent(g["latent"], g["pooled"], ref["latent"], ref["pooled"], eps=wl.eps)
+    check_fp4(g["codes"], g["scales"], g["latent"], ref["codes"], ref["scales"], ref["latent"], g["dequant"])

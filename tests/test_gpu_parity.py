@@ -6,7 +6,7 @@ import torch
 
 import kv_cache_compression_fp32_amd.kvc as kvc
 import oracle
-from gpu_util import dev, host_bf16, note, oracle_cfg, oracle_weights, prefill
+from gpu_util import dev, host_bf16, note, oracle_cfg, oracle_weights, outputs_to_host, prefill
 from parity import check_fp4, check_latent, check_pooled
 
 pytestmark = pytest.mark.gpu
@@ -315,3 +315,102 @@ def test_decode_with_projection_matches_oracle():
     # and the GPU prefill over the same tokens
     full = prefill(cfg, w, batch, steps, x=x)
     check_pooled(dec["pooled"], full["pooled"], "decode vs prefill")
+
+
+@pytest.mark.parametrize("ratio,batch,dim,steps", [(2, 8, 256, 21), (128, 4, 128, 2 * 128 + 3)])
+def test_decode_streaming_with_projection_ratio_2_and_128(ratio, batch, dim, steps):
+    note(f"decode with x, ratio {ratio}, batch {batch}, dim {dim}, {steps} steps")
+    from gpu_util import weights
+    rng = np.random.default_rng(ratio + steps)
+    cfg = kvc.Config(ratio, 512, dim)
+    proj = 512
+    x = rng.standard_normal((batch, steps, dim), dtype=np.float32)
+    w = {"wkv": rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.05),
+         "wgate": rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.05),
+         "ape": rng.standard_normal((ratio, proj), dtype=np.float32) * np.float32(0.1)}
+    dec = _decode_gpu(cfg, weights(w), batch, xs=x)
+    st = oracle.State(oracle_cfg(cfg), batch)
+    ref = oracle.prefill(oracle_cfg(cfg), oracle_weights(w), st, x=x, quantize=True)
+    assert dec["pooled"].shape[1] == steps // ratio
+    check_pooled(dec["pooled"], ref["pooled"])
+    check_latent(dec["latent"], dec["pooled"], ref["latent"], ref["pooled"])
+    check_fp4(dec["codes"], dec["scales"], dec["latent"], ref["codes"], ref["scales"], ref["latent"], dec["dequant"])
+    # the tail left in the state is the oracle's carry
+    live = _live_rows(ratio, steps)
+    check_pooled(dec["state_kv"][:, live], st.kv[:, live], "state kv")
+    check_pooled(dec["state_sc"][:, live], st.score[:, live], "state score")
+
+
+# ---------------------------------------------------------------- ratio 1
+RATIO1_CASES = [
+    # head_dim, dim, tokens, norm weight
+    (512, 256, 300, False),         # 128 x 128 tiles, ragged
+    (128, 128, 1000, True),
+    (512, 64, 16384 + 37, False),   # 256 x 128 tiles, ragged
+    (512, 64, 65536 + 37, True),    # 256 x 256 tiles, ragged
+    (128, 64, 65536 + 5, False),    # 256 x 128 tiles at head_dim 128
+]
+
+
+def _bf16_pair(a: np.ndarray):
+    """bf16 tensor (rounded from a) and the float32 array of its values."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t, t.float().numpy()
+
+
+@pytest.mark.parametrize("hd,dim,tokens,normw", RATIO1_CASES)
+def test_ratio1_forward_matches_oracle(hd, dim, tokens, normw):
+    note(f"ratio 1 hd={hd} dim={dim} tokens={tokens}")
+    rng = np.random.default_rng(hd + dim + tokens)
+    cfg = kvc.Config(1, hd, dim)
+    xt, x = _bf16_pair(rng.standard_normal((tokens, dim), dtype=np.float32))
+    wt, wkv = _bf16_pair(rng.standard_normal((hd, dim), dtype=np.float32) * np.float32(0.05))
+    nw = (1.0 + 0.1 * rng.standard_normal(hd)).astype(np.float32) if normw else None
+    ws = torch.empty(kvc.kvc_ratio1_workspace_floats(cfg, tokens), dtype=torch.float32, device="cuda")
+    out = kvc.new_outputs(cfg, 1, tokens, latent=True, pooled=True, fp4=True, dequant=True)
+    kvc.compressor_ratio1_forward(cfg, wt.cuda(), xt.cuda(), tokens, ws, out, norm_w=dev(nw))
+    torch.cuda.synchronize()
+    g = {k: v[0] for k, v in outputs_to_host(out).items()}
+    assert np.array_equal(ws.view(tokens, hd).cpu().numpy(), g["pooled"])  # the workspace holds it too
+    # tokens are independent: large cases compare the first row tile, the
+    # ragged last tiles and random rows, small cases every row
+    if tokens > 20000:
+        rows = np.array(sorted(set(range(256)) | set(range(tokens - 300, tokens)) |
+                               set(rng.choice(tokens, 512, replace=False).tolist())))
+    else:
+        rows = np.arange(tokens)
+    x, g = x[rows], {k: v[rows] for k, v in g.items()}
+    ref = oracle.plain_projection(oracle.Config(ratio=1, head_dim=hd, dim=dim), oracle.Weights(wkv=wkv, norm_w=nw),
+                                  x, quantize=True)
+    # the f32 projection: inside the worst-case bound of any f32 summation
+    # order of the (exact) bf16 products
+    absdot = np.abs(x).astype(np.float64) @ np.abs(wkv).astype(np.float64).T
+    bound = dim * 2.0 ** -24 * absdot + np.spacing(np.abs(ref["pooled"])) + 1e-30
+    err = np.abs(g["pooled"].astype(np.float64) - ref["pooled"])
+    assert np.all(err <= bound), f"projection: {np.sum(err > bound)} beyond the bound"
+    check_pooled(g["pooled"], ref["pooled"], "projection")
+    check_latent(g["latent"], g["pooled"], ref["latent"], ref["pooled"], nw, cfg.eps)
+    check_fp4(g["codes"], g["scales"], g["latent"], ref["codes"], ref["scales"], ref["latent"], g["dequant"])
+
+
+def test_ratio1_power_of_two_fp4_and_outputs_subset():
+    note("ratio 1 hd=128 e8m0 fp4, latent-only call")
+    rng = np.random.default_rng(91)
+    hd, dim, tokens = 128, 192, 777
+    cfg = kvc.Config(1, hd, dim, fp4_format=kvc.KVC_FP4_E8M0_B32)
+    xt, x = _bf16_pair(rng.standard_normal((tokens, dim), dtype=np.float32))
+    wt, wkv = _bf16_pair(rng.standard_normal((hd, dim), dtype=np.float32) * np.float32(0.05))
+    ws = torch.empty(tokens * hd, dtype=torch.float32, device="cuda")
+    full = kvc.new_outputs(cfg, 1, tokens, latent=True, pooled=True, fp4=True, dequant=True)
+    kvc.compressor_ratio1_forward(cfg, wt.cuda(), xt.cuda(), tokens, ws, full)
+    only = kvc.Outputs(latent=torch.empty((tokens, hd), dtype=torch.bfloat16, device="cuda"))
+    kvc.compressor_ratio1_forward(cfg, wt.cuda(), xt.cuda(), tokens, ws, only)
+    torch.cuda.synchronize()
+    g = outputs_to_host(full)
+    assert g["scales"].shape[-1] == hd // 32
+    ref = oracle.plain_projection(oracle.Config(ratio=1, head_dim=hd, dim=dim, fp4="e8m0"),
+                                  oracle.Weights(wkv=wkv), x, quantize=True)
+    check_latent(g["latent"][0], g["pooled"][0], ref["latent"], ref["pooled"])
+    check_fp4(g["codes"][0], g["scales"][0], g["latent"][0], ref["codes"], ref["scales"], ref["latent"],
+              g["dequant"][0], e8m0=True)
+    assert np.array_equal(only.latent.view(torch.int16).cpu().numpy(), full.latent[0].view(torch.int16).cpu().numpy())
