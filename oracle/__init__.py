@@ -9,3 +9,4 @@ from .compressor import (Config, State, Weights, add_bias, decode_step, entry_ca
 from .formats import (AMAX_FLOOR, E2M1_VALUES, E4M3FN_VALUES, E8M0_AMAX_FLOOR, FP4_BLOCK, LATENT_BLOCK,
                       bf16_bits, bf16_from_bits, bf16_round, e2m1_decode, e2m1_encode, e4m3fn_decode,
                       e4m3fn_encode, fp4_quant_e4m3, fp4_quant_e8m0, fp4_unpack, pow2_ceil_exponent)
+from .rope import apply_rope, rope_table, yarn_inv_freq

@@ -47,7 +47,12 @@ What it computes, step by step, in the pages' order:
    block-16 fp4 round trip of formats.fp4_quant_e4m3 (the KV latent's form),
    or the power-of-two-scaled block-32 one of formats.fp4_quant_e8m0 (the
    indexer's form).
-8. Ratio 1 (plain_projection). No gate, no pooling, no state: every token is
+8. RoPE (oracle/rope.py, optional, cfg.rope_dim > 0): "rotated" holds the
+   latent with its rotary slice turned by the table row of the entry's index
+   (w.rope_cs), and the fp4 cache form is taken from the rotated latent
+   ("Compressed Sparse Attention . ratio m = 4", Normalize + RoPE + cache). The
+   compressor's own output, "latent", stays unrotated.
+9. Ratio 1 (plain_projection). No gate, no pooling, no state: every token is
    one entry, latent = RMSNorm(wkv(x)) in the checkpoint's bf16 (Compressor
    listing, __init__ and the ratio-1 branch of forward; "Module compress",
    CompressorWeights: wkv holds bf16 values at ratio 1). Reading: x and wkv
@@ -74,6 +79,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from .formats import bf16_round, fp4_quant_e4m3, fp4_quant_e8m0
+from .rope import apply_rope
 
 
 @dataclass(frozen=True)
@@ -83,6 +89,7 @@ class Config:
     dim: int = 0        # hidden width of x (0 when projections are given)
     eps: float = 1e-6   # RMSNorm epsilon
     fp4: str = "e4m3"   # fp4 form of the output: "e4m3" (block 16) or "e8m0" (block 32)
+    rope_dim: int = 0   # rotary slice width (last features of an entry); 0: no RoPE
 
     @property
     def overlap(self) -> bool:
@@ -105,6 +112,7 @@ class Weights:
     wgate: np.ndarray | None = None   # [proj, dim] f32
     ape: np.ndarray | None = None     # [ratio, proj] f32, None = no bias
     norm_w: np.ndarray | None = None  # [hd] f32, None = ones
+    rope_cs: np.ndarray | None = None  # [entries, rope_dim / 2, 2] f32 (cos, sin) per compressed entry
 
 
 class State:
@@ -200,11 +208,19 @@ def _projections(cfg: Config, w: Weights, x, kv, score):
     return np.asarray(kv, dtype=np.float32), np.asarray(score, dtype=np.float32)
 
 
-def _finish(cfg: Config, w: Weights, pooled: np.ndarray, quantize: bool) -> dict:
+def _finish(cfg: Config, w: Weights, pooled: np.ndarray, quantize: bool, entry_index=None) -> dict:
+    """Norm, optional RoPE (entry_index [n]: the compressed index of each of
+    the n entries along pooled's second-to-last axis) and optional fp4."""
     latent = rms_norm_bf16(pooled, w.norm_w, cfg.eps)
     out = {"pooled": pooled, "latent": latent}
+    cached = latent
+    if cfg.rope_dim:
+        idx = np.asarray(entry_index)
+        rows = np.asarray(w.rope_cs, dtype=np.float32)[idx]
+        rows = np.broadcast_to(rows, latent.shape[:-1] + rows.shape[-2:])
+        out["rotated"] = cached = apply_rope(latent, rows, cfg.rope_dim)
     if quantize:
-        flat = latent.reshape(-1, cfg.head_dim)
+        flat = cached.reshape(-1, cfg.head_dim)
         quant, block = (fp4_quant_e8m0, 32) if cfg.fp4 == "e8m0" else (fp4_quant_e4m3, 16)
         codes, scales, deq = quant(flat)
         lead = latent.shape[:-1]
@@ -255,7 +271,7 @@ def prefill(cfg: Config, w: Weights, state: State, x=None, kv=None, score=None,
         for k, j in enumerate(entries):
             kc, sc = entry_candidates(cfg, kv[b], score[b], j)
             pooled[b, k] = pool(kc, sc)
-    return _finish(cfg, w, pooled, quantize)
+    return _finish(cfg, w, pooled, quantize, np.array(entries))
 
 
 def decode_step(cfg: Config, w: Weights, state: State, start_pos: int, x=None,
@@ -286,7 +302,7 @@ def decode_step(cfg: Config, w: Weights, state: State, start_pos: int, x=None,
     if cfg.overlap:
         state.kv[:batch, :r] = state.kv[:batch, r:]
         state.score[:batch, :r] = state.score[:batch, r:]
-    return _finish(cfg, w, pooled, quantize)
+    return _finish(cfg, w, pooled, quantize, np.array([(start_pos + 1) // r - 1]))
 
 
 def plain_projection(cfg: Config, w: Weights, x: np.ndarray, quantize: bool = False) -> dict:
@@ -302,4 +318,6 @@ def plain_projection(cfg: Config, w: Weights, x: np.ndarray, quantize: bool = Fa
         raise ValueError("x and wkv must hold bf16 values at ratio 1")
     if wkv.shape != (cfg.head_dim, x.shape[-1]):
         raise ValueError("wkv must be [head_dim, dim]")
+    if cfg.rope_dim:
+        raise ValueError("RoPE is not offered at ratio 1")
     return _finish(cfg, w, project(x, wkv), quantize)

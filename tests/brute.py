@@ -205,3 +205,31 @@ def plain_projection(xs, wkv, eps=1e-6):
         p = [f32(dot(x, w)) for w in wkv]
         out.append((p, rmsnorm(p, eps)))
     return out
+
+
+def bf16_of_fraction(v: Fraction) -> float:
+    """Nearest bf16 to an exact rational, ties to even (normal range)."""
+    if v == 0:
+        return 0.0
+    mag = abs(v)
+    e = math.frexp(float(mag))[1] - 1          # 2^e <= mag < 2^(e+1), up to float's own rounding
+    while Fraction(2) ** e > mag:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= mag:
+        e += 1
+    q = round(mag / Fraction(2) ** (e - 7))    # 8 significant bits, half to even
+    r = math.ldexp(q, e - 7)
+    return r if v > 0 else -r
+
+
+def rope(latent: list[float], rows: list[tuple[float, float]], rope_dim: int) -> list[float]:
+    """Rotate the last rope_dim features of one entry as pairs (2i, 2i+1) by
+    (cos, sin) row i, exactly, one rounding to bf16."""
+    out = list(latent)
+    start = len(latent) - rope_dim
+    for i, (c, s) in enumerate(rows):
+        a, b = Fraction(latent[start + 2 * i]), Fraction(latent[start + 2 * i + 1])
+        fc, fs = Fraction(c), Fraction(s)
+        out[start + 2 * i] = bf16_of_fraction(a * fc - b * fs)
+        out[start + 2 * i + 1] = bf16_of_fraction(a * fs + b * fc)
+    return out
