@@ -78,6 +78,16 @@ typedef struct ihipStream_t *kvc_stream; /* a hipStream_t */
  *                KV latent's, "Module compress", Functions,
  *                fp4_quant_e4m3_inplace) or KVC_FP4_E8M0_B32 (the indexer's,
  *                fp4_quant_e8m0_inplace; Precision paragraph: block 32).
+ *   rope_dim   : width of the rotary slice ("Compressed Sparse Attention .
+ *                ratio m = 4", Normalize + RoPE + cache; Released Flash
+ *                configuration, RoPE sub-dimension 64), or 0 for no RoPE.
+ *                Even, at most head_dim; not offered at ratio 1. With RoPE,
+ *                the entry's last rope_dim features turn as pairs (2i, 2i+1)
+ *                by row j of kvc_weights.rope_cs for compressed entry j:
+ *                (a, b) -> (a c - b s, a s + b c), each exact value rounded
+ *                once to bf16; the rotated entry goes to kvc_outputs.rotated
+ *                and is what the fp4 outputs encode, while latent stays the
+ *                unrotated compressor output.
  * proj = 2 * head_dim at ratio 4, head_dim otherwise: the width of each
  * projection plane. */
 typedef struct kvc_config {
@@ -86,18 +96,27 @@ typedef struct kvc_config {
     int64_t dim;
     float eps;
     int32_t fp4_format;
+    int32_t rope_dim;
 } kvc_config;
 
 /* Weights (device, f32).
  *   wkv, wgate : [proj][dim]; required whenever x is not NULL.
  *   ape        : [ratio][proj] positional bias of the gate logits, or NULL
  *                (no bias).
- *   norm_w     : [head_dim] RMSNorm weight, or NULL (all ones). */
+ *   norm_w     : [head_dim] RMSNorm weight, or NULL (all ones).
+ *   rope_cs    : [rope_rows][rope_dim / 2][2] (cos, sin) of each compressed
+ *                entry's rotation ("Module compress", Functions,
+ *                yarn_freqs_cis: the caller builds it from its own theta and
+ *                YaRN parameters, row j for compressed entry j); required when
+ *                rope_dim > 0 and an entry is written, else ignored.
+ *   rope_rows  : rows of rope_cs; every entry written needs j < rope_rows. */
 typedef struct kvc_weights {
     const float *wkv;
     const float *wgate;
     const float *ape;
     const float *norm_w;
+    const float *rope_cs;
+    int64_t rope_rows;
 } kvc_weights;
 
 /* Outputs (device). Each is written iff its pointer is not NULL; G is the
@@ -110,13 +129,17 @@ typedef struct kvc_weights {
  *   scales  : [batch][G][head_dim / 16] e4m3fn scale of each block of 16, or
  *             with KVC_FP4_E8M0_B32 [batch][G][head_dim / 32] e8m0 scale
  *             bytes (2^(byte - 127)) of each block of 32.
- *   dequant : [batch][G][head_dim] bf16, codes times scales. */
+ *   dequant : [batch][G][head_dim] bf16, codes times scales.
+ *   rotated : [batch][G][head_dim] bf16, the latent after RoPE (requires
+ *             rope_dim > 0). With RoPE, codes / scales / dequant encode this
+ *             rotated entry. */
 typedef struct kvc_outputs {
     uint16_t *latent;
     float *pooled;
     uint8_t *codes;
     uint8_t *scales;
     uint16_t *dequant;
+    uint16_t *rotated;
 } kvc_outputs;
 
 /* proj for `cfg`, or a negative KVC_E* code if cfg is invalid. */
@@ -242,6 +265,21 @@ int latent_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *c
  * Errors: KVC_EINVAL, KVC_EHIP. */
 int indexer_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *codes,
                       uint8_t *scales, uint16_t *out, kvc_stream stream);
+
+/* RoPE of [rows][width] bf16 latent rows, the step between the norm and the
+ * cache ("Compressed Sparse Attention . ratio m = 4", Normalize + RoPE +
+ * cache): row r's last rope_dim features turn as pairs (2i, 2i+1) by
+ * rope_cs row first_row + r, (a, b) -> (a c - b s, a s + b c), each exact
+ * value rounded once to bf16 (round to nearest even); the same rotation the
+ * compressor entry points apply with kvc_config.rope_dim.
+ *   in, out   : [rows][width] bf16; out may equal in (in place), other
+ *               overlaps are not allowed.
+ *   rows >= 0; width > 0 and even; rope_dim even, 0 < rope_dim <= width.
+ *   rope_cs   : [rope_rows][rope_dim / 2][2] f32 (cos, sin);
+ *               first_row + rows <= rope_rows.
+ * Errors: KVC_EINVAL, KVC_EHIP. */
+int latent_rope(const uint16_t *in, int64_t rows, int64_t width, int32_t rope_dim, const float *rope_cs,
+                int64_t rope_rows, int64_t first_row, uint16_t *out, kvc_stream stream);
 
 /* A static description of a KVC_* code. */
 const char *kvc_strerror(int code);

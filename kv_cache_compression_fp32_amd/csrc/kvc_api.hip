@@ -23,6 +23,7 @@ int check_common(const kvc_config *cfg) {
   if (!(cfg->eps >= 0.0f) || !isfinite(cfg->eps)) return KVC_EINVAL;
   if (cfg->fp4_format != KVC_FP4_E4M3_B16 && cfg->fp4_format != KVC_FP4_E8M0_B32) return KVC_EINVAL;
   if (cfg->head_dim != 128 && cfg->head_dim != 512) return KVC_EUNSUPPORTED;
+  if (cfg->rope_dim < 0 || cfg->rope_dim > cfg->head_dim || cfg->rope_dim % 2 != 0) return KVC_EINVAL;
   return KVC_OK;
 }
 
@@ -38,7 +39,8 @@ int check_config(const kvc_config *cfg) {
 int check_ratio1(const kvc_config *cfg) {
   const int rc = check_common(cfg);
   if (rc) return rc;
-  return cfg->ratio == 1 ? KVC_OK : KVC_EINVAL;
+  if (cfg->ratio != 1) return KVC_EINVAL;
+  return cfg->rope_dim == 0 ? KVC_OK : KVC_EUNSUPPORTED;
 }
 
 bool overlapped(const kvc_config *cfg) { return cfg->ratio == 4; }
@@ -53,16 +55,26 @@ int check_projection_inputs(const kvc_config *cfg, const kvc_weights *w) {
   return KVC_OK;
 }
 
-int check_outputs(const kvc_outputs *out) {
+int check_outputs(const kvc_config *cfg, const kvc_outputs *out) {
   if (!out) return KVC_OK;
-  if (!aligned(out->latent) || !aligned(out->pooled) || !aligned(out->dequant)) return KVC_EINVAL;
+  if (!aligned(out->latent) || !aligned(out->pooled) || !aligned(out->dequant) || !aligned(out->rotated))
+    return KVC_EINVAL;
+  if (out->rotated && cfg->rope_dim == 0) return KVC_EINVAL;
   // codes rows are head_dim / 2 bytes: 64 or 256, each lane stores up to 4
   if (out->codes && (reinterpret_cast<uintptr_t>(out->codes) % 4) != 0) return KVC_EINVAL;
   return KVC_OK;
 }
 
 bool wants_entries(const kvc_outputs *out) {
-  return out && (out->latent || out->pooled || out->codes || out->scales || out->dequant);
+  return out && (out->latent || out->pooled || out->codes || out->scales || out->dequant || out->rotated);
+}
+
+// With RoPE, every entry written needs its table row: entries
+// [first, first + count) of the sequence.
+int check_rope(const kvc_config *cfg, const kvc_weights *w, int64_t first, int64_t count) {
+  if (cfg->rope_dim == 0 || count <= 0) return KVC_OK;
+  if (!w || !w->rope_cs || !aligned(w->rope_cs)) return KVC_EINVAL;
+  return first + count <= w->rope_rows ? KVC_OK : KVC_EINVAL;
 }
 
 // Decode splits the K range over workgroups so that about 256 of them (one
@@ -90,6 +102,11 @@ kvc::PoolArgs pool_args(const kvc_config *cfg, const kvc_weights *w, const kvc_o
   p.scales = out->scales;
   p.deq = out->dequant;
   p.e8m0 = cfg->fp4_format == KVC_FP4_E8M0_B32;
+  // the table is read only when entries are written (its rows are checked then)
+  p.rope_cs = (cfg->rope_dim > 0 && w && wants_entries(out)) ? w->rope_cs : nullptr;
+  p.rope_dim = cfg->rope_dim;
+  p.rope_row0 = 0;
+  p.rotated = out->rotated;
   return p;
 }
 
@@ -151,9 +168,10 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const float 
   if (!aligned(workspace)) return KVC_EINVAL;
   if ((kv_state == nullptr) != (score_state == nullptr)) return KVC_EINVAL;
   if (kv_state && (state_batch < batch || !aligned(kv_state) || !aligned(score_state))) return KVC_EINVAL;
-  if ((rc = check_outputs(out))) return rc;
+  if ((rc = check_outputs(cfg, out))) return rc;
 
   const int64_t groups = seqlen / cfg->ratio;
+  if (wants_entries(out) && (rc = check_rope(cfg, w, 0, groups))) return rc;
   if (n_groups) *n_groups = groups;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t m = batch * seqlen;
@@ -233,10 +251,13 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const fl
   if (workspace_floats < (int64_t)splits * 2 * batch * proj) return KVC_ESPACE;
   if (!kv_state || !score_state || state_batch < batch || !aligned(kv_state) || !aligned(score_state))
     return KVC_EINVAL;
-  if ((rc = check_outputs(out))) return rc;
+  if ((rc = check_outputs(cfg, out))) return rc;
 
   const int r = cfg->ratio;
   const bool emit = start_pos > 0 && (start_pos + 1) % r == 0;
+  // the emitted entry's index in the sequence (its RoPE table row)
+  const int64_t entry = (start_pos + 1) / r - 1;
+  if (emit && wants_entries(out) && (rc = check_rope(cfg, w, entry, 1))) return rc;
   if (emitted) *emitted = emit ? 1 : 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
@@ -287,6 +308,7 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const fl
   p.batch = batch;
   p.groups = 1;
   p.first_entry = overlapped(cfg) ? 1 : 0;
+  p.rope_row0 = entry;
   p.entries_per_wave = 1;
   p.out_batch_stride = 1;
   if (overlapped(cfg)) {
@@ -324,7 +346,7 @@ int compressor_ratio1_forward(const kvc_config *cfg, const uint16_t *wkv, const 
   if (!aligned(x) || !aligned(wkv) || !aligned(norm_w) || !aligned(workspace)) return KVC_EINVAL;
   const int64_t hd = cfg->head_dim;
   if (workspace_floats < tokens * hd) return KVC_ESPACE;
-  if ((rc = check_outputs(out))) return rc;
+  if ((rc = check_outputs(cfg, out))) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   kvc::GemmBf16Args g{};
@@ -378,6 +400,25 @@ int latent_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *c
 int indexer_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *codes, uint8_t *scales,
                       uint16_t *out, kvc_stream stream) {
   return fp4_quant(in, rows, width, codes, scales, out, 32, stream);
+}
+
+int latent_rope(const uint16_t *in, int64_t rows, int64_t width, int32_t rope_dim, const float *rope_cs,
+                int64_t rope_rows, int64_t first_row, uint16_t *out, kvc_stream stream) {
+  if (rows < 0 || width <= 0 || width % 2 != 0 || rope_dim <= 0 || rope_dim % 2 != 0 || rope_dim > width)
+    return KVC_EINVAL;
+  if (rows == 0) return KVC_OK;
+  if (!in || !out || !rope_cs || first_row < 0 || first_row + rows > rope_rows) return KVC_EINVAL;
+  // 4-byte pairs and 8-byte (cos, sin) loads
+  if (reinterpret_cast<uintptr_t>(in) % 4 || reinterpret_cast<uintptr_t>(out) % 4 ||
+      reinterpret_cast<uintptr_t>(rope_cs) % 8)
+    return KVC_EINVAL;
+  if (out != in) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(in), a1 = a0 + rows * width * 2;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(out), b1 = b0 + rows * width * 2;
+    if (a0 < b1 && b0 < a1) return KVC_EINVAL;
+  }
+  kvc::RopeArgs a{in, out, rows, width, rope_dim, rope_cs, first_row};
+  return hip_status(kvc::launch_rope(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
 const char *kvc_strerror(int code) {

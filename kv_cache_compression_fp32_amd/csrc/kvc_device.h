@@ -143,4 +143,40 @@ __device__ __forceinline__ void fp4_block_e8m0(const float (&y)[VEC], uint32_t &
   }
 }
 
+// bf16 bits of the exact sum p + q of two doubles, round to nearest even
+// (single rounding). hi = p + q rounded to double with the exact error lo
+// (TwoSum); lo can change the bf16 result only when hi lies exactly on a bf16
+// midpoint, and then hi moves one double step towards lo. hi is then rounded
+// to f32 with round-to-odd (toward zero, last bit set when inexact), and that
+// f32 to bf16 with round to nearest even: f32 keeps 16 more bits than bf16, so
+// the two steps round like one.
+__device__ __forceinline__ uint32_t bf16_of_sum(double p, double q) {
+  double hi = p + q;
+  const double z = hi - p;
+  const double lo = (p - (hi - z)) + (q - z);
+  float f = (float)hi;
+  const bool f_exact = (double)f == hi;
+  if (f_exact && lo != 0.0 && (as_u32(f) & 0xffffu) == 0x8000u) {
+    // move one double step towards lo (hi is nonzero here)
+    const uint64_t hb = (uint64_t)__double_as_longlong(hi);
+    const bool up = (lo > 0.0) == (hi > 0.0);  // away from zero?
+    hi = __longlong_as_double((long long)(up ? hb + 1 : hb - 1));
+    f = (float)hi;
+  }
+  if (__builtin_fabs((double)f) > __builtin_fabs(hi)) f = as_f32(as_u32(f) - 1u);  // toward zero
+  uint32_t u = as_u32(f);
+  if ((double)f != hi) u |= 1u;  // round to odd
+  return bf16_rne(as_f32(u));
+}
+
+// One rotary pair (a, b) of bf16 values turned by (c, s): the exact
+// a c - b s and a s + b c (products of a bf16 and an f32 value are exact in
+// double), each rounded once to bf16.
+__device__ __forceinline__ void rope_pair(float a, float b, float c, float s, uint32_t &r0, uint32_t &r1) {
+  const double da = a, db = b, dc = c, ds = s;
+  const double ac = da * dc, bs = db * ds, as = da * ds, bc = db * dc;
+  r0 = bf16_of_sum(ac, -bs);
+  r1 = bf16_of_sum(as, bc);
+}
+
 }  // namespace kvc

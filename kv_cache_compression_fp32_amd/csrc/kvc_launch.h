@@ -60,6 +60,10 @@ struct PoolArgs {
   uint8_t *codes, *scales;
   uint16_t *deq;
   int32_t e8m0;               // codes/scales in the power-of-two, block-32 form
+  const float *rope_cs;       // [rows][rope_dim / 2][2] (cos, sin), or null: no RoPE
+  int32_t rope_dim;           // rotary slice: the last rope_dim features
+  int64_t rope_row0;          // table row of output entry 0 (entry e uses row rope_row0 + e)
+  uint16_t *rotated;          // the latent after RoPE, or null
   int64_t out_batch_stride;   // entries per batch row in the outputs
   float *shift_kv, *shift_sc; // ratio 4: move the last block's rows to the previous rows, or null
 };
@@ -95,6 +99,18 @@ struct IngestArgs {
   int32_t slot, state_row, ratio, reset_prev;
 };
 hipError_t launch_decode_finish(const IngestArgs &g, const PoolArgs *pool, int head_dim, hipStream_t stream);
+
+// Standalone RoPE of bf16 rows: row r turns its last rope_dim features by
+// table row first_row + r. in may equal out.
+struct RopeArgs {
+  const uint16_t *in;
+  uint16_t *out;
+  int64_t rows, width;
+  int32_t rope_dim;
+  const float *rope_cs;  // [.][rope_dim / 2][2]
+  int64_t first_row;
+};
+hipError_t launch_rope(const RopeArgs &a, hipStream_t stream);
 
 // Standalone fp4 round trip of bf16 rows: e4m3 scales per block of 16, or
 // (e8m0 set) power-of-two scales per block of 32.

@@ -108,10 +108,12 @@ __device__ __forceinline__ void softmax_pool(const float (&k)[NC][VEC], const fl
 
 // Per-entry epilogue of one wavefront holding the entry's pooled features
 // (layout Lanes<HD>): optional f32 store, bf16 round, RMSNorm over the entry
-// (wave reduction), bf16 latent, fp4 codes / scales / dequantised values.
+// (wave reduction), bf16 latent, optional RoPE of the rotary slice (table row
+// rope_row; a lane's rotary pairs lie inside its own chunks), and the fp4
+// codes / scales / dequantised values of the cached (rotated, with RoPE) entry.
 template <int HD>
 __device__ __forceinline__ void finish_entry(const float (&p)[HD / kWave], const PoolArgs &a, int64_t out_row,
-                                             int lane) {
+                                             int64_t rope_row, int lane) {
   using L = Lanes<HD>;
   constexpr int VEC = L::VEC, QV = L::QV;
   if (a.pooled) store_row<HD>(a.pooled + out_row * HD, lane, p);
@@ -139,6 +141,26 @@ __device__ __forceinline__ void finish_entry(const float (&p)[HD / kWave], const
   if (a.latent) {
 #pragma unroll
     for (int h = 0; h < L::H; ++h) store_bf16_q<QV>(a.latent + out_row * HD + L::feature(lane, h), yb + h * QV);
+  }
+  if (a.rope_cs) {
+    const float *row = a.rope_cs + rope_row * a.rope_dim;
+    const int start = HD - a.rope_dim;
+#pragma unroll
+    for (int h = 0; h < L::H; ++h)
+#pragma unroll
+      for (int q = 0; q < QV; q += 2) {
+        const int f = L::feature(lane, h) + q, v = h * QV + q;
+        if (f >= start) {
+          const float2 cs = *reinterpret_cast<const float2 *>(row + (f - start));
+          rope_pair(y[v], y[v + 1], cs.x, cs.y, yb[v], yb[v + 1]);
+          y[v] = bf16_val(yb[v]);
+          y[v + 1] = bf16_val(yb[v + 1]);
+        }
+      }
+    if (a.rotated) {
+#pragma unroll
+      for (int h = 0; h < L::H; ++h) store_bf16_q<QV>(a.rotated + out_row * HD + L::feature(lane, h), yb + h * QV);
+    }
   }
   if (a.codes || a.scales || a.deq) {
 #pragma unroll
@@ -217,7 +239,7 @@ __device__ __forceinline__ void small_entry(const PoolArgs &a, int64_t b, int64_
   }
   float p[VEC];
   softmax_pool<NC, VEC>(ck, cs, p);
-  finish_entry<HD>(p, a, b * a.out_batch_stride + e, lane);
+  finish_entry<HD>(p, a, b * a.out_batch_stride + e, a.rope_row0 + e, lane);
 
   if constexpr (OV) {
     if (a.shift_kv) {
@@ -264,7 +286,7 @@ __global__ __launch_bounds__(256) void rows_finish_kernel(PoolArgs a) {
   if (e >= a.groups) return;
   float p[HD / kWave];
   load_row<HD>(a.kv + e * a.row_stride, lane, p);
-  finish_entry<HD>(p, a, e, lane);
+  finish_entry<HD>(p, a, e, a.rope_row0 + e, lane);
 }
 
 // Long groups (ratio 128). One workgroup of 512 threads per entry: thread t
@@ -356,7 +378,7 @@ __global__ __launch_bounds__(512) void pool_long_kernel(PoolArgs a) {
     }
     p[v] = num * __builtin_amdgcn_rcpf(den);
   }
-  finish_entry<HD>(p, a, b * a.out_batch_stride + e, lane);
+  finish_entry<HD>(p, a, b * a.out_batch_stride + e, a.rope_row0 + e, lane);
 }
 
 __global__ __launch_bounds__(256) void state_store_kernel(StateStoreArgs s) {

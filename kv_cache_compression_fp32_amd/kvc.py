@@ -34,18 +34,20 @@ class KvcError(RuntimeError):
 
 class _Config(ctypes.Structure):
     _fields_ = [("ratio", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("dim", ctypes.c_int64), ("eps", ctypes.c_float), ("fp4_format", ctypes.c_int32)]
+                ("dim", ctypes.c_int64), ("eps", ctypes.c_float), ("fp4_format", ctypes.c_int32),
+                ("rope_dim", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
     _fields_ = [("wkv", ctypes.c_void_p), ("wgate", ctypes.c_void_p),
-                ("ape", ctypes.c_void_p), ("norm_w", ctypes.c_void_p)]
+                ("ape", ctypes.c_void_p), ("norm_w", ctypes.c_void_p),
+                ("rope_cs", ctypes.c_void_p), ("rope_rows", ctypes.c_int64)]
 
 
 class _Outputs(ctypes.Structure):
     _fields_ = [("latent", ctypes.c_void_p), ("pooled", ctypes.c_void_p),
                 ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("dequant", ctypes.c_void_p)]
+                ("dequant", ctypes.c_void_p), ("rotated", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -65,6 +67,7 @@ _SIGNATURES = {
     "compressor_ratio1_forward": (ctypes.c_int, [ctypes.POINTER(_Config), _P, _P, _P, _I64, _P, _I64,
                                                  ctypes.POINTER(_Outputs), _P]),
     "latent_fp4_quant": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
+    "latent_rope": (ctypes.c_int, [_P, _I64, _I64, ctypes.c_int32, _P, _I64, _I64, _P, _P]),
     "indexer_fp4_quant": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
     "kvc_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "kvc_version": (ctypes.c_char_p, []),
@@ -102,13 +105,14 @@ class Config:
     dim: int = 0
     eps: float = 1e-6
     fp4_format: int = KVC_FP4_E4M3_B16
+    rope_dim: int = 0
 
     @property
     def fp4_block(self) -> int:
         return 32 if self.fp4_format == KVC_FP4_E8M0_B32 else 16
 
     def c(self) -> _Config:
-        return _Config(self.ratio, self.head_dim, self.dim, self.eps, self.fp4_format)
+        return _Config(self.ratio, self.head_dim, self.dim, self.eps, self.fp4_format, self.rope_dim)
 
 
 def kvc_proj_width(cfg: Config) -> int:
@@ -167,10 +171,13 @@ class Weights:
     wgate: torch.Tensor | None = None
     ape: torch.Tensor | None = None
     norm_w: torch.Tensor | None = None
+    rope_cs: torch.Tensor | None = None  # [rows, rope_dim // 2, 2] float32 (cos, sin)
 
     def c(self) -> _Weights:
+        rows = self.rope_cs.shape[0] if self.rope_cs is not None else 0
         return _Weights(_ptr(self.wkv, torch.float32, "wkv"), _ptr(self.wgate, torch.float32, "wgate"),
-                        _ptr(self.ape, torch.float32, "ape"), _ptr(self.norm_w, torch.float32, "norm_w"))
+                        _ptr(self.ape, torch.float32, "ape"), _ptr(self.norm_w, torch.float32, "norm_w"),
+                        _ptr(self.rope_cs, torch.float32, "rope_cs"), rows)
 
 
 @dataclass
@@ -180,6 +187,7 @@ class Outputs:
     codes: torch.Tensor | None = None    # uint8
     scales: torch.Tensor | None = None   # uint8
     dequant: torch.Tensor | None = None  # bf16
+    rotated: torch.Tensor | None = None  # bf16
 
     def c(self) -> _Outputs:
         def bf(t, n):
@@ -190,7 +198,7 @@ class Outputs:
             return _ptr(t, None, n)
         return _Outputs(bf(self.latent, "latent"), _ptr(self.pooled, torch.float32, "pooled"),
                         _ptr(self.codes, torch.uint8, "codes"), _ptr(self.scales, torch.uint8, "scales"),
-                        bf(self.dequant, "dequant"))
+                        bf(self.dequant, "dequant"), bf(self.rotated, "rotated"))
 
 
 def compressor_prefill(cfg: Config, w: Weights, x: torch.Tensor | None, batch: int, seqlen: int,
@@ -242,6 +250,19 @@ def compressor_ratio1_forward(cfg: Config, wkv: torch.Tensor, x: torch.Tensor, t
     _check(rc, "compressor_ratio1_forward")
 
 
+def latent_rope(inp: torch.Tensor, rope_dim: int, rope_cs: torch.Tensor, first_row: int = 0,
+                out: torch.Tensor | None = None, stream=None) -> None:
+    """Enqueue RoPE of [rows, width] bf16 rows (in place when out is None or
+    inp): row r turns its last rope_dim features by rope_cs[first_row + r]."""
+    if inp.dim() != 2:
+        raise ValueError("inp must be [rows, width]")
+    rows, width = inp.shape
+    dst = inp if out is None else out
+    rc = lib().latent_rope(_bf16_ptr(inp, "inp"), rows, width, rope_dim, _ptr(rope_cs, torch.float32, "rope_cs"),
+                           rope_cs.shape[0], first_row, _bf16_ptr(dst, "out"), _stream(stream))
+    _check(rc, "latent_rope")
+
+
 def _fp4_quant(fn, name, inp, codes, scales, out, stream):
     if inp.dim() != 2:
         raise ValueError("inp must be [rows, width]")
@@ -280,7 +301,7 @@ def new_state(cfg: Config, batch: int, device="cuda") -> tuple[torch.Tensor, tor
 
 
 def new_outputs(cfg: Config, batch: int, groups: int, latent=True, pooled=False, fp4=False,
-                dequant=False, device="cuda") -> Outputs:
+                dequant=False, rotated=False, device="cuda") -> Outputs:
     hd = cfg.head_dim
     o = Outputs()
     if latent:
@@ -292,4 +313,6 @@ def new_outputs(cfg: Config, batch: int, groups: int, latent=True, pooled=False,
         o.scales = torch.empty((batch, groups, hd // cfg.fp4_block), dtype=torch.uint8, device=device)
     if dequant:
         o.dequant = torch.empty((batch, groups, hd), dtype=torch.bfloat16, device=device)
+    if rotated:
+        o.rotated = torch.empty((batch, groups, hd), dtype=torch.bfloat16, device=device)
     return o

@@ -28,7 +28,7 @@ def host_bf16(t: torch.Tensor) -> np.ndarray:
 
 def weights(w: dict) -> kvc.Weights:
     return kvc.Weights(wkv=dev(w.get("wkv")), wgate=dev(w.get("wgate")), ape=dev(w.get("ape")),
-                       norm_w=dev(w.get("norm_w")))
+                       norm_w=dev(w.get("norm_w")), rope_cs=dev(w.get("rope_cs")))
 
 
 def outputs_to_host(o: kvc.Outputs) -> dict:
@@ -42,6 +42,8 @@ def outputs_to_host(o: kvc.Outputs) -> dict:
         res["scales"] = o.scales.cpu().numpy()
     if o.dequant is not None:
         res["dequant"] = host_bf16(o.dequant)
+    if o.rotated is not None:
+        res["rotated"] = host_bf16(o.rotated)
     return res
 
 
@@ -59,7 +61,8 @@ def prefill(cfg: kvc.Config, w: dict, batch: int, seqlen: int, x=None, kv=None, 
     if state is None:
         state = kvc.new_state(cfg, batch)
     groups = seqlen // cfg.ratio
-    out = kvc.new_outputs(cfg, batch, groups, latent=True, pooled=True, fp4=fp4, dequant=fp4)
+    out = kvc.new_outputs(cfg, batch, groups, latent=True, pooled=True, fp4=fp4, dequant=fp4,
+                          rotated=cfg.rope_dim > 0)
     n = kvc.compressor_prefill(cfg, weights(w), xd, batch, seqlen, ws, state[0], state[1], out)
     torch.cuda.synchronize()
     res = outputs_to_host(out) if groups > 0 else {}
@@ -73,8 +76,9 @@ def prefill(cfg: kvc.Config, w: dict, batch: int, seqlen: int, x=None, kv=None, 
 
 def oracle_cfg(cfg: kvc.Config) -> oracle.Config:
     return oracle.Config(ratio=cfg.ratio, head_dim=cfg.head_dim, dim=cfg.dim, eps=cfg.eps,
-                         fp4="e8m0" if cfg.fp4_format == kvc.KVC_FP4_E8M0_B32 else "e4m3")
+                         fp4="e8m0" if cfg.fp4_format == kvc.KVC_FP4_E8M0_B32 else "e4m3", rope_dim=cfg.rope_dim)
 
 
 def oracle_weights(w: dict) -> oracle.Weights:
-    return oracle.Weights(wkv=w.get("wkv"), wgate=w.get("wgate"), ape=w.get("ape"), norm_w=w.get("norm_w"))
+    return oracle.Weights(wkv=w.get("wkv"), wgate=w.get("wgate"), ape=w.get("ape"), norm_w=w.get("norm_w"),
+                          rope_cs=w.get("rope_cs"))

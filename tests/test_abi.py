@@ -177,3 +177,33 @@ def test_ratio1_argument_errors_return_before_enqueueing():
     assert call(ok, tokens=0, x=None, wkv=None, ws=None) == kvc.KVC_OK     # nothing to do
     # and the pooled entry points reject ratio 1
     assert _prefill_raw(kvc.Config(1, 512, 4096))[0] == kvc.KVC_EUNSUPPORTED
+
+
+def test_rope_arguments_are_checked():
+    lib = kvc.lib()
+    fake = 0x100000
+    # rope_dim: even, within the entry; not offered at ratio 1
+    for bad in (3, 514, -2):
+        with pytest.raises(kvc.KvcError):
+            kvc.kvc_proj_width(kvc.Config(4, 512, 4096, rope_dim=bad))
+    assert kvc.kvc_proj_width(kvc.Config(4, 512, 4096, rope_dim=64)) == 1024
+    with pytest.raises(kvc.KvcError) as err:
+        kvc.kvc_ratio1_workspace_floats(kvc.Config(1, 512, 4096, rope_dim=64), 8)
+    assert err.value.code == kvc.KVC_EUNSUPPORTED
+    cfg = kvc.Config(4, 512, 4096, rope_dim=64)
+    out = kvc._Outputs(fake)  # latent only
+    # entries written but no table, or a table with too few rows (16 tokens = 4 entries)
+    assert _prefill_raw(cfg, seqlen=16, ws=fake, ws_n=1 << 30, out=ctypes.byref(out))[0] == kvc.KVC_EINVAL
+    w = kvc._Weights(None, None, None, None, fake, 3)
+    assert _prefill_raw(cfg, w=w, seqlen=16, ws=fake, ws_n=1 << 30, out=ctypes.byref(out))[0] == kvc.KVC_EINVAL
+    # a rotated output without RoPE
+    rot = kvc._Outputs(None, None, None, None, None, fake)
+    assert _prefill_raw(kvc.Config(4, 512, 4096), seqlen=16, ws=fake, ws_n=1 << 30,
+                        out=ctypes.byref(rot))[0] == kvc.KVC_EINVAL
+    # the standalone rotation
+    assert lib.latent_rope(fake, 4, 512, 63, fake, 8, 0, fake, None) == kvc.KVC_EINVAL   # odd rope_dim
+    assert lib.latent_rope(fake, 4, 512, 1024, fake, 8, 0, fake, None) == kvc.KVC_EINVAL  # wider than a row
+    assert lib.latent_rope(fake, 4, 512, 64, fake, 8, 5, fake, None) == kvc.KVC_EINVAL    # rows past the table
+    assert lib.latent_rope(fake, 4, 512, 64, fake + 4, 8, 0, fake, None) == kvc.KVC_EINVAL  # misaligned table
+    assert lib.latent_rope(fake, 4, 512, 64, fake, 8, 0, fake + 64, None) == kvc.KVC_EINVAL  # partial overlap
+    assert lib.latent_rope(None, 0, 512, 64, None, 0, 0, None, None) == kvc.KVC_OK         # nothing to do

@@ -218,7 +218,8 @@ def _decode_gpu(cfg, w, batch, xs=None, kvs=None, scs=None, start=0, state=None,
     emitted = []
     for i in range(steps):
         p = start + i
-        out = kvc.new_outputs(cfg, batch, 1, latent=True, pooled=True, fp4=fp4, dequant=fp4)
+        out = kvc.new_outputs(cfg, batch, 1, latent=True, pooled=True, fp4=fp4, dequant=fp4,
+                              rotated=cfg.rope_dim > 0)
         if xd is None:
             ws[:batch * proj] = kvd[:, i].reshape(-1)
             ws[batch * proj:2 * batch * proj] = scd[:, i].reshape(-1)
@@ -414,3 +415,71 @@ def test_ratio1_power_of_two_fp4_and_outputs_subset():
     check_fp4(g["codes"][0], g["scales"][0], g["latent"][0], ref["codes"], ref["scales"], ref["latent"],
               g["dequant"][0], e8m0=True)
     assert np.array_equal(only.latent.view(torch.int16).cpu().numpy(), full.latent[0].view(torch.int16).cpu().numpy())
+
+
+# ---------------------------------------------------------------- RoPE
+def _yarn_table(rows, rope_dim, ratio):
+    # entry j stands for the last token of its group; YaRN-extended table
+    pos = np.arange(rows) * ratio + ratio - 1
+    return oracle.rope_table(pos, oracle.yarn_inv_freq(rope_dim, 10000.0, 16.0, 4096))
+
+
+def test_latent_rope_matches_oracle_exactly():
+    note("latent_rope: random rows, constructed bf16 midpoints, in place")
+    rng = np.random.default_rng(21)
+    rows, width, rd = 3000, 512, 64
+    lat = oracle.bf16_round((rng.standard_normal((rows, width)) * np.exp2(rng.integers(-8, 8, (rows, 1))))
+                            .astype(np.float32))
+    table = oracle.rope_table(rng.integers(0, 1 << 20, rows + 7), oracle.yarn_inv_freq(rd, 10000.0, 40.0, 4096))
+    # rows whose a c lands on a bf16 midpoint with b s below double resolution there
+    for r, sign in ((0, 1.0), (1, -1.0), (2, 1.0)):
+        lat[r, width - rd:] = 0.0
+        lat[r, width - rd + 2 * np.arange(rd // 2)] = 1.0
+        lat[r, width - rd + 1 + 2 * np.arange(rd // 2)] = 2.0 ** -40
+        table[7 + r, :, 0] = np.float32(1.0 + 2.0 ** -8)
+        table[7 + r, :, 1] = np.float32(-sign * 2.0 ** -30)
+    ref = oracle.apply_rope(lat, table[7:7 + rows], rd)
+    assert ref[0, width - rd] == np.float32(1.0 + 2.0 ** -7) and ref[1, width - rd] == np.float32(1.0)
+    bits = lat.view(np.uint32) >> 16
+    inp = torch.from_numpy(bits.astype(np.int32).astype(np.int16)).cuda()
+    out = torch.empty_like(inp)
+    tab = dev(table)
+    kvc.latent_rope(inp, rd, tab, first_row=7, out=out)
+    kvc.latent_rope(inp, rd, tab, first_row=7)  # in place
+    torch.cuda.synchronize()
+    for t in (out, inp):
+        got = host_bf16(t)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"{np.sum(got != ref)} values differ"
+
+
+@pytest.mark.parametrize("ratio,hd,batch,seqlen", [(4, 512, 2, 4 * 37 + 1), (2, 128, 2, 50), (128, 512, 1, 384 + 3)])
+def test_pool_with_rope_matches_oracle_and_decode(ratio, hd, batch, seqlen):
+    note(f"pool + RoPE ratio={ratio} hd={hd}")
+    from gpu_util import weights
+    rng = np.random.default_rng(ratio + hd + seqlen)
+    rd = 64
+    cfg = kvc.Config(ratio, hd, 0, rope_dim=rd)
+    proj = kvc.kvc_proj_width(cfg)
+    kv = rng.standard_normal((batch, seqlen, proj), dtype=np.float32)
+    sc = rng.standard_normal((batch, seqlen, proj), dtype=np.float32) * np.float32(2)
+    groups = seqlen // ratio
+    w = {"ape": rng.standard_normal((ratio, proj), dtype=np.float32) * np.float32(0.1),
+         "rope_cs": _yarn_table(groups + 2, rd, ratio)}
+    g = prefill(cfg, w, batch, seqlen, kv=kv, sc=sc)
+    plain = prefill(kvc.Config(ratio, hd, 0), {"ape": w["ape"]}, batch, seqlen, kv=kv, sc=sc)
+    # the compressor's own output is unrotated
+    assert np.array_equal(g["latent"].view(np.uint32), plain["latent"].view(np.uint32))
+    # entry j of every batch row turns by table row j, exactly as the oracle
+    rows = np.broadcast_to(w["rope_cs"][:groups], (batch, groups, rd // 2, 2))
+    ref_rot = oracle.apply_rope(g["latent"], rows, rd)
+    assert np.array_equal(g["rotated"].view(np.uint32), ref_rot.view(np.uint32))
+    # the cache form encodes the rotated entry
+    check_fp4(g["codes"], g["scales"], g["rotated"], gpu_dequant=g["dequant"])
+    # end to end against the oracle, and decode == prefill bitwise
+    ref = oracle.prefill(oracle_cfg(cfg), oracle_weights(w), oracle.State(oracle_cfg(cfg), batch), kv=kv, score=sc,
+                         quantize=True)
+    same = np.all(g["latent"] == ref["latent"], axis=-1)
+    assert np.array_equal(g["rotated"][same].view(np.uint32), ref["rotated"][same].view(np.uint32))
+    dec = _decode_gpu(cfg, weights(w), batch, kvs=kv, scs=sc)
+    for k in ("rotated", "codes", "scales", "dequant", "latent"):
+        assert np.array_equal(dec[k].view(np.uint8), g[k].view(np.uint8)), k
