@@ -38,7 +38,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # null as soon as any of them changes)
 KERNEL_SOURCES = {
     "gemm": ["kv_cache_compression_fp32_amd/csrc/gemm_common.h", "kv_cache_compression_fp32_amd/csrc/gemm_f32_kernel.h",
-             "kv_cache_compression_fp32_amd/csrc/gemm_f32.hip"],
+             "kv_cache_compression_fp32_amd/csrc/gemm_f32.hip", "kv_cache_compression_fp32_amd/csrc/kvc_device.h"],
     "pool": ["kv_cache_compression_fp32_amd/csrc/pool.hip", "kv_cache_compression_fp32_amd/csrc/kvc_device.h"],
 }
 

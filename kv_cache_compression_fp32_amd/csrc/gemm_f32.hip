@@ -29,4 +29,9 @@ hipError_t launch_gemm(const GemmArgs &g, GemmShape shape, hipStream_t stream) {
   return gemm::launch_tiled<128, 128, 64, 64, 4, 2, false>(g, stream);
 }
 
+hipError_t launch_gemm_pool(const GemmArgs &g, hipStream_t stream) {
+  if (g.m <= 0) return hipSuccess;
+  return gemm::launch_pooling(g, stream);
+}
+
 }  // namespace kvc

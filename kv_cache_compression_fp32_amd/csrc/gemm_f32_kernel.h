@@ -19,6 +19,7 @@
 #include <stdint.h>
 
 #include "gemm_common.h"
+#include "kvc_device.h"
 #include "kvc_launch.h"
 
 namespace kvc {
@@ -41,7 +42,20 @@ constexpr int kBK = 32;  // k per LDS stage
 // registers) runs after the barrier, behind the next tile's first LDS reads.
 // Rows of a ragged last row tile are clamped to the last row of A (loaded,
 // never stored).
-template <int BM, int BN, int WM, int WN, int NW, int MINW, bool DEFER>
+//
+// POOL (ratio 4, 256 x 256 tiles of eight 64 x 128 wavefronts): column tile nt
+// covers the 64 features f0 = 64 nt .. f0 + 63, and wavefront column wn the 32
+// features f0 + 32 wn .. +31 as four 32-column segments: kv branch A (wkv row
+// f), kv branch B (wkv row hd + f), score branch A (wgate row f), score branch
+// B (wgate row hd + f). A lane's accumulator then holds, for two features,
+// the four rows of one 4-token block of each segment: its own block's branch
+// A candidates. The previous block's branch B rows come from the lanes 16
+// below (the block above), through LDS (the idle stage buffers) so that the
+// first block of a wavefront reads the wavefront above. Each entry's pooled
+// f32 values go to g.pooled, computed by the same softmax code as the pool
+// kernels; the first entry of the row tile (whose previous block belongs to
+// another workgroup) is pooled afterwards from plane rows written here.
+template <int BM, int BN, int WM, int WN, int NW, int MINW, bool DEFER, bool POOL = false>
 __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
   constexpr int BK = kBK, G = BK / 4;
   constexpr int WAVES_N = BN / WN;
@@ -53,11 +67,17 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
   constexpr int A_INS = BM * BK / 256 / NW, B_INS = BN * BK / 256 / NW;  // 1 KiB loads per wavefront
   static_assert(A_INS >= 1 && B_INS >= 1 && BM * BK % (256 * NW) == 0 && BN * BK % (256 * NW) == 0,
                 "tile/wavefront mismatch");
-  __shared__ __attribute__((aligned(16))) float As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) float Bs[2][BN * BK];
+  static_assert(!POOL || (BM == 256 && BN == 256 && WM == 64 && WN == 128 && NW == 8), "pooling tile shape");
+  // branch-B exchange of the pooling epilogue: [4 wavefront rows][64 rows][2 x 64 + 4 pad]
+  constexpr int XROW = 132;
+  constexpr int STAGE_FLOATS = 2 * (BM + BN) * BK;
+  constexpr int SMEM_FLOATS = POOL && 4 * 64 * XROW > STAGE_FLOATS ? 4 * 64 * XROW : STAGE_FLOATS;
+  __shared__ __attribute__((aligned(16))) float smem[SMEM_FLOATS];
+  float(*As)[BM * BK] = reinterpret_cast<float(*)[BM * BK]>(smem);
+  float(*Bs)[BN * BK] = reinterpret_cast<float(*)[BN * BK]>(smem + 2 * BM * BK);
 
   const int64_t m_tiles = (g.m + BM - 1) / BM;
-  const int64_t n_tiles = 2 * g.n_half / BN;
+  const int64_t n_tiles = POOL ? g.pool_hd / 64 : 2 * g.n_half / BN;
   const uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t mt = tile / n_tiles, nt = tile - mt * n_tiles;
   if (mt >= m_tiles) return;
@@ -80,7 +100,16 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
   // tile's first row; the k offset is wavefront-uniform.
   const int64_t a_rows = (g.m - m0 < BM) ? (g.m - m0) : BM;
   const i32x4 a_rsrc = make_rsrc(g.a + m0 * g.lda, (uint32_t)(a_rows * g.lda * 4));
-  const i32x4 b_rsrc = make_rsrc(B + n0 * g.ldb, (uint32_t)(BN * g.ldb * 4));
+  // B rows of this wavefront's loads: n0 + 8 (wave INS + u) + l / 8; with
+  // POOL, the 32 rows of segment wave % 4 for features f0 + 32 (wave / 4) ..
+  // (the wavefront's own resource, its rows from the resource's start)
+  const int64_t f0 = 64 * nt;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const i32x4 b_rsrc =
+      POOL ? make_rsrc((wave_u & 3) < 2 ? g.b0 + (((wave_u & 1) * g.pool_hd + f0 + 32 * (wave_u >> 2)) * g.ldb)
+                                        : g.b1 + (((wave_u & 1) * g.pool_hd + f0 + 32 * (wave_u >> 2)) * g.ldb),
+                       (uint32_t)(32 * g.ldb * 4))
+           : make_rsrc(B + n0 * g.ldb, (uint32_t)(BN * g.ldb * 4));
   const int lr = lane / G, lq = (lane % G) ^ (lr & 7);
   uint32_t a_voff[A_INS];
 #pragma unroll
@@ -89,7 +118,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
     if (r >= a_rows) r = a_rows - 1;  // ragged last tile: read a valid row, never store it
     a_voff[u] = (uint32_t)((r * g.lda + 4 * lq) * 4);
   }
-  const uint32_t b_voff = (uint32_t)(((8 * wave * B_INS + lr) * g.ldb + 4 * lq) * 4);
+  const uint32_t b_voff = (uint32_t)(((POOL ? 0 : 8 * wave * B_INS) + lr) * g.ldb * 4 + 4 * lq * 4);
   auto issue = [&](int kt, int st) {
     const uint32_t koff = (uint32_t)((k_begin + (int64_t)kt * BK) * 4);
 #pragma unroll
@@ -158,24 +187,100 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
   }
   if (DEFER) mfma_slice(LAST, 3);
 
-  const float *bias = second ? g.bias1 : nullptr;
+  if constexpr (POOL) {
+    // ---- pooling epilogue (see above) ----
+    const int g4 = lane >> 4, c = lane & 15;
+    const int64_t hd = g.pool_hd, seqlen = g.pool_seqlen, groups = g.pool_groups;
+    const int64_t gpr = seqlen / 4;  // 4-token blocks per batch row (batch > 1 needs seqlen % 4 == 0)
+    // the state's source rows: from the last complete block of each batch row on
+    const int64_t state_from = groups > 0 ? 4 * (groups - 1) : 0;
+    float *X = smem;
+    __syncthreads();  // every wavefront is done with the stage buffers
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = m0 + wm * WM + 16 * i + 4 * slot + r;
-      if (row < g.m) {
-        float *crow = C + row * g.ldc + n0 + wn * WN + row_in;
-        if (bias) {
-          const float *brow = bias + ((row % g.bias_seqlen) % g.bias_ratio) * g.ldc + n0 + wn * WN + row_in;
+      for (int jj = 0; jj < 2; ++jj) {
+        const int64_t f = f0 + 32 * wn + 16 * jj + c;
+        f4 &kA = acc[i][jj], &kB = acc[i][2 + jj], &sA = acc[i][4 + jj], &sB = acc[i][6 + jj];
 #pragma unroll
-          for (int j = 0; j < FN; ++j) crow[16 * j] = acc[i][j][r] + brow[16 * j];
-        } else {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) crow[16 * j] = acc[i][j][r];
+        for (int r = 0; r < 4; ++r) {
+          const int rl = 16 * i + 4 * g4 + r;  // row within the wavefront
+          const int64_t row = m0 + wm * WM + rl;
+          if (g.bias1) {  // token position mod 4 is r: blocks start at multiples of 4
+            sA[r] = sA[r] + g.bias1[r * g.ldc + f];
+            sB[r] = sB[r] + g.bias1[r * g.ldc + hd + f];
+          }
+          if (row < g.m) {
+            const int64_t tpos = g.pool_batch == 1 ? row : row % seqlen;
+            const int tile_row = wm * WM + rl;
+            const bool state_row = tpos >= state_from;
+            float *kv = g.c0 + row * g.ldc, *sc = g.c1 + row * g.ldc;
+            if (state_row || tile_row < 4) {  // branch A: state rows and the tile's first block
+              kv[f] = kA[r];
+              sc[f] = sA[r];
+            }
+            if (state_row || tile_row >= BM - 4) {  // branch B: state rows and the tile's last block
+              kv[hd + f] = kB[r];
+              sc[hd + f] = sB[r];
+            }
+          }
+          X[(wm * 64 + rl) * XROW + wn * 64 + 16 * jj + c] = kB[r];
+          X[(wm * 64 + rl) * XROW + wn * 64 + 32 + 16 * jj + c] = sB[r];
         }
       }
+    __syncthreads();  // branch B of every block is in LDS
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t gf = (m0 + wm * WM + 16 * i) / 4 + g4;  // 4-token block of the flattened rows
+      const int64_t b = g.pool_batch == 1 ? 0 : gf / gpr;
+      const int64_t j = g.pool_batch == 1 ? gf : gf - b * gpr;
+      // entries of complete blocks; the row tile's first entry needs the
+      // previous workgroup's block and is pooled afterwards (unless it is
+      // its batch row's entry 0, whose previous block is padding)
+      const bool first_of_tile = wm == 0 && i == 0 && g4 == 0;
+      if (b >= g.pool_batch || j >= groups || (first_of_tile && j > 0)) continue;
+      // the previous block's rows in LDS: 4 rows up, into the wavefront above
+      const int prow = wm * 64 + 16 * i + 4 * g4 - 4;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        float ck[8][1], cs[8][1];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (j == 0) {
+            ck[r][0] = 0.0f;
+            cs[r][0] = -INFINITY;
+          } else {
+            ck[r][0] = X[(prow + r) * XROW + wn * 64 + 16 * jj + c];
+            cs[r][0] = X[(prow + r) * XROW + wn * 64 + 32 + 16 * jj + c];
+          }
+          ck[4 + r][0] = acc[i][jj][r];
+          cs[4 + r][0] = acc[i][4 + jj][r];
+        }
+        float p[1];
+        softmax_pool<8, 1>(ck, cs, p);
+        g.pooled[(b * groups + j) * hd + f0 + 32 * wn + 16 * jj + c] = p[0];
+      }
     }
+  } else {
+    const float *bias = second ? g.bias1 : nullptr;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + wm * WM + 16 * i + 4 * slot + r;
+        if (row < g.m) {
+          float *crow = C + row * g.ldc + n0 + wn * WN + row_in;
+          if (bias) {
+            const float *brow = bias + ((row % g.bias_seqlen) % g.bias_ratio) * g.ldc + n0 + wn * WN + row_in;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) crow[16 * j] = acc[i][j][r] + brow[16 * j];
+          } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) crow[16 * j] = acc[i][j][r];
+          }
+        }
+      }
+  }
 }
 
 // Decode projection (M = batch rows, 64 per row tile in blockIdx.z): 32
@@ -280,6 +385,19 @@ inline hipError_t launch_decode_gemm(const GemmArgs &g, hipStream_t stream) {
   if (g.n_half % 32 != 0 || g.k % 16 != 0 || g.splits < 1 || g.bias1) return hipErrorInvalidValue;
   const dim3 grid((uint32_t)(2 * g.n_half / 32), (uint32_t)g.splits, (uint32_t)((g.m + 63) / 64));
   hipLaunchKernelGGL(decode_gemm_kernel<4>, grid, dim3(512), 0, stream, g);
+  return hipGetLastError();
+}
+
+inline hipError_t launch_pooling(const GemmArgs &g, hipStream_t stream) {
+  // whole 32-k stages, 64-feature column tiles, 4-token blocks aligned with
+  // the flattened rows, tile rows addressable with 32-bit buffer offsets
+  if (g.k % kBK != 0 || g.pool_hd % 64 != 0 || g.ldc != 2 * g.pool_hd || g.lda < g.k || g.ldb < g.k ||
+      g.m != g.pool_batch * g.pool_seqlen || (g.pool_batch > 1 && g.pool_seqlen % 4 != 0) || !g.pooled ||
+      (int64_t)256 * g.lda * 4 > INT32_MAX || (int64_t)32 * g.ldb * 4 > INT32_MAX)
+    return hipErrorInvalidValue;
+  const int64_t m_tiles = (g.m + 255) / 256;
+  hipLaunchKernelGGL((gemm_f32_kernel<256, 256, 64, 128, 8, 1, true, true>),
+                     dim3((uint32_t)(m_tiles * (g.pool_hd / 64))), dim3(512), 0, stream, g);
   return hipGetLastError();
 }
 

@@ -91,6 +91,23 @@ int32_t decode_splits(const kvc_config *cfg, int64_t batch) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_EHIP; }
 
+// Ratio 4: f32 pooled entries of the fused projection + pooling path, after
+// the two projection planes in the prefill workspace.
+int64_t pooled_floats(const kvc_config *cfg, int64_t batch, int64_t seqlen) {
+  return overlapped(cfg) ? batch * (seqlen / cfg->ratio) * cfg->head_dim : 0;
+}
+
+// The fused path (projection GEMM with pooling in its epilogue) needs 4-token
+// blocks aligned with the flattened rows and enough 256 x 256 tiles to fill
+// the chip twice; smaller problems run the GEMM and pool kernels separately.
+bool use_fused_pooling(const kvc_config *cfg, int64_t batch, int64_t seqlen, int64_t workspace_floats) {
+  if (!overlapped(cfg) || seqlen / cfg->ratio == 0) return false;
+  if (batch > 1 && seqlen % 4 != 0) return false;
+  const int64_t m = batch * seqlen;
+  if (kvc::gemm_pool_row_tiles(m) * (cfg->head_dim / 64) < 512) return false;
+  return workspace_floats >= 2 * m * proj_of(cfg) + pooled_floats(cfg, batch, seqlen);
+}
+
 kvc::PoolArgs pool_args(const kvc_config *cfg, const kvc_weights *w, const kvc_outputs *out) {
   kvc::PoolArgs p{};
   p.ape = w ? w->ape : nullptr;
@@ -138,7 +155,7 @@ int64_t kvc_prefill_workspace_floats(const kvc_config *cfg, int64_t batch, int64
   const int rc = check_config(cfg);
   if (rc) return rc;
   if (batch < 1 || seqlen < 0) return KVC_EINVAL;
-  return 2 * batch * seqlen * proj_of(cfg);
+  return 2 * batch * seqlen * proj_of(cfg) + pooled_floats(cfg, batch, seqlen);
 }
 
 int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch) {
@@ -178,6 +195,7 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const float 
   float *kv_plane = workspace;
   float *sc_plane = workspace ? workspace + m * proj : nullptr;
 
+  const bool fused = x && m > 0 && wants_entries(out) && use_fused_pooling(cfg, batch, seqlen, workspace_floats);
   if (x && m > 0) {
     kvc::GemmArgs g{};
     g.a = x;
@@ -197,11 +215,43 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const float 
     g.bias1 = w->ape;
     g.bias_seqlen = seqlen;
     g.bias_ratio = cfg->ratio;
-    if ((rc = hip_status(kvc::launch_gemm(g, kvc::GemmShape::kPrefill, s)))) return rc;
+    if (fused) {
+      g.pooled = workspace + 2 * m * proj;
+      g.pool_batch = batch;
+      g.pool_seqlen = seqlen;
+      g.pool_groups = groups;
+      g.pool_hd = cfg->head_dim;
+      if ((rc = hip_status(kvc::launch_gemm_pool(g, s)))) return rc;
+    } else if ((rc = hip_status(kvc::launch_gemm(g, kvc::GemmShape::kPrefill, s)))) {
+      return rc;
+    }
   }
   // projections the caller put in the workspace carry no bias yet
   const float *ape_after = x ? nullptr : (w ? w->ape : nullptr);
-  if (groups > 0 && wants_entries(out)) {
+  if (fused) {
+    // pooled entries of the fused GEMM, then the row tiles' first entries,
+    // then the per-entry epilogue over the pooled rows
+    float *pooled = workspace + 2 * m * proj;
+    kvc::PoolArgs pb{};
+    pb.kv = kv_plane;
+    pb.sc = sc_plane;
+    pb.row_stride = proj;
+    pb.batch_stride = seqlen * proj;
+    pb.batch = batch;
+    pb.groups = groups;
+    pb.eps = cfg->eps;
+    pb.pooled = pooled;
+    pb.out_batch_stride = groups;
+    if ((rc = hip_status(kvc::launch_pool_boundary(pb, kvc::gemm_pool_row_tiles(m), seqlen, cfg->head_dim, s))))
+      return rc;
+    kvc::PoolArgs pf = pool_args(cfg, w, out);
+    pf.kv = pooled;
+    pf.row_stride = cfg->head_dim;
+    pf.batch = 1;
+    pf.groups = batch * groups;
+    pf.out_batch_stride = groups;
+    if ((rc = hip_status(kvc::launch_rows_finish(pf, cfg->head_dim, s)))) return rc;
+  } else if (groups > 0 && wants_entries(out)) {
     kvc::PoolArgs p = pool_args(cfg, w, out);
     p.ape = ape_after;
     p.kv = kv_plane;

@@ -69,6 +69,29 @@ __device__ __forceinline__ float e2m1_val(uint32_t c) {
   return (c & 8u) ? -v : v;
 }
 
+// Softmax-weighted sum over NC candidates for each of VEC features, f32
+// (the pooling formula of "DeepSeek V4.1 . Pool token pairs"). Shared by the
+// pool kernels and the pooling GEMM epilogue, so both give the same bits.
+// Candidates with logit -inf get weight exactly 0 (exp2(-inf) = 0).
+template <int NC, int VEC>
+__device__ __forceinline__ void softmax_pool(const float (&k)[NC][VEC], const float (&s)[NC][VEC],
+                                             float (&out)[VEC]) {
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    float m = s[0][v];
+#pragma unroll
+    for (int i = 1; i < NC; ++i) m = __builtin_fmaxf(m, s[i][v]);
+    float den = 0.0f, num = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const float e = __builtin_amdgcn_exp2f((s[i][v] - m) * kLog2e);
+      den += e;
+      num = __builtin_fmaf(e, k[i][v], num);
+    }
+    out[v] = num * __builtin_amdgcn_rcpf(den);  // den in [1, NC]: v_rcp_f32 is within 1 ulp
+  }
+}
+
 // Sum over all 64 lanes; every lane receives the same bits (each butterfly
 // step adds the same two operands in both lanes of a pair).
 __device__ __forceinline__ float wave_sum(float v) {

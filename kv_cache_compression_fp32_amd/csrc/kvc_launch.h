@@ -26,12 +26,29 @@ struct GemmArgs {
   const float *bias1;   // [bias_ratio][ldc] or null (splits must be 1)
   int64_t bias_seqlen;
   int32_t bias_ratio;
+  // Pooling epilogue (ratio 4, launch_gemm_pool): the kernel computes the
+  // kv and score values of both branches of 64 features per column tile and
+  // pools every entry inside its row tile into `pooled`; the first entry of
+  // each row tile is left to launch_pool_boundary. Rows written to c0 / c1
+  // (with the bias on the score plane): the first block of each row tile
+  // (branch A), its last block (branch B), and every row from the last
+  // complete block of each batch row on (the state's source).
+  float *pooled;        // [pool_batch][pool_groups][pool_hd] f32
+  int64_t pool_batch, pool_seqlen, pool_groups;
+  int32_t pool_hd;
 };
 
 // Prefill tiles need n_half % 128 == 0 and k % 32 == 0; decode needs
 // n_half % 32 == 0 and k % 16 == 0 (any split count; no bias).
 enum class GemmShape { kPrefill, kDecode };
 hipError_t launch_gemm(const GemmArgs &g, GemmShape shape, hipStream_t stream);
+
+// The ratio-4 projection with pooling in the epilogue (fields above):
+// b0 = wkv, b1 = wgate ([2 * pool_hd][k] each), m = pool_batch * pool_seqlen,
+// needs pool_batch == 1 or pool_seqlen % 4 == 0, k % 32 == 0.
+hipError_t launch_gemm_pool(const GemmArgs &g, hipStream_t stream);
+// Number of 256-row tiles of launch_gemm_pool (the boundary entries' count + 1).
+inline int64_t gemm_pool_row_tiles(int64_t m) { return (m + 255) / 256; }
 
 // Ratio-1 projection: C[m][n] = sum_k A[m][k] * B[n][k], bf16 A and B, f32
 // accumulation and output, bf16 MFMA. Needs k % 64 == 0 and n % 128 == 0.
@@ -73,6 +90,13 @@ hipError_t launch_pool(const PoolArgs &p, int ratio, int head_dim, hipStream_t s
 // `groups` rows of f32 projections, row e at kv + e * row_stride; one entry
 // per row (batch 1 in the PoolArgs; sc, ape and the shift are unused).
 hipError_t launch_rows_finish(const PoolArgs &p, int head_dim, hipStream_t stream);
+
+// Ratio 4 after launch_gemm_pool: pools the first entry of every row tile but
+// the first (entry 64 t of the flattened sequence, when it is not the first
+// entry of its batch row) from the plane rows that kernel wrote, into
+// p.pooled (only output set). p describes the planes as for launch_pool.
+hipError_t launch_pool_boundary(const PoolArgs &p, int64_t row_tiles, int64_t seqlen, int head_dim,
+                                hipStream_t stream);
 
 // Writes the carry of a prefill into the state planes (ratio 4: last complete
 // block or padding, then the trailing tokens; other ratios: trailing tokens).

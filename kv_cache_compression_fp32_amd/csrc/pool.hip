@@ -85,27 +85,6 @@ __device__ __forceinline__ void store_row(float *base, int lane, const float (&d
   for (int h = 0; h < L::H; ++h) store_q<L::QV>(base + L::feature(lane, h), d + h * L::QV);
 }
 
-// Softmax-weighted sum over NC candidates for each of VEC features, f32.
-// Candidates with logit -inf get weight exactly 0 (exp2(-inf) = 0).
-template <int NC, int VEC>
-__device__ __forceinline__ void softmax_pool(const float (&k)[NC][VEC], const float (&s)[NC][VEC],
-                                             float (&out)[VEC]) {
-#pragma unroll
-  for (int v = 0; v < VEC; ++v) {
-    float m = s[0][v];
-#pragma unroll
-    for (int i = 1; i < NC; ++i) m = __builtin_fmaxf(m, s[i][v]);
-    float den = 0.0f, num = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const float e = __builtin_amdgcn_exp2f((s[i][v] - m) * kLog2e);
-      den += e;
-      num = __builtin_fmaf(e, k[i][v], num);
-    }
-    out[v] = num * __builtin_amdgcn_rcpf(den);  // den in [1, NC]: v_rcp_f32 is within 1 ulp
-  }
-}
-
 // Per-entry epilogue of one wavefront holding the entry's pooled features
 // (layout Lanes<HD>): optional f32 store, bf16 round, RMSNorm over the entry
 // (wave reduction), bf16 latent, optional RoPE of the rotary slice (table row
@@ -286,7 +265,24 @@ __global__ __launch_bounds__(256) void rows_finish_kernel(PoolArgs a) {
   if (e >= a.groups) return;
   float p[HD / kWave];
   load_row<HD>(a.kv + e * a.row_stride, lane, p);
-  finish_entry<HD>(p, a, e, a.rope_row0 + e, lane);
+  // rows are [batch][entries]: the RoPE row is the entry's index in its batch row
+  finish_entry<HD>(p, a, e, a.rope_row0 + e % a.out_batch_stride, lane);
+}
+
+// Ratio 4 after the pooling GEMM: the first entry of every row tile t >= 1
+// (4-token block 64 t of the flattened rows) whose previous block belongs to
+// the row tile above, pooled by the small-group code from the plane rows the
+// GEMM wrote; only p.pooled is written.
+template <int HD>
+__global__ __launch_bounds__(256) void pool_boundary_kernel(PoolArgs a, int64_t row_tiles, int64_t seqlen) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t = 1 + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= row_tiles) return;
+  const int64_t gf = 64 * t;
+  const int64_t b = a.batch == 1 ? 0 : gf / (seqlen / 4);
+  const int64_t j = a.batch == 1 ? gf : gf - b * (seqlen / 4);
+  if (b >= a.batch || j == 0 || j >= a.groups) return;
+  small_entry<HD, 4, true>(a, b, j, lane);
 }
 
 // Long groups (ratio 128). One workgroup of 512 threads per entry: thread t
@@ -528,6 +524,18 @@ hipError_t launch_rows_finish(const PoolArgs &p, int head_dim, hipStream_t strea
   switch (head_dim) {
     case 512: hipLaunchKernelGGL(rows_finish_kernel<512>, grid, block, 0, stream, p); break;
     case 128: hipLaunchKernelGGL(rows_finish_kernel<128>, grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_boundary(const PoolArgs &p, int64_t row_tiles, int64_t seqlen, int head_dim,
+                                hipStream_t stream) {
+  if (row_tiles <= 1 || p.groups <= 0) return hipSuccess;
+  const dim3 grid((uint32_t)((row_tiles - 1 + 3) / 4)), block(256);
+  switch (head_dim) {
+    case 512: hipLaunchKernelGGL(pool_boundary_kernel<512>, grid, block, 0, stream, p, row_tiles, seqlen); break;
+    case 128: hipLaunchKernelGGL(pool_boundary_kernel<128>, grid, block, 0, stream, p, row_tiles, seqlen); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -56,7 +56,7 @@ def prefill(cfg: kvc.Config, w: dict, batch: int, seqlen: int, x=None, kv=None, 
     if x is None and x_dev is None:
         m = batch * seqlen * proj
         ws[:m] = dev(kv).reshape(-1)
-        ws[m:] = dev(sc).reshape(-1)
+        ws[m:2 * m] = dev(sc).reshape(-1)
     xd = x_dev if x_dev is not None else dev(x)
     if state is None:
         state = kvc.new_state(cfg, batch)
@@ -70,7 +70,7 @@ def prefill(cfg: kvc.Config, w: dict, batch: int, seqlen: int, x=None, kv=None, 
     res["state_kv"] = state[0].cpu().numpy()
     res["state_sc"] = state[1].cpu().numpy()
     res["proj_kv"] = ws[:batch * seqlen * proj].reshape(batch, seqlen, proj).cpu().numpy()
-    res["proj_sc"] = ws[batch * seqlen * proj:].reshape(batch, seqlen, proj).cpu().numpy()
+    res["proj_sc"] = ws[batch * seqlen * proj:2 * batch * seqlen * proj].reshape(batch, seqlen, proj).cpu().numpy()
     return res
 
 

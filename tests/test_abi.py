@@ -49,7 +49,9 @@ def test_sizes(ratio, hd, proj, rows):
     cfg = kvc.Config(ratio, hd, 4096)
     assert kvc.kvc_proj_width(cfg) == proj
     assert kvc.kvc_state_rows(cfg) == rows
-    assert kvc.kvc_prefill_workspace_floats(cfg, 3, 100) == 2 * 3 * 100 * proj
+    # the two projection planes, and at ratio 4 the pooled entries of the fused path
+    pooled = 3 * (100 // ratio) * hd if ratio == 4 else 0
+    assert kvc.kvc_prefill_workspace_floats(cfg, 3, 100) == 2 * 3 * 100 * proj + pooled
     ws = kvc.kvc_decode_workspace_floats(cfg, 64)
     assert ws >= 2 * 64 * proj and ws % (2 * 64 * proj) == 0
 

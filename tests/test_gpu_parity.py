@@ -179,6 +179,15 @@ def test_projection_gemm_and_full_prefill(ratio, hd, dim, batch, seqlen):
          "wgate": rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.02),
          "ape": rng.standard_normal((ratio, proj), dtype=np.float32) * np.float32(0.1)}
     g = prefill(cfg, w, batch, seqlen, x=x)
+    # the projection planes of a GEMM-only call (a ratio-4 prefill with
+    # outputs may pool inside the GEMM and write only the rows it needs)
+    from gpu_util import weights
+    ws = torch.empty(kvc.kvc_prefill_workspace_floats(cfg, batch, seqlen), dtype=torch.float32, device="cuda")
+    kvc.compressor_prefill(cfg, weights(w), dev(x), batch, seqlen, ws)
+    torch.cuda.synchronize()
+    m = batch * seqlen * proj
+    g["proj_kv"] = ws[:m].view(batch, seqlen, proj).cpu().numpy()
+    g["proj_sc"] = ws[m:2 * m].view(batch, seqlen, proj).cpu().numpy()
     # projections: inside the worst-case bound of any f32 summation order,
     # dim * 2^-24 * sum |x| |w| (plus one rounding of the bias addition on the
     # score plane), and 1e-5 of each row's largest value
@@ -483,3 +492,66 @@ def test_pool_with_rope_matches_oracle_and_decode(ratio, hd, batch, seqlen):
     dec = _decode_gpu(cfg, weights(w), batch, kvs=kv, scs=sc)
     for k in ("rotated", "codes", "scales", "dequant", "latent"):
         assert np.array_equal(dec[k].view(np.uint8), g[k].view(np.uint8)), k
+
+
+# ---------------------------------------------------------------- fused projection + pooling
+FUSED_CASES = [
+    # head_dim, batch, seqlen, dim, options
+    (512, 1, 16384 + 4 * 7 + 3, 64, "norm"),    # ragged last row tile, 3 tail tokens
+    (512, 4, 4100, 64, "rope"),                  # row tiles straddle batch rows
+    (128, 1, 65536 + 9, 64, "e8m0"),             # 128-wide: two column tiles
+]
+
+
+@pytest.mark.parametrize("hd,batch,seqlen,dim,opt", FUSED_CASES)
+def test_fused_pooling_equals_separate_kernels_bitwise(hd, batch, seqlen, dim, opt):
+    note(f"fused GEMM + pool hd={hd} batch={batch} seqlen={seqlen} {opt}")
+    from gpu_util import weights
+    rng = np.random.default_rng(hd + batch + seqlen)
+    cfg = kvc.Config(4, hd, dim, rope_dim=64 if opt == "rope" else 0,
+                     fp4_format=kvc.KVC_FP4_E8M0_B32 if opt == "e8m0" else kvc.KVC_FP4_E4M3_B16)
+    proj = 2 * hd
+    groups = seqlen // 4
+    x = rng.standard_normal((batch, seqlen, dim), dtype=np.float32)
+    w = {"wkv": rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.1),
+         "wgate": rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.1),
+         "ape": rng.standard_normal((4, proj), dtype=np.float32) * np.float32(0.1)}
+    if opt == "norm":
+        w["norm_w"] = (1.0 + 0.1 * rng.standard_normal(hd)).astype(np.float32)
+    if opt == "rope":
+        w["rope_cs"] = _yarn_table(groups, 64, 4)
+    W = weights(w)
+    xd = dev(x)
+    outs = lambda: kvc.new_outputs(cfg, batch, groups, latent=True, pooled=True, fp4=True, dequant=True,  # noqa: E731
+                                   rotated=cfg.rope_dim > 0)
+    # fused: projection with pooling in the GEMM epilogue (NaN sentinel in the planes)
+    ws = torch.full((kvc.kvc_prefill_workspace_floats(cfg, batch, seqlen),), float("nan"), device="cuda")
+    st_f = kvc.new_state(cfg, batch)
+    fused = outs()
+    kvc.compressor_prefill(cfg, W, xd, batch, seqlen, ws, st_f[0], st_f[1], fused)
+    # separate: the GEMM alone (planes with the bias), then the pool kernel on them
+    ws2 = torch.empty_like(ws)
+    kvc.compressor_prefill(cfg, W, xd, batch, seqlen, ws2)
+    st_u = kvc.new_state(cfg, batch)
+    sep = outs()
+    kvc.compressor_prefill(cfg, kvc.Weights(norm_w=W.norm_w, rope_cs=W.rope_cs), None, batch, seqlen, ws2,
+                           st_u[0], st_u[1], sep)
+    torch.cuda.synchronize()
+    # the fused path ran: interior plane rows were never written
+    planes = ws[:2 * batch * seqlen * proj].view(2, batch * seqlen, proj)
+    assert torch.isnan(planes[0, 100, 0]).item() and torch.isnan(planes[1, 1000, hd]).item()
+    a, b = outputs_to_host(fused), outputs_to_host(sep)
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+    live = _live_rows(4, seqlen)
+    assert np.array_equal(st_f[0][:, live].cpu().numpy(), st_u[0][:, live].cpu().numpy())
+    assert np.array_equal(st_f[1][:, live].cpu().numpy(), st_u[1][:, live].cpu().numpy())
+    # and sampled entries against the oracle
+    ent = np.array(sorted(set([0, 1, 63, 64, 65, 127, 128, groups - 1]) | set(rng.choice(groups, 40).tolist())))
+    ocfg = oracle_cfg(cfg)
+    for bb in range(batch):
+        ref = oracle.prefill(ocfg, oracle_weights(w), oracle.State(ocfg, 1), x=x[bb:bb + 1], quantize=True,
+                             entries=ent)
+        check_pooled(a["pooled"][bb][ent], ref["pooled"][0])
+        check_latent(a["latent"][bb][ent], a["pooled"][bb][ent], ref["latent"][0], ref["pooled"][0],
+                     w.get("norm_w"), cfg.eps)
