@@ -4,16 +4,23 @@
 
 One step is one pass of the whole path over one batch: for the default
 workload (ratio-4 prefill of 65536 tokens, hidden 4096) that is the 512-wide
-compressor (fp32 projection GEMM, fused pool + RMSNorm + fp4 cache codes) and
-the 128-wide indexer compressor (GEMM, pool + RMSNorm, bf16 latent), with the
-hidden states resident in HBM. Prints one JSON line.
+compressor (f32 projections, pooling + RMSNorm + fp4 cache codes) and the
+128-wide indexer compressor (projections, pooling + RMSNorm, bf16 latent),
+with the hidden states resident in HBM. The hidden states are the model's
+bf16 ones (--x-format f32 passes the same values as f32 rows): the
+projections are f32 products of bf16 x and f32 weights either way, computed
+from the weights' three exact bf16 parts on the bf16 matrix cores for bf16 x,
+on the f32 matrix cores for f32 x. The other x format's step is reported
+beside the headline. Prints one JSON line.
 
 Kernel durations are measured with HIP events on the launch stream around
 repeated launches of each kernel alone (the same library calls with the other
-stages switched off through their arguments: no outputs = projection GEMM only;
+stages switched off through their arguments: no outputs = projection only,
+which for bf16 x is the weight split (about 0.6% of it) and the GEMM;
 projections given = pooling only). The roofline object reports the dominant
-kernel (the 512-wide projection GEMM, fp32 matrix-core bound); `pool` reports
-the fused pooling kernel against HBM bandwidth.
+kernel (the 512-wide projection GEMM, matrix-core bound: for bf16 x its three
+bf16 passes against the bf16 peak); `pool` reports the pooling kernel against
+HBM bandwidth.
 """
 from __future__ import annotations
 
@@ -38,7 +45,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # null as soon as any of them changes)
 KERNEL_SOURCES = {
     "gemm": ["kv_cache_compression_fp32_amd/csrc/gemm_common.h", "kv_cache_compression_fp32_amd/csrc/gemm_f32_kernel.h",
-             "kv_cache_compression_fp32_amd/csrc/gemm_f32.hip", "kv_cache_compression_fp32_amd/csrc/kvc_device.h"],
+             "kv_cache_compression_fp32_amd/csrc/gemm_f32.hip", "kv_cache_compression_fp32_amd/csrc/kvc_device.h",
+             "kv_cache_compression_fp32_amd/csrc/gemm_epilogue.h"],
+    "gemm_x3": ["kv_cache_compression_fp32_amd/csrc/gemm_common.h", "kv_cache_compression_fp32_amd/csrc/gemm_x3.hip",
+                "kv_cache_compression_fp32_amd/csrc/kvc_device.h", "kv_cache_compression_fp32_amd/csrc/gemm_epilogue.h"],
     "pool": ["kv_cache_compression_fp32_amd/csrc/pool.hip", "kv_cache_compression_fp32_amd/csrc/kvc_device.h"],
 }
 
@@ -78,9 +88,16 @@ def pool_bytes(batch, seqlen, ratio, hd, quantize, latent, block=16):
     return read + write
 
 
-def cpu_baseline(wl, W, seconds=10.0):
+def bf16_hidden(torch, x: np.ndarray) -> np.ndarray:
+    """The bf16 rounding of synthetic hidden states (torch's conversion), as
+    float32 values."""
+    return torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+
+
+def cpu_baseline(wl, W, seconds=10.0, x_bf16=True):
     """The oracle, as it stands, on the first tokens of the workload: doubles
     the sample until it takes `seconds` or covers the whole sequence."""
+    import torch
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -90,6 +107,8 @@ def cpu_baseline(wl, W, seconds=10.0):
     tokens = 512
     while True:
         x = np.stack([W.hidden_rows(wl, b, 0, tokens) for b in range(wl.batch)])
+        if x_bf16:
+            x = bf16_hidden(torch, x)
         t0 = time.perf_counter()
         entries = 0
         for comp in wl.compressors:
@@ -124,15 +143,18 @@ def _rounded(d):
     return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
 
 
-def run_prefill(wl, steps, warmup, reps, torch, kvc, W):
-    """Time whole prefill steps of `wl`, then each kernel alone."""
+def run_prefill(wl, steps, warmup, reps, torch, kvc, W, x_format):
+    """Time whole prefill steps of `wl`, then each kernel alone. x holds the
+    bf16 hidden states, as bf16 rows or (x_format f32) as f32 rows."""
     dev = "cuda"
-    print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
-    x = torch.from_numpy(W.hidden(wl)).to(dev)
+    print(f"[bench] {wl.name}: generating inputs (x_format {x_format})", file=sys.stderr, flush=True)
+    x = torch.from_numpy(W.hidden(wl)).to(dev).to(torch.bfloat16)
+    if x_format == kvc.KVC_X_F32:
+        x = x.float()
     torch.cuda.synchronize()
     comps = []
     for comp in wl.compressors:
-        cfg = kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps)
+        cfg = kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps, x_format=x_format)
         w = {k: torch.from_numpy(v).to(dev) for k, v in W.weights(wl, comp).items()}
         wts = kvc.Weights(wkv=w["wkv"], wgate=w["wgate"], ape=w["ape"])
         groups = wl.seqlen // comp.ratio
@@ -166,6 +188,9 @@ def run_prefill(wl, steps, warmup, reps, torch, kvc, W):
         flops = 2.0 * wl.batch * wl.seqlen * wl.dim * 2 * proj
         pbytes = pool_bytes(wl.batch, wl.seqlen, comp.ratio, comp.head_dim, comp.quantize, not comp.quantize)
         kernels[f"gemm_{tag}"] = {"ms": gemm_ms, "tflops": flops / gemm_ms / 1e9, "flop": flops}
+        if x_format == kvc.KVC_X_BF16:
+            # the matrix-core work: three bf16 passes (hi, mid, lo weight parts)
+            kernels[f"gemm_{tag}"].update({"mfma_flop": 3 * flops, "mfma_tflops": 3 * flops / gemm_ms / 1e9})
         kernels[f"pool_{tag}"] = {"ms": pool_ms, "gbps": pbytes / pool_ms / 1e6, "bytes": pbytes}
         if comp.head_dim == 128 and not comp.quantize:
             # the same pooling with the index keys' fp4 form (power-of-two
@@ -183,15 +208,18 @@ def run_prefill(wl, steps, warmup, reps, torch, kvc, W):
             "entries_per_s": entries / (ms_per_step / 1e3), "kernels": kernels}
 
 
-def run_decode(wl, passes, torch, kvc, W):
+def run_decode(wl, passes, torch, kvc, W, x_format):
     """Time whole decode passes (every row streams all its tokens from
     start_pos 0, one decode step per token), captured once in a HIP graph so
     that host launch overhead is not measured."""
     dev = "cuda"
     comp = wl.compressors[0]
-    cfg = kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps)
+    cfg = kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps, x_format=x_format)
     print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
-    x = torch.from_numpy(W.hidden(wl)).to(dev).transpose(0, 1).contiguous()  # [steps, batch, dim]
+    x = torch.from_numpy(W.hidden(wl)).to(dev).to(torch.bfloat16)
+    if x_format == kvc.KVC_X_F32:
+        x = x.float()
+    x = x.transpose(0, 1).contiguous()  # [steps, batch, dim]
     w = {k: torch.from_numpy(v).to(dev) for k, v in W.weights(wl, comp).items()}
     wts = kvc.Weights(wkv=w["wkv"], wgate=w["wgate"], ape=w["ape"])
     ws = torch.empty(kvc.kvc_decode_workspace_floats(cfg, wl.batch), dtype=torch.float32, device=dev)
@@ -290,10 +318,14 @@ def run_fp4_quant(rows, width, reps, torch, kvc):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the clock climbs for about 100 ms of sustained matrix-core load: the
+    # default warmup (about 60 ms of steps) times the loaded state
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill_r4_n65536_fp4_idx128")
-    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--x-format", choices=("bf16", "f32"), default="bf16",
+                    help="element type of the hidden states handed to the library")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -325,15 +357,25 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
 
-    head = run_prefill(wl, args.steps, args.warmup, args.kernel_reps, torch, kvc, W)
+    x_format = kvc.KVC_X_BF16 if args.x_format == "bf16" else kvc.KVC_X_F32
+    head = run_prefill(wl, args.steps, args.warmup, args.kernel_reps, torch, kvc, W, x_format)
     kernels = head["kernels"]
     main_tag = f"hd{wl.compressors[0].head_dim}"
     g = kernels[f"gemm_{main_tag}"]
     p = kernels[f"pool_{main_tag}"]
-    roofline = {"bound": "mfma", "achieved": round(g["tflops"], 2), "peak": PEAK_FP32_MFMA_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(g["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4),
-                "traffic": measured_traffic("gemm"), "kernel": "gemm_f32_kernel (512-wide projection)",
-                "per_launch": g["flop"], "avg_ms": round(g["ms"], 4)}
+    if x_format == kvc.KVC_X_BF16:
+        roofline = {"bound": "mfma", "achieved": round(g["mfma_tflops"], 2), "peak": PEAK_BF16_MFMA_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(g["mfma_tflops"] / PEAK_BF16_MFMA_TFLOPS, 4),
+                    "traffic": measured_traffic("gemm_x3"),
+                    "kernel": "gemm_x3_kernel (512-wide projection, bf16 x times the three bf16 parts of the f32 "
+                              "weights, f32 accumulation)",
+                    "per_launch": g["mfma_flop"], "avg_ms": round(g["ms"], 4),
+                    "f32_equivalent_tflops": round(g["tflops"], 2)}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(g["tflops"], 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(g["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4),
+                    "traffic": measured_traffic("gemm"), "kernel": "gemm_f32_kernel (512-wide projection)",
+                    "per_launch": g["flop"], "avg_ms": round(g["ms"], 4)}
     pool = {"bound": "hbm", "achieved": round(p["gbps"], 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(p["gbps"] / PEAK_HBM_GBPS, 4), "traffic": measured_traffic("pool"),
             "kernel": "pool_small_kernel<512,4,true>", "per_launch": p["bytes"], "avg_ms": round(p["ms"], 4)}
@@ -342,6 +384,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "seqlen": wl.seqlen, "dim": wl.dim,
+                   "x": "bf16 hidden states" if x_format == kvc.KVC_X_BF16 else "f32 rows (bf16 values)",
+                   "weights": "f32",
                    "compressors": [{"ratio": c.ratio, "head_dim": c.head_dim, "fp4": c.quantize}
                                    for c in wl.compressors],
                    "entries_per_step": head["entries_per_step"]},
@@ -352,18 +396,23 @@ def main():
     }
     if not args.no_extras:
         extras = {}
+        other = kvc.KVC_X_F32 if x_format == kvc.KVC_X_BF16 else kvc.KVC_X_BF16
+        r = run_prefill(wl, 5, 2, 5, torch, kvc, W, other)
+        extras[f"{wl.name}_x_{'f32' if other == kvc.KVC_X_F32 else 'bf16'}"] = {
+            "ms_per_step": round(r["ms_per_step"], 4), "entries_per_s": round(r["entries_per_s"], 1),
+            "kernels": {k: _rounded(v) for k, v in r["kernels"].items()}}
         for name in ("prefill_r4_n4096", "prefill_r128_b2_n16384"):
-            r = run_prefill(W.WORKLOADS[name], 5, 2, 5, torch, kvc, W)
+            r = run_prefill(W.WORKLOADS[name], 5, 2, 5, torch, kvc, W, x_format)
             extras[name] = {"ms_per_step": round(r["ms_per_step"], 4), "entries_per_s": round(r["entries_per_s"], 1),
                             "kernels": {k: _rounded(v) for k, v in r["kernels"].items()}}
-        d = run_decode(W.WORKLOADS["decode_r4_b64_s512"], 5, torch, kvc, W)
+        d = run_decode(W.WORKLOADS["decode_r4_b64_s512"], 5, torch, kvc, W, x_format)
         extras["decode_r4_b64_s512"] = _rounded(d)
         extras["fp4_quant_262144x512"] = run_fp4_quant(262144, 512, 10, torch, kvc)
         extras["prefill_r1_n65536"] = run_ratio1(W.WORKLOADS["prefill_r1_n65536"], 10, 3, 10, torch, kvc, W)
         result["workloads"] = extras
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, W)
+        result["cpu_baseline"] = cpu_baseline(wl, W, x_bf16=x_format == kvc.KVC_X_BF16)
     print(json.dumps(result), flush=True)
 
 

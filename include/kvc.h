@@ -63,6 +63,10 @@ typedef struct ihipStream_t *kvc_stream; /* a hipStream_t */
 #define KVC_ESPACE (-3)       /* a caller-provided buffer is too small */
 #define KVC_EHIP (-4)         /* the HIP runtime rejected a launch */
 
+/* element type of the hidden states x (kvc_config.x_format) */
+#define KVC_X_F32 0  /* f32 rows */
+#define KVC_X_BF16 1 /* bf16 rows: the model's hidden state */
+
 /* fp4 forms of a compressed entry (kvc_config.fp4_format) */
 #define KVC_FP4_E4M3_B16 0 /* the KV latent's form: e4m3fn scale per block of 16 */
 #define KVC_FP4_E8M0_B32 1 /* the indexer's form: power-of-two (e8m0) scale per block of 32 */
@@ -88,6 +92,17 @@ typedef struct ihipStream_t *kvc_stream; /* a hipStream_t */
  *                once to bf16; the rotated entry goes to kvc_outputs.rotated
  *                and is what the fp4 outputs encode, while latent stays the
  *                unrotated compressor output.
+ *   x_format   : KVC_X_F32 or KVC_X_BF16, the element type of x in
+ *                compressor_prefill and compressor_decode_step (ratio > 1).
+ *                The compressor promotes the model's bf16 hidden state to f32
+ *                before its f32 projections ("DeepSeek V4.1 . Pool token
+ *                pairs", Compressor listing, forward); with KVC_X_BF16 the
+ *                caller passes that bf16 state and the library computes the
+ *                same f32 products: each f32 weight is split exactly into
+ *                three bf16 parts (hi, mid, lo), each bf16 x bf16 product is
+ *                exact in f32, and the bf16 matrix cores sum them with f32
+ *                accumulation. Ignored by compressor_ratio1_forward, whose x
+ *                is always bf16.
  * proj = 2 * head_dim at ratio 4, head_dim otherwise: the width of each
  * projection plane. */
 typedef struct kvc_config {
@@ -97,6 +112,7 @@ typedef struct kvc_config {
     float eps;
     int32_t fp4_format;
     int32_t rope_dim;
+    int32_t x_format;
 } kvc_config;
 
 /* Weights (device, f32).
@@ -149,27 +165,37 @@ int64_t kvc_proj_width(const kvc_config *cfg);
  * negative KVC_E* code. */
 int64_t kvc_state_rows(const kvc_config *cfg);
 
-/* f32 elements of the workspace compressor_prefill needs:
- * 2 * batch * seqlen * proj; or a negative KVC_E* code. */
+/* f32 elements of the workspace compressor_prefill needs: the projection
+ * planes, 2 * batch * seqlen * proj; at ratio 4 the f32 pooled entries,
+ * batch * (seqlen / 4) * head_dim (used when the projection and the pooling
+ * run as one kernel: a smaller workspace runs them separately); with
+ * KVC_X_BF16 the three-part weights, 3 * proj * dim (bf16 [2 proj][3][dim]).
+ * Or a negative KVC_E* code. */
 int64_t kvc_prefill_workspace_floats(const kvc_config *cfg, int64_t batch, int64_t seqlen);
 
 /* f32 elements of the workspace compressor_decode_step needs (split
- * projection partial sums); at least 2 * batch * proj; or a negative code. */
+ * projection partial sums); at least 2 * batch * proj; or a negative code.
+ * The same for either x_format. */
 int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch);
 
 /* Compressor forward at start_pos == 0 (prefill) over `seqlen` tokens of
  * `batch` rows ("DeepSeek V4.1 . Pool token pairs", Compressor listing,
  * forward, prefill branch; the overlap of "Compressed Sparse Attention .
  * ratio m = 4").
- *   x            : [batch][seqlen][dim] f32, or NULL. NULL means the caller
+ *   x            : [batch][seqlen][dim] f32, or bf16 with KVC_X_BF16 (16-byte
+ *                  aligned either way), or NULL. NULL means the caller
  *                  has put the projections (without bias) in `workspace`:
  *                  the kv plane [batch][seqlen][proj] followed by the score
  *                  plane [batch][seqlen][proj]; no weights are read then
  *                  except ape and norm_w.
  *   batch        : >= 1.   seqlen : >= 0.
- *   workspace    : f32, >= kvc_prefill_workspace_floats() elements; receives
- *                  the two projection planes when x is not NULL (the score
- *                  plane then with the positional bias added).
+ *   workspace    : f32, at least 2 * batch * seqlen * proj elements, and
+ *                  with x in bf16 all kvc_prefill_workspace_floats() elements
+ *                  (KVC_ESPACE otherwise); receives the two projection planes
+ *                  when x is not NULL (the score plane then with the
+ *                  positional bias added; at ratio 4 with the fused kernel,
+ *                  only the rows the state and the row tiles' first entries
+ *                  read).
  *   kv_state,
  *   score_state  : [state_batch][kvc_state_rows()][proj] f32 each, or both
  *                  NULL (nothing carried). Rows of batch row b are written as
@@ -183,7 +209,7 @@ int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch);
  *                  to compute only projections and state).
  *   n_groups     : host, optional; receives seqlen / ratio (0: no entry).
  * Errors: KVC_EINVAL, KVC_EUNSUPPORTED, KVC_ESPACE, KVC_EHIP. */
-int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const float *x, int64_t batch,
+int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *x, int64_t batch,
                        int64_t seqlen, float *workspace, int64_t workspace_floats, float *kv_state,
                        float *score_state, int64_t state_batch, const kvc_outputs *out,
                        int64_t *n_groups, kvc_stream stream);
@@ -194,7 +220,8 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const float 
  * group is pooled and one entry per batch row is written to `out` (G = 1);
  * at ratio 4 the current block then becomes the previous one. start_pos == 0
  * is a prefill of one token, which resets the carried block.
- *   x            : [batch][dim] f32 (one token per row), or NULL: then the
+ *   x            : [batch][dim] f32, or bf16 with KVC_X_BF16 (one token per
+ *                  row), or NULL: then the
  *                  caller has put the token's projections (without bias) in
  *                  workspace[0 : 2 * batch * proj] as the kv rows
  *                  [batch][proj] followed by the score rows [batch][proj].
@@ -205,7 +232,7 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const float 
  *                  of the previous calls of this sequence.
  *   emitted      : host, optional; receives 1 if entries were written, else 0.
  * Errors: as compressor_prefill. */
-int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const float *x, int64_t batch,
+int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const void *x, int64_t batch,
                            int64_t start_pos, float *workspace, int64_t workspace_floats,
                            float *kv_state, float *score_state, int64_t state_batch,
                            const kvc_outputs *out, int32_t *emitted, kvc_stream stream);

@@ -19,6 +19,7 @@
 #include <stdint.h>
 
 #include "gemm_common.h"
+#include "gemm_epilogue.h"
 #include "kvc_device.h"
 #include "kvc_launch.h"
 
@@ -43,18 +44,10 @@ constexpr int kBK = 32;  // k per LDS stage
 // Rows of a ragged last row tile are clamped to the last row of A (loaded,
 // never stored).
 //
-// POOL (ratio 4, 256 x 256 tiles of eight 64 x 128 wavefronts): column tile nt
-// covers the 64 features f0 = 64 nt .. f0 + 63, and wavefront column wn the 32
-// features f0 + 32 wn .. +31 as four 32-column segments: kv branch A (wkv row
-// f), kv branch B (wkv row hd + f), score branch A (wgate row f), score branch
-// B (wgate row hd + f). A lane's accumulator then holds, for two features,
-// the four rows of one 4-token block of each segment: its own block's branch
-// A candidates. The previous block's branch B rows come from the lanes 16
-// below (the block above), through LDS (the idle stage buffers) so that the
-// first block of a wavefront reads the wavefront above. Each entry's pooled
-// f32 values go to g.pooled, computed by the same softmax code as the pool
-// kernels; the first entry of the row tile (whose previous block belongs to
-// another workgroup) is pooled afterwards from plane rows written here.
+// POOL (ratio 4, 256 x 256 tiles of eight 64 x 128 wavefronts): column
+// tile nt covers the 64 features 64 nt .. +63, each wavefront's B rows are
+// the four 32-row segments of pool_epilogue (gemm_epilogue.h) for its 32
+// features, and the tile ends in that pooling epilogue.
 template <int BM, int BN, int WM, int WN, int NW, int MINW, bool DEFER, bool POOL = false>
 __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
   constexpr int BK = kBK, G = BK / 4;
@@ -68,10 +61,9 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
   static_assert(A_INS >= 1 && B_INS >= 1 && BM * BK % (256 * NW) == 0 && BN * BK % (256 * NW) == 0,
                 "tile/wavefront mismatch");
   static_assert(!POOL || (BM == 256 && BN == 256 && WM == 64 && WN == 128 && NW == 8), "pooling tile shape");
-  // branch-B exchange of the pooling epilogue: [4 wavefront rows][64 rows][2 x 64 + 4 pad]
-  constexpr int XROW = 132;
+  // the stage buffers, reused by the pooling epilogue's branch-B exchange
   constexpr int STAGE_FLOATS = 2 * (BM + BN) * BK;
-  constexpr int SMEM_FLOATS = POOL && 4 * 64 * XROW > STAGE_FLOATS ? 4 * 64 * XROW : STAGE_FLOATS;
+  constexpr int SMEM_FLOATS = POOL && kPoolXFloats > STAGE_FLOATS ? kPoolXFloats : STAGE_FLOATS;
   __shared__ __attribute__((aligned(16))) float smem[SMEM_FLOATS];
   float(*As)[BM * BK] = reinterpret_cast<float(*)[BM * BK]>(smem);
   float(*Bs)[BN * BK] = reinterpret_cast<float(*)[BN * BK]>(smem + 2 * BM * BK);
@@ -188,99 +180,18 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
   if (DEFER) mfma_slice(LAST, 3);
 
   if constexpr (POOL) {
-    // ---- pooling epilogue (see above) ----
-    const int g4 = lane >> 4, c = lane & 15;
-    const int64_t hd = g.pool_hd, seqlen = g.pool_seqlen, groups = g.pool_groups;
-    const int64_t gpr = seqlen / 4;  // 4-token blocks per batch row (batch > 1 needs seqlen % 4 == 0)
-    // the state's source rows: from the last complete block of each batch row on
-    const int64_t state_from = groups > 0 ? 4 * (groups - 1) : 0;
-    float *X = smem;
-    __syncthreads();  // every wavefront is done with the stage buffers
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int64_t f = f0 + 32 * wn + 16 * jj + c;
-        f4 &kA = acc[i][jj], &kB = acc[i][2 + jj], &sA = acc[i][4 + jj], &sB = acc[i][6 + jj];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rl = 16 * i + 4 * g4 + r;  // row within the wavefront
-          const int64_t row = m0 + wm * WM + rl;
-          if (g.bias1) {  // token position mod 4 is r: blocks start at multiples of 4
-            sA[r] = sA[r] + g.bias1[r * g.ldc + f];
-            sB[r] = sB[r] + g.bias1[r * g.ldc + hd + f];
-          }
-          if (row < g.m) {
-            const int64_t tpos = g.pool_batch == 1 ? row : row % seqlen;
-            const int tile_row = wm * WM + rl;
-            const bool state_row = tpos >= state_from;
-            float *kv = g.c0 + row * g.ldc, *sc = g.c1 + row * g.ldc;
-            if (state_row || tile_row < 4) {  // branch A: state rows and the tile's first block
-              kv[f] = kA[r];
-              sc[f] = sA[r];
-            }
-            if (state_row || tile_row >= BM - 4) {  // branch B: state rows and the tile's last block
-              kv[hd + f] = kB[r];
-              sc[hd + f] = sB[r];
-            }
-          }
-          X[(wm * 64 + rl) * XROW + wn * 64 + 16 * jj + c] = kB[r];
-          X[(wm * 64 + rl) * XROW + wn * 64 + 32 + 16 * jj + c] = sB[r];
-        }
-      }
-    __syncthreads();  // branch B of every block is in LDS
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int64_t gf = (m0 + wm * WM + 16 * i) / 4 + g4;  // 4-token block of the flattened rows
-      const int64_t b = g.pool_batch == 1 ? 0 : gf / gpr;
-      const int64_t j = g.pool_batch == 1 ? gf : gf - b * gpr;
-      // entries of complete blocks; the row tile's first entry needs the
-      // previous workgroup's block and is pooled afterwards (unless it is
-      // its batch row's entry 0, whose previous block is padding)
-      const bool first_of_tile = wm == 0 && i == 0 && g4 == 0;
-      if (b >= g.pool_batch || j >= groups || (first_of_tile && j > 0)) continue;
-      // the previous block's rows in LDS: 4 rows up, into the wavefront above
-      const int prow = wm * 64 + 16 * i + 4 * g4 - 4;
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        float ck[8][1], cs[8][1];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (j == 0) {
-            ck[r][0] = 0.0f;
-            cs[r][0] = -INFINITY;
-          } else {
-            ck[r][0] = X[(prow + r) * XROW + wn * 64 + 16 * jj + c];
-            cs[r][0] = X[(prow + r) * XROW + wn * 64 + 32 + 16 * jj + c];
-          }
-          ck[4 + r][0] = acc[i][jj][r];
-          cs[4 + r][0] = acc[i][4 + jj][r];
-        }
-        float p[1];
-        softmax_pool<8, 1>(ck, cs, p);
-        g.pooled[(b * groups + j) * hd + f0 + 32 * wn + 16 * jj + c] = p[0];
-      }
-    }
+    pool_epilogue<WM, WN>(g, acc, smem, m0, f0, wm, wn, lane);
   } else {
-    const float *bias = second ? g.bias1 : nullptr;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = m0 + wm * WM + 16 * i + 4 * slot + r;
-        if (row < g.m) {
-          float *crow = C + row * g.ldc + n0 + wn * WN + row_in;
-          if (bias) {
-            const float *brow = bias + ((row % g.bias_seqlen) % g.bias_ratio) * g.ldc + n0 + wn * WN + row_in;
-#pragma unroll
-            for (int j = 0; j < FN; ++j) crow[16 * j] = acc[i][j][r] + brow[16 * j];
-          } else {
-#pragma unroll
-            for (int j = 0; j < FN; ++j) crow[16 * j] = acc[i][j][r];
-          }
-        }
-      }
+    store_tile<FM, FN>(g, acc, C, second ? g.bias1 : nullptr, m0 + wm * WM, n0 + wn * WN, lane);
   }
+}
+
+__device__ __forceinline__ f4 load_a4(const float *p) { return *reinterpret_cast<const f4 *>(p); }
+// 4 bf16 values promoted to f32 (exact)
+__device__ __forceinline__ f4 load_a4(const uint16_t *p) {
+  const uint2 v = *reinterpret_cast<const uint2 *>(p);
+  return f4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+            __uint_as_float(v.y & 0xffff0000u)};
 }
 
 // Decode projection (M = batch rows, 64 per row tile in blockIdx.z): 32
@@ -290,8 +201,9 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
 // memory (lane l reads 4 consecutive k of row l % 16 at k-slot l / 16, the
 // layout of v_mfma_f32_16x16x4_f32 with the same k permutation as the tiled
 // kernel); the loads of CPW chunks of 16 k are issued before their MFMAs. The
-// 8 partial 64 x 32 tiles are summed through LDS in a fixed order.
-template <int CPW>
+// 8 partial 64 x 32 tiles are summed through LDS in a fixed order. x rows
+// are f32 (TA = float) or bf16 (TA = uint16_t, promoted on load).
+template <int CPW, typename TA>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_gemm_kernel(GemmArgs g) {
   constexpr int NWV = 8, FM = 4, FN = 2;
   __shared__ float red[NWV][64][33];
@@ -308,13 +220,15 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int64_t c_begin = chunks * me / parts, c_end = chunks * (me + 1) / parts;
   const int row_in = lane & 15, slot = lane >> 4;
 
-  const float *ap[FM];
+  const TA *A;
+  if constexpr (sizeof(TA) == 2) A = g.a16; else A = g.a;
+  const TA *ap[FM];
   const float *bp[FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     int64_t row = m0 + 16 * i + row_in;
     if (row >= g.m) row = g.m - 1;  // rows past the batch: read a valid row, never store it
-    ap[i] = g.a + row * g.lda + 4 * slot;
+    ap[i] = A + row * g.lda + 4 * slot;
   }
 #pragma unroll
   for (int j = 0; j < FN; ++j) bp[j] = B + (n0 + 16 * j + row_in) * g.ldb + 4 * slot;
@@ -331,7 +245,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[u][i] = *reinterpret_cast<const f4 *>(ap[i] + (c + u) * 16);
+      for (int i = 0; i < FM; ++i) af[u][i] = load_a4(ap[i] + (c + u) * 16);
 #pragma unroll
       for (int j = 0; j < FN; ++j) bf[u][j] = *reinterpret_cast<const f4 *>(bp[j] + (c + u) * 16);
     }
@@ -350,7 +264,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   for (; c < c_end; ++c) {
     f4 af[FM], bf[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const f4 *>(ap[i] + c * 16);
+    for (int i = 0; i < FM; ++i) af[i] = load_a4(ap[i] + c * 16);
 #pragma unroll
     for (int j = 0; j < FN; ++j) bf[j] = *reinterpret_cast<const f4 *>(bp[j] + c * 16);
 #pragma unroll
@@ -384,7 +298,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 inline hipError_t launch_decode_gemm(const GemmArgs &g, hipStream_t stream) {
   if (g.n_half % 32 != 0 || g.k % 16 != 0 || g.splits < 1 || g.bias1) return hipErrorInvalidValue;
   const dim3 grid((uint32_t)(2 * g.n_half / 32), (uint32_t)g.splits, (uint32_t)((g.m + 63) / 64));
-  hipLaunchKernelGGL(decode_gemm_kernel<4>, grid, dim3(512), 0, stream, g);
+  if (g.a16) hipLaunchKernelGGL((decode_gemm_kernel<4, uint16_t>), grid, dim3(512), 0, stream, g);
+  else hipLaunchKernelGGL((decode_gemm_kernel<4, float>), grid, dim3(512), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -406,7 +321,7 @@ hipError_t launch_tiled(const GemmArgs &g, hipStream_t stream) {
   // every column tile inside one half, every split whole k tiles, and a
   // tile's rows addressable by a 32-bit buffer offset
   if (g.n_half % BN != 0 || g.splits < 1 || g.k % (kBK * g.splits) != 0 || (g.bias1 && g.splits != 1) ||
-      (g.bias1 && (g.bias_seqlen < 1 || g.bias_ratio < 1)) || g.lda < g.k || g.ldb < g.k ||
+      (g.bias1 && (g.bias_seqlen < 1 || g.bias_ratio < 1 || (g.bias_ratio & (g.bias_ratio - 1)) != 0)) || g.lda < g.k || g.ldb < g.k ||
       (int64_t)BM * g.lda * 4 > INT32_MAX || (int64_t)BN * g.ldb * 4 > INT32_MAX)
     return hipErrorInvalidValue;
   const int64_t m_tiles = (g.m + BM - 1) / BM;

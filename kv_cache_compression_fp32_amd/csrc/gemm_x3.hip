@@ -1,0 +1,267 @@
+// Prefill projection for bf16 hidden states (gfx950, wave64): C = x . w^T
+// with x bf16 and w f32, computed on the bf16 matrix cores without rounding
+// anything but the f32 accumulation.
+//
+// "DeepSeek V4.1 . Pool token pairs", Compressor listing, forward: the
+// model's hidden state x (bf16) is promoted to f32 and multiplied by the f32
+// wkv / wgate ("Module compress", Functions, linear_f32). The promotion is
+// exact, and every f32 weight is the exact sum of three bf16 values:
+//   hi = w with its low 16 bits cleared, mid = (w - hi) with its low 16 bits
+//   cleared, lo = w - hi - mid.
+// (w - hi and w - hi - mid are exact f32 differences; the bits of w below hi
+// number 16, so mid takes the top 8 significant ones and lo the at most 8
+// left, which a bf16 holds exactly. Clearing bits never rounds up, so no part
+// overflows.) Each bf16 x bf16 product is exact in f32, and
+//   x . w = x . hi + x . mid + x . lo
+// term by term, so three bf16 matrix-core passes with f32 accumulation give
+// the f32 product with no error beyond the accumulation's own rounding, in
+// K / 32 * 3 accumulation steps per output (the f32 instruction takes K / 4).
+//
+// split_weights_kernel writes the parts as bsplit[2 n_half][3][k] (wkv rows,
+// then wgate rows); for the pooling kernel the rows are permuted into the
+// order its column tiles read (pool_epilogue, gemm_epilogue.h).
+//
+// gemm_x3_kernel: BM x BN workgroup tile, WM x WN per wavefront, two LDS
+// stages of 32 k, each stage holding the x tile [BM][32] and the three weight
+// parts [3][BN][32] as 64-byte rows of four 8-bf16 k-groups, group q of row r
+// at position q ^ ((r / 2) & 3) (the 16-byte reads of 8 neighbouring rows hit
+// 8 distinct 16-byte bank groups). Loads are buffer loads that write LDS
+// directly, 16 rows x 32 k (1 KiB) per instruction. Per stage: the x
+// fragments and weight part 0 and 1 fragments are read, part 0's MFMAs run
+// behind part 1's reads, part 2's reads follow, then the next stage's loads
+// go out (after the stage's last LDS read), then parts 1 and 2's MFMAs, wait
+// and barrier. Matrix-core layout (v_mfma_f32_16x16x32_bf16, lane l): 8
+// consecutive k of row l % 16, k-group l / 16; accumulator r holds
+// D[4 (l / 16) + r][l % 16], as in the f32 kernel.
+#include "gemm_common.h"
+#include "gemm_epilogue.h"
+#include "kvc_launch.h"
+
+namespace kvc {
+namespace gemm {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kBK3 = 32;  // k per LDS stage
+// the pooling kernel's wavefront: 128 rows x 64 columns, the 64 columns the
+// four 16-wide segments (kvA, kvB, scA, scB) of 16 features
+constexpr int kPoolWM = 128, kPoolWN = 64, kPoolF = kPoolWN / 4;
+
+// one thread per 8 consecutive k of one output row
+__global__ __launch_bounds__(256) void split_weights_kernel(SplitArgs a) {
+  const int64_t per_row = a.k / 8;
+  const int64_t total = 2 * a.n_half * per_row;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int64_t row = i / per_row, k0 = 8 * (i - row * per_row);
+  const float *src;
+  if (a.pool_hd) {
+    // pooling order: column tile t = row / 256 holds features 64 t .. +63;
+    // within it, [4 wavefront columns][kvA, kvB, scA, scB][16 features]
+    const int64_t t = row / 256, rem = row % 256, wn = rem / (4 * kPoolF), seg = (rem % (4 * kPoolF)) / kPoolF,
+                  c = rem % kPoolF;
+    const int64_t f = 64 * t + kPoolF * wn + c;
+    src = (seg < 2 ? a.w0 : a.w1) + ((seg & 1) * a.pool_hd + f) * a.ldw;
+  } else {
+    src = row < a.n_half ? a.w0 + row * a.ldw : a.w1 + (row - a.n_half) * a.ldw;
+  }
+  const float4 v0 = *reinterpret_cast<const float4 *>(src + k0);
+  const float4 v1 = *reinterpret_cast<const float4 *>(src + k0 + 4);
+  const float w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    uint32_t h2[2], m2[2], l2[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t hb = __float_as_uint(w[e + u]) & 0xffff0000u;
+      const float r1 = w[e + u] - __uint_as_float(hb);
+      const uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
+      const float r2 = r1 - __uint_as_float(mb);
+      h2[u] = hb >> 16;
+      m2[u] = mb >> 16;
+      l2[u] = __float_as_uint(r2) >> 16;
+    }
+    hi[e / 2] = h2[0] | (h2[1] << 16);
+    mid[e / 2] = m2[0] | (m2[1] << 16);
+    lo[e / 2] = l2[0] | (l2[1] << 16);
+  }
+  uint16_t *dst = a.out + row * 3 * a.k + k0;
+  *reinterpret_cast<uint4 *>(dst) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  *reinterpret_cast<uint4 *>(dst + a.k) = make_uint4(mid[0], mid[1], mid[2], mid[3]);
+  *reinterpret_cast<uint4 *>(dst + 2 * a.k) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+}
+
+template <int BM, int BN, int WM, int WN, int NW, int MINW, bool POOL>
+__global__ __launch_bounds__(NW * 64, MINW) void gemm_x3_kernel(GemmArgs g) {
+  constexpr int BK = kBK3;
+  constexpr int WAVES_N = BN / WN;
+  static_assert((BM / WM) * (BN / WN) == NW, "wavefront grid must cover the tile");
+  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int BRB = BN / 16;  // 16-row load blocks per weight part
+  constexpr int A_INS = BM / 16 / NW, B_INS = 3 * BRB / NW;  // 1 KiB loads per wavefront
+  static_assert(A_INS * 16 * NW == BM && B_INS * NW == 3 * BRB, "tile/wavefront mismatch");
+  static_assert(!POOL || (BM == 256 && BN == 256 && WM == kPoolWM && WN == kPoolWN && NW == 8), "pooling tile shape");
+  // stage buffers as floats (x tile then weight parts), reused by the pooling epilogue
+  constexpr int STAGE_FLOATS = 2 * (BM + 3 * BN) * BK / 2;
+  constexpr int SMEM_FLOATS = POOL && kPoolXFloats > STAGE_FLOATS ? kPoolXFloats : STAGE_FLOATS;
+  __shared__ __attribute__((aligned(16))) float smem[SMEM_FLOATS];
+  uint16_t(*As)[BM * BK] = reinterpret_cast<uint16_t(*)[BM * BK]>(smem);
+  uint16_t(*Bs)[3][BN * BK] = reinterpret_cast<uint16_t(*)[3][BN * BK]>(smem + BM * BK);
+
+  const int64_t m_tiles = (g.m + BM - 1) / BM;
+  const int64_t n_tiles = 2 * g.n_half / BN;  // with POOL: pool_hd / 64 tiles of 256 permuted rows
+  const uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t mt = tile / n_tiles, nt = tile - mt * n_tiles;
+  if (mt >= m_tiles) return;
+  const int64_t m0 = mt * BM;
+  const int64_t n_glob = nt * BN;
+  const bool second = n_glob >= g.n_half;
+  const int64_t n0 = second ? n_glob - g.n_half : n_glob;
+  const int kt_count = (int)(g.k / BK);
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+  // Load u of this wavefront fills 1 KiB = 16 rows of 64 bytes: lane l ->
+  // row l / 4 of the block, group position l % 4, which holds k-group
+  // lq = (l % 4) ^ (((l / 4) / 2) & 3). The x resource starts at the tile's
+  // first row, the weight resource at the tile's first split row; weight
+  // load q covers part q / BRB, rows 16 (q % BRB) ..; its row block, part
+  // and k offsets are wavefront-uniform (soffset).
+  const int64_t a_rows = (g.m - m0 < BM) ? (g.m - m0) : BM;
+  const i32x4 a_rsrc = make_rsrc(g.a16 + m0 * g.lda, (uint32_t)(a_rows * g.lda * 2));
+  const i32x4 b_rsrc = make_rsrc(g.bsplit + n_glob * 3 * g.k, (uint32_t)(BN * 3 * g.k * 2));
+  const int lr = lane >> 2, lq = (lane & 3) ^ ((lr >> 1) & 3);
+  uint32_t a_voff[A_INS];
+#pragma unroll
+  for (int u = 0; u < A_INS; ++u) {
+    int64_t r = 16 * (wave * A_INS + u) + lr;
+    if (r >= a_rows) r = a_rows - 1;  // ragged last tile: read a valid row, never store it
+    a_voff[u] = (uint32_t)((r * g.lda + 8 * lq) * 2);
+  }
+  const uint32_t b_voff = (uint32_t)((lr * 3 * g.k + 8 * lq) * 2);
+  auto issue = [&](int kt, int st) {
+    const uint32_t koff = (uint32_t)(kt * BK * 2);
+#pragma unroll
+    for (int u = 0; u < A_INS; ++u)
+      buffer_load_lds(a_rsrc, (lds_u32 *)(&As[st][512 * (wave * A_INS + u)]), 16, (int32_t)a_voff[u],
+                      (int32_t)koff, 0, 0);
+#pragma unroll
+    for (int u = 0; u < B_INS; ++u) {
+      const int q = wave * B_INS + u, p = q / BRB, rb = q % BRB;
+      buffer_load_lds(b_rsrc, (lds_u32 *)(&Bs[st][p][512 * rb]), 16, (int32_t)b_voff,
+                      (int32_t)(koff + (uint32_t)((rb * 16 * 3 * g.k + p * g.k) * 2)), 0, 0);
+    }
+  };
+
+  f4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+  const int row_in = lane & 15, slot = lane >> 4;
+  bf16x8 fa[FM], fb[2][FN];
+  auto aload = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WM + 16 * i + row_in;
+      fa[i] = *reinterpret_cast<const bf16x8 *>(&As[st][r * BK + 8 * (slot ^ ((r >> 1) & 3))]);
+    }
+  };
+  auto bload = [&](int st, int p, int sl) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * WN + 16 * j + row_in;
+      fb[sl][j] = *reinterpret_cast<const bf16x8 *>(&Bs[st][p][r * BK + 8 * (slot ^ ((r >> 1) & 3))]);
+    }
+  };
+  auto mfma = [&](int sl) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[sl][j], acc[i][j], 0, 0, 0);
+  };
+
+  issue(0, 0);
+  wait_vm0();
+  __syncthreads();
+  for (int kt = 0; kt < kt_count; ++kt) {
+    const int st = kt & 1;
+    aload(st);
+    bload(st, 0, 0);
+    bload(st, 1, 1);
+    mfma(0);  // hi
+    __builtin_amdgcn_sched_barrier(0);
+    bload(st, 2, 0);
+    // unconditional, so the loop body stays one block: the last iteration
+    // reloads its own stage into the idle one, which is never read
+    issue(kt + 1 < kt_count ? kt + 1 : kt, st ^ 1);
+    mfma(1);  // mid
+    mfma(0);  // lo
+    __builtin_amdgcn_sched_barrier(0);  // the stage's MFMAs stay ahead of the wait
+    wait_vm0();                         // this wavefront's loads of the next stage landed
+    __syncthreads();                    // everyone's landed; everyone is done reading this stage
+  }
+
+  if constexpr (POOL) {
+    pool_epilogue<WM, WN>(g, acc, smem, m0, 64 * nt, wm, wn, lane);
+  } else {
+    store_tile<FM, FN>(g, acc, second ? g.c1 : g.c0, second ? g.bias1 : nullptr, m0 + wm * WM, n0 + wn * WN,
+                       lane);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int NW, int MINW, bool POOL>
+hipError_t launch(const GemmArgs &g, int64_t n_tiles, hipStream_t stream) {
+  const int64_t m_tiles = (g.m + BM - 1) / BM;
+  hipLaunchKernelGGL((gemm_x3_kernel<BM, BN, WM, WN, NW, MINW, POOL>), dim3((uint32_t)(m_tiles * n_tiles)),
+                     dim3(NW * 64), 0, stream, g);
+  return hipGetLastError();
+}
+
+// rows of x and of the split weights addressable with 32-bit buffer offsets
+bool addressable(const GemmArgs &g, int64_t bn) {
+  return g.lda >= g.k && g.k % kBK3 == 0 && (int64_t)256 * g.lda * 2 <= INT32_MAX &&
+         bn * 3 * g.k * 2 <= INT32_MAX;
+}
+
+}  // namespace
+}  // namespace gemm
+
+hipError_t launch_split_weights(const SplitArgs &a, hipStream_t stream) {
+  if (a.n_half <= 0 || a.k <= 0) return hipSuccess;
+  if (a.k % 8 != 0 || a.ldw < a.k || (a.pool_hd && 2 * a.n_half != 4 * (int64_t)a.pool_hd) ||
+      (a.pool_hd && a.pool_hd % 64 != 0))
+    return hipErrorInvalidValue;
+  const int64_t total = 2 * a.n_half * (a.k / 8);
+  hipLaunchKernelGGL(gemm::split_weights_kernel, dim3((uint32_t)((total + 255) / 256)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// 256 x 256 tiles (eight 128 x 64 wavefronts: the taller wavefront reads
+// fewer weight fragments, which come in three parts) when the column tiles
+// fit the halves, else 256 x 128 (eight 64 x 64 wavefronts).
+hipError_t launch_gemm_x3(const GemmArgs &g, hipStream_t stream) {
+  if (g.m <= 0) return hipSuccess;
+  if (g.n_half % 128 != 0 || !gemm::addressable(g, 256) ||
+      (g.bias1 && (g.bias_seqlen < 1 || g.bias_ratio < 1 || (g.bias_ratio & (g.bias_ratio - 1)) != 0)))
+    return hipErrorInvalidValue;
+  if (g.n_half % 256 == 0) return gemm::launch<256, 256, 128, 64, 8, 1, false>(g, 2 * g.n_half / 256, stream);
+  return gemm::launch<256, 128, 64, 64, 8, 1, false>(g, 2 * g.n_half / 128, stream);
+}
+
+hipError_t launch_gemm_x3_pool(const GemmArgs &g, hipStream_t stream) {
+  if (g.m <= 0) return hipSuccess;
+  // 64-feature column tiles, 4-token blocks aligned with the flattened rows
+  if (g.pool_hd % 64 != 0 || g.n_half != 2 * (int64_t)g.pool_hd || g.ldc != 2 * g.pool_hd ||
+      !gemm::addressable(g, 256) || g.m != g.pool_batch * g.pool_seqlen ||
+      (g.pool_batch > 1 && g.pool_seqlen % 4 != 0) || !g.pooled)
+    return hipErrorInvalidValue;
+  return gemm::launch<256, 256, gemm::kPoolWM, gemm::kPoolWN, 8, 1, true>(g, g.pool_hd / 64, stream);
+}
+
+}  // namespace kvc

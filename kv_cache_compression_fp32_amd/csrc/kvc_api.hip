@@ -24,6 +24,7 @@ int check_common(const kvc_config *cfg) {
   if (cfg->fp4_format != KVC_FP4_E4M3_B16 && cfg->fp4_format != KVC_FP4_E8M0_B32) return KVC_EINVAL;
   if (cfg->head_dim != 128 && cfg->head_dim != 512) return KVC_EUNSUPPORTED;
   if (cfg->rope_dim < 0 || cfg->rope_dim > cfg->head_dim || cfg->rope_dim % 2 != 0) return KVC_EINVAL;
+  if (cfg->x_format != KVC_X_F32 && cfg->x_format != KVC_X_BF16) return KVC_EINVAL;
   return KVC_OK;
 }
 
@@ -91,10 +92,17 @@ int32_t decode_splits(const kvc_config *cfg, int64_t batch) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_EHIP; }
 
-// Ratio 4: f32 pooled entries of the fused projection + pooling path, after
-// the two projection planes in the prefill workspace.
+// Prefill workspace: the kv and score planes, then (ratio 4) the f32 pooled
+// entries of the fused projection + pooling path, then (bf16 x) the
+// three-part weights, bf16 [2 proj][3][dim].
 int64_t pooled_floats(const kvc_config *cfg, int64_t batch, int64_t seqlen) {
   return overlapped(cfg) ? batch * (seqlen / cfg->ratio) * cfg->head_dim : 0;
+}
+int64_t split_offset(const kvc_config *cfg, int64_t batch, int64_t seqlen) {
+  return 2 * batch * seqlen * proj_of(cfg) + pooled_floats(cfg, batch, seqlen);
+}
+int64_t split_floats(const kvc_config *cfg) {
+  return cfg->x_format == KVC_X_BF16 && cfg->dim > 0 ? 3 * proj_of(cfg) * cfg->dim : 0;
 }
 
 // The fused path (projection GEMM with pooling in its epilogue) needs 4-token
@@ -155,7 +163,7 @@ int64_t kvc_prefill_workspace_floats(const kvc_config *cfg, int64_t batch, int64
   const int rc = check_config(cfg);
   if (rc) return rc;
   if (batch < 1 || seqlen < 0) return KVC_EINVAL;
-  return 2 * batch * seqlen * proj_of(cfg) + pooled_floats(cfg, batch, seqlen);
+  return split_offset(cfg, batch, seqlen) + split_floats(cfg);
 }
 
 int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch) {
@@ -166,7 +174,7 @@ int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch) {
   return (int64_t)splits * 2 * batch * proj_of(cfg);
 }
 
-int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const float *x, int64_t batch,
+int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *x, int64_t batch,
                        int64_t seqlen, float *workspace, int64_t workspace_floats, float *kv_state,
                        float *score_state, int64_t state_batch, const kvc_outputs *out, int64_t *n_groups,
                        kvc_stream stream) {
@@ -179,7 +187,10 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const float 
   }
   if (w && (!aligned(w->ape) || !aligned(w->norm_w))) return KVC_EINVAL;
   const int64_t proj = proj_of(cfg);
-  const int64_t need = 2 * batch * seqlen * proj;
+  const int64_t m = batch * seqlen;
+  const bool x_bf16 = cfg->x_format == KVC_X_BF16;
+  // with bf16 x the three-part weights sit after the planes and pooled rows
+  const int64_t need = (x && x_bf16 && m > 0) ? split_offset(cfg, batch, seqlen) + split_floats(cfg) : 2 * m * proj;
   if (need > 0 && !workspace) return KVC_EINVAL;
   if (workspace_floats < need) return KVC_ESPACE;
   if (!aligned(workspace)) return KVC_EINVAL;
@@ -191,14 +202,14 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const float 
   if (wants_entries(out) && (rc = check_rope(cfg, w, 0, groups))) return rc;
   if (n_groups) *n_groups = groups;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int64_t m = batch * seqlen;
   float *kv_plane = workspace;
   float *sc_plane = workspace ? workspace + m * proj : nullptr;
 
   const bool fused = x && m > 0 && wants_entries(out) && use_fused_pooling(cfg, batch, seqlen, workspace_floats);
   if (x && m > 0) {
     kvc::GemmArgs g{};
-    g.a = x;
+    g.a = x_bf16 ? nullptr : static_cast<const float *>(x);
+    g.a16 = x_bf16 ? static_cast<const uint16_t *>(x) : nullptr;
     g.b0 = w->wkv;
     g.b1 = w->wgate;
     g.c0 = kv_plane;
@@ -221,10 +232,25 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const float 
       g.pool_seqlen = seqlen;
       g.pool_groups = groups;
       g.pool_hd = cfg->head_dim;
-      if ((rc = hip_status(kvc::launch_gemm_pool(g, s)))) return rc;
-    } else if ((rc = hip_status(kvc::launch_gemm(g, kvc::GemmShape::kPrefill, s)))) {
-      return rc;
     }
+    if (x_bf16) {
+      // the weights' three bf16 parts, in the row order the kernel reads
+      uint16_t *split = reinterpret_cast<uint16_t *>(workspace + split_offset(cfg, batch, seqlen));
+      kvc::SplitArgs sa{};
+      sa.w0 = w->wkv;
+      sa.w1 = w->wgate;
+      sa.ldw = cfg->dim;
+      sa.n_half = proj;
+      sa.k = cfg->dim;
+      sa.pool_hd = fused ? cfg->head_dim : 0;
+      sa.out = split;
+      if ((rc = hip_status(kvc::launch_split_weights(sa, s)))) return rc;
+      g.bsplit = split;
+      rc = hip_status(fused ? kvc::launch_gemm_x3_pool(g, s) : kvc::launch_gemm_x3(g, s));
+    } else {
+      rc = hip_status(fused ? kvc::launch_gemm_pool(g, s) : kvc::launch_gemm(g, kvc::GemmShape::kPrefill, s));
+    }
+    if (rc) return rc;
   }
   // projections the caller put in the workspace carry no bias yet
   const float *ape_after = x ? nullptr : (w ? w->ape : nullptr);
@@ -283,7 +309,7 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const float 
   return KVC_OK;
 }
 
-int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const float *x, int64_t batch,
+int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const void *x, int64_t batch,
                            int64_t start_pos, float *workspace, int64_t workspace_floats, float *kv_state,
                            float *score_state, int64_t state_batch, const kvc_outputs *out, int32_t *emitted,
                            kvc_stream stream) {
@@ -312,8 +338,10 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const fl
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   if (x) {
+    const bool x_bf16 = cfg->x_format == KVC_X_BF16;
     kvc::GemmArgs g{};
-    g.a = x;
+    g.a = x_bf16 ? nullptr : static_cast<const float *>(x);
+    g.a16 = x_bf16 ? static_cast<const uint16_t *>(x) : nullptr;
     g.b0 = w->wkv;
     g.b1 = w->wgate;
     g.c0 = workspace;

@@ -11,10 +11,11 @@ namespace kvc {
 // C_h[m][n] = sum_k A[m][k] * B_h[n][k] for the two halves h = 0, 1 of the
 // output columns (kv with wkv, score with wgate), f32 in and out, fp32 MFMA.
 // The K range is cut into `splits` equal parts; split s writes its partial
-// sums at C_h + s * c_split_stride.
+// sums at C_h + s * c_split_stride. With a16 set (decode only), A is bf16.
 // Optionally the second half gets a positional bias row added to each output
 // row (one f32 addition): row r of C_1 adds bias1[((r mod bias_seqlen) mod
-// bias_ratio) * ldc + n] (the gate logits' bias of token r mod seqlen).
+// bias_ratio) * ldc + n] (the gate logits' bias of token r mod seqlen;
+// bias_ratio a power of two).
 struct GemmArgs {
   const float *a;       // [m][k], row stride lda
   const float *b0, *b1; // [n_half][k] each, row stride ldb
@@ -36,6 +37,10 @@ struct GemmArgs {
   float *pooled;        // [pool_batch][pool_groups][pool_hd] f32
   int64_t pool_batch, pool_seqlen, pool_groups;
   int32_t pool_hd;
+  // bf16 hidden states (launch_gemm_x3*, and decode when set): [m][k], row stride lda
+  const uint16_t *a16;
+  // three-part weights of launch_gemm_x3* (launch_split_weights' output)
+  const uint16_t *bsplit;
 };
 
 // Prefill tiles need n_half % 128 == 0 and k % 32 == 0; decode needs
@@ -49,6 +54,25 @@ hipError_t launch_gemm(const GemmArgs &g, GemmShape shape, hipStream_t stream);
 hipError_t launch_gemm_pool(const GemmArgs &g, hipStream_t stream);
 // Number of 256-row tiles of launch_gemm_pool (the boundary entries' count + 1).
 inline int64_t gemm_pool_row_tiles(int64_t m) { return (m + 255) / 256; }
+
+// bf16 x times f32 weights as three exact bf16 parts (gemm_x3.hip):
+// launch_split_weights writes out[2 n_half][3][k] (bf16 hi, mid, lo of each
+// weight) from w0 (rows 0 .. n_half - 1) and w1 (the rest); with pool_hd set
+// (ratio 4, n_half = 2 pool_hd) the rows are in the order of the pooling
+// kernel's column tiles (see split_weights_kernel). Needs k % 8 == 0,
+// 16-byte aligned rows.
+struct SplitArgs {
+  const float *w0, *w1;  // [n_half][k] each, row stride ldw
+  int64_t ldw, n_half, k;
+  int32_t pool_hd;       // 0: plain order
+  uint16_t *out;
+};
+hipError_t launch_split_weights(const SplitArgs &a, hipStream_t stream);
+// The prefill projection from a16 and bsplit (plain order), the bias as in
+// launch_gemm; n_half % 128 == 0, k % 32 == 0.
+hipError_t launch_gemm_x3(const GemmArgs &g, hipStream_t stream);
+// As launch_gemm_pool, from a16 and bsplit (pooling order).
+hipError_t launch_gemm_x3_pool(const GemmArgs &g, hipStream_t stream);
 
 // Ratio-1 projection: C[m][n] = sum_k A[m][k] * B[n][k], bf16 A and B, f32
 // accumulation and output, bf16 MFMA. Needs k % 64 == 0 and n % 128 == 0.

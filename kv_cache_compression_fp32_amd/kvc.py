@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libkvc.so")
 
 KVC_OK, KVC_EINVAL, KVC_EUNSUPPORTED, KVC_ESPACE, KVC_EHIP = 0, -1, -2, -3, -4
 KVC_FP4_E4M3_B16, KVC_FP4_E8M0_B32 = 0, 1
+KVC_X_F32, KVC_X_BF16 = 0, 1
 
 _lib = None
 
@@ -35,7 +36,7 @@ class KvcError(RuntimeError):
 class _Config(ctypes.Structure):
     _fields_ = [("ratio", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("dim", ctypes.c_int64), ("eps", ctypes.c_float), ("fp4_format", ctypes.c_int32),
-                ("rope_dim", ctypes.c_int32)]
+                ("rope_dim", ctypes.c_int32), ("x_format", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
@@ -106,13 +107,15 @@ class Config:
     eps: float = 1e-6
     fp4_format: int = KVC_FP4_E4M3_B16
     rope_dim: int = 0
+    x_format: int = KVC_X_F32  # KVC_X_BF16: x is the bf16 hidden state
 
     @property
     def fp4_block(self) -> int:
         return 32 if self.fp4_format == KVC_FP4_E8M0_B32 else 16
 
     def c(self) -> _Config:
-        return _Config(self.ratio, self.head_dim, self.dim, self.eps, self.fp4_format, self.rope_dim)
+        return _Config(self.ratio, self.head_dim, self.dim, self.eps, self.fp4_format, self.rope_dim,
+                       self.x_format)
 
 
 def kvc_proj_width(cfg: Config) -> int:
@@ -201,6 +204,10 @@ class Outputs:
                         bf(self.dequant, "dequant"), bf(self.rotated, "rotated"))
 
 
+def _x_ptr(cfg: Config, x):
+    return _bf16_ptr(x, "x") if cfg.x_format == KVC_X_BF16 else _ptr(x, torch.float32, "x")
+
+
 def compressor_prefill(cfg: Config, w: Weights, x: torch.Tensor | None, batch: int, seqlen: int,
                        workspace: torch.Tensor, kv_state: torch.Tensor | None = None,
                        score_state: torch.Tensor | None = None, out: Outputs | None = None,
@@ -209,7 +216,7 @@ def compressor_prefill(cfg: Config, w: Weights, x: torch.Tensor | None, batch: i
     n = ctypes.c_int64(0)
     state_batch = kv_state.shape[0] if kv_state is not None else 0
     rc = lib().compressor_prefill(
-        ctypes.byref(cfg.c()), ctypes.byref(w.c()), _ptr(x, torch.float32, "x"), batch, seqlen,
+        ctypes.byref(cfg.c()), ctypes.byref(w.c()), _x_ptr(cfg, x), batch, seqlen,
         _ptr(workspace, torch.float32, "workspace"), workspace.numel(),
         _ptr(kv_state, torch.float32, "kv_state"), _ptr(score_state, torch.float32, "score_state"),
         state_batch, ctypes.byref(out.c()) if out is not None else None, ctypes.byref(n), _stream(stream))
@@ -223,7 +230,7 @@ def compressor_decode_step(cfg: Config, w: Weights, x: torch.Tensor | None, batc
     """Enqueue one decode step; returns True if entries were written."""
     e = ctypes.c_int32(0)
     rc = lib().compressor_decode_step(
-        ctypes.byref(cfg.c()), ctypes.byref(w.c()), _ptr(x, torch.float32, "x"), batch, start_pos,
+        ctypes.byref(cfg.c()), ctypes.byref(w.c()), _x_ptr(cfg, x), batch, start_pos,
         _ptr(workspace, torch.float32, "workspace"), workspace.numel(),
         _ptr(kv_state, torch.float32, "kv_state"), _ptr(score_state, torch.float32, "score_state"),
         kv_state.shape[0], ctypes.byref(out.c()) if out is not None else None, ctypes.byref(e),

@@ -20,6 +20,25 @@ def dev(a: np.ndarray | None) -> torch.Tensor | None:
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+def bf16_inputs(a: np.ndarray) -> np.ndarray:
+    """Hidden states as the model holds them: the bf16 rounding of `a`
+    (torch's conversion), returned as float32 values."""
+    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).float().numpy()
+
+
+def dev_x(cfg: kvc.Config, x: np.ndarray | None) -> torch.Tensor | None:
+    """x on the GPU in the element type cfg.x_format names (bf16 x must hold
+    bf16 values already: the conversion is then exact)."""
+    if x is None:
+        return None
+    t = dev(x)
+    if cfg.x_format == kvc.KVC_X_BF16:
+        b = t.to(torch.bfloat16)
+        assert torch.equal(b.float(), t), "x is not bf16-valued"
+        return b
+    return t
+
+
 def host_bf16(t: torch.Tensor) -> np.ndarray:
     """bf16 tensor -> float32 NumPy array of the same values."""
     bits = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
@@ -57,7 +76,7 @@ def prefill(cfg: kvc.Config, w: dict, batch: int, seqlen: int, x=None, kv=None, 
         m = batch * seqlen * proj
         ws[:m] = dev(kv).reshape(-1)
         ws[m:2 * m] = dev(sc).reshape(-1)
-    xd = x_dev if x_dev is not None else dev(x)
+    xd = x_dev if x_dev is not None else dev_x(cfg, x)
     if state is None:
         state = kvc.new_state(cfg, batch)
     groups = seqlen // cfg.ratio

@@ -54,6 +54,10 @@ def test_sizes(ratio, hd, proj, rows):
     assert kvc.kvc_prefill_workspace_floats(cfg, 3, 100) == 2 * 3 * 100 * proj + pooled
     ws = kvc.kvc_decode_workspace_floats(cfg, 64)
     assert ws >= 2 * 64 * proj and ws % (2 * 64 * proj) == 0
+    # bf16 hidden states: the weights' three bf16 parts follow, [2 proj][3][dim]
+    cfg16 = kvc.Config(ratio, hd, 4096, x_format=kvc.KVC_X_BF16)
+    assert kvc.kvc_prefill_workspace_floats(cfg16, 3, 100) == 2 * 3 * 100 * proj + pooled + 2 * proj * 3 * 4096 // 2
+    assert kvc.kvc_decode_workspace_floats(cfg16, 64) == ws
 
 
 def test_decode_workspace_of_the_b64_ratio4_step():
@@ -71,6 +75,7 @@ def test_decode_workspace_of_the_b64_ratio4_step():
     (kvc.Config(4, 256, 4096), kvc.KVC_EUNSUPPORTED),
     (kvc.Config(4, 512, 4096, eps=-1.0), kvc.KVC_EINVAL),
     (kvc.Config(4, 512, 4096, eps=float("nan")), kvc.KVC_EINVAL),
+    (kvc.Config(4, 512, 4096, x_format=2), kvc.KVC_EINVAL),
 ])
 def test_invalid_configs(cfg, code):
     with pytest.raises(kvc.KvcError) as err:
@@ -113,6 +118,22 @@ def test_prefill_argument_errors_return_before_enqueueing():
     # one state plane without the other, or a state smaller than the batch
     assert _prefill_raw(cfg, ws=fake, ws_n=1 << 30, kv=fake)[0] == kvc.KVC_EINVAL
     assert _prefill_raw(cfg, batch=2, ws=fake, ws_n=1 << 30, kv=fake, sc=fake, sb=1)[0] == kvc.KVC_EINVAL
+
+
+def test_bf16_x_needs_room_for_the_split_weights():
+    fake = 0x100000  # never dereferenced: every case below fails its host checks
+    w = kvc._Weights(fake, fake, None, None)
+    cfg = kvc.Config(4, 512, 4096, x_format=kvc.KVC_X_BF16)
+    full = kvc.kvc_prefill_workspace_floats(cfg, 1, 8)
+    # the planes alone are enough for f32 x, not for bf16 x (the parts come after them)
+    planes = kvc.kvc_prefill_workspace_floats(kvc.Config(4, 512, 4096), 1, 8)
+    assert planes < full
+    assert _prefill_raw(cfg, x=fake, w=w, ws=fake, ws_n=planes)[0] == kvc.KVC_ESPACE
+    assert _prefill_raw(cfg, x=fake, w=w, ws=fake, ws_n=full - 1)[0] == kvc.KVC_ESPACE
+    # without x only the planes are read
+    assert _prefill_raw(cfg, ws=fake, ws_n=10)[0] == kvc.KVC_ESPACE
+    # bf16 x must still be 16-byte aligned
+    assert _prefill_raw(cfg, x=fake + 2, w=w, ws=fake, ws_n=full)[0] == kvc.KVC_EINVAL
 
 
 def test_decode_argument_errors_return_before_enqueueing():

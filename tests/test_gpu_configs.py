@@ -8,7 +8,7 @@ import torch
 import kv_cache_compression_fp32_amd.kvc as kvc
 import kv_cache_compression_fp32_amd.workloads as W
 import oracle
-from gpu_util import dev, note, oracle_cfg, oracle_weights, outputs_to_host, prefill, weights
+from gpu_util import bf16_inputs, dev, dev_x, note, oracle_cfg, oracle_weights, outputs_to_host, prefill, weights
 from parity import check_fp4, check_latent, check_pooled
 
 pytestmark = pytest.mark.gpu
@@ -21,8 +21,8 @@ def _gpu():
     kvc.lib()
 
 
-def _cfg(wl, comp):
-    return kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps)
+def _cfg(wl, comp, x_format=kvc.KVC_X_F32):
+    return kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps, x_format=x_format)
 
 
 def _sample_entries(groups, n=24, seed=0):
@@ -32,10 +32,11 @@ def _sample_entries(groups, n=24, seed=0):
     return sorted(e for e in fixed | rand if 0 <= e < groups)
 
 
-def _oracle_entry(wl, comp, w, b, j, fp4="e4m3"):
+def _oracle_entry(wl, comp, w, b, j, fp4="e4m3", x_bf16=False):
     """One entry from only the token rows it depends on: ratio 4 needs the
     previous block too (the slice then starts at a multiple of 4, so the bias
-    rows line up), other ratios only the group itself."""
+    rows line up), other ratios only the group itself. With x_bf16 the rows
+    are the bf16 hidden states the GPU received."""
     cfg = oracle.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps, fp4=fp4)
     r = comp.ratio
     if r == 4 and j > 0:
@@ -43,15 +44,17 @@ def _oracle_entry(wl, comp, w, b, j, fp4="e4m3"):
     else:
         t0, idx = r * j, 0
     x = W.hidden_rows(wl, b, t0, r * j + r)[None]
+    if x_bf16:
+        x = bf16_inputs(x)
     out = oracle.prefill(cfg, oracle_weights(w), oracle.State(cfg, 1), x=x, quantize=comp.quantize or fp4 == "e8m0")
     return {k: v[0, idx] for k, v in out.items()}
 
 
-def _check_sampled(wl, comp, w, got, entries, batch_rows, fp4="e4m3"):
+def _check_sampled(wl, comp, w, got, entries, batch_rows, fp4="e4m3", x_bf16=False):
     ref = {}
     for b in batch_rows:
         for j in entries:
-            e = _oracle_entry(wl, comp, w, b, j, fp4)
+            e = _oracle_entry(wl, comp, w, b, j, fp4, x_bf16)
             for k, v in e.items():
                 ref.setdefault(k, []).append(v)
     ref = {k: np.stack(v) for k, v in ref.items()}
@@ -171,6 +174,25 @@ def test_prefill_r4_n65536_fp4_idx128_sampled():
             # every entry: the fp4 codes of the GPU's latent, bit-exact
             check_fp4(g["codes"], g["scales"], g["latent"], gpu_dequant=g["dequant"])
         del g
+
+
+def test_prefill_r4_n65536_bf16_hidden_states_sampled():
+    # the long workload with the model's bf16 hidden states (the projection
+    # on the bf16 matrix cores from the weights' three exact bf16 parts),
+    # both compressors, fused pooling: the benchmark's launch configuration
+    wl = W.WORKLOADS["prefill_r4_n65536_fp4_idx128"]
+    note(f"{wl.name} bf16 x")
+    for comp in wl.compressors:
+        w = W.weights(wl, comp)
+        cfg = _cfg(wl, comp, kvc.KVC_X_BF16)
+        xd = dev_x(cfg, bf16_inputs(W.hidden(wl)))
+        note(f"  compressor ratio={comp.ratio} hd={comp.head_dim} fp4={comp.quantize}")
+        g = prefill(cfg, w, wl.batch, wl.seqlen, x_dev=xd, fp4=True)
+        assert g["n_groups"] == 16384
+        _check_sampled(wl, comp, w, g, _sample_entries(16384, 40, seed=2), [0], x_bf16=True)
+        if comp.quantize:
+            check_fp4(g["codes"], g["scales"], g["latent"], gpu_dequant=g["dequant"])
+        del g, xd
 
 
 def test_prefill_r4_n65536_index_keys_power_of_two_fp4_sampled():

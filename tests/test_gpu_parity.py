@@ -6,7 +6,8 @@ import torch
 
 import kv_cache_compression_fp32_amd.kvc as kvc
 import oracle
-from gpu_util import dev, host_bf16, note, oracle_cfg, oracle_weights, outputs_to_host, prefill
+from gpu_util import (bf16_inputs, dev, dev_x, host_bf16, note, oracle_cfg, oracle_weights, outputs_to_host,
+                      prefill)
 from parity import check_fp4, check_latent, check_pooled
 
 pytestmark = pytest.mark.gpu
@@ -168,13 +169,16 @@ GEMM_CASES = [
 ]
 
 
+@pytest.mark.parametrize("x_format", [kvc.KVC_X_F32, kvc.KVC_X_BF16])
 @pytest.mark.parametrize("ratio,hd,dim,batch,seqlen", GEMM_CASES)
-def test_projection_gemm_and_full_prefill(ratio, hd, dim, batch, seqlen):
-    note(f"gemm+prefill ratio={ratio} hd={hd} dim={dim} batch={batch} seqlen={seqlen}")
+def test_projection_gemm_and_full_prefill(ratio, hd, dim, batch, seqlen, x_format):
+    note(f"gemm+prefill ratio={ratio} hd={hd} dim={dim} batch={batch} seqlen={seqlen} x_format={x_format}")
     rng = np.random.default_rng(dim + seqlen)
-    cfg = kvc.Config(ratio, hd, dim)
+    cfg = kvc.Config(ratio, hd, dim, x_format=x_format)
     proj = kvc.kvc_proj_width(cfg)
     x = rng.standard_normal((batch, seqlen, dim), dtype=np.float32)
+    if x_format == kvc.KVC_X_BF16:  # the model's bf16 hidden state
+        x = bf16_inputs(x)
     w = {"wkv": rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.02),
          "wgate": rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.02),
          "ape": rng.standard_normal((ratio, proj), dtype=np.float32) * np.float32(0.1)}
@@ -183,7 +187,7 @@ def test_projection_gemm_and_full_prefill(ratio, hd, dim, batch, seqlen):
     # outputs may pool inside the GEMM and write only the rows it needs)
     from gpu_util import weights
     ws = torch.empty(kvc.kvc_prefill_workspace_floats(cfg, batch, seqlen), dtype=torch.float32, device="cuda")
-    kvc.compressor_prefill(cfg, weights(w), dev(x), batch, seqlen, ws)
+    kvc.compressor_prefill(cfg, weights(w), dev_x(cfg, x), batch, seqlen, ws)
     torch.cuda.synchronize()
     m = batch * seqlen * proj
     g["proj_kv"] = ws[:m].view(batch, seqlen, proj).cpu().numpy()
@@ -222,7 +226,7 @@ def _decode_gpu(cfg, w, batch, xs=None, kvs=None, scs=None, start=0, state=None,
     ws = torch.empty(kvc.kvc_decode_workspace_floats(cfg, batch), dtype=torch.float32, device="cuda")
     if state is None:
         state = kvc.new_state(cfg, batch)
-    xd = dev(xs) if xs is not None else None
+    xd = dev_x(cfg, xs) if xs is not None else None
     kvd, scd = (dev(kvs), dev(scs)) if kvs is not None else (None, None)
     emitted = []
     for i in range(steps):
@@ -305,14 +309,17 @@ def test_prefill_then_decode_continuation(ratio):
         assert np.array_equal(got.view(np.uint32), full["latent"].view(np.uint32)), n0
 
 
-def test_decode_with_projection_matches_oracle():
-    note("decode with x, ratio 4, batch 64, dim 4096, 16 steps")
+@pytest.mark.parametrize("x_format", [kvc.KVC_X_F32, kvc.KVC_X_BF16])
+def test_decode_with_projection_matches_oracle(x_format):
+    note(f"decode with x, ratio 4, batch 64, dim 4096, 16 steps, x_format={x_format}")
     from gpu_util import weights
     rng = np.random.default_rng(5)
-    cfg = kvc.Config(4, 512, 4096)
+    cfg = kvc.Config(4, 512, 4096, x_format=x_format)
     proj = 1024
     batch, steps = 64, 16
     x = rng.standard_normal((batch, steps, 4096), dtype=np.float32)
+    if x_format == kvc.KVC_X_BF16:
+        x = bf16_inputs(x)
     w = {"wkv": rng.standard_normal((proj, 4096), dtype=np.float32) * np.float32(0.02),
          "wgate": rng.standard_normal((proj, 4096), dtype=np.float32) * np.float32(0.02),
          "ape": rng.standard_normal((4, proj), dtype=np.float32) * np.float32(0.1)}
@@ -503,16 +510,20 @@ FUSED_CASES = [
 ]
 
 
+@pytest.mark.parametrize("x_format", [kvc.KVC_X_F32, kvc.KVC_X_BF16])
 @pytest.mark.parametrize("hd,batch,seqlen,dim,opt", FUSED_CASES)
-def test_fused_pooling_equals_separate_kernels_bitwise(hd, batch, seqlen, dim, opt):
-    note(f"fused GEMM + pool hd={hd} batch={batch} seqlen={seqlen} {opt}")
+def test_fused_pooling_equals_separate_kernels_bitwise(hd, batch, seqlen, dim, opt, x_format):
+    note(f"fused GEMM + pool hd={hd} batch={batch} seqlen={seqlen} {opt} x_format={x_format}")
     from gpu_util import weights
     rng = np.random.default_rng(hd + batch + seqlen)
     cfg = kvc.Config(4, hd, dim, rope_dim=64 if opt == "rope" else 0,
-                     fp4_format=kvc.KVC_FP4_E8M0_B32 if opt == "e8m0" else kvc.KVC_FP4_E4M3_B16)
+                     fp4_format=kvc.KVC_FP4_E8M0_B32 if opt == "e8m0" else kvc.KVC_FP4_E4M3_B16,
+                     x_format=x_format)
     proj = 2 * hd
     groups = seqlen // 4
     x = rng.standard_normal((batch, seqlen, dim), dtype=np.float32)
+    if x_format == kvc.KVC_X_BF16:
+        x = bf16_inputs(x)
     w = {"wkv": rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.1),
          "wgate": rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.1),
          "ape": rng.standard_normal((4, proj), dtype=np.float32) * np.float32(0.1)}
@@ -521,7 +532,7 @@ def test_fused_pooling_equals_separate_kernels_bitwise(hd, batch, seqlen, dim, o
     if opt == "rope":
         w["rope_cs"] = _yarn_table(groups, 64, 4)
     W = weights(w)
-    xd = dev(x)
+    xd = dev_x(cfg, x)
     outs = lambda: kvc.new_outputs(cfg, batch, groups, latent=True, pooled=True, fp4=True, dequant=True,  # noqa: E731
                                    rotated=cfg.rope_dim > 0)
     # fused: projection with pooling in the GEMM epilogue (NaN sentinel in the planes)
@@ -555,3 +566,56 @@ def test_fused_pooling_equals_separate_kernels_bitwise(hd, batch, seqlen, dim, o
         check_pooled(a["pooled"][bb][ent], ref["pooled"][0])
         check_latent(a["latent"][bb][ent], a["pooled"][bb][ent], ref["latent"][0], ref["pooled"][0],
                      w.get("norm_w"), cfg.eps)
+
+
+# ---------------------------------------------------------------- bf16 hidden states: exact weight split
+SPLIT_CASES = [
+    # ratio, head_dim, dim, batch, seqlen
+    (4, 128, 256, 1, 256 + 64),    # 256 x 256 tiles, ragged last row tile
+    (2, 128, 128, 2, 130),         # 128-wide halves: 256 x 128 tiles
+    (128, 512, 256, 1, 300),
+]
+
+
+@pytest.mark.parametrize("ratio,hd,dim,batch,seqlen", SPLIT_CASES)
+def test_bf16_x_one_hot_rows_reproduce_the_f32_weights_exactly(ratio, hd, dim, batch, seqlen):
+    """x row r = the unit vector e_(r mod dim): each output is then one f32
+    weight times 1, i.e. 1 * hi + 1 * mid + 1 * lo of its three bf16 parts,
+    which must give the weight back bit for bit (the score plane then adds
+    the positional bias in one f32 addition). Weights span the f32 exponent
+    range whose parts are all normal numbers, with zeros, the largest finite
+    value and values whose low parts have leading zeros."""
+    note(f"bf16 x one-hot ratio={ratio} hd={hd} dim={dim} batch={batch} seqlen={seqlen}")
+    from gpu_util import weights
+    rng = np.random.default_rng(ratio + dim + seqlen)
+    cfg = kvc.Config(ratio, hd, dim, x_format=kvc.KVC_X_BF16)
+    proj = kvc.kvc_proj_width(cfg)
+    m = batch * seqlen
+    x = np.zeros((m, dim), np.float32)
+    x[np.arange(m), np.arange(m) % dim] = 1.0
+
+    def wide(shape):
+        v = rng.choice([-1.0, 1.0], shape) * np.ldexp(rng.uniform(1.0, 2.0, shape), rng.integers(-100, 127, shape))
+        v = v.astype(np.float32)
+        flat = v.reshape(-1)
+        special = np.array([0.0, -0.0, np.finfo(np.float32).max, -np.finfo(np.float32).max, 1 + 2.0 ** -23,
+                            -(1 + 2.0 ** -16), 1 + 2.0 ** -8 + 2.0 ** -23, np.float32(0.1)], np.float32)
+        flat[rng.choice(flat.size, special.size, replace=False)] = special
+        return v
+
+    w = {"wkv": wide((proj, dim)), "wgate": wide((proj, dim)),
+         "ape": rng.standard_normal((ratio, proj)).astype(np.float32)}
+    ws = torch.full((kvc.kvc_prefill_workspace_floats(cfg, batch, seqlen),), float("nan"), device="cuda")
+    kvc.compressor_prefill(cfg, weights(w), dev_x(cfg, x.reshape(batch, seqlen, dim)), batch, seqlen, ws)
+    torch.cuda.synchronize()
+    kv = ws[:m * proj].view(m, proj).cpu().numpy()
+    sc = ws[m * proj:2 * m * proj].view(m, proj).cpu().numpy()
+    col = np.arange(m) % dim
+    # a sum accumulated from +0 turns a -0 weight into +0 (as any f32 dot product does)
+    want = w["wkv"].T[col] + np.float32(0.0)
+    bad = kv.view(np.uint32) != want.view(np.uint32)
+    assert not bad.any(), f"{bad.sum()} differ, e.g. weights {want[bad][:4]} -> {kv[bad][:4]}"
+    pos = np.arange(m) % seqlen
+    want = w["wgate"].T[col] + w["ape"][pos % ratio]   # one f32 rounding, as on the GPU
+    bad = sc.view(np.uint32) != want.view(np.uint32)
+    assert not bad.any(), f"{bad.sum()} differ, e.g. {want[bad][:4]} -> {sc[bad][:4]}"
