@@ -26,18 +26,55 @@ namespace kvc {
 namespace gemm {
 
 // Store of one wavefront's FM x FN fragments at rows row0 + .., columns
-// col0 + .. of C (row stride g.ldc); rows at or past g.m are dropped. With
-// bias set, row (row % bias_seqlen) % bias_ratio of it is added (bias_ratio a
-// power of two). The token position is taken modulo bias_seqlen once per
-// lane and then advanced row by row, wrapping at bias_seqlen (one wrap at
-// most when bias_seqlen >= 16 FM, else each row takes its own modulo).
+// col0 + .. of C (row stride g.ldc; row0 a multiple of 4); rows at or past
+// g.m are dropped. With bias set, row (row % bias_seqlen) % bias_ratio of it
+// is added (bias_ratio a power of two). At ratio 2 or 4 with positions that
+// restart at multiples of the ratio (one sequence, or bias_seqlen a multiple
+// of the ratio) that row is r % ratio for the lane's r-th row of each group
+// of 4, so the lane's 4 x FN bias values are loaded once. Otherwise the
+// token position is taken modulo bias_seqlen once per lane and advanced row
+// by row, wrapping at bias_seqlen (one wrap at most when bias_seqlen >=
+// 16 FM, else each row takes its own modulo).
 template <int FM, int FN>
 __device__ __forceinline__ void store_tile(const GemmArgs &g, const f4 (&acc)[FM][FN], float *C, const float *bias,
                                            int64_t row0, int64_t col0, int lane) {
   const int row_in = lane & 15, slot = lane >> 4;
-  const int64_t seqlen = g.bias_seqlen;
+  const int64_t seqlen = g.bias_seqlen, ratio = g.bias_ratio;
+  if (!bias) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = row0 + 16 * i + 4 * slot + r;
+        if (row < g.m) {
+          float *crow = C + row * g.ldc + col0 + row_in;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) crow[16 * j] = acc[i][j][r];
+        }
+      }
+    return;
+  }
+  if (ratio <= 4 && (g.m <= seqlen || seqlen % ratio == 0)) {
+    float bv[4][FN];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bv[r][j] = bias[(r & (ratio - 1)) * g.ldc + col0 + row_in + 16 * j];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = row0 + 16 * i + 4 * slot + r;
+        if (row < g.m) {
+          float *crow = C + row * g.ldc + col0 + row_in;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) crow[16 * j] = acc[i][j][r] + bv[r][j];
+        }
+      }
+    return;
+  }
   const bool one_wrap = seqlen >= 16 * FM;
-  const int64_t pos0 = bias ? (row0 + 4 * slot) % seqlen : 0;
+  const int64_t pos0 = (row0 + 4 * slot) % seqlen;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -45,21 +82,16 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, const f4 (&acc)[FM
       const int64_t row = row0 + 16 * i + 4 * slot + r;
       if (row < g.m) {
         float *crow = C + row * g.ldc + col0 + row_in;
-        if (bias) {
-          int64_t pos;
-          if (one_wrap) {
-            pos = pos0 + 16 * i + r;
-            if (pos >= seqlen) pos -= seqlen;
-          } else {
-            pos = row % seqlen;
-          }
-          const float *brow = bias + (pos & (g.bias_ratio - 1)) * g.ldc + col0 + row_in;
-#pragma unroll
-          for (int j = 0; j < FN; ++j) crow[16 * j] = acc[i][j][r] + brow[16 * j];
+        int64_t pos;
+        if (one_wrap) {
+          pos = pos0 + 16 * i + r;
+          if (pos >= seqlen) pos -= seqlen;
         } else {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) crow[16 * j] = acc[i][j][r];
+          pos = row % seqlen;
         }
+        const float *brow = bias + (pos & (ratio - 1)) * g.ldc + col0 + row_in;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) crow[16 * j] = acc[i][j][r] + brow[16 * j];
       }
     }
 }
