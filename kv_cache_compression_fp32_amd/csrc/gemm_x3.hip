@@ -26,13 +26,24 @@
 // parts [3][BN][32] as 64-byte rows of four 8-bf16 k-groups, group q of row r
 // at position q ^ ((r / 2) & 3) (the 16-byte reads of 8 neighbouring rows hit
 // 8 distinct 16-byte bank groups). Loads are buffer loads that write LDS
-// directly, 16 rows x 32 k (1 KiB) per instruction. Per stage: the x
-// fragments and weight part 0 and 1 fragments are read, part 0's MFMAs run
-// behind part 1's reads, part 2's reads follow, then the next stage's loads
-// go out (after the stage's last LDS read), then parts 1 and 2's MFMAs, wait
-// and barrier. Matrix-core layout (v_mfma_f32_16x16x32_bf16, lane l): 8
-// consecutive k of row l % 16, k-group l / 16; accumulator r holds
-// D[4 (l / 16) + r][l % 16], as in the f32 kernel.
+// directly, 16 rows x 32 k (1 KiB) per instruction. Matrix-core layout
+// (v_mfma_f32_16x16x32_bf16, lane l): 8 consecutive k of row l % 16, k-group
+// l / 16; accumulator r holds D[4 (l / 16) + r][l % 16], as in the f32 kernel.
+//
+// Schedule ("ping-pong"): the 8 wavefronts form two groups, 0..3 and 4..7,
+// so that every SIMD holds one wavefront of each. Both groups run the same
+// loop, phase by phase with a barrier between phases: read a stage's
+// fragments (x and all three parts) from LDS, then run its 96 MFMAs from
+// registers. Group 4..7 starts one phase late, so on every SIMD one
+// wavefront multiplies while the other reads: the matrix cores do not wait
+// for the barrier's stragglers or the first LDS reads after it. Group 0..3
+// alone issues the global -> LDS loads, each stage's loads right after its
+// reads of the previous stage (so no LDS read of the group follows a load in
+// flight), and waits for them at the end of its multiply phase, before the
+// barrier after which it reads them. Buffer reuse: a stage buffer is
+// reloaded one phase after group 4..7 read it; that group waits for its own
+// LDS reads before each barrier. Every wavefront meets the same 2 k / 32 + 2
+// barriers.
 #include "gemm_common.h"
 #include "gemm_epilogue.h"
 #include "kvc_launch.h"
@@ -42,6 +53,16 @@ namespace gemm {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// A workgroup barrier without the memory fence of __syncthreads (which would
+// also wait for the loading group's loads in flight), kept in place by the
+// scheduler; the waits each phase needs are explicit.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 constexpr int kBK3 = 32;  // k per LDS stage
 // the pooling kernel's wavefront: 128 rows x 64 columns, the 64 columns the
@@ -100,8 +121,10 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_x3_kernel(GemmArgs g) {
   static_assert((BM / WM) * (BN / WN) == NW, "wavefront grid must cover the tile");
   constexpr int FM = WM / 16, FN = WN / 16;
   constexpr int BRB = BN / 16;  // 16-row load blocks per weight part
-  constexpr int A_INS = BM / 16 / NW, B_INS = 3 * BRB / NW;  // 1 KiB loads per wavefront
-  static_assert(A_INS * 16 * NW == BM && B_INS * NW == 3 * BRB, "tile/wavefront mismatch");
+  static_assert(NW == 8, "two groups of four wavefronts");
+  constexpr int NL = 4;  // loading wavefronts (group 0..3)
+  constexpr int A_INS = BM / 16 / NL, B_INS = 3 * BRB / NL;  // 1 KiB loads per loading wavefront
+  static_assert(A_INS * 16 * NL == BM && B_INS * NL == 3 * BRB, "tile/wavefront mismatch");
   static_assert(!POOL || (BM == 256 && BN == 256 && WM == kPoolWM && WN == kPoolWN && NW == 8), "pooling tile shape");
   // stage buffers as floats (x tile then weight parts), reused by the pooling epilogue
   constexpr int STAGE_FLOATS = 2 * (BM + 3 * BN) * BK / 2;
@@ -123,6 +146,11 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_x3_kernel(GemmArgs g) {
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  // the wavefront index as a scalar: the loads' LDS addresses and offsets
+  // derived from it are then wavefront-uniform values, not per-lane ones
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const bool loader = wave_u < NL;  // group 0..3
+  const int lw = wave_u % NL;       // its index among the loading wavefronts
 
   // Load u of this wavefront fills 1 KiB = 16 rows of 64 bytes: lane l ->
   // row l / 4 of the block, group position l % 4, which holds k-group
@@ -137,7 +165,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_x3_kernel(GemmArgs g) {
   uint32_t a_voff[A_INS];
 #pragma unroll
   for (int u = 0; u < A_INS; ++u) {
-    int64_t r = 16 * (wave * A_INS + u) + lr;
+    int64_t r = 16 * (lw * A_INS + u) + lr;
     if (r >= a_rows) r = a_rows - 1;  // ragged last tile: read a valid row, never store it
     a_voff[u] = (uint32_t)((r * g.lda + 8 * lq) * 2);
   }
@@ -146,11 +174,11 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_x3_kernel(GemmArgs g) {
     const uint32_t koff = (uint32_t)(kt * BK * 2);
 #pragma unroll
     for (int u = 0; u < A_INS; ++u)
-      buffer_load_lds(a_rsrc, (lds_u32 *)(&As[st][512 * (wave * A_INS + u)]), 16, (int32_t)a_voff[u],
+      buffer_load_lds(a_rsrc, (lds_u32 *)(&As[st][512 * (lw * A_INS + u)]), 16, (int32_t)a_voff[u],
                       (int32_t)koff, 0, 0);
 #pragma unroll
     for (int u = 0; u < B_INS; ++u) {
-      const int q = wave * B_INS + u, p = q / BRB, rb = q % BRB;
+      const int q = lw * B_INS + u, p = q / BRB, rb = q % BRB;
       buffer_load_lds(b_rsrc, (lds_u32 *)(&Bs[st][p][512 * rb]), 16, (int32_t)b_voff,
                       (int32_t)(koff + (uint32_t)((rb * 16 * 3 * g.k + p * g.k) * 2)), 0, 0);
     }
@@ -163,49 +191,48 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_x3_kernel(GemmArgs g) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
   const int row_in = lane & 15, slot = lane >> 4;
-  bf16x8 fa[FM], fb[2][FN];
-  auto aload = [&](int st) {
+  bf16x8 fa[FM], fb[3][FN];
+  auto reads = [&](int st) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = wm * WM + 16 * i + row_in;
       fa[i] = *reinterpret_cast<const bf16x8 *>(&As[st][r * BK + 8 * (slot ^ ((r >> 1) & 3))]);
     }
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * WN + 16 * j + row_in;
+        fb[p][j] = *reinterpret_cast<const bf16x8 *>(&Bs[st][p][r * BK + 8 * (slot ^ ((r >> 1) & 3))]);
+      }
   };
-  auto bload = [&](int st, int p, int sl) {
+  auto mfmas = [&]() {  // hi, then mid, then lo
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int r = wn * WN + 16 * j + row_in;
-      fb[sl][j] = *reinterpret_cast<const bf16x8 *>(&Bs[st][p][r * BK + 8 * (slot ^ ((r >> 1) & 3))]);
-    }
-  };
-  auto mfma = [&](int sl) {
+    for (int p = 0; p < 3; ++p)
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[sl][j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[p][j], acc[i][j], 0, 0, 0);
   };
 
-  issue(0, 0);
-  wait_vm0();
-  __syncthreads();
+  if (loader) {
+    issue(0, 0);
+    wait_vm0();
+  }
+  phase_barrier();
+  if (!loader) phase_barrier();  // group 4..7 runs one phase behind
   for (int kt = 0; kt < kt_count; ++kt) {
     const int st = kt & 1;
-    aload(st);
-    bload(st, 0, 0);
-    bload(st, 1, 1);
-    mfma(0);  // hi
-    __builtin_amdgcn_sched_barrier(0);
-    bload(st, 2, 0);
-    // unconditional, so the loop body stays one block: the last iteration
-    // reloads its own stage into the idle one, which is never read
-    issue(kt + 1 < kt_count ? kt + 1 : kt, st ^ 1);
-    mfma(1);  // mid
-    mfma(0);  // lo
-    __builtin_amdgcn_sched_barrier(0);  // the stage's MFMAs stay ahead of the wait
-    wait_vm0();                         // this wavefront's loads of the next stage landed
-    __syncthreads();                    // everyone's landed; everyone is done reading this stage
+    reads(st);
+    if (loader && kt + 1 < kt_count) issue(kt + 1, st ^ 1);  // after the stage's last LDS read
+    wait_lgkm0();  // this stage's reads are done before its buffer can be reloaded
+    phase_barrier();
+    mfmas();
+    if (loader) wait_vm0();  // the next stage has landed before this group reads it
+    phase_barrier();
   }
+  if (loader) phase_barrier();  // the same number of barriers for every wavefront
 
   if constexpr (POOL) {
     pool_epilogue<WM, WN>(g, acc, smem, m0, 64 * nt, wm, wn, lane);
