@@ -47,7 +47,7 @@ KERNEL_SOURCES = {
     "gemm": ["kv_cache_compression_fp32_amd/csrc/gemm_common.h", "kv_cache_compression_fp32_amd/csrc/gemm_f32_kernel.h",
              "kv_cache_compression_fp32_amd/csrc/gemm_f32.hip", "kv_cache_compression_fp32_amd/csrc/kvc_device.h",
              "kv_cache_compression_fp32_amd/csrc/gemm_epilogue.h"],
-    "gemm_x3": ["kv_cache_compression_fp32_amd/csrc/gemm_common.h", "kv_cache_compression_fp32_amd/csrc/gemm_x3.hip",
+    "gemm_x3": ["kv_cache_compression_fp32_amd/csrc/gemm_common.h", "kv_cache_compression_fp32_amd/csrc/gemm_bf16.hip",
                 "kv_cache_compression_fp32_amd/csrc/kvc_device.h", "kv_cache_compression_fp32_amd/csrc/gemm_epilogue.h"],
     "pool": ["kv_cache_compression_fp32_amd/csrc/pool.hip", "kv_cache_compression_fp32_amd/csrc/kvc_device.h"],
 }
@@ -367,7 +367,7 @@ def main():
         roofline = {"bound": "mfma", "achieved": round(g["mfma_tflops"], 2), "peak": PEAK_BF16_MFMA_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(g["mfma_tflops"] / PEAK_BF16_MFMA_TFLOPS, 4),
                     "traffic": measured_traffic("gemm_x3"),
-                    "kernel": "gemm_x3_kernel (512-wide projection, bf16 x times the three bf16 parts of the f32 "
+                    "kernel": "gemm_mc_kernel (512-wide projection, bf16 x times the three bf16 parts of the f32 "
                               "weights, f32 accumulation)",
                     "per_launch": g["mfma_flop"], "avg_ms": round(g["ms"], 4),
                     "f32_equivalent_tflops": round(g["tflops"], 2)}

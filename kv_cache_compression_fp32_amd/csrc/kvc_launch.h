@@ -55,7 +55,7 @@ hipError_t launch_gemm_pool(const GemmArgs &g, hipStream_t stream);
 // Number of 256-row tiles of launch_gemm_pool (the boundary entries' count + 1).
 inline int64_t gemm_pool_row_tiles(int64_t m) { return (m + 255) / 256; }
 
-// bf16 x times f32 weights as three exact bf16 parts (gemm_x3.hip):
+// bf16 x times f32 weights as three exact bf16 parts (gemm_bf16.hip):
 // launch_split_weights writes out[2 n_half][3][k] (bf16 hi, mid, lo of each
 // weight) from w0 (rows 0 .. n_half - 1) and w1 (the rest); with pool_hd set
 // (ratio 4, n_half = 2 pool_hd) the rows are in the order of the pooling
