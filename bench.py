@@ -6,21 +6,21 @@ One step is one pass of the whole path over one batch: for the default
 workload (ratio-4 prefill of 65536 tokens, hidden 4096) that is the 512-wide
 compressor (f32 projections, pooling + RMSNorm + fp4 cache codes) and the
 128-wide indexer compressor (projections, pooling + RMSNorm, bf16 latent),
-with the hidden states resident in HBM. The hidden states are the model's
-bf16 ones (--x-format f32 passes the same values as f32 rows): the
-projections are f32 products of bf16 x and f32 weights either way, computed
-from the weights' three exact bf16 parts on the bf16 matrix cores for bf16 x,
-on the f32 matrix cores for f32 x. The other x format's step is reported
-beside the headline. Prints one JSON line.
+with the hidden states resident in HBM: x f32 [1, 65536, 4096] ~ N(0, 1), the
+projections on the f32 matrix cores. Beside it (`workloads`) the same step
+from the model's bf16 hidden states (the bf16 rounding of the same draws,
+handed over as bf16 rows; --x-format bf16 makes that the headline): the
+projections are then the same f32 products, computed from the weights' three
+exact bf16 parts on the bf16 matrix cores. Prints one JSON line.
 
 Kernel durations are measured with HIP events on the launch stream around
 repeated launches of each kernel alone (the same library calls with the other
 stages switched off through their arguments: no outputs = projection only,
-which for bf16 x is the weight split (about 0.6% of it) and the GEMM;
+which for bf16 x is the weight split (about 0.7% of it) and the GEMM;
 projections given = pooling only). The roofline object reports the dominant
-kernel (the 512-wide projection GEMM, matrix-core bound: for bf16 x its three
-bf16 passes against the bf16 peak); `pool` reports the pooling kernel against
-HBM bandwidth.
+kernel (the 512-wide projection GEMM, matrix-core bound: for f32 x against
+the fp32 peak; for bf16 x its three bf16 passes against the bf16 peak);
+`pool` reports the pooling kernel against HBM bandwidth.
 """
 from __future__ import annotations
 
@@ -94,7 +94,7 @@ def bf16_hidden(torch, x: np.ndarray) -> np.ndarray:
     return torch.from_numpy(x).to(torch.bfloat16).float().numpy()
 
 
-def cpu_baseline(wl, W, seconds=10.0, x_bf16=True):
+def cpu_baseline(wl, W, seconds=10.0, x_bf16=False):
     """The oracle, as it stands, on the first tokens of the workload: doubles
     the sample until it takes `seconds` or covers the whole sequence."""
     import torch
@@ -144,13 +144,13 @@ def _rounded(d):
 
 
 def run_prefill(wl, steps, warmup, reps, torch, kvc, W, x_format):
-    """Time whole prefill steps of `wl`, then each kernel alone. x holds the
-    bf16 hidden states, as bf16 rows or (x_format f32) as f32 rows."""
+    """Time whole prefill steps of `wl`, then each kernel alone. x is the
+    workload's f32 draws, or (x_format bf16) their bf16 rounding as bf16 rows."""
     dev = "cuda"
     print(f"[bench] {wl.name}: generating inputs (x_format {x_format})", file=sys.stderr, flush=True)
-    x = torch.from_numpy(W.hidden(wl)).to(dev).to(torch.bfloat16)
-    if x_format == kvc.KVC_X_F32:
-        x = x.float()
+    x = torch.from_numpy(W.hidden(wl)).to(dev)
+    if x_format == kvc.KVC_X_BF16:
+        x = x.to(torch.bfloat16)
     torch.cuda.synchronize()
     comps = []
     for comp in wl.compressors:
@@ -216,9 +216,9 @@ def run_decode(wl, passes, torch, kvc, W, x_format):
     comp = wl.compressors[0]
     cfg = kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps, x_format=x_format)
     print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
-    x = torch.from_numpy(W.hidden(wl)).to(dev).to(torch.bfloat16)
-    if x_format == kvc.KVC_X_F32:
-        x = x.float()
+    x = torch.from_numpy(W.hidden(wl)).to(dev)
+    if x_format == kvc.KVC_X_BF16:
+        x = x.to(torch.bfloat16)
     x = x.transpose(0, 1).contiguous()  # [steps, batch, dim]
     w = {k: torch.from_numpy(v).to(dev) for k, v in W.weights(wl, comp).items()}
     wts = kvc.Weights(wkv=w["wkv"], wgate=w["wgate"], ape=w["ape"])
@@ -324,8 +324,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill_r4_n65536_fp4_idx128")
     ap.add_argument("--kernel-reps", type=int, default=20)
-    ap.add_argument("--x-format", choices=("bf16", "f32"), default="bf16",
-                    help="element type of the hidden states handed to the library")
+    ap.add_argument("--x-format", choices=("f32", "bf16"), default="f32",
+                    help="hidden states handed to the library: the f32 draws, or their bf16 rounding as bf16 rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -384,7 +384,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "seqlen": wl.seqlen, "dim": wl.dim,
-                   "x": "bf16 hidden states" if x_format == kvc.KVC_X_BF16 else "f32 rows (bf16 values)",
+                   "x": ("bf16 rows: the bf16 rounding of the N(0,1) draws" if x_format == kvc.KVC_X_BF16
+                         else "f32 rows, N(0,1)"),
                    "weights": "f32",
                    "compressors": [{"ratio": c.ratio, "head_dim": c.head_dim, "fp4": c.quantize}
                                    for c in wl.compressors],
@@ -397,10 +398,25 @@ def main():
     if not args.no_extras:
         extras = {}
         other = kvc.KVC_X_F32 if x_format == kvc.KVC_X_BF16 else kvc.KVC_X_BF16
-        r = run_prefill(wl, 5, 2, 5, torch, kvc, W, other)
-        extras[f"{wl.name}_x_{'f32' if other == kvc.KVC_X_F32 else 'bf16'}"] = {
-            "ms_per_step": round(r["ms_per_step"], 4), "entries_per_s": round(r["entries_per_s"], 1),
-            "kernels": {k: _rounded(v) for k, v in r["kernels"].items()}}
+        r = run_prefill(wl, 20, 20, args.kernel_reps, torch, kvc, W, other)
+        line = {"x": ("bf16 rows: the bf16 rounding of the N(0,1) draws, the model's hidden-state type"
+                      if other == kvc.KVC_X_BF16 else "f32 rows, N(0,1)"),
+                "ms_per_step": round(r["ms_per_step"], 4), "entries_per_s": round(r["entries_per_s"], 1),
+                "kernels": {k: _rounded(v) for k, v in r["kernels"].items()}}
+        og = r["kernels"][f"gemm_{main_tag}"]
+        if other == kvc.KVC_X_BF16:
+            line["roofline"] = {"bound": "mfma", "achieved": round(og["mfma_tflops"], 2), "peak": PEAK_BF16_MFMA_TFLOPS,
+                                "unit": "TFLOP/s", "frac": round(og["mfma_tflops"] / PEAK_BF16_MFMA_TFLOPS, 4),
+                                "traffic": measured_traffic("gemm_x3"),
+                                "kernel": "gemm_mc_kernel (512-wide projection, three bf16 passes)",
+                                "per_launch": og["mfma_flop"], "avg_ms": round(og["ms"], 4),
+                                "f32_equivalent_tflops": round(og["tflops"], 2)}
+        else:
+            line["roofline"] = {"bound": "mfma", "achieved": round(og["tflops"], 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+                                "unit": "TFLOP/s", "frac": round(og["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4),
+                                "traffic": measured_traffic("gemm"), "kernel": "gemm_f32_kernel (512-wide projection)",
+                                "per_launch": og["flop"], "avg_ms": round(og["ms"], 4)}
+        extras[f"{wl.name}_x_{'f32' if other == kvc.KVC_X_F32 else 'bf16'}"] = line
         for name in ("prefill_r4_n4096", "prefill_r128_b2_n16384"):
             r = run_prefill(W.WORKLOADS[name], 5, 2, 5, torch, kvc, W, x_format)
             extras[name] = {"ms_per_step": round(r["ms_per_step"], 4), "entries_per_s": round(r["entries_per_s"], 1),
