@@ -6,12 +6,14 @@ One step is one pass of the whole path over one batch: for the default
 workload (ratio-4 prefill of 65536 tokens, hidden 4096) that is the 512-wide
 compressor (f32 projections, pooling + RMSNorm + fp4 cache codes) and the
 128-wide indexer compressor (projections, pooling + RMSNorm, bf16 latent),
-with the hidden states resident in HBM: x f32 [1, 65536, 4096] ~ N(0, 1), the
-projections on the f32 matrix cores. Beside it (`workloads`) the same step
-from the model's bf16 hidden states (the bf16 rounding of the same draws,
-handed over as bf16 rows; --x-format bf16 makes that the headline): the
-projections are then the same f32 products, computed from the weights' three
-exact bf16 parts on the bf16 matrix cores. Prints one JSON line.
+with the hidden states resident in HBM: x f32 [1, 65536, 4096] ~ N(0, 1).
+The projections are f32 products computed on the bf16 matrix cores from
+exact bf16 parts (x and the weights split into hi + mid + lo, the six part
+products of size >= 2^-16 |x w| summed in f32; --projection f32-mfma uses the
+f32 matrix cores instead). Beside the headline (`workloads`) the same step on
+the f32 matrix cores, and from the model's bf16 hidden states (the bf16
+rounding of the same draws as bf16 rows: exact products from the weights'
+three parts; --x-format bf16 makes that the headline). Prints one JSON line.
 
 Kernel durations are measured with HIP events on the launch stream around
 repeated launches of each kernel alone (the same library calls with the other
@@ -47,6 +49,8 @@ KERNEL_SOURCES = {
     "gemm": ["kv_cache_compression_fp32_amd/csrc/gemm_common.h", "kv_cache_compression_fp32_amd/csrc/gemm_f32_kernel.h",
              "kv_cache_compression_fp32_amd/csrc/gemm_f32.hip", "kv_cache_compression_fp32_amd/csrc/kvc_device.h",
              "kv_cache_compression_fp32_amd/csrc/gemm_epilogue.h"],
+    "gemm_x6": ["kv_cache_compression_fp32_amd/csrc/gemm_common.h", "kv_cache_compression_fp32_amd/csrc/gemm_bf16.hip",
+                "kv_cache_compression_fp32_amd/csrc/kvc_device.h", "kv_cache_compression_fp32_amd/csrc/gemm_epilogue.h"],
     "gemm_x3": ["kv_cache_compression_fp32_amd/csrc/gemm_common.h", "kv_cache_compression_fp32_amd/csrc/gemm_bf16.hip",
                 "kv_cache_compression_fp32_amd/csrc/kvc_device.h", "kv_cache_compression_fp32_amd/csrc/gemm_epilogue.h"],
     "pool": ["kv_cache_compression_fp32_amd/csrc/pool.hip", "kv_cache_compression_fp32_amd/csrc/kvc_device.h"],
@@ -139,11 +143,40 @@ def _timed(torch, stream, fn, reps):
     return a.elapsed_time(b) / reps
 
 
+def gemm_roofline(kvc, g, x_format, projection):
+    """Roofline object of the 512-wide projection launch `g`: on the bf16
+    matrix cores its passes against the bf16 peak (with the f32-equivalent
+    rate beside it), on the f32 matrix cores its flops against the fp32 peak."""
+    passes = mfma_passes(kvc, x_format, projection)
+    if passes:
+        what = ("bf16 x times the three bf16 parts of the f32 weights" if passes == 3 else
+                "f32 x split into three bf16 parts times the three parts of the f32 weights, six part products")
+        return {"bound": "mfma", "achieved": round(g["mfma_tflops"], 2), "peak": PEAK_BF16_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(g["mfma_tflops"] / PEAK_BF16_MFMA_TFLOPS, 4),
+                "traffic": measured_traffic("gemm_x3" if passes == 3 else "gemm_x6"),
+                "kernel": f"{'gemm_mc_kernel' if passes == 3 else 'gemm_x6_kernel'} (512-wide projection, {what}, "
+                          "f32 accumulation)",
+                "per_launch": g["mfma_flop"], "avg_ms": round(g["ms"], 4),
+                "f32_equivalent_tflops": round(g["tflops"], 2),
+                "f32_equivalent_frac_of_fp32_peak": round(g["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4)}
+    return {"bound": "mfma", "achieved": round(g["tflops"], 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(g["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4),
+            "traffic": measured_traffic("gemm"), "kernel": "gemm_f32_kernel (512-wide projection, f32 matrix cores)",
+            "per_launch": g["flop"], "avg_ms": round(g["ms"], 4)}
+
+
 def _rounded(d):
     return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
 
 
-def run_prefill(wl, steps, warmup, reps, torch, kvc, W, x_format):
+def mfma_passes(kvc, x_format, projection):
+    """bf16 matrix-core passes per f32 product (0: the f32 matrix cores)."""
+    if projection == kvc.KVC_PROJ_F32_MFMA:
+        return 0
+    return 3 if x_format == kvc.KVC_X_BF16 else 6
+
+
+def run_prefill(wl, steps, warmup, reps, torch, kvc, W, x_format, projection):
     """Time whole prefill steps of `wl`, then each kernel alone. x is the
     workload's f32 draws, or (x_format bf16) their bf16 rounding as bf16 rows."""
     dev = "cuda"
@@ -154,7 +187,7 @@ def run_prefill(wl, steps, warmup, reps, torch, kvc, W, x_format):
     torch.cuda.synchronize()
     comps = []
     for comp in wl.compressors:
-        cfg = kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps, x_format=x_format)
+        cfg = kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps, x_format=x_format, projection=projection)
         w = {k: torch.from_numpy(v).to(dev) for k, v in W.weights(wl, comp).items()}
         wts = kvc.Weights(wkv=w["wkv"], wgate=w["wgate"], ape=w["ape"])
         groups = wl.seqlen // comp.ratio
@@ -188,9 +221,10 @@ def run_prefill(wl, steps, warmup, reps, torch, kvc, W, x_format):
         flops = 2.0 * wl.batch * wl.seqlen * wl.dim * 2 * proj
         pbytes = pool_bytes(wl.batch, wl.seqlen, comp.ratio, comp.head_dim, comp.quantize, not comp.quantize)
         kernels[f"gemm_{tag}"] = {"ms": gemm_ms, "tflops": flops / gemm_ms / 1e9, "flop": flops}
-        if x_format == kvc.KVC_X_BF16:
-            # the matrix-core work: three bf16 passes (hi, mid, lo weight parts)
-            kernels[f"gemm_{tag}"].update({"mfma_flop": 3 * flops, "mfma_tflops": 3 * flops / gemm_ms / 1e9})
+        passes = mfma_passes(kvc, x_format, projection)
+        if passes:
+            # the bf16 matrix-core work: one pass per part product
+            kernels[f"gemm_{tag}"].update({"mfma_flop": passes * flops, "mfma_tflops": passes * flops / gemm_ms / 1e9})
         kernels[f"pool_{tag}"] = {"ms": pool_ms, "gbps": pbytes / pool_ms / 1e6, "bytes": pbytes}
         if comp.head_dim == 128 and not comp.quantize:
             # the same pooling with the index keys' fp4 form (power-of-two
@@ -326,6 +360,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--x-format", choices=("f32", "bf16"), default="f32",
                     help="hidden states handed to the library: the f32 draws, or their bf16 rounding as bf16 rows")
+    ap.add_argument("--projection", choices=("split", "f32-mfma"), default="split",
+                    help="prefill projection on the bf16 matrix cores from exact bf16 parts, or on the f32 matrix cores")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -358,24 +394,13 @@ def main():
         torch.cuda.empty_cache()
 
     x_format = kvc.KVC_X_BF16 if args.x_format == "bf16" else kvc.KVC_X_F32
-    head = run_prefill(wl, args.steps, args.warmup, args.kernel_reps, torch, kvc, W, x_format)
+    projection = kvc.KVC_PROJ_F32_MFMA if args.projection == "f32-mfma" else kvc.KVC_PROJ_BF16_SPLIT
+    head = run_prefill(wl, args.steps, args.warmup, args.kernel_reps, torch, kvc, W, x_format, projection)
     kernels = head["kernels"]
     main_tag = f"hd{wl.compressors[0].head_dim}"
     g = kernels[f"gemm_{main_tag}"]
     p = kernels[f"pool_{main_tag}"]
-    if x_format == kvc.KVC_X_BF16:
-        roofline = {"bound": "mfma", "achieved": round(g["mfma_tflops"], 2), "peak": PEAK_BF16_MFMA_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(g["mfma_tflops"] / PEAK_BF16_MFMA_TFLOPS, 4),
-                    "traffic": measured_traffic("gemm_x3"),
-                    "kernel": "gemm_mc_kernel (512-wide projection, bf16 x times the three bf16 parts of the f32 "
-                              "weights, f32 accumulation)",
-                    "per_launch": g["mfma_flop"], "avg_ms": round(g["ms"], 4),
-                    "f32_equivalent_tflops": round(g["tflops"], 2)}
-    else:
-        roofline = {"bound": "mfma", "achieved": round(g["tflops"], 2), "peak": PEAK_FP32_MFMA_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(g["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4),
-                    "traffic": measured_traffic("gemm"), "kernel": "gemm_f32_kernel (512-wide projection)",
-                    "per_launch": g["flop"], "avg_ms": round(g["ms"], 4)}
+    roofline = gemm_roofline(kvc, g, x_format, projection)
     pool = {"bound": "hbm", "achieved": round(p["gbps"], 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(p["gbps"] / PEAK_HBM_GBPS, 4), "traffic": measured_traffic("pool"),
             "kernel": "pool_small_kernel<512,4,true>", "per_launch": p["bytes"], "avg_ms": round(p["ms"], 4)}
@@ -386,6 +411,8 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "seqlen": wl.seqlen, "dim": wl.dim,
                    "x": ("bf16 rows: the bf16 rounding of the N(0,1) draws" if x_format == kvc.KVC_X_BF16
                          else "f32 rows, N(0,1)"),
+                   "projection": ("f32 matrix cores" if projection == kvc.KVC_PROJ_F32_MFMA else
+                                  "bf16 matrix cores on exact bf16 parts, f32 accumulation"),
                    "weights": "f32",
                    "compressors": [{"ratio": c.ratio, "head_dim": c.head_dim, "fp4": c.quantize}
                                    for c in wl.compressors],
@@ -397,28 +424,23 @@ def main():
     }
     if not args.no_extras:
         extras = {}
-        other = kvc.KVC_X_F32 if x_format == kvc.KVC_X_BF16 else kvc.KVC_X_BF16
-        r = run_prefill(wl, 20, 20, args.kernel_reps, torch, kvc, W, other)
-        line = {"x": ("bf16 rows: the bf16 rounding of the N(0,1) draws, the model's hidden-state type"
-                      if other == kvc.KVC_X_BF16 else "f32 rows, N(0,1)"),
-                "ms_per_step": round(r["ms_per_step"], 4), "entries_per_s": round(r["entries_per_s"], 1),
+        # the same step by the other projection paths
+        for name, xf, pr, desc in (
+                ("f32_mfma", kvc.KVC_X_F32, kvc.KVC_PROJ_F32_MFMA, "f32 rows, N(0,1); f32 matrix cores"),
+                ("split", kvc.KVC_X_F32, kvc.KVC_PROJ_BF16_SPLIT,
+                 "f32 rows, N(0,1); bf16 matrix cores on exact bf16 parts (six part products)"),
+                ("x_bf16", kvc.KVC_X_BF16, kvc.KVC_PROJ_BF16_SPLIT,
+                 "bf16 rows: the bf16 rounding of the N(0,1) draws, the model's hidden-state type; bf16 matrix "
+                 "cores on the exact bf16 parts of the weights")):
+            if (xf, pr) == (x_format, projection):
+                continue
+            r = run_prefill(wl, 20, 20, args.kernel_reps, torch, kvc, W, xf, pr)
+            extras[f"{wl.name}_{name}"] = {
+                "x": desc, "ms_per_step": round(r["ms_per_step"], 4), "entries_per_s": round(r["entries_per_s"], 1),
+                "roofline": gemm_roofline(kvc, r["kernels"][f"gemm_{main_tag}"], xf, pr),
                 "kernels": {k: _rounded(v) for k, v in r["kernels"].items()}}
-        og = r["kernels"][f"gemm_{main_tag}"]
-        if other == kvc.KVC_X_BF16:
-            line["roofline"] = {"bound": "mfma", "achieved": round(og["mfma_tflops"], 2), "peak": PEAK_BF16_MFMA_TFLOPS,
-                                "unit": "TFLOP/s", "frac": round(og["mfma_tflops"] / PEAK_BF16_MFMA_TFLOPS, 4),
-                                "traffic": measured_traffic("gemm_x3"),
-                                "kernel": "gemm_mc_kernel (512-wide projection, three bf16 passes)",
-                                "per_launch": og["mfma_flop"], "avg_ms": round(og["ms"], 4),
-                                "f32_equivalent_tflops": round(og["tflops"], 2)}
-        else:
-            line["roofline"] = {"bound": "mfma", "achieved": round(og["tflops"], 2), "peak": PEAK_FP32_MFMA_TFLOPS,
-                                "unit": "TFLOP/s", "frac": round(og["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4),
-                                "traffic": measured_traffic("gemm"), "kernel": "gemm_f32_kernel (512-wide projection)",
-                                "per_launch": og["flop"], "avg_ms": round(og["ms"], 4)}
-        extras[f"{wl.name}_x_{'f32' if other == kvc.KVC_X_F32 else 'bf16'}"] = line
         for name in ("prefill_r4_n4096", "prefill_r128_b2_n16384"):
-            r = run_prefill(W.WORKLOADS[name], 5, 2, 5, torch, kvc, W, x_format)
+            r = run_prefill(W.WORKLOADS[name], 5, 2, 5, torch, kvc, W, x_format, projection)
             extras[name] = {"ms_per_step": round(r["ms_per_step"], 4), "entries_per_s": round(r["entries_per_s"], 1),
                             "kernels": {k: _rounded(v) for k, v in r["kernels"].items()}}
         d = run_decode(W.WORKLOADS["decode_r4_b64_s512"], 5, torch, kvc, W, x_format)

@@ -67,6 +67,10 @@ typedef struct ihipStream_t *kvc_stream; /* a hipStream_t */
 #define KVC_X_F32 0  /* f32 rows */
 #define KVC_X_BF16 1 /* bf16 rows: the model's hidden state */
 
+/* matrix cores of the prefill projection (kvc_config.projection) */
+#define KVC_PROJ_BF16_SPLIT 0 /* bf16 matrix cores on exact bf16 parts (default; see x_format) */
+#define KVC_PROJ_F32_MFMA 1   /* f32 matrix cores (x_format KVC_X_F32 only) */
+
 /* fp4 forms of a compressed entry (kvc_config.fp4_format) */
 #define KVC_FP4_E4M3_B16 0 /* the KV latent's form: e4m3fn scale per block of 16 */
 #define KVC_FP4_E8M0_B32 1 /* the indexer's form: power-of-two (e8m0) scale per block of 32 */
@@ -97,12 +101,19 @@ typedef struct ihipStream_t *kvc_stream; /* a hipStream_t */
  *                The compressor promotes the model's bf16 hidden state to f32
  *                before its f32 projections ("DeepSeek V4.1 . Pool token
  *                pairs", Compressor listing, forward); with KVC_X_BF16 the
- *                caller passes that bf16 state and the library computes the
- *                same f32 products: each f32 weight is split exactly into
- *                three bf16 parts (hi, mid, lo), each bf16 x bf16 product is
- *                exact in f32, and the bf16 matrix cores sum them with f32
- *                accumulation. Ignored by compressor_ratio1_forward, whose x
- *                is always bf16.
+ *                caller passes that bf16 state. Ignored by
+ *                compressor_ratio1_forward, whose x is always bf16.
+ *   projection : how compressor_prefill computes the f32 products x . w^T.
+ *                KVC_PROJ_BF16_SPLIT (default): on the bf16 matrix cores with
+ *                f32 accumulation, from the exact split of each f32 weight
+ *                into three bf16 parts (hi, mid, lo: bits cleared, so
+ *                w = hi + mid + lo); bf16 x then gives exact products (x .
+ *                hi + x . mid + x . lo), and f32 x is split the same way
+ *                and the six part products of size >= 2^-16 |x w| are summed
+ *                (the three left out total below 2^-21 |x w|, far inside the
+ *                f32 summation's own error bound). KVC_PROJ_F32_MFMA: on the
+ *                f32 matrix cores (x_format KVC_X_F32 only; KVC_EINVAL
+ *                otherwise). Decode steps always use the f32 matrix cores.
  * proj = 2 * head_dim at ratio 4, head_dim otherwise: the width of each
  * projection plane. */
 typedef struct kvc_config {
@@ -113,6 +124,7 @@ typedef struct kvc_config {
     int32_t fp4_format;
     int32_t rope_dim;
     int32_t x_format;
+    int32_t projection;
 } kvc_config;
 
 /* Weights (device, f32).
@@ -168,9 +180,9 @@ int64_t kvc_state_rows(const kvc_config *cfg);
 /* f32 elements of the workspace compressor_prefill needs: the projection
  * planes, 2 * batch * seqlen * proj; at ratio 4 the f32 pooled entries,
  * batch * (seqlen / 4) * head_dim (used when the projection and the pooling
- * run as one kernel: a smaller workspace runs them separately); with
- * KVC_X_BF16 the three-part weights, 3 * proj * dim (bf16 [2 proj][3][dim]).
- * Or a negative KVC_E* code. */
+ * run as one kernel: a smaller workspace runs them separately); the weights'
+ * three bf16 parts, 3 * proj * dim (bf16 [2 proj][3][dim]; read only by the
+ * KVC_PROJ_BF16_SPLIT projection). Or a negative KVC_E* code. */
 int64_t kvc_prefill_workspace_floats(const kvc_config *cfg, int64_t batch, int64_t seqlen);
 
 /* f32 elements of the workspace compressor_decode_step needs (split
@@ -190,7 +202,7 @@ int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch);
  *                  except ape and norm_w.
  *   batch        : >= 1.   seqlen : >= 0.
  *   workspace    : f32, at least 2 * batch * seqlen * proj elements, and
- *                  with x in bf16 all kvc_prefill_workspace_floats() elements
+ *                  with x all kvc_prefill_workspace_floats() elements
  *                  (KVC_ESPACE otherwise); receives the two projection planes
  *                  when x is not NULL (the score plane then with the
  *                  positional bias added; at ratio 4 with the fused kernel,

@@ -83,11 +83,13 @@ __global__ __launch_bounds__(256) void split_weights_kernel(SplitArgs a) {
   const int64_t row = i / per_row, k0 = 8 * (i - row * per_row);
   const float *src;
   if (a.pool_hd) {
-    // pooling order: column tile t = row / 256 holds features 64 t .. +63;
-    // within it, [4 wavefront columns][kvA, kvB, scA, scB][16 features]
-    const int64_t t = row / 256, rem = row % 256, wn = rem / (4 * kPoolF), seg = (rem % (4 * kPoolF)) / kPoolF,
+    // pooling order: column tile t = row / T (T = pool_tile rows) holds
+    // features T / 4 t .. +T / 4 - 1; within it, [T / 64 wavefront
+    // columns][kvA, kvB, scA, scB][16 features]
+    const int64_t T = a.pool_tile;
+    const int64_t t = row / T, rem = row % T, wn = rem / (4 * kPoolF), seg = (rem % (4 * kPoolF)) / kPoolF,
                   c = rem % kPoolF;
-    const int64_t f = 64 * t + kPoolF * wn + c;
+    const int64_t f = (T / 4) * t + kPoolF * wn + c;
     src = (seg < 2 ? a.w0 : a.w1) + ((seg & 1) * a.pool_hd + f) * a.ldw;
   } else {
     src = row < a.n_half ? a.w0 + row * a.ldw : a.w1 + (row - a.n_half) * a.ldw;
@@ -266,6 +268,168 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_mc_kernel(GemmArgs g) {
   }
 }
 
+
+// f32 x times the three-part weights: gemm_x6_kernel. A 256 x 128 tile of
+// eight 64 x 64 wavefronts, the same ping-pong schedule and weight slices as
+// gemm_mc_kernel; the x tile stays f32 in LDS ([256][32] floats per stage,
+// 16-byte k-group q of row r at position q ^ (r & 7), loaded 8 rows per
+// instruction as in the f32 kernel). The read phase splits each x fragment
+// (8 consecutive k of a row) like the weights, x = xh + xm + xl (exact, bits
+// cleared), and the multiply phase sums the six part products whose size is
+// at least 2^-16 |x w|: xh wh, xh wm, xm wh, xh wl, xm wm, xl wh. The three
+// left out (xm wl, xl wm, xl wl) are below 2^-21 |x w| together, far inside
+// the f32 summation's own error bound (K 2^-24 sum |x w|).
+__device__ __forceinline__ void split8(const f4 lo4, const f4 hi4, bf16x8 &h, bf16x8 &m, bf16x8 &l) {
+  const float v[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+  uint32_t hw[4], mw[4], lw[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t hb[2], mb[2], lb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t b = __float_as_uint(v[2 * e + u]);
+      hb[u] = b & 0xffff0000u;
+      const float r1 = v[2 * e + u] - __uint_as_float(hb[u]);
+      mb[u] = __float_as_uint(r1) & 0xffff0000u;
+      lb[u] = __float_as_uint(r1 - __uint_as_float(mb[u])) & 0xffff0000u;
+    }
+    hw[e] = (hb[0] >> 16) | hb[1];
+    mw[e] = (mb[0] >> 16) | mb[1];
+    lw[e] = (lb[0] >> 16) | lb[1];
+  }
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  const u4 hv = {hw[0], hw[1], hw[2], hw[3]}, mv = {mw[0], mw[1], mw[2], mw[3]}, lv = {lw[0], lw[1], lw[2], lw[3]};
+  h = __builtin_bit_cast(bf16x8, hv);
+  m = __builtin_bit_cast(bf16x8, mv);
+  l = __builtin_bit_cast(bf16x8, lv);
+}
+
+template <bool POOL>
+__global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
+  constexpr int BM = 256, BN = 128, WM = 64, WN = 64, BK = kBK3;
+  constexpr int WAVES_N = BN / WN;  // 2
+  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int BRB = BN / 16;
+  constexpr int NL = 4;
+  constexpr int A_INS = BM / 8 / NL, B_INS = 3 * BRB / NL;  // x: 8 rows of 32 floats per load
+  constexpr int STAGE_FLOATS = 2 * (BM * BK + 3 * BN * BK / 2);
+  constexpr int SMEM_FLOATS = POOL && kPoolXFloats > STAGE_FLOATS ? kPoolXFloats : STAGE_FLOATS;
+  __shared__ __attribute__((aligned(16))) float smem[SMEM_FLOATS];
+  float(*As)[BM * BK] = reinterpret_cast<float(*)[BM * BK]>(smem);
+  uint16_t(*Bs)[3][BN * BK] = reinterpret_cast<uint16_t(*)[3][BN * BK]>(smem + 2 * BM * BK);
+
+  const int64_t m_tiles = (g.m + BM - 1) / BM;
+  const int64_t n_tiles = 2 * g.n_half / BN;  // with POOL: pool_hd / 32 tiles of 128 permuted rows
+  const uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t mt = tile / n_tiles, nt = tile - mt * n_tiles;
+  if (mt >= m_tiles) return;
+  const int64_t m0 = mt * BM, n_glob = nt * BN;
+  const bool second = n_glob >= g.n_half;
+  const int64_t n0 = second ? n_glob - g.n_half : n_glob;
+  const int kt_count = (int)(g.k / BK);
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const bool loader = wave_u < NL;
+  const int lw = wave_u % NL;
+
+  // x: load u of a loading wavefront fills rows 8 (lw A_INS + u) .. +7,
+  // lane l -> row l / 8, group position l % 8 holding k-group
+  // (l % 8) ^ ((l / 8) & 7); weights as gemm_mc_kernel (rows of 3 k).
+  const int64_t RS = 3 * g.k;
+  const int64_t a_rows = (g.m - m0 < BM) ? (g.m - m0) : BM;
+  const i32x4 a_rsrc = make_rsrc(g.a + m0 * g.lda, (uint32_t)(a_rows * g.lda * 4));
+  const i32x4 b_rsrc = make_rsrc(g.bsplit + n_glob * RS, (uint32_t)(BN * RS * 2));
+  const int xr = lane >> 3, xq = (lane & 7) ^ (xr & 7);
+  uint32_t a_voff[A_INS];
+#pragma unroll
+  for (int u = 0; u < A_INS; ++u) {
+    int64_t r = 8 * (lw * A_INS + u) + xr;
+    if (r >= a_rows) r = a_rows - 1;  // ragged last tile: read a valid row, never store it
+    a_voff[u] = (uint32_t)((r * g.lda + 4 * xq) * 4);
+  }
+  const int lr = lane >> 2, lq = (lane & 3) ^ ((lr >> 1) & 3);
+  const uint32_t b_voff = (uint32_t)((lr * RS + 8 * lq) * 2);
+  auto issue = [&](int kt, int st) {
+#pragma unroll
+    for (int u = 0; u < A_INS; ++u)
+      buffer_load_lds(a_rsrc, (lds_u32 *)(&As[st][256 * (lw * A_INS + u)]), 16, (int32_t)a_voff[u],
+                      (int32_t)(kt * BK * 4), 0, 0);
+#pragma unroll
+    for (int u = 0; u < B_INS; ++u) {
+      const int q = lw * B_INS + u, p = q / BRB, rb = q % BRB;
+      buffer_load_lds(b_rsrc, (lds_u32 *)(&Bs[st][p][512 * rb]), 16, (int32_t)b_voff,
+                      (int32_t)((uint32_t)(kt * BK * 2) + (uint32_t)((rb * 16 * RS + p * g.k) * 2)), 0, 0);
+    }
+  };
+
+  f4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+  const int row_in = lane & 15, slot = lane >> 4;
+  bf16x8 fa[3][FM], fb[3][FN];
+  auto reads = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WM + 16 * i + row_in;
+      const f4 lo4 = *reinterpret_cast<const f4 *>(&As[st][r * BK + 4 * ((2 * slot) ^ (r & 7))]);
+      const f4 hi4 = *reinterpret_cast<const f4 *>(&As[st][r * BK + 4 * ((2 * slot + 1) ^ (r & 7))]);
+      split8(lo4, hi4, fa[0][i], fa[1][i], fa[2][i]);
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * WN + 16 * j + row_in;
+        fb[p][j] = *reinterpret_cast<const bf16x8 *>(&Bs[st][p][r * BK + 8 * (slot ^ ((r >> 1) & 3))]);
+      }
+  };
+  auto pair = [&](int xp, int wp) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[xp][i], fb[wp][j], acc[i][j], 0, 0, 0);
+  };
+  auto mfmas = [&]() {
+    pair(0, 0);
+    pair(0, 1);
+    pair(1, 0);
+    pair(0, 2);
+    pair(1, 1);
+    pair(2, 0);
+  };
+
+  if (loader) {
+    issue(0, 0);
+    wait_vm0();
+  }
+  phase_barrier();
+  if (!loader) phase_barrier();  // group 4..7 runs one phase behind
+  for (int kt = 0; kt < kt_count; ++kt) {
+    const int st = kt & 1;
+    reads(st);
+    if (loader && kt + 1 < kt_count) issue(kt + 1, st ^ 1);  // after the stage's last LDS read
+    wait_lgkm0();
+    phase_barrier();
+    mfmas();
+    if (loader) wait_vm0();
+    phase_barrier();
+  }
+  if (loader) phase_barrier();  // the same number of barriers for every wavefront
+
+  if constexpr (POOL) {
+    pool_epilogue<WM, WN>(g, acc, smem, m0, 32 * nt, wm, wn, lane);
+  } else {
+    store_tile<FM, FN>(g, acc, second ? g.c1 : g.c0, second ? g.bias1 : nullptr, m0 + wm * WM, n0 + wn * WN,
+                       lane);
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int NW, int MINW, bool POOL, bool SPLIT3 = true>
 hipError_t launch(const GemmArgs &g, int64_t n_tiles, hipStream_t stream) {
   const int64_t m_tiles = (g.m + BM - 1) / BM;
@@ -287,7 +451,7 @@ bool addressable(const GemmArgs &g, int64_t k_per_stage, int64_t row_elems) {
 hipError_t launch_split_weights(const SplitArgs &a, hipStream_t stream) {
   if (a.n_half <= 0 || a.k <= 0) return hipSuccess;
   if (a.k % 8 != 0 || a.ldw < a.k || (a.pool_hd && 2 * a.n_half != 4 * (int64_t)a.pool_hd) ||
-      (a.pool_hd && a.pool_hd % 64 != 0))
+      (a.pool_hd && (a.pool_tile != 256 && a.pool_tile != 128)) || (a.pool_hd && a.pool_hd % (a.pool_tile / 4) != 0))
     return hipErrorInvalidValue;
   const int64_t total = 2 * a.n_half * (a.k / 8);
   hipLaunchKernelGGL(gemm::split_weights_kernel, dim3((uint32_t)((total + 255) / 256)), dim3(256), 0, stream, a);
@@ -338,6 +502,34 @@ hipError_t launch_gemm_bf16(const GemmBf16Args &a, hipStream_t stream) {
     return hipErrorInvalidValue;
   if (a.n % 256 == 0) return gemm::launch<256, 256, 128, 64, 8, 1, false, false>(g, a.n / 256, stream);
   return gemm::launch<256, 128, 64, 64, 8, 1, false, false>(g, a.n / 128, stream);
+}
+
+}  // namespace kvc
+
+namespace kvc {
+
+hipError_t launch_gemm_x6(const GemmArgs &g, hipStream_t stream) {
+  if (g.m <= 0) return hipSuccess;
+  if (g.n_half % 128 != 0 || g.lda < g.k || g.k % gemm::kBK3 != 0 || (int64_t)256 * g.lda * 4 > INT32_MAX ||
+      (int64_t)128 * 3 * g.k * 2 > INT32_MAX ||
+      (g.bias1 && (g.bias_seqlen < 1 || g.bias_ratio < 1 || (g.bias_ratio & (g.bias_ratio - 1)) != 0)))
+    return hipErrorInvalidValue;
+  const int64_t m_tiles = (g.m + 255) / 256;
+  hipLaunchKernelGGL(gemm::gemm_x6_kernel<false>, dim3((uint32_t)(m_tiles * (2 * g.n_half / 128))), dim3(512), 0,
+                     stream, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_x6_pool(const GemmArgs &g, hipStream_t stream) {
+  if (g.m <= 0) return hipSuccess;
+  if (g.pool_hd % 32 != 0 || g.n_half != 2 * (int64_t)g.pool_hd || g.ldc != 2 * g.pool_hd || g.lda < g.k ||
+      g.k % gemm::kBK3 != 0 || (int64_t)256 * g.lda * 4 > INT32_MAX || (int64_t)128 * 3 * g.k * 2 > INT32_MAX ||
+      g.m != g.pool_batch * g.pool_seqlen || (g.pool_batch > 1 && g.pool_seqlen % 4 != 0) || !g.pooled)
+    return hipErrorInvalidValue;
+  const int64_t m_tiles = (g.m + 255) / 256;
+  hipLaunchKernelGGL(gemm::gemm_x6_kernel<true>, dim3((uint32_t)(m_tiles * (g.pool_hd / 32))), dim3(512), 0, stream,
+                     g);
+  return hipGetLastError();
 }
 
 }  // namespace kvc

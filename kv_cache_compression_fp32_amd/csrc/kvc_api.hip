@@ -25,6 +25,8 @@ int check_common(const kvc_config *cfg) {
   if (cfg->head_dim != 128 && cfg->head_dim != 512) return KVC_EUNSUPPORTED;
   if (cfg->rope_dim < 0 || cfg->rope_dim > cfg->head_dim || cfg->rope_dim % 2 != 0) return KVC_EINVAL;
   if (cfg->x_format != KVC_X_F32 && cfg->x_format != KVC_X_BF16) return KVC_EINVAL;
+  if (cfg->projection != KVC_PROJ_BF16_SPLIT && cfg->projection != KVC_PROJ_F32_MFMA) return KVC_EINVAL;
+  if (cfg->projection == KVC_PROJ_F32_MFMA && cfg->x_format != KVC_X_F32) return KVC_EINVAL;
   return KVC_OK;
 }
 
@@ -101,9 +103,7 @@ int64_t pooled_floats(const kvc_config *cfg, int64_t batch, int64_t seqlen) {
 int64_t split_offset(const kvc_config *cfg, int64_t batch, int64_t seqlen) {
   return 2 * batch * seqlen * proj_of(cfg) + pooled_floats(cfg, batch, seqlen);
 }
-int64_t split_floats(const kvc_config *cfg) {
-  return cfg->x_format == KVC_X_BF16 && cfg->dim > 0 ? 3 * proj_of(cfg) * cfg->dim : 0;
-}
+int64_t split_floats(const kvc_config *cfg) { return cfg->dim > 0 ? 3 * proj_of(cfg) * cfg->dim : 0; }
 
 // The fused path (projection GEMM with pooling in its epilogue) needs 4-token
 // blocks aligned with the flattened rows and enough 256 x 256 tiles to fill
@@ -189,8 +189,9 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *
   const int64_t proj = proj_of(cfg);
   const int64_t m = batch * seqlen;
   const bool x_bf16 = cfg->x_format == KVC_X_BF16;
-  // with bf16 x the three-part weights sit after the planes and pooled rows
-  const int64_t need = (x && x_bf16 && m > 0) ? split_offset(cfg, batch, seqlen) + split_floats(cfg) : 2 * m * proj;
+  // with x the three-part weights sit after the planes and pooled rows
+  const bool split_proj = x && m > 0 && cfg->projection == KVC_PROJ_BF16_SPLIT;
+  const int64_t need = split_proj ? split_offset(cfg, batch, seqlen) + split_floats(cfg) : 2 * m * proj;
   if (need > 0 && !workspace) return KVC_EINVAL;
   if (workspace_floats < need) return KVC_ESPACE;
   if (!aligned(workspace)) return KVC_EINVAL;
@@ -233,7 +234,9 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *
       g.pool_groups = groups;
       g.pool_hd = cfg->head_dim;
     }
-    if (x_bf16) {
+    if (cfg->projection == KVC_PROJ_F32_MFMA) {
+      rc = hip_status(fused ? kvc::launch_gemm_pool(g, s) : kvc::launch_gemm(g, kvc::GemmShape::kPrefill, s));
+    } else {
       // the weights' three bf16 parts, in the row order the kernel reads
       uint16_t *split = reinterpret_cast<uint16_t *>(workspace + split_offset(cfg, batch, seqlen));
       kvc::SplitArgs sa{};
@@ -243,12 +246,12 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *
       sa.n_half = proj;
       sa.k = cfg->dim;
       sa.pool_hd = fused ? cfg->head_dim : 0;
+      sa.pool_tile = x_bf16 ? 256 : 128;  // the column tile of the kernel below
       sa.out = split;
       if ((rc = hip_status(kvc::launch_split_weights(sa, s)))) return rc;
       g.bsplit = split;
-      rc = hip_status(fused ? kvc::launch_gemm_x3_pool(g, s) : kvc::launch_gemm_x3(g, s));
-    } else {
-      rc = hip_status(fused ? kvc::launch_gemm_pool(g, s) : kvc::launch_gemm(g, kvc::GemmShape::kPrefill, s));
+      if (x_bf16) rc = hip_status(fused ? kvc::launch_gemm_x3_pool(g, s) : kvc::launch_gemm_x3(g, s));
+      else rc = hip_status(fused ? kvc::launch_gemm_x6_pool(g, s) : kvc::launch_gemm_x6(g, s));
     }
     if (rc) return rc;
   }

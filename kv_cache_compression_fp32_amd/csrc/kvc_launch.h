@@ -65,14 +65,21 @@ struct SplitArgs {
   const float *w0, *w1;  // [n_half][k] each, row stride ldw
   int64_t ldw, n_half, k;
   int32_t pool_hd;       // 0: plain order
+  int32_t pool_tile;     // pooling order: split rows per column tile (256 or 128)
   uint16_t *out;
 };
 hipError_t launch_split_weights(const SplitArgs &a, hipStream_t stream);
 // The prefill projection from a16 and bsplit (plain order), the bias as in
 // launch_gemm; n_half % 128 == 0, k % 32 == 0.
 hipError_t launch_gemm_x3(const GemmArgs &g, hipStream_t stream);
-// As launch_gemm_pool, from a16 and bsplit (pooling order).
+// As launch_gemm_pool, from a16 and bsplit (pooling order, 256-row tiles).
 hipError_t launch_gemm_x3_pool(const GemmArgs &g, hipStream_t stream);
+// f32 x (a) times the three-part weights (bsplit) on the bf16 matrix cores:
+// x split into three bf16 parts in registers, the six part products of
+// magnitude order >= 2^-16 summed in f32. n_half % 128 == 0, k % 32 == 0;
+// the pooling variant takes bsplit in pooling order with 128-row tiles.
+hipError_t launch_gemm_x6(const GemmArgs &g, hipStream_t stream);
+hipError_t launch_gemm_x6_pool(const GemmArgs &g, hipStream_t stream);
 
 // Ratio-1 projection: C[m][n] = sum_k A[m][k] * B[n][k], bf16 A and B, f32
 // accumulation and output, bf16 MFMA. Needs k % 64 == 0 and n % 128 == 0.

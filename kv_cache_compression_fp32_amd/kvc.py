@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libkvc.so")
 KVC_OK, KVC_EINVAL, KVC_EUNSUPPORTED, KVC_ESPACE, KVC_EHIP = 0, -1, -2, -3, -4
 KVC_FP4_E4M3_B16, KVC_FP4_E8M0_B32 = 0, 1
 KVC_X_F32, KVC_X_BF16 = 0, 1
+KVC_PROJ_BF16_SPLIT, KVC_PROJ_F32_MFMA = 0, 1
 
 _lib = None
 
@@ -36,7 +37,7 @@ class KvcError(RuntimeError):
 class _Config(ctypes.Structure):
     _fields_ = [("ratio", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("dim", ctypes.c_int64), ("eps", ctypes.c_float), ("fp4_format", ctypes.c_int32),
-                ("rope_dim", ctypes.c_int32), ("x_format", ctypes.c_int32)]
+                ("rope_dim", ctypes.c_int32), ("x_format", ctypes.c_int32), ("projection", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
@@ -108,6 +109,7 @@ class Config:
     fp4_format: int = KVC_FP4_E4M3_B16
     rope_dim: int = 0
     x_format: int = KVC_X_F32  # KVC_X_BF16: x is the bf16 hidden state
+    projection: int = KVC_PROJ_BF16_SPLIT  # KVC_PROJ_F32_MFMA: the f32 matrix cores
 
     @property
     def fp4_block(self) -> int:
@@ -115,7 +117,7 @@ class Config:
 
     def c(self) -> _Config:
         return _Config(self.ratio, self.head_dim, self.dim, self.eps, self.fp4_format, self.rope_dim,
-                       self.x_format)
+                       self.x_format, self.projection)
 
 
 def kvc_proj_width(cfg: Config) -> int:

@@ -49,14 +49,16 @@ def test_sizes(ratio, hd, proj, rows):
     cfg = kvc.Config(ratio, hd, 4096)
     assert kvc.kvc_proj_width(cfg) == proj
     assert kvc.kvc_state_rows(cfg) == rows
-    # the two projection planes, and at ratio 4 the pooled entries of the fused path
+    # the two projection planes, at ratio 4 the pooled entries of the fused
+    # path, then the weights' three bf16 parts, [2 proj][3][dim]
     pooled = 3 * (100 // ratio) * hd if ratio == 4 else 0
-    assert kvc.kvc_prefill_workspace_floats(cfg, 3, 100) == 2 * 3 * 100 * proj + pooled
+    parts = 2 * proj * 3 * 4096 // 2
+    assert kvc.kvc_prefill_workspace_floats(cfg, 3, 100) == 2 * 3 * 100 * proj + pooled + parts
     ws = kvc.kvc_decode_workspace_floats(cfg, 64)
     assert ws >= 2 * 64 * proj and ws % (2 * 64 * proj) == 0
-    # bf16 hidden states: the weights' three bf16 parts follow, [2 proj][3][dim]
+    # the same for bf16 hidden states
     cfg16 = kvc.Config(ratio, hd, 4096, x_format=kvc.KVC_X_BF16)
-    assert kvc.kvc_prefill_workspace_floats(cfg16, 3, 100) == 2 * 3 * 100 * proj + pooled + 2 * proj * 3 * 4096 // 2
+    assert kvc.kvc_prefill_workspace_floats(cfg16, 3, 100) == 2 * 3 * 100 * proj + pooled + parts
     assert kvc.kvc_decode_workspace_floats(cfg16, 64) == ws
 
 
@@ -76,6 +78,9 @@ def test_decode_workspace_of_the_b64_ratio4_step():
     (kvc.Config(4, 512, 4096, eps=-1.0), kvc.KVC_EINVAL),
     (kvc.Config(4, 512, 4096, eps=float("nan")), kvc.KVC_EINVAL),
     (kvc.Config(4, 512, 4096, x_format=2), kvc.KVC_EINVAL),
+    (kvc.Config(4, 512, 4096, projection=2), kvc.KVC_EINVAL),
+    # the f32 matrix cores read f32 rows only
+    (kvc.Config(4, 512, 4096, x_format=kvc.KVC_X_BF16, projection=kvc.KVC_PROJ_F32_MFMA), kvc.KVC_EINVAL),
 ])
 def test_invalid_configs(cfg, code):
     with pytest.raises(kvc.KvcError) as err:
@@ -120,20 +125,29 @@ def test_prefill_argument_errors_return_before_enqueueing():
     assert _prefill_raw(cfg, batch=2, ws=fake, ws_n=1 << 30, kv=fake, sc=fake, sb=1)[0] == kvc.KVC_EINVAL
 
 
-def test_bf16_x_needs_room_for_the_split_weights():
+@pytest.mark.parametrize("x_format", [kvc.KVC_X_F32, kvc.KVC_X_BF16])
+def test_projection_needs_room_for_the_split_weights(x_format):
     fake = 0x100000  # never dereferenced: every case below fails its host checks
     w = kvc._Weights(fake, fake, None, None)
-    cfg = kvc.Config(4, 512, 4096, x_format=kvc.KVC_X_BF16)
+    cfg = kvc.Config(4, 512, 4096, x_format=x_format)
     full = kvc.kvc_prefill_workspace_floats(cfg, 1, 8)
-    # the planes alone are enough for f32 x, not for bf16 x (the parts come after them)
-    planes = kvc.kvc_prefill_workspace_floats(kvc.Config(4, 512, 4096), 1, 8)
-    assert planes < full
+    planes = 2 * 8 * 1024 + 2 * 512   # the projection planes and the pooled rows
+    assert full == planes + 2 * 1024 * 3 * 4096 // 2
+    # with x the three-part weights must fit after them
     assert _prefill_raw(cfg, x=fake, w=w, ws=fake, ws_n=planes)[0] == kvc.KVC_ESPACE
     assert _prefill_raw(cfg, x=fake, w=w, ws=fake, ws_n=full - 1)[0] == kvc.KVC_ESPACE
     # without x only the planes are read
     assert _prefill_raw(cfg, ws=fake, ws_n=10)[0] == kvc.KVC_ESPACE
-    # bf16 x must still be 16-byte aligned
+    # x must be 16-byte aligned
     assert _prefill_raw(cfg, x=fake + 2, w=w, ws=fake, ws_n=full)[0] == kvc.KVC_EINVAL
+
+
+def test_f32_matrix_core_projection_needs_only_the_planes():
+    fake = 0x100000
+    w = kvc._Weights(fake, fake, None, None)
+    cfg = kvc.Config(4, 512, 4096, projection=kvc.KVC_PROJ_F32_MFMA)
+    planes = 2 * 8 * 1024
+    assert _prefill_raw(cfg, x=fake, w=w, ws=fake, ws_n=planes - 1)[0] == kvc.KVC_ESPACE
 
 
 def test_decode_argument_errors_return_before_enqueueing():

@@ -21,8 +21,8 @@ def _gpu():
     kvc.lib()
 
 
-def _cfg(wl, comp, x_format=kvc.KVC_X_F32):
-    return kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps, x_format=x_format)
+def _cfg(wl, comp, x_format=kvc.KVC_X_F32, projection=kvc.KVC_PROJ_BF16_SPLIT):
+    return kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps, x_format=x_format, projection=projection)
 
 
 def _sample_entries(groups, n=24, seed=0):
@@ -159,13 +159,14 @@ def test_decode_r4_b64_s512_equals_prefill():
                   ref["latent"][0], dec["dequant"][b])
 
 
-def test_prefill_r4_n65536_fp4_idx128_sampled():
+@pytest.mark.parametrize("projection", [kvc.KVC_PROJ_BF16_SPLIT, kvc.KVC_PROJ_F32_MFMA])
+def test_prefill_r4_n65536_fp4_idx128_sampled(projection):
     wl = W.WORKLOADS["prefill_r4_n65536_fp4_idx128"]
-    note(f"{wl.name}")
+    note(f"{wl.name} projection={projection}")
     xd = dev(W.hidden(wl))
     for comp in wl.compressors:
         w = W.weights(wl, comp)
-        cfg = _cfg(wl, comp)
+        cfg = _cfg(wl, comp, projection=projection)
         note(f"  compressor ratio={comp.ratio} hd={comp.head_dim} fp4={comp.quantize}")
         g = prefill(cfg, w, wl.batch, wl.seqlen, x_dev=xd, fp4=True)
         assert g["n_groups"] == 16384

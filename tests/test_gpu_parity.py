@@ -166,15 +166,23 @@ GEMM_CASES = [
     (4, 512, 4096, 1, 130),
     (4, 512, 64, 1, 16384 + 37),   # 256 x 256 tiles, ragged last row tile
     (4, 512, 64, 1, 4096 + 37),    # 256 x 128 tiles, ragged last row tile
+    (2, 128, 32, 2, 300),          # one 32-k stage
 ]
 
 
-@pytest.mark.parametrize("x_format", [kvc.KVC_X_F32, kvc.KVC_X_BF16])
+# (x format, projection): f32 rows split on the bf16 matrix cores (the
+# default), f32 rows on the f32 matrix cores, bf16 rows on the bf16 matrix cores
+PROJ_PATHS = [(kvc.KVC_X_F32, kvc.KVC_PROJ_BF16_SPLIT), (kvc.KVC_X_F32, kvc.KVC_PROJ_F32_MFMA),
+              (kvc.KVC_X_BF16, kvc.KVC_PROJ_BF16_SPLIT)]
+
+
+@pytest.mark.parametrize("x_format,projection", PROJ_PATHS)
 @pytest.mark.parametrize("ratio,hd,dim,batch,seqlen", GEMM_CASES)
-def test_projection_gemm_and_full_prefill(ratio, hd, dim, batch, seqlen, x_format):
-    note(f"gemm+prefill ratio={ratio} hd={hd} dim={dim} batch={batch} seqlen={seqlen} x_format={x_format}")
+def test_projection_gemm_and_full_prefill(ratio, hd, dim, batch, seqlen, x_format, projection):
+    note(f"gemm+prefill ratio={ratio} hd={hd} dim={dim} batch={batch} seqlen={seqlen} x_format={x_format} "
+         f"projection={projection}")
     rng = np.random.default_rng(dim + seqlen)
-    cfg = kvc.Config(ratio, hd, dim, x_format=x_format)
+    cfg = kvc.Config(ratio, hd, dim, x_format=x_format, projection=projection)
     proj = kvc.kvc_proj_width(cfg)
     x = rng.standard_normal((batch, seqlen, dim), dtype=np.float32)
     if x_format == kvc.KVC_X_BF16:  # the model's bf16 hidden state
@@ -510,15 +518,15 @@ FUSED_CASES = [
 ]
 
 
-@pytest.mark.parametrize("x_format", [kvc.KVC_X_F32, kvc.KVC_X_BF16])
+@pytest.mark.parametrize("x_format,projection", PROJ_PATHS)
 @pytest.mark.parametrize("hd,batch,seqlen,dim,opt", FUSED_CASES)
-def test_fused_pooling_equals_separate_kernels_bitwise(hd, batch, seqlen, dim, opt, x_format):
-    note(f"fused GEMM + pool hd={hd} batch={batch} seqlen={seqlen} {opt} x_format={x_format}")
+def test_fused_pooling_equals_separate_kernels_bitwise(hd, batch, seqlen, dim, opt, x_format, projection):
+    note(f"fused GEMM + pool hd={hd} batch={batch} seqlen={seqlen} {opt} x_format={x_format} projection={projection}")
     from gpu_util import weights
     rng = np.random.default_rng(hd + batch + seqlen)
     cfg = kvc.Config(4, hd, dim, rope_dim=64 if opt == "rope" else 0,
                      fp4_format=kvc.KVC_FP4_E8M0_B32 if opt == "e8m0" else kvc.KVC_FP4_E4M3_B16,
-                     x_format=x_format)
+                     x_format=x_format, projection=projection)
     proj = 2 * hd
     groups = seqlen // 4
     x = rng.standard_normal((batch, seqlen, dim), dtype=np.float32)
@@ -577,18 +585,20 @@ SPLIT_CASES = [
 ]
 
 
+@pytest.mark.parametrize("x_format", [kvc.KVC_X_BF16, kvc.KVC_X_F32])
 @pytest.mark.parametrize("ratio,hd,dim,batch,seqlen", SPLIT_CASES)
-def test_bf16_x_one_hot_rows_reproduce_the_f32_weights_exactly(ratio, hd, dim, batch, seqlen):
+def test_one_hot_rows_reproduce_the_f32_weights_exactly(ratio, hd, dim, batch, seqlen, x_format):
     """x row r = the unit vector e_(r mod dim): each output is then one f32
-    weight times 1, i.e. 1 * hi + 1 * mid + 1 * lo of its three bf16 parts,
-    which must give the weight back bit for bit (the score plane then adds
-    the positional bias in one f32 addition). Weights span the f32 exponent
-    range whose parts are all normal numbers, with zeros, the largest finite
-    value and values whose low parts have leading zeros."""
-    note(f"bf16 x one-hot ratio={ratio} hd={hd} dim={dim} batch={batch} seqlen={seqlen}")
+    weight times 1, i.e. 1 * hi + 1 * mid + 1 * lo of its three bf16 parts
+    (f32 x: 1 splits into 1 + 0 + 0), which must give the weight back bit
+    for bit (the score plane then adds the positional bias in one f32
+    addition). Weights span the f32 exponent range whose parts are all normal
+    numbers, with zeros, the largest finite value and values whose low parts
+    have leading zeros."""
+    note(f"one-hot x ratio={ratio} hd={hd} dim={dim} batch={batch} seqlen={seqlen} x_format={x_format}")
     from gpu_util import weights
     rng = np.random.default_rng(ratio + dim + seqlen)
-    cfg = kvc.Config(ratio, hd, dim, x_format=kvc.KVC_X_BF16)
+    cfg = kvc.Config(ratio, hd, dim, x_format=x_format)
     proj = kvc.kvc_proj_width(cfg)
     m = batch * seqlen
     x = np.zeros((m, dim), np.float32)
@@ -619,3 +629,38 @@ def test_bf16_x_one_hot_rows_reproduce_the_f32_weights_exactly(ratio, hd, dim, b
     want = w["wgate"].T[col] + w["ape"][pos % ratio]   # one f32 rounding, as on the GPU
     bad = sc.view(np.uint32) != want.view(np.uint32)
     assert not bad.any(), f"{bad.sum()} differ, e.g. {want[bad][:4]} -> {sc[bad][:4]}"
+
+
+@pytest.mark.parametrize("ratio,hd,dim,batch,seqlen", SPLIT_CASES)
+def test_f32_x_split_gives_faithfully_rounded_products(ratio, hd, dim, batch, seqlen):
+    """f32 x rows v_r e_(r mod dim) with bf16-valued weights (mid = lo = 0):
+    the kernel sums xh w, xm w and xl w, each product exact, where xh w + xm w
+    is still exact in f32 and only the last addition rounds. Every output
+    must therefore be one of the two f32 neighbours of the exact v_r w
+    (computed in float64). The matrix cores' addition is not always the
+    nearest one (a few percent of these outputs land on the other
+    neighbour), so nearest-even rounding is counted, not required."""
+    note(f"f32 x split ratio={ratio} hd={hd} dim={dim} batch={batch} seqlen={seqlen}")
+    from gpu_util import bf16_inputs, weights
+    rng = np.random.default_rng(7 + ratio + dim)
+    cfg = kvc.Config(ratio, hd, dim)
+    proj = kvc.kvc_proj_width(cfg)
+    m = batch * seqlen
+    v = (rng.standard_normal(m) * np.exp2(rng.integers(-30, 30, m))).astype(np.float32)
+    x = np.zeros((m, dim), np.float32)
+    x[np.arange(m), np.arange(m) % dim] = v
+    w = {"wkv": bf16_inputs(rng.standard_normal((proj, dim)).astype(np.float32)),
+         "wgate": bf16_inputs(rng.standard_normal((proj, dim)).astype(np.float32))}
+    ws = torch.full((kvc.kvc_prefill_workspace_floats(cfg, batch, seqlen),), float("nan"), device="cuda")
+    kvc.compressor_prefill(cfg, weights(w), dev(x.reshape(batch, seqlen, dim)), batch, seqlen, ws)
+    torch.cuda.synchronize()
+    col = np.arange(m) % dim
+    for plane, name in ((0, "wkv"), (1, "wgate")):
+        got = ws[plane * m * proj:(plane + 1) * m * proj].view(m, proj).cpu().numpy()
+        exact = v[:, None].astype(np.float64) * w[name].T[col].astype(np.float64)  # exact: 24 x 8 bits
+        lo = exact.astype(np.float32)                      # nearest; then its neighbour on the other side
+        other = np.where(lo.astype(np.float64) < exact, np.nextafter(lo, np.float32(np.inf)),
+                         np.nextafter(lo, np.float32(-np.inf)))
+        faithful = (got == lo) | (got == other) | ((exact == 0) & (got == 0))
+        assert faithful.all(), f"{name}: {(~faithful).sum()} not within one rounding of v w"
+        note(f"  {name}: {(got != lo).sum()} of {got.size} outputs on the farther neighbour")
