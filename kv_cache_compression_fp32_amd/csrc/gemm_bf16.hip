@@ -291,7 +291,7 @@ __device__ __forceinline__ void split8(const f4 lo4, const f4 hi4, bf16x8 &h, bf
       hb[u] = b & 0xffff0000u;
       const float r1 = v[2 * e + u] - __uint_as_float(hb[u]);
       mb[u] = __float_as_uint(r1) & 0xffff0000u;
-      lb[u] = __float_as_uint(r1 - __uint_as_float(mb[u])) & 0xffff0000u;
+      lb[u] = __float_as_uint(r1 - __uint_as_float(mb[u]));  // exact: its low 16 bits are zero
     }
     hw[e] = (hb[0] >> 16) | hb[1];
     mw[e] = (mb[0] >> 16) | mb[1];
@@ -371,14 +371,16 @@ __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
   const int row_in = lane & 15, slot = lane >> 4;
-  bf16x8 fa[3][FM], fb[3][FN];
+  // the read phase keeps x as f32 (8 values per row fragment); the multiply
+  // phase splits row fragment i + 1 while row fragment i's MFMAs run
+  f4 xf[FM][2];
+  bf16x8 fa[2][3], fb[3][FN];
   auto reads = [&](int st) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = wm * WM + 16 * i + row_in;
-      const f4 lo4 = *reinterpret_cast<const f4 *>(&As[st][r * BK + 4 * ((2 * slot) ^ (r & 7))]);
-      const f4 hi4 = *reinterpret_cast<const f4 *>(&As[st][r * BK + 4 * ((2 * slot + 1) ^ (r & 7))]);
-      split8(lo4, hi4, fa[0][i], fa[1][i], fa[2][i]);
+      xf[i][0] = *reinterpret_cast<const f4 *>(&As[st][r * BK + 4 * ((2 * slot) ^ (r & 7))]);
+      xf[i][1] = *reinterpret_cast<const f4 *>(&As[st][r * BK + 4 * ((2 * slot + 1) ^ (r & 7))]);
     }
 #pragma unroll
     for (int p = 0; p < 3; ++p)
@@ -388,20 +390,21 @@ __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
         fb[p][j] = *reinterpret_cast<const bf16x8 *>(&Bs[st][p][r * BK + 8 * (slot ^ ((r >> 1) & 3))]);
       }
   };
-  auto pair = [&](int xp, int wp) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[xp][i], fb[wp][j], acc[i][j], 0, 0, 0);
-  };
+  // per row fragment, the six part products in the order xh wh, xh wm,
+  // xm wh, xh wl, xm wm, xl wh (every output sums them in that order)
   auto mfmas = [&]() {
-    pair(0, 0);
-    pair(0, 1);
-    pair(1, 0);
-    pair(0, 2);
-    pair(1, 1);
-    pair(2, 0);
+    split8(xf[0][0], xf[0][1], fa[0][0], fa[0][1], fa[0][2]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int cur = i & 1;
+      if (i + 1 < FM) split8(xf[i + 1][0], xf[i + 1][1], fa[cur ^ 1][0], fa[cur ^ 1][1], fa[cur ^ 1][2]);
+      constexpr int XP[6] = {0, 0, 1, 0, 1, 2}, WP[6] = {0, 1, 0, 2, 1, 0};
+#pragma unroll
+      for (int q = 0; q < 6; ++q)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[cur][XP[q]], fb[WP[q]][j], acc[i][j], 0, 0, 0);
+    }
   };
 
   if (loader) {
