@@ -371,8 +371,9 @@ __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
   const int row_in = lane & 15, slot = lane >> 4;
-  // the read phase keeps x as f32 (8 values per row fragment); the multiply
-  // phase splits row fragment i + 1 while row fragment i's MFMAs run
+  // the read phase keeps x as f32 (8 values per row fragment) and splits row
+  // fragment 0; the multiply phase splits row fragment i + 1 while row
+  // fragment i's MFMAs run
   f4 xf[FM][2];
   bf16x8 fa[2][3], fb[3][FN];
   auto reads = [&](int st) {
@@ -389,11 +390,12 @@ __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
         const int r = wn * WN + 16 * j + row_in;
         fb[p][j] = *reinterpret_cast<const bf16x8 *>(&Bs[st][p][r * BK + 8 * (slot ^ ((r >> 1) & 3))]);
       }
+    // row fragment 0 split here, so the multiply phase opens with MFMAs
+    split8(xf[0][0], xf[0][1], fa[0][0], fa[0][1], fa[0][2]);
   };
   // per row fragment, the six part products in the order xh wh, xh wm,
   // xm wh, xh wl, xm wm, xl wh (every output sums them in that order)
   auto mfmas = [&]() {
-    split8(xf[0][0], xf[0][1], fa[0][0], fa[0][1], fa[0][2]);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int cur = i & 1;
