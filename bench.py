@@ -53,6 +53,8 @@ KERNEL_SOURCES = {
                 "kv_cache_compression_fp32_amd/csrc/kvc_device.h", "kv_cache_compression_fp32_amd/csrc/gemm_epilogue.h"],
     "gemm_x3": ["kv_cache_compression_fp32_amd/csrc/gemm_common.h", "kv_cache_compression_fp32_amd/csrc/gemm_bf16.hip",
                 "kv_cache_compression_fp32_amd/csrc/kvc_device.h", "kv_cache_compression_fp32_amd/csrc/gemm_epilogue.h"],
+    "gemm_h3": ["kv_cache_compression_fp32_amd/csrc/gemm_common.h", "kv_cache_compression_fp32_amd/csrc/gemm_bf16.hip",
+                "kv_cache_compression_fp32_amd/csrc/kvc_device.h", "kv_cache_compression_fp32_amd/csrc/gemm_epilogue.h"],
     "pool": ["kv_cache_compression_fp32_amd/csrc/pool.hip", "kv_cache_compression_fp32_amd/csrc/kvc_device.h"],
 }
 
@@ -144,18 +146,25 @@ def _timed(torch, stream, fn, reps):
 
 
 def gemm_roofline(kvc, g, x_format, projection):
-    """Roofline object of the 512-wide projection launch `g`: on the bf16
-    matrix cores its passes against the bf16 peak (with the f32-equivalent
+    """Roofline object of the 512-wide projection launch `g`: on the bf16 or
+    f16 matrix cores its passes against that peak (with the f32-equivalent
     rate beside it), on the f32 matrix cores its flops against the fp32 peak."""
     passes = mfma_passes(kvc, x_format, projection)
     if passes:
-        what = ("bf16 x times the three bf16 parts of the f32 weights" if passes == 3 else
-                "f32 x split into three bf16 parts times the three parts of the f32 weights, six part products")
+        if projection == kvc.KVC_PROJ_F16_SPLIT:
+            what = ("f32 x and f32 weights, rows scaled by powers of two and split into two f16 parts, three part "
+                    "products on the f16 matrix cores")
+            kernel, traffic = "gemm_x6_kernel<*, F16>", "gemm_h3"
+        elif passes == 3:
+            what = "bf16 x times the three bf16 parts of the f32 weights"
+            kernel, traffic = "gemm_mc_kernel", "gemm_x3"
+        else:
+            what = "f32 x split into three bf16 parts times the three parts of the f32 weights, six part products"
+            kernel, traffic = "gemm_x6_kernel", "gemm_x6"
         return {"bound": "mfma", "achieved": round(g["mfma_tflops"], 2), "peak": PEAK_BF16_MFMA_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(g["mfma_tflops"] / PEAK_BF16_MFMA_TFLOPS, 4),
-                "traffic": measured_traffic("gemm_x3" if passes == 3 else "gemm_x6"),
-                "kernel": f"{'gemm_mc_kernel' if passes == 3 else 'gemm_x6_kernel'} (512-wide projection, {what}, "
-                          "f32 accumulation)",
+                "traffic": measured_traffic(traffic),
+                "kernel": f"{kernel} (512-wide projection, {what}, f32 accumulation)",
                 "per_launch": g["mfma_flop"], "avg_ms": round(g["ms"], 4),
                 "f32_equivalent_tflops": round(g["tflops"], 2),
                 "f32_equivalent_frac_of_fp32_peak": round(g["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4)}
@@ -170,9 +179,12 @@ def _rounded(d):
 
 
 def mfma_passes(kvc, x_format, projection):
-    """bf16 matrix-core passes per f32 product (0: the f32 matrix cores)."""
+    """16-bit matrix-core passes per f32 product (bf16 or f16, both at the
+    same peak; 0: the f32 matrix cores)."""
     if projection == kvc.KVC_PROJ_F32_MFMA:
         return 0
+    if projection == kvc.KVC_PROJ_F16_SPLIT:
+        return 3
     return 3 if x_format == kvc.KVC_X_BF16 else 6
 
 
@@ -360,8 +372,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--x-format", choices=("f32", "bf16"), default="f32",
                     help="hidden states handed to the library: the f32 draws, or their bf16 rounding as bf16 rows")
-    ap.add_argument("--projection", choices=("split", "f32-mfma"), default="split",
-                    help="prefill projection on the bf16 matrix cores from exact bf16 parts, or on the f32 matrix cores")
+    ap.add_argument("--projection", choices=("split", "f32-mfma", "f16-split"), default="split",
+                    help="prefill projection on the bf16 matrix cores from exact bf16 parts, on the f32 matrix "
+                         "cores, or on the f16 matrix cores from scaled two-part f16 splits")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -394,7 +407,8 @@ def main():
         torch.cuda.empty_cache()
 
     x_format = kvc.KVC_X_BF16 if args.x_format == "bf16" else kvc.KVC_X_F32
-    projection = kvc.KVC_PROJ_F32_MFMA if args.projection == "f32-mfma" else kvc.KVC_PROJ_BF16_SPLIT
+    projection = {"split": kvc.KVC_PROJ_BF16_SPLIT, "f32-mfma": kvc.KVC_PROJ_F32_MFMA,
+                  "f16-split": kvc.KVC_PROJ_F16_SPLIT}[args.projection]
     head = run_prefill(wl, args.steps, args.warmup, args.kernel_reps, torch, kvc, W, x_format, projection)
     kernels = head["kernels"]
     main_tag = f"hd{wl.compressors[0].head_dim}"
@@ -411,8 +425,10 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "seqlen": wl.seqlen, "dim": wl.dim,
                    "x": ("bf16 rows: the bf16 rounding of the N(0,1) draws" if x_format == kvc.KVC_X_BF16
                          else "f32 rows, N(0,1)"),
-                   "projection": ("f32 matrix cores" if projection == kvc.KVC_PROJ_F32_MFMA else
-                                  "bf16 matrix cores on exact bf16 parts, f32 accumulation"),
+                   "projection": {kvc.KVC_PROJ_F32_MFMA: "f32 matrix cores",
+                                  kvc.KVC_PROJ_BF16_SPLIT: "bf16 matrix cores on exact bf16 parts, f32 accumulation",
+                                  kvc.KVC_PROJ_F16_SPLIT: "f16 matrix cores on row-scaled two-part f16 splits, "
+                                                          "f32 accumulation"}[projection],
                    "weights": "f32",
                    "compressors": [{"ratio": c.ratio, "head_dim": c.head_dim, "fp4": c.quantize}
                                    for c in wl.compressors],
@@ -429,6 +445,8 @@ def main():
                 ("f32_mfma", kvc.KVC_X_F32, kvc.KVC_PROJ_F32_MFMA, "f32 rows, N(0,1); f32 matrix cores"),
                 ("split", kvc.KVC_X_F32, kvc.KVC_PROJ_BF16_SPLIT,
                  "f32 rows, N(0,1); bf16 matrix cores on exact bf16 parts (six part products)"),
+                ("f16_split", kvc.KVC_X_F32, kvc.KVC_PROJ_F16_SPLIT,
+                 "f32 rows, N(0,1); f16 matrix cores on row-scaled two-part f16 splits (three part products)"),
                 ("x_bf16", kvc.KVC_X_BF16, kvc.KVC_PROJ_BF16_SPLIT,
                  "bf16 rows: the bf16 rounding of the N(0,1) draws, the model's hidden-state type; bf16 matrix "
                  "cores on the exact bf16 parts of the weights")):

@@ -70,6 +70,7 @@ typedef struct ihipStream_t *kvc_stream; /* a hipStream_t */
 /* matrix cores of the prefill projection (kvc_config.projection) */
 #define KVC_PROJ_BF16_SPLIT 0 /* bf16 matrix cores on exact bf16 parts (default; see x_format) */
 #define KVC_PROJ_F32_MFMA 1   /* f32 matrix cores (x_format KVC_X_F32 only) */
+#define KVC_PROJ_F16_SPLIT 2  /* f16 matrix cores on scaled two-part f16 splits (x_format KVC_X_F32 only) */
 
 /* fp4 forms of a compressed entry (kvc_config.fp4_format) */
 #define KVC_FP4_E4M3_B16 0 /* the KV latent's form: e4m3fn scale per block of 16 */
@@ -112,8 +113,17 @@ typedef struct ihipStream_t *kvc_stream; /* a hipStream_t */
  *                and the six part products of size >= 2^-16 |x w| are summed
  *                (the three left out total below 2^-21 |x w|, far inside the
  *                f32 summation's own error bound). KVC_PROJ_F32_MFMA: on the
- *                f32 matrix cores (x_format KVC_X_F32 only; KVC_EINVAL
- *                otherwise). Decode steps always use the f32 matrix cores.
+ *                f32 matrix cores. KVC_PROJ_F16_SPLIT: on the f16 matrix
+ *                cores with f32 accumulation; every row of x and every
+ *                weight row is scaled by the power of two that brings its
+ *                largest magnitude into [2^14, 2^15), each scaled value y is
+ *                split into h = f16(y) and l = f16(y - h) (y - h - l at most
+ *                2^-22 |y|, or 2^-40 of the row's largest magnitude where l
+ *                falls below the f16 normal range), the three part products
+ *                xh wh + xh wl + xl wh are summed (xl wl, left out, is at
+ *                most 2^-22 |x w|) and the sum is scaled back exactly. The
+ *                last two need x_format KVC_X_F32 (KVC_EINVAL otherwise).
+ *                Decode steps always use the f32 matrix cores.
  * proj = 2 * head_dim at ratio 4, head_dim otherwise: the width of each
  * projection plane. */
 typedef struct kvc_config {
@@ -180,9 +190,12 @@ int64_t kvc_state_rows(const kvc_config *cfg);
 /* f32 elements of the workspace compressor_prefill needs: the projection
  * planes, 2 * batch * seqlen * proj; at ratio 4 the f32 pooled entries,
  * batch * (seqlen / 4) * head_dim (used when the projection and the pooling
- * run as one kernel: a smaller workspace runs them separately); the weights'
- * three bf16 parts, 3 * proj * dim (bf16 [2 proj][3][dim]; read only by the
- * KVC_PROJ_BF16_SPLIT projection). Or a negative KVC_E* code. */
+ * run as one kernel: a smaller workspace runs them separately); the split
+ * weights: with KVC_PROJ_BF16_SPLIT (and KVC_PROJ_F32_MFMA, which does not
+ * read them) three bf16 parts, 3 * proj * dim (bf16 [2 proj][3][dim]); with
+ * KVC_PROJ_F16_SPLIT two f16 parts and the scale exponents of the weight rows
+ * and of x's rows, 2 * proj * dim + 2 * proj + batch * seqlen rounded up to a
+ * multiple of 4. Or a negative KVC_E* code. */
 int64_t kvc_prefill_workspace_floats(const kvc_config *cfg, int64_t batch, int64_t seqlen);
 
 /* f32 elements of the workspace compressor_decode_step needs (split

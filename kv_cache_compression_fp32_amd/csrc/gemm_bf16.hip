@@ -49,6 +49,8 @@
 // Buffer reuse: a stage buffer is reloaded one phase after group 4..7 read
 // it; that group waits for its own LDS reads before each barrier. Every
 // wavefront meets the same 2 k / (k per stage) + 2 barriers.
+#include <type_traits>
+
 #include "gemm_common.h"
 #include "gemm_epilogue.h"
 #include "kvc_launch.h"
@@ -68,11 +70,26 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm12() { asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); }
 
 constexpr int kBK3 = 32;  // k per LDS stage
 // the pooling kernel's wavefront: 128 rows x 64 columns, the 64 columns the
 // four 16-wide segments (kvA, kvB, scA, scB) of 16 features
 constexpr int kPoolWM = 128, kPoolWN = 64, kPoolF = kPoolWN / 4;
+
+// Source weight row of split row `row`. Pooling order: column tile
+// t = row / T (T = pool_tile rows) holds features T / 4 t .. +T / 4 - 1;
+// within it, [T / W wavefront columns][kvA, kvB, scA, scB][W / 4 features]
+// (W = pool_wn, the wavefront's columns).
+__device__ __forceinline__ const float *split_source_row(const SplitArgs &a, int64_t row) {
+  if (a.pool_hd) {
+    const int64_t T = a.pool_tile, W = a.pool_wn, F = W / 4;
+    const int64_t t = row / T, rem = row % T, wn = rem / W, seg = (rem % W) / F, c = rem % F;
+    const int64_t f = (T / 4) * t + F * wn + c;
+    return (seg < 2 ? a.w0 : a.w1) + ((seg & 1) * a.pool_hd + f) * a.ldw;
+  }
+  return row < a.n_half ? a.w0 + row * a.ldw : a.w1 + (row - a.n_half) * a.ldw;
+}
 
 // one thread per 8 consecutive k of one output row
 __global__ __launch_bounds__(256) void split_weights_kernel(SplitArgs a) {
@@ -81,19 +98,7 @@ __global__ __launch_bounds__(256) void split_weights_kernel(SplitArgs a) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
   const int64_t row = i / per_row, k0 = 8 * (i - row * per_row);
-  const float *src;
-  if (a.pool_hd) {
-    // pooling order: column tile t = row / T (T = pool_tile rows) holds
-    // features T / 4 t .. +T / 4 - 1; within it, [T / 64 wavefront
-    // columns][kvA, kvB, scA, scB][16 features]
-    const int64_t T = a.pool_tile;
-    const int64_t t = row / T, rem = row % T, wn = rem / (4 * kPoolF), seg = (rem % (4 * kPoolF)) / kPoolF,
-                  c = rem % kPoolF;
-    const int64_t f = (T / 4) * t + kPoolF * wn + c;
-    src = (seg < 2 ? a.w0 : a.w1) + ((seg & 1) * a.pool_hd + f) * a.ldw;
-  } else {
-    src = row < a.n_half ? a.w0 + row * a.ldw : a.w1 + (row - a.n_half) * a.ldw;
-  }
+  const float *src = split_source_row(a, row);
   const float4 v0 = *reinterpret_cast<const float4 *>(src + k0);
   const float4 v1 = *reinterpret_cast<const float4 *>(src + k0 + 4);
   const float w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -119,6 +124,84 @@ __global__ __launch_bounds__(256) void split_weights_kernel(SplitArgs a) {
   *reinterpret_cast<uint4 *>(dst) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
   *reinterpret_cast<uint4 *>(dst + a.k) = make_uint4(mid[0], mid[1], mid[2], mid[3]);
   *reinterpret_cast<uint4 *>(dst + 2 * a.k) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+}
+
+// f16 parts. A row (of x, or a weight row) is scaled by 2^e so that its
+// largest magnitude lies in [2^14, 2^15), inside the f16 range; a scaled
+// value y splits into h = f16(y) and l = f16(y - h), both rounded to nearest
+// even. y - h is exact in f32 (the bits of y below h's last place), so
+// |y - h - l| <= 2^-22 |y|, or at most 2^-25 (2^-40 of the row's largest
+// magnitude, unscaled) where l lies below the f16 normal range.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ int f16_row_exponent(float amax) {
+  if (!(amax > 0.0f) || !(amax < INFINITY)) return 0;  // zeros, infinities
+  return 15 - __builtin_amdgcn_frexp_expf(amax);         // amax in [2^(E-1), 2^E)
+}
+
+__device__ __forceinline__ void split_f16(float v, int e, _Float16 &h, _Float16 &l) {
+  const float y = __builtin_amdgcn_ldexpf(v, e);
+  h = (_Float16)y;
+  l = (_Float16)(y - (float)h);
+}
+
+__device__ __forceinline__ float block_max_256(float v) {
+  __shared__ float part[4];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+}
+
+// one workgroup of 256 per split row: the row's largest magnitude, then the
+// two f16 parts of the scaled row (h at out + 2 k row, l at + k)
+__global__ __launch_bounds__(256) void split_weights_f16_kernel(SplitArgs a) {
+  const int64_t row = blockIdx.x;
+  const float *src = split_source_row(a, row);
+  float amax = 0.0f;
+  for (int64_t k0 = 8 * (int64_t)threadIdx.x; k0 < a.k; k0 += 8 * 256) {
+    const float4 v0 = *reinterpret_cast<const float4 *>(src + k0);
+    const float4 v1 = *reinterpret_cast<const float4 *>(src + k0 + 4);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))));
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
+  }
+  const int e = f16_row_exponent(block_max_256(amax));
+  if (threadIdx.x == 0) a.exp_out[row] = e;
+  uint16_t *dst = a.out + row * 2 * a.k;
+  for (int64_t k0 = 8 * (int64_t)threadIdx.x; k0 < a.k; k0 += 8 * 256) {
+    const float4 v0 = *reinterpret_cast<const float4 *>(src + k0);
+    const float4 v1 = *reinterpret_cast<const float4 *>(src + k0 + 4);
+    const float w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    f16x8 h, l;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      _Float16 hu, lu;
+      split_f16(w[u], e, hu, lu);
+      h[u] = hu;
+      l[u] = lu;
+    }
+    *reinterpret_cast<f16x8 *>(dst + k0) = h;
+    *reinterpret_cast<f16x8 *>(dst + a.k + k0) = l;
+  }
+}
+
+// one wavefront per row of x: the scale exponent of the row
+__global__ __launch_bounds__(256) void row_exponents_kernel(const float *x, int64_t m, int64_t k, int64_t lda,
+                                                            int32_t *out) {
+  const int64_t row = 4 * (int64_t)blockIdx.x + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= m) return;
+  const float *p = x + row * lda;
+  float amax = 0.0f;
+#pragma unroll 4
+  for (int64_t c = 4 * lane; c < k; c += 256) {
+    const float4 v = *reinterpret_cast<const float4 *>(p + c);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if (lane == 0) out[row] = f16_row_exponent(amax);
 }
 
 // SPLIT3: a stage is one 32-k slice of x times the three parts of the split
@@ -304,19 +387,63 @@ __device__ __forceinline__ void split8(const f4 lo4, const f4 hi4, bf16x8 &h, bf
   l = __builtin_bit_cast(bf16x8, lv);
 }
 
-template <bool POOL>
+// F16: the same kernel on the f16 matrix cores (v_mfma_f32_16x16x32_f16)
+// with the two-part f16 weights: the read phase takes the scale exponent of
+// each row fragment's x row (g.xexp), the split gives xh, xl (split_f16),
+// and the multiply phase sums xh wh, xh wl, xl wh (the left-out xl wl is at
+// most 2^-22 |x w| of the scaled values); the epilogue scales every sum back
+// by 2^-(xexp + wexp), exactly, before the bias and the pooling.
+// y - h for h one half of a packed f16 pair: one fused multiply-add with the
+// f16 operand taken as is (-h * 1 + y, exact), in place of converting h back
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float residual_lo(uint32_t hpair, float y) {
+  float r;
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hpair), "v"(y));
+  return r;
+}
+__device__ __forceinline__ float residual_hi(uint32_t hpair, float y) {
+  float r;
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hpair), "v"(y));
+  return r;
+}
+
+__device__ __forceinline__ void split8_f16(const f4 lo4, const f4 hi4, int e, f16x8 &h, f16x8 &l) {
+  const float v[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float y0 = __builtin_amdgcn_ldexpf(v[2 * u], e), y1 = __builtin_amdgcn_ldexpf(v[2 * u + 1], e);
+    hw[u] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{y0, y1}), f16x2));
+    const float r0 = residual_lo(hw[u], y0), r1 = residual_hi(hw[u], y1);
+    lw[u] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{r0, r1}), f16x2));
+  }
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  h = __builtin_bit_cast(f16x8, (u4{hw[0], hw[1], hw[2], hw[3]}));
+  l = __builtin_bit_cast(f16x8, (u4{lw[0], lw[1], lw[2], lw[3]}));
+}
+
+template <bool POOL, bool F16, int BN = 128, int WN = 64>
 __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
-  constexpr int BM = 256, BN = 128, WM = 64, WN = 64, BK = kBK3;
+  constexpr int BM = 256, WM = 64, BK = kBK3;
   constexpr int WAVES_N = BN / WN;  // 2
+  static_assert(WAVES_N == 2 && (BN == 128 || (F16 && BN == 256)), "tile");
   constexpr int FM = WM / 16, FN = WN / 16;
   constexpr int BRB = BN / 16;
   constexpr int NL = 4;
-  constexpr int A_INS = BM / 8 / NL, B_INS = 3 * BRB / NL;  // x: 8 rows of 32 floats per load
-  constexpr int STAGE_FLOATS = 2 * (BM * BK + 3 * BN * BK / 2);
+  constexpr int NP = F16 ? 2 : 3;                   // weight parts
+  constexpr int A_INS = BM / 8 / NL, B_INS = NP * BRB / NL;  // x: 8 rows of 32 floats per load
+  // F16 with 128-column tiles: three LDS stages (the loads of a stage are
+  // issued two stages ahead)
+  constexpr int NS = F16 && BN == 128 ? 3 : 2;
+  constexpr bool kReadSplit = F16 && BN == 128;
+  constexpr int STAGE_FLOATS = NS * (BM * BK + NP * BN * BK / 2);
   constexpr int SMEM_FLOATS = POOL && kPoolXFloats > STAGE_FLOATS ? kPoolXFloats : STAGE_FLOATS;
+  static_assert(SMEM_FLOATS * 4 <= 160 * 1024, "LDS");
+  typedef typename std::conditional<F16, f16x8, bf16x8>::type v8;
   __shared__ __attribute__((aligned(16))) float smem[SMEM_FLOATS];
   float(*As)[BM * BK] = reinterpret_cast<float(*)[BM * BK]>(smem);
-  uint16_t(*Bs)[3][BN * BK] = reinterpret_cast<uint16_t(*)[3][BN * BK]>(smem + 2 * BM * BK);
+  uint16_t(*Bs)[NP][BN * BK] = reinterpret_cast<uint16_t(*)[NP][BN * BK]>(smem + NS * BM * BK);
 
   const int64_t m_tiles = (g.m + BM - 1) / BM;
   const int64_t n_tiles = 2 * g.n_half / BN;  // with POOL: pool_hd / 32 tiles of 128 permuted rows
@@ -336,11 +463,11 @@ __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
 
   // x: load u of a loading wavefront fills rows 8 (lw A_INS + u) .. +7,
   // lane l -> row l / 8, group position l % 8 holding k-group
-  // (l % 8) ^ ((l / 8) & 7); weights as gemm_mc_kernel (rows of 3 k).
-  const int64_t RS = 3 * g.k;
+  // (l % 8) ^ ((l / 8) & 7); weights as gemm_mc_kernel (rows of NP k).
+  const int64_t RS = NP * g.k;
   const int64_t a_rows = (g.m - m0 < BM) ? (g.m - m0) : BM;
-  const i32x4 a_rsrc = make_rsrc(g.a + m0 * g.lda, (uint32_t)(a_rows * g.lda * 4));
-  const i32x4 b_rsrc = make_rsrc(g.bsplit + n_glob * RS, (uint32_t)(BN * RS * 2));
+  const i32x4 a_rsrc = uniform_rsrc(make_rsrc(g.a + m0 * g.lda, (uint32_t)(a_rows * g.lda * 4)));
+  const i32x4 b_rsrc = uniform_rsrc(make_rsrc(g.bsplit + n_glob * RS, (uint32_t)(BN * RS * 2)));
   const int xr = lane >> 3, xq = (lane & 7) ^ (xr & 7);
   uint32_t a_voff[A_INS];
 #pragma unroll
@@ -371,11 +498,28 @@ __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
   const int row_in = lane & 15, slot = lane >> 4;
+  // F16: the scale exponent of the x row each row fragment reads
+  int xe[FM];
+  if constexpr (F16) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      int64_t r = wm * WM + 16 * i + row_in;
+      if (r >= a_rows) r = a_rows - 1;
+      xe[i] = g.xexp[m0 + r];
+    }
+  }
   // the read phase keeps x as f32 (8 values per row fragment) and splits row
   // fragment 0; the multiply phase splits row fragment i + 1 while row
   // fragment i's MFMAs run
+  // F16: the two parts of every row fragment take the registers of its f32
+  // values, so the read phase splits them all and the multiply phase is
+  // matrix-core work only (its vector work overlaps the other group's MFMAs)
   f4 xf[FM][2];
-  bf16x8 fa[2][3], fb[3][FN];
+  v8 fa[2][NP], fb[NP][FN], fx[kReadSplit ? FM : 1][2];
+  auto split = [&](int i, v8 (&parts)[NP]) {
+    if constexpr (F16) split8_f16(xf[i][0], xf[i][1], xe[i], parts[0], parts[1]);
+    else split8(xf[i][0], xf[i][1], parts[0], parts[1], parts[2]);
+  };
   auto reads = [&](int st) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -384,51 +528,103 @@ __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
       xf[i][1] = *reinterpret_cast<const f4 *>(&As[st][r * BK + 4 * ((2 * slot + 1) ^ (r & 7))]);
     }
 #pragma unroll
-    for (int p = 0; p < 3; ++p)
+    for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int r = wn * WN + 16 * j + row_in;
-        fb[p][j] = *reinterpret_cast<const bf16x8 *>(&Bs[st][p][r * BK + 8 * (slot ^ ((r >> 1) & 3))]);
+        fb[p][j] = *reinterpret_cast<const v8 *>(&Bs[st][p][r * BK + 8 * (slot ^ ((r >> 1) & 3))]);
       }
-    // row fragment 0 split here, so the multiply phase opens with MFMAs
-    split8(xf[0][0], xf[0][1], fa[0][0], fa[0][1], fa[0][2]);
+    if constexpr (kReadSplit) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) split8_f16(xf[i][0], xf[i][1], xe[i], fx[i][0], fx[i][1]);
+    } else {
+      // row fragment 0 split here, so the multiply phase opens with MFMAs
+      split(0, fa[0]);
+    }
   };
-  // per row fragment, the six part products in the order xh wh, xh wm,
-  // xm wh, xh wl, xm wm, xl wh (every output sums them in that order)
+  // per row fragment, the part products in the order xh wh, xh wm, xm wh,
+  // xh wl, xm wm, xl wh (F16: xh wh, xh wl, xl wh); every output sums them in
+  // that order
   auto mfmas = [&]() {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int cur = i & 1;
-      if (i + 1 < FM) split8(xf[i + 1][0], xf[i + 1][1], fa[cur ^ 1][0], fa[cur ^ 1][1], fa[cur ^ 1][2]);
-      constexpr int XP[6] = {0, 0, 1, 0, 1, 2}, WP[6] = {0, 1, 0, 2, 1, 0};
+      if constexpr (kReadSplit) {
+        constexpr int XP[3] = {0, 0, 1}, WP[3] = {0, 1, 0};
 #pragma unroll
-      for (int q = 0; q < 6; ++q)
+        for (int q = 0; q < 3; ++q)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[cur][XP[q]], fb[WP[q]][j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fx[i][XP[q]], fb[WP[q]][j], acc[i][j], 0, 0, 0);
+      } else if constexpr (F16) {
+        if (i + 1 < FM) split(i + 1, fa[cur ^ 1]);
+        constexpr int XP[3] = {0, 0, 1}, WP[3] = {0, 1, 0};
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[cur][XP[q]], fb[WP[q]][j], acc[i][j], 0, 0, 0);
+      } else {
+        if (i + 1 < FM) split(i + 1, fa[cur ^ 1]);
+        constexpr int XP[6] = {0, 0, 1, 0, 1, 2}, WP[6] = {0, 1, 0, 2, 1, 0};
+#pragma unroll
+        for (int q = 0; q < 6; ++q)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[cur][XP[q]], fb[WP[q]][j], acc[i][j], 0, 0, 0);
+      }
     }
   };
 
+  // F16: a loading wavefront has A_INS + B_INS loads per stage in flight
+  static_assert(NS == 2 || A_INS + B_INS == 12, "wait count");
   if (loader) {
     issue(0, 0);
-    wait_vm0();
+    if (NS == 3 && kt_count > 1) {
+      issue(1, 1);
+      wait_vm12();
+    } else {
+      wait_vm0();
+    }
   }
   phase_barrier();
   if (!loader) phase_barrier();  // group 4..7 runs one phase behind
   for (int kt = 0; kt < kt_count; ++kt) {
-    const int st = kt & 1;
+    const int st = kt % NS;
     reads(st);
-    if (loader && kt + 1 < kt_count) issue(kt + 1, st ^ 1);  // after the stage's last LDS read
+    // after the stage's last LDS read: the stage NS - 1 ahead, into the
+    // buffer both groups finished reading in the previous two phases
+    if (loader && kt + NS - 1 < kt_count) issue(kt + NS - 1, (kt + NS - 1) % NS);
     wait_lgkm0();
     phase_barrier();
     mfmas();
-    if (loader) wait_vm0();
+    if (loader) {
+      // stage kt + 1 complete (NS = 3: the loads of stage kt + 2 may remain)
+      if (NS == 3 && kt + 2 < kt_count) wait_vm12();
+      else wait_vm0();
+    }
     phase_barrier();
   }
   if (loader) phase_barrier();  // the same number of barriers for every wavefront
 
+  if constexpr (F16) {
+    // back from the scaled rows: output (row, column) times 2^-(xexp + wexp)
+    int we[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) we[j] = g.wexp[n_glob + wn * WN + 16 * j + row_in];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int64_t rr = wm * WM + 16 * i + 4 * slot + r;
+        if (rr >= a_rows) rr = a_rows - 1;
+        const int e = g.xexp[m0 + rr];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j][r] = __builtin_amdgcn_ldexpf(acc[i][j][r], -(e + we[j]));
+      }
+  }
   if constexpr (POOL) {
-    pool_epilogue<WM, WN>(g, acc, smem, m0, 32 * nt, wm, wn, lane);
+    pool_epilogue<WM, WN>(g, acc, smem, m0, (BN / 4) * nt, wm, wn, lane);
   } else {
     store_tile<FM, FN>(g, acc, second ? g.c1 : g.c0, second ? g.bias1 : nullptr, m0 + wm * WM, n0 + wn * WN,
                        lane);
@@ -456,8 +652,14 @@ bool addressable(const GemmArgs &g, int64_t k_per_stage, int64_t row_elems) {
 hipError_t launch_split_weights(const SplitArgs &a, hipStream_t stream) {
   if (a.n_half <= 0 || a.k <= 0) return hipSuccess;
   if (a.k % 8 != 0 || a.ldw < a.k || (a.pool_hd && 2 * a.n_half != 4 * (int64_t)a.pool_hd) ||
-      (a.pool_hd && (a.pool_tile != 256 && a.pool_tile != 128)) || (a.pool_hd && a.pool_hd % (a.pool_tile / 4) != 0))
+      (a.pool_hd && (a.pool_tile != 256 && a.pool_tile != 128)) || (a.pool_hd && a.pool_hd % (a.pool_tile / 4) != 0) ||
+      (a.pool_hd && (a.pool_wn != 64 && a.pool_wn != 128)) || (a.pool_hd && a.pool_tile % a.pool_wn != 0))
     return hipErrorInvalidValue;
+  if (a.f16) {
+    if (!a.exp_out) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gemm::split_weights_f16_kernel, dim3((uint32_t)(2 * a.n_half)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   const int64_t total = 2 * a.n_half * (a.k / 8);
   hipLaunchKernelGGL(gemm::split_weights_kernel, dim3((uint32_t)((total + 255) / 256)), dim3(256), 0, stream, a);
   return hipGetLastError();
@@ -513,27 +715,47 @@ hipError_t launch_gemm_bf16(const GemmBf16Args &a, hipStream_t stream) {
 
 namespace kvc {
 
-hipError_t launch_gemm_x6(const GemmArgs &g, hipStream_t stream) {
+namespace {
+// shapes of the f32-x kernels (plain: n_half % 128 == 0; pooling: 32-feature
+// column tiles, 4-token blocks aligned with the flattened rows)
+bool x6_shape_ok(const GemmArgs &g, int parts, bool pool, int bn) {
+  if (g.lda < g.k || g.k % gemm::kBK3 != 0 || (int64_t)256 * g.lda * 4 > INT32_MAX ||
+      (int64_t)bn * parts * g.k * 2 > INT32_MAX)
+    return false;
+  if (pool)
+    return g.pool_hd % (bn / 4) == 0 && g.n_half == 2 * (int64_t)g.pool_hd && g.ldc == 2 * g.pool_hd &&
+           g.m == g.pool_batch * g.pool_seqlen && (g.pool_batch == 1 || g.pool_seqlen % 4 == 0) && g.pooled;
+  return g.n_half % bn == 0 &&
+         (!g.bias1 || (g.bias_seqlen >= 1 && g.bias_ratio >= 1 && (g.bias_ratio & (g.bias_ratio - 1)) == 0));
+}
+
+template <bool POOL, bool F16, int BN = 128, int WN = 64>
+hipError_t launch_x6(const GemmArgs &g, hipStream_t stream) {
   if (g.m <= 0) return hipSuccess;
-  if (g.n_half % 128 != 0 || g.lda < g.k || g.k % gemm::kBK3 != 0 || (int64_t)256 * g.lda * 4 > INT32_MAX ||
-      (int64_t)128 * 3 * g.k * 2 > INT32_MAX ||
-      (g.bias1 && (g.bias_seqlen < 1 || g.bias_ratio < 1 || (g.bias_ratio & (g.bias_ratio - 1)) != 0)))
-    return hipErrorInvalidValue;
+  if (!x6_shape_ok(g, F16 ? 2 : 3, POOL, BN) || (F16 && (!g.xexp || !g.wexp))) return hipErrorInvalidValue;
   const int64_t m_tiles = (g.m + 255) / 256;
-  hipLaunchKernelGGL(gemm::gemm_x6_kernel<false>, dim3((uint32_t)(m_tiles * (2 * g.n_half / 128))), dim3(512), 0,
+  const int64_t n_tiles = POOL ? g.pool_hd / (BN / 4) : 2 * g.n_half / BN;
+  hipLaunchKernelGGL((gemm::gemm_x6_kernel<POOL, F16, BN, WN>), dim3((uint32_t)(m_tiles * n_tiles)), dim3(512), 0,
                      stream, g);
   return hipGetLastError();
 }
+}  // namespace
 
-hipError_t launch_gemm_x6_pool(const GemmArgs &g, hipStream_t stream) {
-  if (g.m <= 0) return hipSuccess;
-  if (g.pool_hd % 32 != 0 || g.n_half != 2 * (int64_t)g.pool_hd || g.ldc != 2 * g.pool_hd || g.lda < g.k ||
-      g.k % gemm::kBK3 != 0 || (int64_t)256 * g.lda * 4 > INT32_MAX || (int64_t)128 * 3 * g.k * 2 > INT32_MAX ||
-      g.m != g.pool_batch * g.pool_seqlen || (g.pool_batch > 1 && g.pool_seqlen % 4 != 0) || !g.pooled)
-    return hipErrorInvalidValue;
-  const int64_t m_tiles = (g.m + 255) / 256;
-  hipLaunchKernelGGL(gemm::gemm_x6_kernel<true>, dim3((uint32_t)(m_tiles * (g.pool_hd / 32))), dim3(512), 0, stream,
-                     g);
+hipError_t launch_gemm_x6(const GemmArgs &g, hipStream_t stream) { return launch_x6<false, false>(g, stream); }
+hipError_t launch_gemm_x6_pool(const GemmArgs &g, hipStream_t stream) { return launch_x6<true, false>(g, stream); }
+// f16 parts: 256 x 256 tiles of 64 x 128 wavefronts where the columns allow
+hipError_t launch_gemm_h3(const GemmArgs &g, hipStream_t stream) {
+  if (g.n_half % 256 == 0) return launch_x6<false, true, 256, 128>(g, stream);
+  return launch_x6<false, true>(g, stream);
+}
+hipError_t launch_gemm_h3_pool(const GemmArgs &g, hipStream_t stream) { return launch_x6<true, true, 256, 128>(g, stream); }
+
+hipError_t launch_row_exponents(const float *x, int64_t m, int64_t k, int64_t lda, int32_t *out,
+                                hipStream_t stream) {
+  if (m <= 0) return hipSuccess;
+  if (k <= 0 || k % 4 != 0 || lda < k || lda % 4 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemm::row_exponents_kernel, dim3((uint32_t)((m + 3) / 4)), dim3(256), 0, stream, x, m, k, lda,
+                     out);
   return hipGetLastError();
 }
 

@@ -33,6 +33,14 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_bytes)
   return r;
 }
 
+// The same descriptor, marked wavefront-uniform for the compiler (a buffer
+// instruction takes its descriptor from scalar registers; without the mark a
+// descriptor the compiler keeps in vector registers costs a loop per load).
+__device__ __forceinline__ i32x4 uniform_rsrc(i32x4 r) {
+  return i32x4{__builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y),
+               __builtin_amdgcn_readfirstlane(r.z), __builtin_amdgcn_readfirstlane(r.w)};
+}
+
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace gemm

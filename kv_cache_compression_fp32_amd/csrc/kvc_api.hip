@@ -25,8 +25,10 @@ int check_common(const kvc_config *cfg) {
   if (cfg->head_dim != 128 && cfg->head_dim != 512) return KVC_EUNSUPPORTED;
   if (cfg->rope_dim < 0 || cfg->rope_dim > cfg->head_dim || cfg->rope_dim % 2 != 0) return KVC_EINVAL;
   if (cfg->x_format != KVC_X_F32 && cfg->x_format != KVC_X_BF16) return KVC_EINVAL;
-  if (cfg->projection != KVC_PROJ_BF16_SPLIT && cfg->projection != KVC_PROJ_F32_MFMA) return KVC_EINVAL;
-  if (cfg->projection == KVC_PROJ_F32_MFMA && cfg->x_format != KVC_X_F32) return KVC_EINVAL;
+  if (cfg->projection != KVC_PROJ_BF16_SPLIT && cfg->projection != KVC_PROJ_F32_MFMA &&
+      cfg->projection != KVC_PROJ_F16_SPLIT)
+    return KVC_EINVAL;
+  if (cfg->projection != KVC_PROJ_BF16_SPLIT && cfg->x_format != KVC_X_F32) return KVC_EINVAL;
   return KVC_OK;
 }
 
@@ -95,15 +97,22 @@ int32_t decode_splits(const kvc_config *cfg, int64_t batch) {
 int hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_EHIP; }
 
 // Prefill workspace: the kv and score planes, then (ratio 4) the f32 pooled
-// entries of the fused projection + pooling path, then (bf16 x) the
-// three-part weights, bf16 [2 proj][3][dim].
+// entries of the fused projection + pooling path, then the split weights:
+// bf16 [2 proj][3][dim] (KVC_PROJ_BF16_SPLIT), or f16 [2 proj][2][dim]
+// followed by the int32 scale exponents of the 2 proj weight rows and of the
+// batch * seqlen rows of x (KVC_PROJ_F16_SPLIT; each part 16-byte aligned).
 int64_t pooled_floats(const kvc_config *cfg, int64_t batch, int64_t seqlen) {
   return overlapped(cfg) ? batch * (seqlen / cfg->ratio) * cfg->head_dim : 0;
 }
 int64_t split_offset(const kvc_config *cfg, int64_t batch, int64_t seqlen) {
   return 2 * batch * seqlen * proj_of(cfg) + pooled_floats(cfg, batch, seqlen);
 }
-int64_t split_floats(const kvc_config *cfg) { return cfg->dim > 0 ? 3 * proj_of(cfg) * cfg->dim : 0; }
+int64_t round4(int64_t v) { return (v + 3) / 4 * 4; }
+int64_t split_floats(const kvc_config *cfg, int64_t m) {
+  if (cfg->dim <= 0) return 0;
+  if (cfg->projection == KVC_PROJ_F16_SPLIT) return 2 * proj_of(cfg) * cfg->dim + 2 * proj_of(cfg) + round4(m);
+  return 3 * proj_of(cfg) * cfg->dim;
+}
 
 // The fused path (projection GEMM with pooling in its epilogue) needs 4-token
 // blocks aligned with the flattened rows and enough 256 x 256 tiles to fill
@@ -163,7 +172,7 @@ int64_t kvc_prefill_workspace_floats(const kvc_config *cfg, int64_t batch, int64
   const int rc = check_config(cfg);
   if (rc) return rc;
   if (batch < 1 || seqlen < 0) return KVC_EINVAL;
-  return split_offset(cfg, batch, seqlen) + split_floats(cfg);
+  return split_offset(cfg, batch, seqlen) + split_floats(cfg, batch * seqlen);
 }
 
 int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch) {
@@ -189,9 +198,9 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *
   const int64_t proj = proj_of(cfg);
   const int64_t m = batch * seqlen;
   const bool x_bf16 = cfg->x_format == KVC_X_BF16;
-  // with x the three-part weights sit after the planes and pooled rows
-  const bool split_proj = x && m > 0 && cfg->projection == KVC_PROJ_BF16_SPLIT;
-  const int64_t need = split_proj ? split_offset(cfg, batch, seqlen) + split_floats(cfg) : 2 * m * proj;
+  // with x the split weights sit after the planes and pooled rows
+  const bool split_proj = x && m > 0 && cfg->projection != KVC_PROJ_F32_MFMA;
+  const int64_t need = split_proj ? split_offset(cfg, batch, seqlen) + split_floats(cfg, m) : 2 * m * proj;
   if (need > 0 && !workspace) return KVC_EINVAL;
   if (workspace_floats < need) return KVC_ESPACE;
   if (!aligned(workspace)) return KVC_EINVAL;
@@ -237,8 +246,12 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *
     if (cfg->projection == KVC_PROJ_F32_MFMA) {
       rc = hip_status(fused ? kvc::launch_gemm_pool(g, s) : kvc::launch_gemm(g, kvc::GemmShape::kPrefill, s));
     } else {
-      // the weights' three bf16 parts, in the row order the kernel reads
-      uint16_t *split = reinterpret_cast<uint16_t *>(workspace + split_offset(cfg, batch, seqlen));
+      // the weights' parts, in the row order the kernel reads
+      const bool f16 = cfg->projection == KVC_PROJ_F16_SPLIT;
+      float *split_base = workspace + split_offset(cfg, batch, seqlen);
+      uint16_t *split = reinterpret_cast<uint16_t *>(split_base);
+      int32_t *wexp = reinterpret_cast<int32_t *>(split_base + 2 * proj * cfg->dim);
+      int32_t *xexp = wexp + 2 * proj;
       kvc::SplitArgs sa{};
       sa.w0 = w->wkv;
       sa.w1 = w->wgate;
@@ -246,11 +259,20 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *
       sa.n_half = proj;
       sa.k = cfg->dim;
       sa.pool_hd = fused ? cfg->head_dim : 0;
-      sa.pool_tile = x_bf16 ? 256 : 128;  // the column tile of the kernel below
+      // the column tile and wavefront columns of the kernel below
+      sa.pool_tile = x_bf16 || f16 ? 256 : 128;
+      sa.pool_wn = f16 ? 128 : 64;
       sa.out = split;
+      sa.f16 = f16;
+      sa.exp_out = f16 ? wexp : nullptr;
       if ((rc = hip_status(kvc::launch_split_weights(sa, s)))) return rc;
       g.bsplit = split;
-      if (x_bf16) rc = hip_status(fused ? kvc::launch_gemm_x3_pool(g, s) : kvc::launch_gemm_x3(g, s));
+      if (f16) {
+        g.wexp = wexp;
+        g.xexp = xexp;
+        if ((rc = hip_status(kvc::launch_row_exponents(g.a, m, cfg->dim, cfg->dim, xexp, s)))) return rc;
+        rc = hip_status(fused ? kvc::launch_gemm_h3_pool(g, s) : kvc::launch_gemm_h3(g, s));
+      } else if (x_bf16) rc = hip_status(fused ? kvc::launch_gemm_x3_pool(g, s) : kvc::launch_gemm_x3(g, s));
       else rc = hip_status(fused ? kvc::launch_gemm_x6_pool(g, s) : kvc::launch_gemm_x6(g, s));
     }
     if (rc) return rc;

@@ -41,6 +41,10 @@ struct GemmArgs {
   const uint16_t *a16;
   // three-part weights of launch_gemm_x3* (launch_split_weights' output)
   const uint16_t *bsplit;
+  // f16 parts (launch_gemm_h3*): bsplit holds two f16 parts per weight, and
+  // the row exponents of the scaled split (x rows: launch_row_exponents,
+  // weight rows: launch_split_weights with f16 set)
+  const int32_t *xexp, *wexp;
 };
 
 // Prefill tiles need n_half % 128 == 0 and k % 32 == 0; decode needs
@@ -66,9 +70,19 @@ struct SplitArgs {
   int64_t ldw, n_half, k;
   int32_t pool_hd;       // 0: plain order
   int32_t pool_tile;     // pooling order: split rows per column tile (256 or 128)
+  int32_t pool_wn;       // pooling order: columns per wavefront (64 or 128)
   uint16_t *out;
+  // f16 set: out[2 n_half][2][k] holds the f16 parts (h, l) of each weight
+  // row scaled by 2^exp_out[row] (launch_gemm_h3*), one workgroup per row
+  int32_t f16;
+  int32_t *exp_out;
 };
 hipError_t launch_split_weights(const SplitArgs &a, hipStream_t stream);
+// Scale exponent e of each of the m rows of x ([m][k], row stride lda, k % 4
+// == 0): 2^e brings the row's largest magnitude into [2^14, 2^15); 0 for a
+// row of zeros or one holding an infinity (NaN elements are passed over).
+hipError_t launch_row_exponents(const float *x, int64_t m, int64_t k, int64_t lda, int32_t *out,
+                                hipStream_t stream);
 // The prefill projection from a16 and bsplit (plain order), the bias as in
 // launch_gemm; n_half % 128 == 0, k % 32 == 0.
 hipError_t launch_gemm_x3(const GemmArgs &g, hipStream_t stream);
@@ -80,6 +94,12 @@ hipError_t launch_gemm_x3_pool(const GemmArgs &g, hipStream_t stream);
 // the pooling variant takes bsplit in pooling order with 128-row tiles.
 hipError_t launch_gemm_x6(const GemmArgs &g, hipStream_t stream);
 hipError_t launch_gemm_x6_pool(const GemmArgs &g, hipStream_t stream);
+// f32 x (a) times the two-part f16 weights (bsplit, wexp) on the f16 matrix
+// cores: x rows scaled by 2^xexp and split into two f16 parts in registers,
+// the three part products xh wh, xh wl, xl wh summed in f32, the sum scaled
+// back by 2^-(xexp + wexp). Shapes and orders as launch_gemm_x6*.
+hipError_t launch_gemm_h3(const GemmArgs &g, hipStream_t stream);
+hipError_t launch_gemm_h3_pool(const GemmArgs &g, hipStream_t stream);
 
 // Ratio-1 projection: C[m][n] = sum_k A[m][k] * B[n][k], bf16 A and B, f32
 // accumulation and output, bf16 MFMA. Needs k % 64 == 0 and n % 128 == 0.

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libkvc.so")
 KVC_OK, KVC_EINVAL, KVC_EUNSUPPORTED, KVC_ESPACE, KVC_EHIP = 0, -1, -2, -3, -4
 KVC_FP4_E4M3_B16, KVC_FP4_E8M0_B32 = 0, 1
 KVC_X_F32, KVC_X_BF16 = 0, 1
-KVC_PROJ_BF16_SPLIT, KVC_PROJ_F32_MFMA = 0, 1
+KVC_PROJ_BF16_SPLIT, KVC_PROJ_F32_MFMA, KVC_PROJ_F16_SPLIT = 0, 1, 2
 
 _lib = None
 
@@ -109,7 +109,7 @@ class Config:
     fp4_format: int = KVC_FP4_E4M3_B16
     rope_dim: int = 0
     x_format: int = KVC_X_F32  # KVC_X_BF16: x is the bf16 hidden state
-    projection: int = KVC_PROJ_BF16_SPLIT  # KVC_PROJ_F32_MFMA: the f32 matrix cores
+    projection: int = KVC_PROJ_BF16_SPLIT  # KVC_PROJ_F32_MFMA: the f32 matrix cores; KVC_PROJ_F16_SPLIT: scaled f16 parts
 
     @property
     def fp4_block(self) -> int:

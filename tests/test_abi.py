@@ -60,6 +60,11 @@ def test_sizes(ratio, hd, proj, rows):
     cfg16 = kvc.Config(ratio, hd, 4096, x_format=kvc.KVC_X_BF16)
     assert kvc.kvc_prefill_workspace_floats(cfg16, 3, 100) == 2 * 3 * 100 * proj + pooled + parts
     assert kvc.kvc_decode_workspace_floats(cfg16, 64) == ws
+    # the scaled f16 split: two f16 parts [2 proj][2][dim], the exponents of
+    # the 2 proj weight rows and of the 300 x rows
+    cfgh = kvc.Config(ratio, hd, 4096, projection=kvc.KVC_PROJ_F16_SPLIT)
+    assert kvc.kvc_prefill_workspace_floats(cfgh, 3, 100) == 2 * 3 * 100 * proj + pooled + 2 * proj * 4096 + \
+        2 * proj + 300
 
 
 def test_decode_workspace_of_the_b64_ratio4_step():
@@ -78,9 +83,10 @@ def test_decode_workspace_of_the_b64_ratio4_step():
     (kvc.Config(4, 512, 4096, eps=-1.0), kvc.KVC_EINVAL),
     (kvc.Config(4, 512, 4096, eps=float("nan")), kvc.KVC_EINVAL),
     (kvc.Config(4, 512, 4096, x_format=2), kvc.KVC_EINVAL),
-    (kvc.Config(4, 512, 4096, projection=2), kvc.KVC_EINVAL),
-    # the f32 matrix cores read f32 rows only
+    (kvc.Config(4, 512, 4096, projection=3), kvc.KVC_EINVAL),
+    # the f32 matrix cores and the f16 split read f32 rows only
     (kvc.Config(4, 512, 4096, x_format=kvc.KVC_X_BF16, projection=kvc.KVC_PROJ_F32_MFMA), kvc.KVC_EINVAL),
+    (kvc.Config(4, 512, 4096, x_format=kvc.KVC_X_BF16, projection=kvc.KVC_PROJ_F16_SPLIT), kvc.KVC_EINVAL),
 ])
 def test_invalid_configs(cfg, code):
     with pytest.raises(kvc.KvcError) as err:
@@ -140,6 +146,17 @@ def test_projection_needs_room_for_the_split_weights(x_format):
     assert _prefill_raw(cfg, ws=fake, ws_n=10)[0] == kvc.KVC_ESPACE
     # x must be 16-byte aligned
     assert _prefill_raw(cfg, x=fake + 2, w=w, ws=fake, ws_n=full)[0] == kvc.KVC_EINVAL
+
+
+def test_f16_split_projection_needs_room_for_parts_and_exponents():
+    fake = 0x100000  # never dereferenced: every case below fails its host checks
+    w = kvc._Weights(fake, fake, None, None)
+    cfg = kvc.Config(4, 512, 4096, projection=kvc.KVC_PROJ_F16_SPLIT)
+    full = kvc.kvc_prefill_workspace_floats(cfg, 1, 8)
+    planes = 2 * 8 * 1024 + 2 * 512
+    assert full == planes + 2 * 1024 * 4096 + 2 * 1024 + 8
+    assert _prefill_raw(cfg, x=fake, w=w, ws=fake, ws_n=full - 1)[0] == kvc.KVC_ESPACE
+    assert _prefill_raw(cfg, x=fake, w=w, ws=fake, ws_n=planes + 2 * 1024 * 4096)[0] == kvc.KVC_ESPACE
 
 
 def test_f32_matrix_core_projection_needs_only_the_planes():

@@ -159,7 +159,7 @@ def test_decode_r4_b64_s512_equals_prefill():
                   ref["latent"][0], dec["dequant"][b])
 
 
-@pytest.mark.parametrize("projection", [kvc.KVC_PROJ_BF16_SPLIT, kvc.KVC_PROJ_F32_MFMA])
+@pytest.mark.parametrize("projection", [kvc.KVC_PROJ_BF16_SPLIT, kvc.KVC_PROJ_F32_MFMA, kvc.KVC_PROJ_F16_SPLIT])
 def test_prefill_r4_n65536_fp4_idx128_sampled(projection):
     wl = W.WORKLOADS["prefill_r4_n65536_fp4_idx128"]
     note(f"{wl.name} projection={projection}")

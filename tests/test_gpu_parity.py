@@ -171,9 +171,10 @@ GEMM_CASES = [
 
 
 # (x format, projection): f32 rows split on the bf16 matrix cores (the
-# default), f32 rows on the f32 matrix cores, bf16 rows on the bf16 matrix cores
+# default), f32 rows on the f32 matrix cores, f32 rows as scaled f16 parts on
+# the f16 matrix cores, bf16 rows on the bf16 matrix cores
 PROJ_PATHS = [(kvc.KVC_X_F32, kvc.KVC_PROJ_BF16_SPLIT), (kvc.KVC_X_F32, kvc.KVC_PROJ_F32_MFMA),
-              (kvc.KVC_X_BF16, kvc.KVC_PROJ_BF16_SPLIT)]
+              (kvc.KVC_X_F32, kvc.KVC_PROJ_F16_SPLIT), (kvc.KVC_X_BF16, kvc.KVC_PROJ_BF16_SPLIT)]
 
 
 @pytest.mark.parametrize("x_format,projection", PROJ_PATHS)
@@ -664,3 +665,143 @@ def test_f32_x_split_gives_faithfully_rounded_products(ratio, hd, dim, batch, se
         faithful = (got == lo) | (got == other) | ((exact == 0) & (got == 0))
         assert faithful.all(), f"{name}: {(~faithful).sum()} not within one rounding of v w"
         note(f"  {name}: {(got != lo).sum()} of {got.size} outputs on the farther neighbour")
+
+
+# ---------------------------------------------------------------- the scaled f16 split
+def _f16_parts_sum(w):
+    """h + l of each weight row scaled by 2^b (b brings the row's largest
+    magnitude into [2^14, 2^15)), scaled back: what one-hot x rows give."""
+    amax = np.abs(w).max(axis=1, keepdims=True).astype(np.float64)
+    b = np.where(amax > 0, 15 - np.frexp(np.where(amax > 0, amax, 1.0))[1], 0)
+    y = np.ldexp(w.astype(np.float64), b).astype(np.float32)   # exact: a power-of-two scaling
+    h = y.astype(np.float16)
+    l = (y - h.astype(np.float32)).astype(np.float16)          # y - h is exact in f32
+    return np.ldexp(h.astype(np.float32) + l.astype(np.float32), -b).astype(np.float32)
+
+
+@pytest.mark.parametrize("ratio,hd,dim,batch,seqlen", SPLIT_CASES)
+def test_f16_split_one_hot_rows_give_the_two_part_weights(ratio, hd, dim, batch, seqlen):
+    """x row r = e_(r mod dim) (scaled to 2^14, split into 2^14 + 0) picks
+    one weight: the output is its two f16 parts' sum scaled back, bit for bit,
+    and that sum is within 2^-22 relative of the f32 weight. Weight rows have
+    scales 2^-100 .. 2^100 (each row's exponent is its own) and values
+    spanning 2^9 inside a row."""
+    note(f"f16 split one-hot ratio={ratio} hd={hd} dim={dim} batch={batch} seqlen={seqlen}")
+    from gpu_util import weights
+    rng = np.random.default_rng(11 + ratio + dim + seqlen)
+    cfg = kvc.Config(ratio, hd, dim, projection=kvc.KVC_PROJ_F16_SPLIT)
+    proj = kvc.kvc_proj_width(cfg)
+    m = batch * seqlen
+    x = np.zeros((m, dim), np.float32)
+    x[np.arange(m), np.arange(m) % dim] = 1.0
+
+    def rows(shape):
+        shift = rng.integers(-100, 100, (shape[0], 1))
+        shift[0] = 0   # row 0 also holds the special values below
+        v = rng.choice([-1.0, 1.0], shape) * np.ldexp(rng.uniform(1.0, 2.0, shape), shift + rng.integers(-8, 1, shape))
+        v = v.astype(np.float32)
+        v[0, :4] = [0.0, -0.0, 1 + 2.0 ** -23, -(1 + 2.0 ** -12)]
+        return v
+
+    w = {"wkv": rows((proj, dim)), "wgate": rows((proj, dim)),
+         "ape": rng.standard_normal((ratio, proj)).astype(np.float32)}
+    ws = torch.full((kvc.kvc_prefill_workspace_floats(cfg, batch, seqlen),), float("nan"), device="cuda")
+    kvc.compressor_prefill(cfg, weights(w), dev(x.reshape(batch, seqlen, dim)), batch, seqlen, ws)
+    torch.cuda.synchronize()
+    kv = ws[:m * proj].view(m, proj).cpu().numpy()
+    sc = ws[m * proj:2 * m * proj].view(m, proj).cpu().numpy()
+    col = np.arange(m) % dim
+    for name in ("wkv", "wgate"):
+        parts = _f16_parts_sum(w[name])
+        rel = np.abs(parts.astype(np.float64) - w[name]) / np.maximum(np.abs(w[name]).astype(np.float64), 1e-300)
+        assert rel.max() <= 2.0 ** -22, f"{name}: two-part sum off by {rel.max():.3e} relative"
+        want = parts.T[col] + np.float32(0.0)
+        if name == "wgate":
+            want = want + w["ape"][(np.arange(m) % seqlen) % ratio]   # one f32 rounding, as on the GPU
+        got = kv if name == "wkv" else sc
+        bad = got.view(np.uint32) != want.view(np.uint32)
+        assert not bad.any(), f"{name}: {bad.sum()} differ, e.g. {want[bad][:4]} -> {got[bad][:4]}"
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_f16_split_rows_of_any_scale(fused):
+    """x rows and weight rows with scales 2^-60 .. 2^60 (N(0,1) values times
+    the row's power of two) through the plain kernel (projections inside the
+    f32 bound of the GEMM tests), and x rows of 2^-4 .. 2^4 with weight rows
+    of 2^-10 .. 2^10 through the pooling kernel (sampled entries inside the
+    pooled tolerance): each row's own exponent scales it into the f16 range
+    and back."""
+    note(f"f16 split wide row scales fused={fused}")
+    from gpu_util import weights
+    rng = np.random.default_rng(5 + fused)
+    ratio, batch = 4, 1
+    hd, dim, seqlen = (512, 64, 16384 + 5) if fused else (128, 256, 300)
+    cfg = kvc.Config(ratio, hd, dim, projection=kvc.KVC_PROJ_F16_SPLIT)
+    proj = kvc.kvc_proj_width(cfg)
+    m = batch * seqlen
+    # the pooled check needs gate logits of moderate size (a softmax over
+    # logits of size 2^60 turns on their last bits): narrower scales there
+    xs, ws_ = (4, 10) if fused else (60, 60)
+    x = (rng.standard_normal((m, dim)) * np.exp2(rng.integers(-xs, xs, (m, 1)))).astype(np.float32)
+    x[3] = 0.0   # a row of zeros keeps exponent 0
+    w = {"wkv": (rng.standard_normal((proj, dim)) * np.exp2(rng.integers(-ws_, ws_, (proj, 1)))).astype(np.float32),
+         "wgate": (rng.standard_normal((proj, dim)) * 0.02).astype(np.float32),
+         "ape": (rng.standard_normal((ratio, proj)) * 0.1).astype(np.float32)}
+    xd = dev(x.reshape(batch, seqlen, dim))
+    ws = torch.empty(kvc.kvc_prefill_workspace_floats(cfg, batch, seqlen), dtype=torch.float32, device="cuda")
+    kvc.compressor_prefill(cfg, weights(w), xd, batch, seqlen, ws)
+    torch.cuda.synchronize()
+    rows = np.arange(m) if m <= 4096 else np.unique(np.concatenate([np.arange(300), rng.choice(m, 700)]))
+    for plane, name in ((0, "wkv"), (1, "wgate")):
+        got = ws[plane * m * proj:(plane + 1) * m * proj].view(m, proj).cpu().numpy()[rows].astype(np.float64)
+        ref = oracle.project(x[rows], w[name])
+        if name == "wgate":
+            ref = oracle.add_bias(ref[None], w["ape"], rows % seqlen, ratio)[0]
+        absdot = np.abs(x[rows]).astype(np.float64) @ np.abs(w[name]).astype(np.float64).T
+        bound = dim * 2.0 ** -24 * absdot + np.spacing(np.abs(ref)) + 1e-300
+        err = np.abs(got - ref)
+        assert np.all(err <= bound), f"{name}: {np.sum(err > bound)} beyond the bound, worst {np.max(err / bound):.3g}"
+    if fused:
+        groups = seqlen // ratio
+        out = kvc.new_outputs(cfg, batch, groups, latent=True, pooled=True)
+        kvc.compressor_prefill(cfg, weights(w), xd, batch, seqlen, ws, None, None, out)
+        torch.cuda.synchronize()
+        pooled = out.pooled.cpu().numpy()
+        ent = np.array(sorted(set([0, 1, 63, 64, 65, groups - 1]) | set(rng.choice(groups, 40).tolist())))
+        ocfg = oracle_cfg(cfg)
+        ref = oracle.prefill(ocfg, oracle_weights(w), oracle.State(ocfg, 1), x=x.reshape(batch, seqlen, dim),
+                             quantize=False, entries=ent)
+        check_pooled(pooled[0][ent], ref["pooled"][0])
+
+
+@pytest.mark.parametrize("ratio,hd,dim,batch,seqlen", SPLIT_CASES)
+def test_f16_split_of_f32_rows_is_the_two_part_sum(ratio, hd, dim, batch, seqlen):
+    """x rows v_r e_(r mod dim) (v_r any f32 of scale 2^-40 .. 2^40) with
+    weights that are powers of two (their low parts zero): each output is
+    then (h + l) w of x's two f16 parts scaled back, every step exact, so it
+    must equal that value bit for bit, and lie within 2^-22 relative of the
+    exact v_r w. This pins the split the kernel does in registers."""
+    note(f"f16 split of x rows ratio={ratio} hd={hd} dim={dim} batch={batch} seqlen={seqlen}")
+    from gpu_util import weights
+    rng = np.random.default_rng(23 + ratio + dim)
+    cfg = kvc.Config(ratio, hd, dim, projection=kvc.KVC_PROJ_F16_SPLIT)
+    proj = kvc.kvc_proj_width(cfg)
+    m = batch * seqlen
+    v = (rng.standard_normal(m) * np.exp2(rng.integers(-40, 40, m))).astype(np.float32)
+    v[:3] = [1 + 2.0 ** -23, -(2.0 ** -30) * (1 + 2.0 ** -11 + 2.0 ** -23), 0.0]
+    x = np.zeros((m, dim), np.float32)
+    x[np.arange(m), np.arange(m) % dim] = v
+    pow2 = lambda: (rng.choice([-1.0, 1.0], (proj, dim)) * np.exp2(rng.integers(-8, 1, (proj, dim)))).astype(np.float32)  # noqa: E731
+    w = {"wkv": pow2(), "wgate": pow2()}
+    ws = torch.full((kvc.kvc_prefill_workspace_floats(cfg, batch, seqlen),), float("nan"), device="cuda")
+    kvc.compressor_prefill(cfg, weights(w), dev(x.reshape(batch, seqlen, dim)), batch, seqlen, ws)
+    torch.cuda.synchronize()
+    xs = _f16_parts_sum(v[:, None])[:, 0]           # x's two parts, scaled back
+    rel = np.abs(xs.astype(np.float64) - v) / np.maximum(np.abs(v).astype(np.float64), 1e-300)
+    assert rel.max() <= 2.0 ** -22
+    col = np.arange(m) % dim
+    for plane, name in ((0, "wkv"), (1, "wgate")):
+        got = ws[plane * m * proj:(plane + 1) * m * proj].view(m, proj).cpu().numpy()
+        want = (xs[:, None] * w[name].T[col]).astype(np.float32) + np.float32(0.0)  # exact: times a power of two
+        bad = got.view(np.uint32) != want.view(np.uint32)
+        assert not bad.any(), f"{name}: {bad.sum()} differ, e.g. {want[bad][:4]} -> {got[bad][:4]}"
