@@ -69,8 +69,20 @@ __device__ __forceinline__ void phase_barrier() {
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void wait_vm12() { asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); }
+// Counter waits as s_waitcnt instructions the compiler sees (so it knows the
+// counters drained there and adds no waits of its own for earlier loads, as
+// it would after an opaque asm wait), kept in place by the scheduler.
+// Immediate fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void wait_vm0_seen() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 constexpr int kBK3 = 32;  // k per LDS stage
 // the pooling kernel's wavefront: 128 rows x 64 columns, the 64 columns the
@@ -327,7 +339,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_mc_kernel(GemmArgs g) {
 
   if (loader) {
     issue(0, 0);
-    wait_vm0();
+    wait_vm0_seen();
   }
   phase_barrier();
   if (!loader) phase_barrier();  // group 4..7 runs one phase behind
@@ -338,7 +350,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_mc_kernel(GemmArgs g) {
     wait_lgkm0();  // this stage's reads are done before its buffer can be reloaded
     phase_barrier();
     mfmas();
-    if (loader) wait_vm0();  // the next stage has landed before this group reads it
+    if (loader) wait_vm0_seen();  // the next stage has landed before this group reads it
     phase_barrier();
   }
   if (loader) phase_barrier();  // the same number of barriers for every wavefront
@@ -388,11 +400,14 @@ __device__ __forceinline__ void split8(const f4 lo4, const f4 hi4, bf16x8 &h, bf
 }
 
 // F16: the same kernel on the f16 matrix cores (v_mfma_f32_16x16x32_f16)
-// with the two-part f16 weights: the read phase takes the scale exponent of
-// each row fragment's x row (g.xexp), the split gives xh, xl (split_f16),
-// and the multiply phase sums xh wh, xh wl, xl wh (the left-out xl wl is at
-// most 2^-22 |x w| of the scaled values); the epilogue scales every sum back
-// by 2^-(xexp + wexp), exactly, before the bias and the pooling.
+// with the two-part f16 weights: each row fragment's x row brings its scale
+// exponent (g.xexp), the split gives xh, xl (split8_f16), and the multiply
+// phase sums xh wh, xh wl, xl wh (the left-out xl wl is at most 2^-22 |x w|
+// of the scaled values); the epilogue scales every sum back by
+// 2^-(xexp + wexp), exactly, before the bias and the pooling. With two
+// weight parts the kernel also runs 256 x 256 tiles of eight 64 x 128
+// wavefronts (twice the matrix-core work per LDS stage and per barrier; the
+// x split is shared by twice the MFMAs).
 // y - h for h one half of a packed f16 pair: one fused multiply-add with the
 // f16 operand taken as is (-h * 1 + y, exact), in place of converting h back
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -433,17 +448,13 @@ __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
   constexpr int NL = 4;
   constexpr int NP = F16 ? 2 : 3;                   // weight parts
   constexpr int A_INS = BM / 8 / NL, B_INS = NP * BRB / NL;  // x: 8 rows of 32 floats per load
-  // F16 with 128-column tiles: three LDS stages (the loads of a stage are
-  // issued two stages ahead)
-  constexpr int NS = F16 && BN == 128 ? 3 : 2;
-  constexpr bool kReadSplit = F16 && BN == 128;
-  constexpr int STAGE_FLOATS = NS * (BM * BK + NP * BN * BK / 2);
+  constexpr int STAGE_FLOATS = 2 * (BM * BK + NP * BN * BK / 2);
   constexpr int SMEM_FLOATS = POOL && kPoolXFloats > STAGE_FLOATS ? kPoolXFloats : STAGE_FLOATS;
   static_assert(SMEM_FLOATS * 4 <= 160 * 1024, "LDS");
   typedef typename std::conditional<F16, f16x8, bf16x8>::type v8;
   __shared__ __attribute__((aligned(16))) float smem[SMEM_FLOATS];
   float(*As)[BM * BK] = reinterpret_cast<float(*)[BM * BK]>(smem);
-  uint16_t(*Bs)[NP][BN * BK] = reinterpret_cast<uint16_t(*)[NP][BN * BK]>(smem + NS * BM * BK);
+  uint16_t(*Bs)[NP][BN * BK] = reinterpret_cast<uint16_t(*)[NP][BN * BK]>(smem + 2 * BM * BK);
 
   const int64_t m_tiles = (g.m + BM - 1) / BM;
   const int64_t n_tiles = 2 * g.n_half / BN;  // with POOL: pool_hd / 32 tiles of 128 permuted rows
@@ -469,20 +480,28 @@ __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
   const i32x4 a_rsrc = uniform_rsrc(make_rsrc(g.a + m0 * g.lda, (uint32_t)(a_rows * g.lda * 4)));
   const i32x4 b_rsrc = uniform_rsrc(make_rsrc(g.bsplit + n_glob * RS, (uint32_t)(BN * RS * 2)));
   const int xr = lane >> 3, xq = (lane & 7) ^ (xr & 7);
-  uint32_t a_voff[A_INS];
-#pragma unroll
-  for (int u = 0; u < A_INS; ++u) {
-    int64_t r = 8 * (lw * A_INS + u) + xr;
-    if (r >= a_rows) r = a_rows - 1;  // ragged last tile: read a valid row, never store it
-    a_voff[u] = (uint32_t)((r * g.lda + 4 * xq) * 4);
-  }
+  // a full row tile: one lane offset, the row step of each load in the
+  // scalar offset; the ragged last tile clamps each load's row instead
+  // (rows past m read a valid row and are never stored)
+  const bool full_tile = a_rows == BM;
+  const uint32_t a_voff0 = (uint32_t)(((int64_t)(8 * lw * A_INS) + xr) * g.lda * 4 + 16 * xq);
   const int lr = lane >> 2, lq = (lane & 3) ^ ((lr >> 1) & 3);
   const uint32_t b_voff = (uint32_t)((lr * RS + 8 * lq) * 2);
   auto issue = [&](int kt, int st) {
+    if (full_tile) {
 #pragma unroll
-    for (int u = 0; u < A_INS; ++u)
-      buffer_load_lds(a_rsrc, (lds_u32 *)(&As[st][256 * (lw * A_INS + u)]), 16, (int32_t)a_voff[u],
-                      (int32_t)(kt * BK * 4), 0, 0);
+      for (int u = 0; u < A_INS; ++u)
+        buffer_load_lds(a_rsrc, (lds_u32 *)(&As[st][256 * (lw * A_INS + u)]), 16, (int32_t)a_voff0,
+                        (int32_t)(kt * BK * 4 + u * 8 * g.lda * 4), 0, 0);
+    } else {
+#pragma unroll
+      for (int u = 0; u < A_INS; ++u) {
+        int64_t r = 8 * (lw * A_INS + u) + xr;
+        if (r >= a_rows) r = a_rows - 1;
+        buffer_load_lds(a_rsrc, (lds_u32 *)(&As[st][256 * (lw * A_INS + u)]), 16, (int32_t)((r * g.lda + 4 * xq) * 4),
+                        (int32_t)(kt * BK * 4), 0, 0);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < B_INS; ++u) {
       const int q = lw * B_INS + u, p = q / BRB, rb = q % BRB;
@@ -511,11 +530,8 @@ __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
   // the read phase keeps x as f32 (8 values per row fragment) and splits row
   // fragment 0; the multiply phase splits row fragment i + 1 while row
   // fragment i's MFMAs run
-  // F16: the two parts of every row fragment take the registers of its f32
-  // values, so the read phase splits them all and the multiply phase is
-  // matrix-core work only (its vector work overlaps the other group's MFMAs)
   f4 xf[FM][2];
-  v8 fa[2][NP], fb[NP][FN], fx[kReadSplit ? FM : 1][2];
+  v8 fa[2][NP], fb[NP][FN];
   auto split = [&](int i, v8 (&parts)[NP]) {
     if constexpr (F16) split8_f16(xf[i][0], xf[i][1], xe[i], parts[0], parts[1]);
     else split8(xf[i][0], xf[i][1], parts[0], parts[1], parts[2]);
@@ -534,13 +550,8 @@ __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
         const int r = wn * WN + 16 * j + row_in;
         fb[p][j] = *reinterpret_cast<const v8 *>(&Bs[st][p][r * BK + 8 * (slot ^ ((r >> 1) & 3))]);
       }
-    if constexpr (kReadSplit) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) split8_f16(xf[i][0], xf[i][1], xe[i], fx[i][0], fx[i][1]);
-    } else {
-      // row fragment 0 split here, so the multiply phase opens with MFMAs
-      split(0, fa[0]);
-    }
+    // row fragment 0 split here, so the multiply phase opens with MFMAs
+    split(0, fa[0]);
   };
   // per row fragment, the part products in the order xh wh, xh wm, xm wh,
   // xh wl, xm wm, xl wh (F16: xh wh, xh wl, xl wh); every output sums them in
@@ -549,23 +560,22 @@ __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int cur = i & 1;
-      if constexpr (kReadSplit) {
-        constexpr int XP[3] = {0, 0, 1}, WP[3] = {0, 1, 0};
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fx[i][XP[q]], fb[WP[q]][j], acc[i][j], 0, 0, 0);
-      } else if constexpr (F16) {
-        if (i + 1 < FM) split(i + 1, fa[cur ^ 1]);
+      if (i + 1 < FM) split(i + 1, fa[cur ^ 1]);
+      if constexpr (F16) {
         constexpr int XP[3] = {0, 0, 1}, WP[3] = {0, 1, 0};
 #pragma unroll
         for (int q = 0; q < 3; ++q)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[cur][XP[q]], fb[WP[q]][j], acc[i][j], 0, 0, 0);
+        // the next fragment's split (24 vector instructions) interleaved one
+        // by one with this fragment's MFMAs
+#pragma unroll
+        for (int q = 0; q < 3 * FN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i + 1 < FM && q < 24) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+        }
       } else {
-        if (i + 1 < FM) split(i + 1, fa[cur ^ 1]);
         constexpr int XP[6] = {0, 0, 1, 0, 1, 2}, WP[6] = {0, 1, 0, 2, 1, 0};
 #pragma unroll
         for (int q = 0; q < 6; ++q)
@@ -576,33 +586,20 @@ __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
     }
   };
 
-  // F16: a loading wavefront has A_INS + B_INS loads per stage in flight
-  static_assert(NS == 2 || A_INS + B_INS == 12, "wait count");
-  if (loader) {
-    issue(0, 0);
-    if (NS == 3 && kt_count > 1) {
-      issue(1, 1);
-      wait_vm12();
-    } else {
-      wait_vm0();
-    }
-  }
+  if (loader) issue(0, 0);
+  // every wavefront drains its loads here (the first stage, the exponents),
+  // so that no wait for them lands inside the loop
+  wait_vm0_seen();
   phase_barrier();
   if (!loader) phase_barrier();  // group 4..7 runs one phase behind
   for (int kt = 0; kt < kt_count; ++kt) {
-    const int st = kt % NS;
+    const int st = kt & 1;
     reads(st);
-    // after the stage's last LDS read: the stage NS - 1 ahead, into the
-    // buffer both groups finished reading in the previous two phases
-    if (loader && kt + NS - 1 < kt_count) issue(kt + NS - 1, (kt + NS - 1) % NS);
+    if (loader && kt + 1 < kt_count) issue(kt + 1, st ^ 1);  // after the stage's last LDS read
     wait_lgkm0();
     phase_barrier();
     mfmas();
-    if (loader) {
-      // stage kt + 1 complete (NS = 3: the loads of stage kt + 2 may remain)
-      if (NS == 3 && kt + 2 < kt_count) wait_vm12();
-      else wait_vm0();
-    }
+    if (loader) wait_vm0_seen();
     phase_barrier();
   }
   if (loader) phase_barrier();  // the same number of barriers for every wavefront
