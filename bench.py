@@ -7,21 +7,24 @@ workload (ratio-4 prefill of 65536 tokens, hidden 4096) that is the 512-wide
 compressor (f32 projections, pooling + RMSNorm + fp4 cache codes) and the
 128-wide indexer compressor (projections, pooling + RMSNorm, bf16 latent),
 with the hidden states resident in HBM: x f32 [1, 65536, 4096] ~ N(0, 1).
-The projections are f32 products computed on the bf16 matrix cores from
-exact bf16 parts (x and the weights split into hi + mid + lo, the six part
-products of size >= 2^-16 |x w| summed in f32; --projection f32-mfma uses the
-f32 matrix cores instead). Beside the headline (`workloads`) the same step on
-the f32 matrix cores, and from the model's bf16 hidden states (the bf16
-rounding of the same draws as bf16 rows: exact products from the weights'
-three parts; --x-format bf16 makes that the headline). Prints one JSON line.
+The projections are f32 products on the f16 matrix cores by default (each
+row of x and each weight row scaled by a power of two and split into two f16
+parts, three part products summed in f32; the step computes x's row
+exponents once for both compressors); --projection bf16-split (six bf16 part
+products) and f32-mfma (the f32 matrix cores) select the others. Beside the
+headline (`workloads`) the same step on the other projection paths, and from
+the model's bf16 hidden states (the bf16 rounding of the same draws as bf16
+rows: exact products from the weights' three parts; --x-format bf16 makes
+that the headline). Prints one JSON line.
 
 Kernel durations are measured with HIP events on the launch stream around
 repeated launches of each kernel alone (the same library calls with the other
 stages switched off through their arguments: no outputs = projection only,
-which for bf16 x is the weight split (about 0.7% of it) and the GEMM;
-projections given = pooling only). The roofline object reports the dominant
-kernel (the 512-wide projection GEMM, matrix-core bound: for f32 x against
-the fp32 peak; for bf16 x its three bf16 passes against the bf16 peak);
+which with a split projection is the weight split (under 1% of it) and the
+GEMM; projections given = pooling only). The roofline object reports the
+dominant kernel (the 512-wide projection GEMM, matrix-core bound: the f16 or
+bf16 part products against the 16-bit matrix-core peak, with the
+f32-equivalent rate beside it; the f32 matrix cores against the fp32 peak);
 `pool` reports the pooling kernel against HBM bandwidth.
 """
 from __future__ import annotations
@@ -151,7 +154,7 @@ def gemm_roofline(kvc, g, x_format, projection):
     rate beside it), on the f32 matrix cores its flops against the fp32 peak."""
     passes = mfma_passes(kvc, x_format, projection)
     if passes:
-        if projection == kvc.KVC_PROJ_F16_SPLIT:
+        if resolved(kvc, x_format, projection) == kvc.KVC_PROJ_F16_SPLIT:
             what = ("f32 x and f32 weights, rows scaled by powers of two and split into two f16 parts, three part "
                     "products on the f16 matrix cores")
             kernel, traffic = "gemm_x6_kernel<*, F16>", "gemm_h3"
@@ -178,9 +181,17 @@ def _rounded(d):
     return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
 
 
+def resolved(kvc, x_format, projection):
+    """The projection the library runs for KVC_PROJ_AUTO."""
+    if projection != kvc.KVC_PROJ_AUTO:
+        return projection
+    return kvc.KVC_PROJ_F16_SPLIT if x_format == kvc.KVC_X_F32 else kvc.KVC_PROJ_BF16_SPLIT
+
+
 def mfma_passes(kvc, x_format, projection):
     """16-bit matrix-core passes per f32 product (bf16 or f16, both at the
     same peak; 0: the f32 matrix cores)."""
+    projection = resolved(kvc, x_format, projection)
     if projection == kvc.KVC_PROJ_F32_MFMA:
         return 0
     if projection == kvc.KVC_PROJ_F16_SPLIT:
@@ -209,10 +220,18 @@ def run_prefill(wl, steps, warmup, reps, torch, kvc, W, x_format, projection):
         out = kvc.new_outputs(cfg, wl.batch, groups, latent=not comp.quantize, fp4=comp.quantize)
         comps.append((comp, cfg, wts, ws, state, out, groups))
     stream = torch.cuda.current_stream()
+    m = wl.batch * wl.seqlen
+    # the f16 split scales each row of x by its own power of two: both
+    # compressors read the same hidden states, so the step computes the
+    # row exponents once and hands them to both
+    shared = resolved(kvc, x_format, projection) == kvc.KVC_PROJ_F16_SPLIT
+    exps = torch.empty(m, dtype=torch.int32, device=dev) if shared else None
 
     def step():
+        if shared:
+            kvc.x_row_exponents(x, m, wl.dim, exps)
         for comp, cfg, wts, ws, state, out, groups in comps:
-            kvc.compressor_prefill(cfg, wts, x, wl.batch, wl.seqlen, ws, state[0], state[1], out)
+            kvc.compressor_prefill(cfg, wts, x, wl.batch, wl.seqlen, ws, state[0], state[1], out, x_exponents=exps)
 
     print(f"[bench] {wl.name}: warmup + {steps} timed steps", file=sys.stderr, flush=True)
     for _ in range(warmup):
@@ -222,9 +241,14 @@ def run_prefill(wl, steps, warmup, reps, torch, kvc, W, x_format, projection):
     entries = comps[0][6] * wl.batch
 
     kernels = {}
+    if shared:
+        xe_ms = _timed(torch, stream, lambda: kvc.x_row_exponents(x, m, wl.dim, exps), reps)
+        xe_bytes = m * wl.dim * 4 + m * 4
+        kernels["x_exponents"] = {"ms": xe_ms, "gbps": xe_bytes / xe_ms / 1e6, "bytes": xe_bytes}
     for comp, cfg, wts, ws, state, out, groups in comps:
         tag = f"hd{comp.head_dim}"
-        gemm_ms = _timed(torch, stream, lambda: kvc.compressor_prefill(cfg, wts, x, wl.batch, wl.seqlen, ws), reps)
+        gemm_ms = _timed(torch, stream, lambda: kvc.compressor_prefill(cfg, wts, x, wl.batch, wl.seqlen, ws,
+                                                                       x_exponents=exps), reps)
         # ws now holds this compressor's projections, the bias already in the
         # score plane: pool them alone, exactly as the step's pooling launch
         pool_ms = _timed(torch, stream, lambda: kvc.compressor_prefill(cfg, kvc.Weights(), None, wl.batch,
@@ -372,9 +396,10 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--x-format", choices=("f32", "bf16"), default="f32",
                     help="hidden states handed to the library: the f32 draws, or their bf16 rounding as bf16 rows")
-    ap.add_argument("--projection", choices=("split", "f32-mfma", "f16-split"), default="split",
-                    help="prefill projection on the bf16 matrix cores from exact bf16 parts, on the f32 matrix "
-                         "cores, or on the f16 matrix cores from scaled two-part f16 splits")
+    ap.add_argument("--projection", choices=("auto", "f16-split", "bf16-split", "f32-mfma"), default="auto",
+                    help="prefill projection: the library's default (f16 split for f32 x, bf16 split for bf16 x), "
+                         "the f16 matrix cores on scaled two-part f16 splits, the bf16 matrix cores on exact bf16 "
+                         "parts, or the f32 matrix cores")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -407,8 +432,9 @@ def main():
         torch.cuda.empty_cache()
 
     x_format = kvc.KVC_X_BF16 if args.x_format == "bf16" else kvc.KVC_X_F32
-    projection = {"split": kvc.KVC_PROJ_BF16_SPLIT, "f32-mfma": kvc.KVC_PROJ_F32_MFMA,
+    projection = {"auto": kvc.KVC_PROJ_AUTO, "bf16-split": kvc.KVC_PROJ_BF16_SPLIT, "f32-mfma": kvc.KVC_PROJ_F32_MFMA,
                   "f16-split": kvc.KVC_PROJ_F16_SPLIT}[args.projection]
+    projection = resolved(kvc, x_format, projection)
     head = run_prefill(wl, args.steps, args.warmup, args.kernel_reps, torch, kvc, W, x_format, projection)
     kernels = head["kernels"]
     main_tag = f"hd{wl.compressors[0].head_dim}"
@@ -443,10 +469,10 @@ def main():
         # the same step by the other projection paths
         for name, xf, pr, desc in (
                 ("f32_mfma", kvc.KVC_X_F32, kvc.KVC_PROJ_F32_MFMA, "f32 rows, N(0,1); f32 matrix cores"),
-                ("split", kvc.KVC_X_F32, kvc.KVC_PROJ_BF16_SPLIT,
-                 "f32 rows, N(0,1); bf16 matrix cores on exact bf16 parts (six part products)"),
                 ("f16_split", kvc.KVC_X_F32, kvc.KVC_PROJ_F16_SPLIT,
                  "f32 rows, N(0,1); f16 matrix cores on row-scaled two-part f16 splits (three part products)"),
+                ("bf16_split", kvc.KVC_X_F32, kvc.KVC_PROJ_BF16_SPLIT,
+                 "f32 rows, N(0,1); bf16 matrix cores on exact bf16 parts (six part products)"),
                 ("x_bf16", kvc.KVC_X_BF16, kvc.KVC_PROJ_BF16_SPLIT,
                  "bf16 rows: the bf16 rounding of the N(0,1) draws, the model's hidden-state type; bf16 matrix "
                  "cores on the exact bf16 parts of the weights")):

@@ -68,9 +68,10 @@ typedef struct ihipStream_t *kvc_stream; /* a hipStream_t */
 #define KVC_X_BF16 1 /* bf16 rows: the model's hidden state */
 
 /* matrix cores of the prefill projection (kvc_config.projection) */
-#define KVC_PROJ_BF16_SPLIT 0 /* bf16 matrix cores on exact bf16 parts (default; see x_format) */
+#define KVC_PROJ_AUTO 0       /* default: KVC_PROJ_F16_SPLIT for f32 x, KVC_PROJ_BF16_SPLIT for bf16 x */
 #define KVC_PROJ_F32_MFMA 1   /* f32 matrix cores (x_format KVC_X_F32 only) */
 #define KVC_PROJ_F16_SPLIT 2  /* f16 matrix cores on scaled two-part f16 splits (x_format KVC_X_F32 only) */
+#define KVC_PROJ_BF16_SPLIT 3 /* bf16 matrix cores on exact three-part bf16 splits */
 
 /* fp4 forms of a compressed entry (kvc_config.fp4_format) */
 #define KVC_FP4_E4M3_B16 0 /* the KV latent's form: e4m3fn scale per block of 16 */
@@ -104,26 +105,29 @@ typedef struct ihipStream_t *kvc_stream; /* a hipStream_t */
  *                pairs", Compressor listing, forward); with KVC_X_BF16 the
  *                caller passes that bf16 state. Ignored by
  *                compressor_ratio1_forward, whose x is always bf16.
- *   projection : how compressor_prefill computes the f32 products x . w^T.
- *                KVC_PROJ_BF16_SPLIT (default): on the bf16 matrix cores with
- *                f32 accumulation, from the exact split of each f32 weight
- *                into three bf16 parts (hi, mid, lo: bits cleared, so
- *                w = hi + mid + lo); bf16 x then gives exact products (x .
- *                hi + x . mid + x . lo), and f32 x is split the same way
- *                and the six part products of size >= 2^-16 |x w| are summed
- *                (the three left out total below 2^-21 |x w|, far inside the
- *                f32 summation's own error bound). KVC_PROJ_F32_MFMA: on the
- *                f32 matrix cores. KVC_PROJ_F16_SPLIT: on the f16 matrix
- *                cores with f32 accumulation; every row of x and every
- *                weight row is scaled by the power of two that brings its
- *                largest magnitude into [2^14, 2^15), each scaled value y is
- *                split into h = f16(y) and l = f16(y - h) (y - h - l at most
- *                2^-22 |y|, or 2^-40 of the row's largest magnitude where l
- *                falls below the f16 normal range), the three part products
- *                xh wh + xh wl + xl wh are summed (xl wl, left out, is at
- *                most 2^-22 |x w|) and the sum is scaled back exactly. The
- *                last two need x_format KVC_X_F32 (KVC_EINVAL otherwise).
- *                Decode steps always use the f32 matrix cores.
+ *   projection : how compressor_prefill computes the f32 products x . w^T,
+ *                all with f32 accumulation:
+ *                KVC_PROJ_F16_SPLIT: on the f16 matrix cores. Every row of x
+ *                and every weight row is scaled by the power of two that
+ *                brings its largest magnitude into [2^14, 2^15); each scaled
+ *                value y splits into h = f16(y) and l = f16(y - h) (y - h - l
+ *                at most 2^-22 |y|, or 2^-40 of the row's largest magnitude
+ *                where l falls below the f16 normal range); the three part
+ *                products xh wh + xh wl + xl wh are summed (xl wl, left out,
+ *                is at most 2^-22 |x w|) and the sum is scaled back exactly.
+ *                KVC_PROJ_BF16_SPLIT: on the bf16 matrix cores from the exact
+ *                split of each f32 weight into three bf16 parts (hi, mid, lo:
+ *                bits cleared, so w = hi + mid + lo); bf16 x then gives exact
+ *                products (x . hi + x . mid + x . lo), and f32 x is split the
+ *                same way and the six part products of size >= 2^-16 |x w|
+ *                are summed (the three left out total below 2^-21 |x w|).
+ *                KVC_PROJ_F32_MFMA: on the f32 matrix cores.
+ *                KVC_PROJ_AUTO (0, the default): KVC_PROJ_F16_SPLIT for f32
+ *                x, KVC_PROJ_BF16_SPLIT for bf16 x. KVC_PROJ_F16_SPLIT and
+ *                KVC_PROJ_F32_MFMA need x_format KVC_X_F32 (KVC_EINVAL
+ *                otherwise). Every error above lies far inside the f32
+ *                summation's own bound (K 2^-24 sum |x w|). Decode steps
+ *                always use the f32 matrix cores.
  * proj = 2 * head_dim at ratio 4, head_dim otherwise: the width of each
  * projection plane. */
 typedef struct kvc_config {
@@ -191,11 +195,11 @@ int64_t kvc_state_rows(const kvc_config *cfg);
  * planes, 2 * batch * seqlen * proj; at ratio 4 the f32 pooled entries,
  * batch * (seqlen / 4) * head_dim (used when the projection and the pooling
  * run as one kernel: a smaller workspace runs them separately); the split
- * weights: with KVC_PROJ_BF16_SPLIT (and KVC_PROJ_F32_MFMA, which does not
- * read them) three bf16 parts, 3 * proj * dim (bf16 [2 proj][3][dim]); with
- * KVC_PROJ_F16_SPLIT two f16 parts and the scale exponents of the weight rows
- * and of x's rows, 2 * proj * dim + 2 * proj + batch * seqlen rounded up to a
- * multiple of 4. Or a negative KVC_E* code. */
+ * weights: with KVC_PROJ_F16_SPLIT (KVC_PROJ_AUTO with f32 x) two f16 parts
+ * and the scale exponents of the weight rows and of x's rows,
+ * 2 * proj * dim + 2 * proj + batch * seqlen rounded up to a multiple of 4;
+ * otherwise (KVC_PROJ_F32_MFMA does not read them) three bf16 parts,
+ * 3 * proj * dim (bf16 [2 proj][3][dim]). Or a negative KVC_E* code. */
 int64_t kvc_prefill_workspace_floats(const kvc_config *cfg, int64_t batch, int64_t seqlen);
 
 /* f32 elements of the workspace compressor_decode_step needs (split
@@ -213,6 +217,13 @@ int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch);
  *                  the kv plane [batch][seqlen][proj] followed by the score
  *                  plane [batch][seqlen][proj]; no weights are read then
  *                  except ape and norm_w.
+ *   x_exponents  : [batch * seqlen] int32 scale exponents of x's rows as
+ *                  kvc_x_row_exponents writes them for this x (so that
+ *                  several compressors of the same hidden states compute
+ *                  them once), or NULL: the call computes them into its
+ *                  workspace. Read only by the KVC_PROJ_F16_SPLIT projection;
+ *                  values that do not belong to x give wrong projections but
+ *                  no invalid access.
  *   batch        : >= 1.   seqlen : >= 0.
  *   workspace    : f32, at least 2 * batch * seqlen * proj elements, and
  *                  with x all kvc_prefill_workspace_floats() elements
@@ -234,10 +245,19 @@ int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch);
  *                  to compute only projections and state).
  *   n_groups     : host, optional; receives seqlen / ratio (0: no entry).
  * Errors: KVC_EINVAL, KVC_EUNSUPPORTED, KVC_ESPACE, KVC_EHIP. */
-int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *x, int64_t batch,
-                       int64_t seqlen, float *workspace, int64_t workspace_floats, float *kv_state,
-                       float *score_state, int64_t state_batch, const kvc_outputs *out,
+int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *x, const int32_t *x_exponents,
+                       int64_t batch, int64_t seqlen, float *workspace, int64_t workspace_floats,
+                       float *kv_state, float *score_state, int64_t state_batch, const kvc_outputs *out,
                        int64_t *n_groups, kvc_stream stream);
+
+/* The scale exponent of each of `rows` rows of f32 hidden states x ([rows][dim],
+ * 16-byte aligned; dim a positive multiple of 32, at most 2^20): the e for
+ * which 2^e brings the row's largest magnitude into [2^14, 2^15) (0 for a
+ * row of zeros or one holding an infinity; NaN elements are passed over),
+ * as the KVC_PROJ_F16_SPLIT projection scales the row before splitting it.
+ * exponents: [rows] int32 (device). Errors: KVC_EINVAL, KVC_EUNSUPPORTED,
+ * KVC_EHIP. */
+int kvc_x_row_exponents(const float *x, int64_t rows, int64_t dim, int32_t *exponents, kvc_stream stream);
 
 /* One decode step: one token per batch row at position start_pos
  * (Compressor listing, forward, decode branch). The token fills slot

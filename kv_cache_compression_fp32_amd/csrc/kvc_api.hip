@@ -25,10 +25,11 @@ int check_common(const kvc_config *cfg) {
   if (cfg->head_dim != 128 && cfg->head_dim != 512) return KVC_EUNSUPPORTED;
   if (cfg->rope_dim < 0 || cfg->rope_dim > cfg->head_dim || cfg->rope_dim % 2 != 0) return KVC_EINVAL;
   if (cfg->x_format != KVC_X_F32 && cfg->x_format != KVC_X_BF16) return KVC_EINVAL;
-  if (cfg->projection != KVC_PROJ_BF16_SPLIT && cfg->projection != KVC_PROJ_F32_MFMA &&
-      cfg->projection != KVC_PROJ_F16_SPLIT)
+  if (cfg->projection != KVC_PROJ_AUTO && cfg->projection != KVC_PROJ_BF16_SPLIT &&
+      cfg->projection != KVC_PROJ_F32_MFMA && cfg->projection != KVC_PROJ_F16_SPLIT)
     return KVC_EINVAL;
-  if (cfg->projection != KVC_PROJ_BF16_SPLIT && cfg->x_format != KVC_X_F32) return KVC_EINVAL;
+  if ((cfg->projection == KVC_PROJ_F32_MFMA || cfg->projection == KVC_PROJ_F16_SPLIT) && cfg->x_format != KVC_X_F32)
+    return KVC_EINVAL;
   return KVC_OK;
 }
 
@@ -49,6 +50,12 @@ int check_ratio1(const kvc_config *cfg) {
 }
 
 bool overlapped(const kvc_config *cfg) { return cfg->ratio == 4; }
+// the projection KVC_PROJ_AUTO stands for: the f16 split for f32 rows, the
+// exact bf16 split for bf16 rows
+int32_t projection_of(const kvc_config *cfg) {
+  if (cfg->projection != KVC_PROJ_AUTO) return cfg->projection;
+  return cfg->x_format == KVC_X_F32 ? KVC_PROJ_F16_SPLIT : KVC_PROJ_BF16_SPLIT;
+}
 int64_t proj_of(const kvc_config *cfg) { return overlapped(cfg) ? 2 * (int64_t)cfg->head_dim : cfg->head_dim; }
 int64_t rows_of(const kvc_config *cfg) { return overlapped(cfg) ? 2 * (int64_t)cfg->ratio : cfg->ratio; }
 
@@ -110,7 +117,7 @@ int64_t split_offset(const kvc_config *cfg, int64_t batch, int64_t seqlen) {
 int64_t round4(int64_t v) { return (v + 3) / 4 * 4; }
 int64_t split_floats(const kvc_config *cfg, int64_t m) {
   if (cfg->dim <= 0) return 0;
-  if (cfg->projection == KVC_PROJ_F16_SPLIT) return 2 * proj_of(cfg) * cfg->dim + 2 * proj_of(cfg) + round4(m);
+  if (projection_of(cfg) == KVC_PROJ_F16_SPLIT) return 2 * proj_of(cfg) * cfg->dim + 2 * proj_of(cfg) + round4(m);
   return 3 * proj_of(cfg) * cfg->dim;
 }
 
@@ -183,10 +190,10 @@ int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch) {
   return (int64_t)splits * 2 * batch * proj_of(cfg);
 }
 
-int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *x, int64_t batch,
-                       int64_t seqlen, float *workspace, int64_t workspace_floats, float *kv_state,
-                       float *score_state, int64_t state_batch, const kvc_outputs *out, int64_t *n_groups,
-                       kvc_stream stream) {
+int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *x, const int32_t *x_exponents,
+                       int64_t batch, int64_t seqlen, float *workspace, int64_t workspace_floats,
+                       float *kv_state, float *score_state, int64_t state_batch, const kvc_outputs *out,
+                       int64_t *n_groups, kvc_stream stream) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if (batch < 1 || seqlen < 0) return KVC_EINVAL;
@@ -199,7 +206,8 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *
   const int64_t m = batch * seqlen;
   const bool x_bf16 = cfg->x_format == KVC_X_BF16;
   // with x the split weights sit after the planes and pooled rows
-  const bool split_proj = x && m > 0 && cfg->projection != KVC_PROJ_F32_MFMA;
+  const int32_t projection = projection_of(cfg);
+  const bool split_proj = x && m > 0 && projection != KVC_PROJ_F32_MFMA;
   const int64_t need = split_proj ? split_offset(cfg, batch, seqlen) + split_floats(cfg, m) : 2 * m * proj;
   if (need > 0 && !workspace) return KVC_EINVAL;
   if (workspace_floats < need) return KVC_ESPACE;
@@ -243,11 +251,11 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *
       g.pool_groups = groups;
       g.pool_hd = cfg->head_dim;
     }
-    if (cfg->projection == KVC_PROJ_F32_MFMA) {
+    if (projection == KVC_PROJ_F32_MFMA) {
       rc = hip_status(fused ? kvc::launch_gemm_pool(g, s) : kvc::launch_gemm(g, kvc::GemmShape::kPrefill, s));
     } else {
       // the weights' parts, in the row order the kernel reads
-      const bool f16 = cfg->projection == KVC_PROJ_F16_SPLIT;
+      const bool f16 = projection == KVC_PROJ_F16_SPLIT;
       float *split_base = workspace + split_offset(cfg, batch, seqlen);
       uint16_t *split = reinterpret_cast<uint16_t *>(split_base);
       int32_t *wexp = reinterpret_cast<int32_t *>(split_base + 2 * proj * cfg->dim);
@@ -269,8 +277,12 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *
       g.bsplit = split;
       if (f16) {
         g.wexp = wexp;
-        g.xexp = xexp;
-        if ((rc = hip_status(kvc::launch_row_exponents(g.a, m, cfg->dim, cfg->dim, xexp, s)))) return rc;
+        if (x_exponents) {
+          g.xexp = x_exponents;
+        } else {
+          g.xexp = xexp;
+          if ((rc = hip_status(kvc::launch_row_exponents(g.a, m, cfg->dim, cfg->dim, xexp, s)))) return rc;
+        }
         rc = hip_status(fused ? kvc::launch_gemm_h3_pool(g, s) : kvc::launch_gemm_h3(g, s));
       } else if (x_bf16) rc = hip_status(fused ? kvc::launch_gemm_x3_pool(g, s) : kvc::launch_gemm_x3(g, s));
       else rc = hip_status(fused ? kvc::launch_gemm_x6_pool(g, s) : kvc::launch_gemm_x6(g, s));
@@ -332,6 +344,14 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *
     if ((rc = hip_status(kvc::launch_state_store(st, s)))) return rc;
   }
   return KVC_OK;
+}
+
+int kvc_x_row_exponents(const float *x, int64_t rows, int64_t dim, int32_t *exponents, kvc_stream stream) {
+  if (rows < 0 || dim <= 0) return KVC_EINVAL;
+  if (dim % 32 != 0 || dim > kMaxDim) return KVC_EUNSUPPORTED;
+  if (rows == 0) return KVC_OK;
+  if (!x || !exponents || !aligned(x)) return KVC_EINVAL;
+  return hip_status(kvc::launch_row_exponents(x, rows, dim, dim, exponents, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const void *x, int64_t batch,

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libkvc.so")
 KVC_OK, KVC_EINVAL, KVC_EUNSUPPORTED, KVC_ESPACE, KVC_EHIP = 0, -1, -2, -3, -4
 KVC_FP4_E4M3_B16, KVC_FP4_E8M0_B32 = 0, 1
 KVC_X_F32, KVC_X_BF16 = 0, 1
-KVC_PROJ_BF16_SPLIT, KVC_PROJ_F32_MFMA, KVC_PROJ_F16_SPLIT = 0, 1, 2
+KVC_PROJ_AUTO, KVC_PROJ_F32_MFMA, KVC_PROJ_F16_SPLIT, KVC_PROJ_BF16_SPLIT = 0, 1, 2, 3
 
 _lib = None
 
@@ -59,9 +59,10 @@ _SIGNATURES = {
     "kvc_state_rows": (_I64, [ctypes.POINTER(_Config)]),
     "kvc_prefill_workspace_floats": (_I64, [ctypes.POINTER(_Config), _I64, _I64]),
     "kvc_decode_workspace_floats": (_I64, [ctypes.POINTER(_Config), _I64]),
-    "compressor_prefill": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), _P, _I64, _I64,
+    "compressor_prefill": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), _P, _P, _I64, _I64,
                                           _P, _I64, _P, _P, _I64, ctypes.POINTER(_Outputs),
                                           ctypes.POINTER(_I64), _P]),
+    "kvc_x_row_exponents": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
     "compressor_decode_step": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), _P, _I64, _I64,
                                               _P, _I64, _P, _P, _I64, ctypes.POINTER(_Outputs),
                                               ctypes.POINTER(ctypes.c_int32), _P]),
@@ -109,7 +110,7 @@ class Config:
     fp4_format: int = KVC_FP4_E4M3_B16
     rope_dim: int = 0
     x_format: int = KVC_X_F32  # KVC_X_BF16: x is the bf16 hidden state
-    projection: int = KVC_PROJ_BF16_SPLIT  # KVC_PROJ_F32_MFMA: the f32 matrix cores; KVC_PROJ_F16_SPLIT: scaled f16 parts
+    projection: int = KVC_PROJ_AUTO  # f16 split for f32 x, exact bf16 split for bf16 x
 
     @property
     def fp4_block(self) -> int:
@@ -213,17 +214,30 @@ def _x_ptr(cfg: Config, x):
 def compressor_prefill(cfg: Config, w: Weights, x: torch.Tensor | None, batch: int, seqlen: int,
                        workspace: torch.Tensor, kv_state: torch.Tensor | None = None,
                        score_state: torch.Tensor | None = None, out: Outputs | None = None,
-                       stream=None) -> int:
-    """Enqueue a prefill; returns the number of groups (seqlen // ratio)."""
+                       stream=None, x_exponents: torch.Tensor | None = None) -> int:
+    """Enqueue a prefill; returns the number of groups (seqlen // ratio).
+    x_exponents: int32 [batch * seqlen] from x_row_exponents of the same x,
+    or None (the call computes them)."""
     n = ctypes.c_int64(0)
     state_batch = kv_state.shape[0] if kv_state is not None else 0
+    if x_exponents is not None and x_exponents.numel() < batch * seqlen:
+        raise ValueError("x_exponents holds fewer than batch * seqlen values")
     rc = lib().compressor_prefill(
-        ctypes.byref(cfg.c()), ctypes.byref(w.c()), _x_ptr(cfg, x), batch, seqlen,
+        ctypes.byref(cfg.c()), ctypes.byref(w.c()), _x_ptr(cfg, x), _ptr(x_exponents, torch.int32, "x_exponents"),
+        batch, seqlen,
         _ptr(workspace, torch.float32, "workspace"), workspace.numel(),
         _ptr(kv_state, torch.float32, "kv_state"), _ptr(score_state, torch.float32, "score_state"),
         state_batch, ctypes.byref(out.c()) if out is not None else None, ctypes.byref(n), _stream(stream))
     _check(rc, "compressor_prefill")
     return n.value
+
+
+def x_row_exponents(x: torch.Tensor, rows: int, dim: int, exponents: torch.Tensor, stream=None) -> None:
+    """Enqueue the scale exponents of `rows` f32 rows of x into int32 `exponents`."""
+    if exponents.numel() < rows or x.numel() < rows * dim:
+        raise ValueError("x or exponents smaller than rows x dim / rows")
+    _check(lib().kvc_x_row_exponents(_ptr(x, torch.float32, "x"), rows, dim, _ptr(exponents, torch.int32, "exponents"),
+                                     _stream(stream)), "kvc_x_row_exponents")
 
 
 def compressor_decode_step(cfg: Config, w: Weights, x: torch.Tensor | None, batch: int, start_pos: int,

@@ -50,21 +50,24 @@ def test_sizes(ratio, hd, proj, rows):
     assert kvc.kvc_proj_width(cfg) == proj
     assert kvc.kvc_state_rows(cfg) == rows
     # the two projection planes, at ratio 4 the pooled entries of the fused
-    # path, then the weights' three bf16 parts, [2 proj][3][dim]
+    # path, then the split weights: by default (f32 x: the f16 split) two f16
+    # parts [2 proj][2][dim], the exponents of the 2 proj weight rows and of
+    # the 300 x rows
     pooled = 3 * (100 // ratio) * hd if ratio == 4 else 0
-    parts = 2 * proj * 3 * 4096 // 2
-    assert kvc.kvc_prefill_workspace_floats(cfg, 3, 100) == 2 * 3 * 100 * proj + pooled + parts
+    f16_parts = 2 * proj * 4096 + 2 * proj + 300
+    assert kvc.kvc_prefill_workspace_floats(cfg, 3, 100) == 2 * 3 * 100 * proj + pooled + f16_parts
+    cfgh = kvc.Config(ratio, hd, 4096, projection=kvc.KVC_PROJ_F16_SPLIT)
+    assert kvc.kvc_prefill_workspace_floats(cfgh, 3, 100) == 2 * 3 * 100 * proj + pooled + f16_parts
     ws = kvc.kvc_decode_workspace_floats(cfg, 64)
     assert ws >= 2 * 64 * proj and ws % (2 * 64 * proj) == 0
-    # the same for bf16 hidden states
+    # bf16 hidden states (and the bf16 split of f32 x): the weights' three
+    # bf16 parts, [2 proj][3][dim]
+    parts = 2 * proj * 3 * 4096 // 2
     cfg16 = kvc.Config(ratio, hd, 4096, x_format=kvc.KVC_X_BF16)
     assert kvc.kvc_prefill_workspace_floats(cfg16, 3, 100) == 2 * 3 * 100 * proj + pooled + parts
     assert kvc.kvc_decode_workspace_floats(cfg16, 64) == ws
-    # the scaled f16 split: two f16 parts [2 proj][2][dim], the exponents of
-    # the 2 proj weight rows and of the 300 x rows
-    cfgh = kvc.Config(ratio, hd, 4096, projection=kvc.KVC_PROJ_F16_SPLIT)
-    assert kvc.kvc_prefill_workspace_floats(cfgh, 3, 100) == 2 * 3 * 100 * proj + pooled + 2 * proj * 4096 + \
-        2 * proj + 300
+    cfgb = kvc.Config(ratio, hd, 4096, projection=kvc.KVC_PROJ_BF16_SPLIT)
+    assert kvc.kvc_prefill_workspace_floats(cfgb, 3, 100) == 2 * 3 * 100 * proj + pooled + parts
 
 
 def test_decode_workspace_of_the_b64_ratio4_step():
@@ -83,7 +86,7 @@ def test_decode_workspace_of_the_b64_ratio4_step():
     (kvc.Config(4, 512, 4096, eps=-1.0), kvc.KVC_EINVAL),
     (kvc.Config(4, 512, 4096, eps=float("nan")), kvc.KVC_EINVAL),
     (kvc.Config(4, 512, 4096, x_format=2), kvc.KVC_EINVAL),
-    (kvc.Config(4, 512, 4096, projection=3), kvc.KVC_EINVAL),
+    (kvc.Config(4, 512, 4096, projection=4), kvc.KVC_EINVAL),
     # the f32 matrix cores and the f16 split read f32 rows only
     (kvc.Config(4, 512, 4096, x_format=kvc.KVC_X_BF16, projection=kvc.KVC_PROJ_F32_MFMA), kvc.KVC_EINVAL),
     (kvc.Config(4, 512, 4096, x_format=kvc.KVC_X_BF16, projection=kvc.KVC_PROJ_F16_SPLIT), kvc.KVC_EINVAL),
@@ -101,7 +104,7 @@ def _prefill_raw(cfg, **kw):
     n = ctypes.c_int64(-7)
     w = args["w"]
     rc = lib.compressor_prefill(ctypes.byref(cfg.c()), ctypes.byref(w) if w is not None else None,
-                                args["x"], args["batch"], args["seqlen"], args["ws"], args["ws_n"],
+                                args["x"], None, args["batch"], args["seqlen"], args["ws"], args["ws_n"],
                                 args["kv"], args["sc"], args["sb"], args["out"], ctypes.byref(n), None)
     return rc, n.value
 
@@ -135,7 +138,7 @@ def test_prefill_argument_errors_return_before_enqueueing():
 def test_projection_needs_room_for_the_split_weights(x_format):
     fake = 0x100000  # never dereferenced: every case below fails its host checks
     w = kvc._Weights(fake, fake, None, None)
-    cfg = kvc.Config(4, 512, 4096, x_format=x_format)
+    cfg = kvc.Config(4, 512, 4096, x_format=x_format, projection=kvc.KVC_PROJ_BF16_SPLIT)
     full = kvc.kvc_prefill_workspace_floats(cfg, 1, 8)
     planes = 2 * 8 * 1024 + 2 * 512   # the projection planes and the pooled rows
     assert full == planes + 2 * 1024 * 3 * 4096 // 2
@@ -157,6 +160,18 @@ def test_f16_split_projection_needs_room_for_parts_and_exponents():
     assert full == planes + 2 * 1024 * 4096 + 2 * 1024 + 8
     assert _prefill_raw(cfg, x=fake, w=w, ws=fake, ws_n=full - 1)[0] == kvc.KVC_ESPACE
     assert _prefill_raw(cfg, x=fake, w=w, ws=fake, ws_n=planes + 2 * 1024 * 4096)[0] == kvc.KVC_ESPACE
+
+
+def test_x_row_exponents_argument_errors_return_before_enqueueing():
+    lib = kvc.lib()
+    fake = 0x100000  # never dereferenced: every case below fails its host checks, or has no rows
+    assert lib.kvc_x_row_exponents(fake, -1, 4096, fake, None) == kvc.KVC_EINVAL
+    assert lib.kvc_x_row_exponents(fake, 8, 0, fake, None) == kvc.KVC_EINVAL
+    assert lib.kvc_x_row_exponents(fake, 8, 100, fake, None) == kvc.KVC_EUNSUPPORTED
+    assert lib.kvc_x_row_exponents(None, 8, 4096, fake, None) == kvc.KVC_EINVAL
+    assert lib.kvc_x_row_exponents(fake, 8, 4096, None, None) == kvc.KVC_EINVAL
+    assert lib.kvc_x_row_exponents(fake + 4, 8, 4096, fake, None) == kvc.KVC_EINVAL
+    assert lib.kvc_x_row_exponents(None, 0, 4096, None, None) == kvc.KVC_OK
 
 
 def test_f32_matrix_core_projection_needs_only_the_planes():

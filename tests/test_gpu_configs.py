@@ -21,7 +21,7 @@ def _gpu():
     kvc.lib()
 
 
-def _cfg(wl, comp, x_format=kvc.KVC_X_F32, projection=kvc.KVC_PROJ_BF16_SPLIT):
+def _cfg(wl, comp, x_format=kvc.KVC_X_F32, projection=kvc.KVC_PROJ_AUTO):
     return kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps, x_format=x_format, projection=projection)
 
 
@@ -59,8 +59,9 @@ def _check_sampled(wl, comp, w, got, entries, batch_rows, fp4="e4m3", x_bf16=Fal
                 ref.setdefault(k, []).append(v)
     ref = {k: np.stack(v) for k, v in ref.items()}
     sel = lambda a: np.stack([a[b, j] for b in batch_rows for j in entries])  # noqa: E731
-    check_pooled(sel(got["pooled"]), ref["pooled"])
-    check_latent(sel(got["latent"]), sel(got["pooled"]), ref["latent"], ref["pooled"], eps=wl.eps)
+    worst = check_pooled(sel(got["pooled"]), ref["pooled"])
+    flips, total = check_latent(sel(got["latent"]), sel(got["pooled"]), ref["latent"], ref["pooled"], eps=wl.eps)
+    note(f"    pooled worst {worst:.2e} of the entry's scale; latent bf16 flips {flips} of {total}")
     if comp.quantize or fp4 == "e8m0":
         check_fp4(sel(got["codes"]), sel(got["scales"]), sel(got["latent"]), ref["codes"], ref["scales"],
                   ref["latent"], sel(got["dequant"]), e8m0=fp4 == "e8m0")

@@ -170,9 +170,10 @@ GEMM_CASES = [
 ]
 
 
-# (x format, projection): f32 rows split on the bf16 matrix cores (the
-# default), f32 rows on the f32 matrix cores, f32 rows as scaled f16 parts on
-# the f16 matrix cores, bf16 rows on the bf16 matrix cores
+# (x format, projection): f32 rows split on the bf16 matrix cores, f32 rows
+# on the f32 matrix cores, f32 rows as scaled f16 parts on the f16 matrix
+# cores (the default for f32 rows), bf16 rows on the bf16 matrix cores (the
+# default for bf16 rows)
 PROJ_PATHS = [(kvc.KVC_X_F32, kvc.KVC_PROJ_BF16_SPLIT), (kvc.KVC_X_F32, kvc.KVC_PROJ_F32_MFMA),
               (kvc.KVC_X_F32, kvc.KVC_PROJ_F16_SPLIT), (kvc.KVC_X_BF16, kvc.KVC_PROJ_BF16_SPLIT)]
 
@@ -599,7 +600,7 @@ def test_one_hot_rows_reproduce_the_f32_weights_exactly(ratio, hd, dim, batch, s
     note(f"one-hot x ratio={ratio} hd={hd} dim={dim} batch={batch} seqlen={seqlen} x_format={x_format}")
     from gpu_util import weights
     rng = np.random.default_rng(ratio + dim + seqlen)
-    cfg = kvc.Config(ratio, hd, dim, x_format=x_format)
+    cfg = kvc.Config(ratio, hd, dim, x_format=x_format, projection=kvc.KVC_PROJ_BF16_SPLIT)
     proj = kvc.kvc_proj_width(cfg)
     m = batch * seqlen
     x = np.zeros((m, dim), np.float32)
@@ -644,7 +645,7 @@ def test_f32_x_split_gives_faithfully_rounded_products(ratio, hd, dim, batch, se
     note(f"f32 x split ratio={ratio} hd={hd} dim={dim} batch={batch} seqlen={seqlen}")
     from gpu_util import bf16_inputs, weights
     rng = np.random.default_rng(7 + ratio + dim)
-    cfg = kvc.Config(ratio, hd, dim)
+    cfg = kvc.Config(ratio, hd, dim, projection=kvc.KVC_PROJ_BF16_SPLIT)
     proj = kvc.kvc_proj_width(cfg)
     m = batch * seqlen
     v = (rng.standard_normal(m) * np.exp2(rng.integers(-30, 30, m))).astype(np.float32)
@@ -805,3 +806,41 @@ def test_f16_split_of_f32_rows_is_the_two_part_sum(ratio, hd, dim, batch, seqlen
         want = (xs[:, None] * w[name].T[col]).astype(np.float32) + np.float32(0.0)  # exact: times a power of two
         bad = got.view(np.uint32) != want.view(np.uint32)
         assert not bad.any(), f"{name}: {bad.sum()} differ, e.g. {want[bad][:4]} -> {got[bad][:4]}"
+
+
+@pytest.mark.parametrize("hd,seqlen,dim", [(128, 300, 256), (512, 16384 + 7, 64)])
+def test_shared_x_exponents_give_the_same_outputs(hd, seqlen, dim):
+    """kvc_x_row_exponents gives 15 - E for a row whose largest magnitude is
+    in [2^(E-1), 2^E) (0 for a zero row), and a prefill handed those
+    exponents writes the same bits as one that computes its own (the plain
+    kernel at 300 tokens, the pooling kernel at 16391)."""
+    note(f"shared x exponents hd={hd} seqlen={seqlen} dim={dim}")
+    from gpu_util import weights
+    rng = np.random.default_rng(hd + seqlen)
+    cfg = kvc.Config(4, hd, dim, projection=kvc.KVC_PROJ_F16_SPLIT)
+    proj = kvc.kvc_proj_width(cfg)
+    x = (rng.standard_normal((seqlen, dim)) * np.exp2(rng.integers(-20, 20, (seqlen, 1)))).astype(np.float32)
+    x[1] = 0.0
+    w = {"wkv": (rng.standard_normal((proj, dim)) * 0.05).astype(np.float32),
+         "wgate": (rng.standard_normal((proj, dim)) * 0.05).astype(np.float32),
+         "ape": (rng.standard_normal((4, proj)) * 0.1).astype(np.float32)}
+    xd = dev(x[None])
+    exps = torch.empty(seqlen, dtype=torch.int32, device="cuda")
+    kvc.x_row_exponents(xd, seqlen, dim, exps)
+    torch.cuda.synchronize()
+    amax = np.abs(x).max(axis=1).astype(np.float64)
+    want = np.where(amax > 0, 15 - np.frexp(np.where(amax > 0, amax, 1.0))[1], 0)
+    assert np.array_equal(exps.cpu().numpy(), want)
+    groups = seqlen // 4
+    res = []
+    for given in (None, exps):
+        ws = torch.empty(kvc.kvc_prefill_workspace_floats(cfg, 1, seqlen), dtype=torch.float32, device="cuda")
+        st = kvc.new_state(cfg, 1)
+        out = kvc.new_outputs(cfg, 1, groups, latent=True, pooled=True, fp4=True)
+        kvc.compressor_prefill(cfg, weights(w), xd, 1, seqlen, ws, st[0], st[1], out, x_exponents=given)
+        torch.cuda.synchronize()
+        res.append((outputs_to_host(out), st[0].cpu().numpy(), st[1].cpu().numpy()))
+    (a, ka, sa), (b, kb, sb) = res
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+    assert np.array_equal(ka.view(np.uint32), kb.view(np.uint32)) and np.array_equal(sa.view(np.uint32), sb.view(np.uint32))
