@@ -206,10 +206,15 @@ __global__ __launch_bounds__(256) void row_exponents_kernel(const float *x, int6
   if (row >= m) return;
   const float *p = x + row * lda;
   float amax = 0.0f;
-#pragma unroll 4
-  for (int64_t c = 4 * lane; c < k; c += 256) {
-    const float4 v = *reinterpret_cast<const float4 *>(p + c);
-    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  // 16 loads of 16 bytes in flight per lane (a 4096-wide row in one round)
+  for (int64_t c0 = 4 * lane; c0 < k; c0 += 256 * 16) {
+    float4 v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      v[u] = c0 + 256 * u < k ? *reinterpret_cast<const float4 *>(p + c0 + 256 * u) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));

@@ -126,6 +126,17 @@ __device__ __forceinline__ void pool_epilogue(const GemmArgs &g, f4 (&acc)[WM / 
   const int64_t gpr = seqlen / 4;  // 4-token blocks per batch row (batch > 1 needs seqlen % 4 == 0)
   // the state's source rows: from the last complete block of each batch row on
   const int64_t state_from = groups > 0 ? 4 * (groups - 1) : 0;
+  // the score bias of the lane's features: token position mod 4 is r
+  // (blocks start at multiples of 4), the same for every row fragment
+  float biasA[4][FJ], biasB[4][FJ];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int jj = 0; jj < FJ; ++jj) {
+      const int64_t f = f0 + F * wn + 16 * jj + c;
+      biasA[r][jj] = g.bias1 ? g.bias1[r * g.ldc + f] : 0.0f;
+      biasB[r][jj] = g.bias1 ? g.bias1[r * g.ldc + hd + f] : 0.0f;
+    }
   __syncthreads();  // every wavefront is done with the stage buffers
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -137,9 +148,9 @@ __device__ __forceinline__ void pool_epilogue(const GemmArgs &g, f4 (&acc)[WM / 
       for (int r = 0; r < 4; ++r) {
         const int rl = 16 * i + 4 * g4 + r;  // row within the wavefront
         const int64_t row = m0 + wm * WM + rl;
-        if (g.bias1) {  // token position mod 4 is r: blocks start at multiples of 4
-          sA[r] = sA[r] + g.bias1[r * g.ldc + f];
-          sB[r] = sB[r] + g.bias1[r * g.ldc + hd + f];
+        if (g.bias1) {
+          sA[r] = sA[r] + biasA[r][jj];
+          sB[r] = sB[r] + biasB[r][jj];
         }
         if (row < g.m) {
           const int64_t tpos = g.pool_batch == 1 ? row : row % seqlen;
