@@ -745,6 +745,8 @@ def test_f16_split_rows_of_any_scale(fused):
     xs, ws_ = (4, 10) if fused else (60, 60)
     x = (rng.standard_normal((m, dim)) * np.exp2(rng.integers(-xs, xs, (m, 1)))).astype(np.float32)
     x[3] = 0.0   # a row of zeros keeps exponent 0
+    if not fused:  # a row of f32 subnormals: exponent above 127, results scaled back into the subnormal range
+        x[5] = (rng.standard_normal(dim) * 2.0 ** -135).astype(np.float32)
     w = {"wkv": (rng.standard_normal((proj, dim)) * np.exp2(rng.integers(-ws_, ws_, (proj, 1)))).astype(np.float32),
          "wgate": (rng.standard_normal((proj, dim)) * 0.02).astype(np.float32),
          "ape": (rng.standard_normal((ratio, proj)) * 0.1).astype(np.float32)}
@@ -821,6 +823,7 @@ def test_shared_x_exponents_give_the_same_outputs(hd, seqlen, dim):
     proj = kvc.kvc_proj_width(cfg)
     x = (rng.standard_normal((seqlen, dim)) * np.exp2(rng.integers(-20, 20, (seqlen, 1)))).astype(np.float32)
     x[1] = 0.0
+    x[2] = (rng.standard_normal(dim) * 2.0 ** -140).astype(np.float32)   # f32 subnormals
     w = {"wkv": (rng.standard_normal((proj, dim)) * 0.05).astype(np.float32),
          "wgate": (rng.standard_normal((proj, dim)) * 0.05).astype(np.float32),
          "ape": (rng.standard_normal((4, proj)) * 0.1).astype(np.float32)}
