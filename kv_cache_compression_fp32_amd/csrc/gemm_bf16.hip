@@ -1,4 +1,6 @@
-// bf16 matrix-core GEMMs of the compressor's projections (gfx950, wave64).
+// 16-bit matrix-core GEMMs of the compressor's projections (gfx950, wave64):
+// the f32 products x . w^T ("Module compress", Functions, linear_f32) from
+// parts of the f32 operands, and the ratio-1 bf16 projection.
 //
 // 1. Prefill projection for bf16 hidden states: C = x . w^T with x bf16 and
 //    w f32, computed on the bf16 matrix cores without rounding anything but
@@ -24,6 +26,12 @@
 // 2. The ratio-1 projection (bf16 x times bf16 wkv, f32 accumulation; the
 //    Compressor listing's __init__ and ratio-1 branch of forward; "Module
 //    compress", CompressorWeights): the same kernel with plain bf16 weights.
+// 3. Prefill projection for f32 hidden states: gemm_x6_kernel, with x split
+//    in registers, either like the weights into three bf16 parts (six part
+//    products) or, by default, into two f16 parts of the row scaled by a
+//    power of two, against the weights' two f16 parts
+//    (split_weights_f16_kernel, row_exponents_kernel; three part products,
+//    the sums scaled back exactly).
 //
 // gemm_mc_kernel: BM x BN workgroup tile, WM x WN per wavefront, two LDS
 // stages of 64 KiB: with the split weights, one 32-k slice of the x tile
