@@ -847,3 +847,32 @@ def test_shared_x_exponents_give_the_same_outputs(hd, seqlen, dim):
     for k in a:
         assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
     assert np.array_equal(ka.view(np.uint32), kb.view(np.uint32)) and np.array_equal(sa.view(np.uint32), sb.view(np.uint32))
+
+
+@pytest.mark.parametrize("batch,dim,hd", [(70, 2048, 128), (5, 4096, 512), (33, 1536, 512)])
+def test_decode_projection_tiles(batch, dim, hd):
+    """Decode from f32 rows through the staged projection kernel: batches that
+    are not a multiple of its 64-row tile (70: two row tiles; 5; 33), split
+    ranges of 2, 8 and 3 stages of 128 k; the emitted entries and the carried
+    state against the oracle over the same tokens."""
+    note(f"decode projection tiles batch={batch} dim={dim} hd={hd}")
+    from gpu_util import weights
+    rng = np.random.default_rng(batch + dim + hd)
+    cfg = kvc.Config(4, hd, dim)
+    proj = kvc.kvc_proj_width(cfg)
+    steps = 6
+    x = rng.standard_normal((batch, steps, dim), dtype=np.float32)
+    w = {"wkv": rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.02),
+         "wgate": rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.02),
+         "ape": rng.standard_normal((4, proj), dtype=np.float32) * np.float32(0.1)}
+    dec = _decode_gpu(cfg, weights(w), batch, xs=x)
+    st = oracle.State(oracle_cfg(cfg), batch)
+    ref = oracle.prefill(oracle_cfg(cfg), oracle_weights(w), st, x=x, quantize=True)
+    check_pooled(dec["pooled"], ref["pooled"])
+    check_latent(dec["latent"], dec["pooled"], ref["latent"], ref["pooled"])
+    # the carry after 6 tokens: the previous block (rows 0..3) and 2 current rows
+    live = _live_rows(4, steps)
+    fin = np.isfinite(st.score[:, live])
+    assert np.array_equal(np.isfinite(dec["state_sc"][:, live]), fin)
+    check_pooled(dec["state_kv"][:, live], st.kv[:, live], "state kv")
+    check_pooled(np.where(fin, dec["state_sc"][:, live], 0), np.where(fin, st.score[:, live], 0), "state score")
