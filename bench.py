@@ -406,7 +406,7 @@ def main():
                     help="first run one plain copy kernel (read + write) of this many MiB")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
+        print(f"bench.py runs on one GPU: the library has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
