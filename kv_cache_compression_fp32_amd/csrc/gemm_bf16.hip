@@ -92,6 +92,21 @@ __device__ __forceinline__ void wait_vm0_seen() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// vmcnt(1): every load but the last one issued has landed (loads land in
+// the order they were issued)
+__device__ __forceinline__ void wait_vm1_seen() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0F71);  // vmcnt(1)
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// f32 x tiles: the x lines of the stage after the one being loaded are
+// touched too (one 4-byte load per 128-byte line, landing in a scratch LDS
+// row), so that they are on their way to L2 one step before the stage load
+// asks for them; with two LDS stages the stage load itself has only one
+// multiply phase to arrive. Stages ahead of the stage load (0: off).
+constexpr int kXPrefetch = 1;
+
 constexpr int kBK3 = 32;  // k per LDS stage
 // the pooling kernel's wavefront: 128 rows x 64 columns, the 64 columns the
 // four 16-wide segments (kvA, kvB, scA, scB) of 16 features
@@ -523,6 +538,14 @@ __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
     }
   };
 
+  // L2 prefetch of a later stage's x lines: loading lane (lw, l) touches row
+  // 64 lw + l (full row tiles only); the 4 bytes land in a scratch LDS row
+  __shared__ __attribute__((aligned(16))) uint32_t pf_sink[NL][64];
+  const uint32_t pf_voff = (uint32_t)((64 * lw + lane) * g.lda * 4);
+  auto prefetch = [&](int kt) {
+    buffer_load_lds(a_rsrc, (lds_u32 *)(&pf_sink[lw][0]), 4, (int32_t)pf_voff, (int32_t)(kt * BK * 4), 0, 0);
+  };
+
   f4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -603,16 +626,26 @@ __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
   // every wavefront drains its loads here (the first stage, the exponents),
   // so that no wait for them lands inside the loop
   wait_vm0_seen();
+  if (kXPrefetch > 0 && loader && full_tile) {
+    for (int s = 2; s <= kXPrefetch && s < kt_count; ++s) prefetch(s);
+  }
   phase_barrier();
   if (!loader) phase_barrier();  // group 4..7 runs one phase behind
   for (int kt = 0; kt < kt_count; ++kt) {
     const int st = kt & 1;
     reads(st);
     if (loader && kt + 1 < kt_count) issue(kt + 1, st ^ 1);  // after the stage's last LDS read
+    // the line touch of stage kt + 1 + kXPrefetch goes after the stage load,
+    // so that waiting for all loads but the last one covers the stage
+    const bool pf = kXPrefetch > 0 && loader && full_tile && kt + 1 + kXPrefetch < kt_count;
+    if (pf) prefetch(kt + 1 + kXPrefetch);
     wait_lgkm0();
     phase_barrier();
     mfmas();
-    if (loader) wait_vm0_seen();
+    if (loader) {
+      if (pf) wait_vm1_seen();  // the stage load has landed, the line touch may still be in flight
+      else wait_vm0_seen();
+    }
     phase_barrier();
   }
   if (loader) phase_barrier();  // the same number of barriers for every wavefront
