@@ -331,6 +331,20 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_mc_kernel(GemmArgs g) {
     }
   };
 
+  // L2 prefetch of a later stage's x lines (as in gemm_x6_kernel): loading
+  // lane (lw, l) touches row 64 lw + l of a full row tile. A row's stage is
+  // KPS bf16 values; with 64 of them two stages share a 128-byte line, which
+  // is then touched on even stages only.
+  static_assert(KPS * 2 == 64 || KPS * 2 == 128, "x bytes per row and stage");
+  static_assert(BM == 64 * NL, "one tile row per loading lane");
+  constexpr int PF_EVERY = 128 / (KPS * 2);
+  const bool full_tile = a_rows == BM;
+  __shared__ __attribute__((aligned(16))) uint32_t pf_sink[NL][64];
+  const uint32_t pf_voff = (uint32_t)((64 * lw + lane) * g.lda * 2);
+  auto prefetch = [&](int kt) {
+    buffer_load_lds(a_rsrc, (lds_u32 *)(&pf_sink[lw][0]), 4, (int32_t)pf_voff, (int32_t)(kt * KPS * 2), 0, 0);
+  };
+
   f4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -375,10 +389,16 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_mc_kernel(GemmArgs g) {
     const int st = kt & 1;
     reads(st);
     if (loader && kt + 1 < kt_count) issue(kt + 1, st ^ 1);  // after the stage's last LDS read
+    const int pf_stage = kt + 1 + kXPrefetch;
+    const bool pf = kXPrefetch > 0 && loader && full_tile && pf_stage < kt_count && pf_stage % PF_EVERY == 0;
+    if (pf) prefetch(pf_stage);
     wait_lgkm0();  // this stage's reads are done before its buffer can be reloaded
     phase_barrier();
     mfmas();
-    if (loader) wait_vm0_seen();  // the next stage has landed before this group reads it
+    if (loader) {  // the next stage has landed before this group reads it
+      if (pf) wait_vm1_seen();  // (the line touch may still be in flight)
+      else wait_vm0_seen();
+    }
     phase_barrier();
   }
   if (loader) phase_barrier();  // the same number of barriers for every wavefront
