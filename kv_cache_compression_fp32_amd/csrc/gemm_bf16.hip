@@ -387,11 +387,16 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_mc_kernel(GemmArgs g) {
   if (!loader) phase_barrier();  // group 4..7 runs one phase behind
   for (int kt = 0; kt < kt_count; ++kt) {
     const int st = kt & 1;
-    reads(st);
-    if (loader && kt + 1 < kt_count) issue(kt + 1, st ^ 1);  // after the stage's last LDS read
+    // the stage load may go out before this phase's LDS reads (as in
+    // gemm_x6_kernel); only the pooling instance does so, the others would
+    // get a wait for every load in flight before their first LDS read
+    constexpr bool kLoadFirst = POOL;
+    if (!kLoadFirst) reads(st);
+    if (loader && kt + 1 < kt_count) issue(kt + 1, st ^ 1);
     const int pf_stage = kt + 1 + kXPrefetch;
     const bool pf = kXPrefetch > 0 && loader && full_tile && pf_stage < kt_count && pf_stage % PF_EVERY == 0;
     if (pf) prefetch(pf_stage);
+    if (kLoadFirst) reads(st);
     wait_lgkm0();  // this stage's reads are done before its buffer can be reloaded
     phase_barrier();
     mfmas();
@@ -653,12 +658,20 @@ __global__ __launch_bounds__(512, 1) void gemm_x6_kernel(GemmArgs g) {
   if (!loader) phase_barrier();  // group 4..7 runs one phase behind
   for (int kt = 0; kt < kt_count; ++kt) {
     const int st = kt & 1;
-    reads(st);
-    if (loader && kt + 1 < kt_count) issue(kt + 1, st ^ 1);  // after the stage's last LDS read
+    // The stage load may go out before this phase's LDS reads: its buffer
+    // was last read before the previous phase barrier (the other group's
+    // reads of it end before the barrier that ends this group's multiply
+    // phase). The f16 256 x 256 instances do so; in the others the compiler
+    // then waits for every load in flight before the first LDS read (it
+    // cannot tell the stage buffers apart), so those read first.
+    constexpr bool kLoadFirst = F16 && BN == 256;
+    if (!kLoadFirst) reads(st);
+    if (loader && kt + 1 < kt_count) issue(kt + 1, st ^ 1);
     // the line touch of stage kt + 1 + kXPrefetch goes after the stage load,
     // so that waiting for all loads but the last one covers the stage
     const bool pf = kXPrefetch > 0 && loader && full_tile && kt + 1 + kXPrefetch < kt_count;
     if (pf) prefetch(kt + 1 + kXPrefetch);
+    if (kLoadFirst) reads(st);
     wait_lgkm0();
     phase_barrier();
     mfmas();
