@@ -409,7 +409,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_mc_kernel(GemmArgs g) {
   if (loader) phase_barrier();  // the same number of barriers for every wavefront
 
   if constexpr (POOL) {
-    pool_epilogue<WM, WN>(g, acc, smem, m0, 64 * nt, wm, wn, lane);
+    pool_epilogue<WM, WN, true>(g, acc, smem, m0, 64 * nt, wm, wn, lane);
   } else {
     store_tile<FM, FN>(g, acc, second ? g.c1 : g.c0, second ? g.bias1 : nullptr, m0 + wm * WM, n0 + wn * WN,
                        lane);
