@@ -6,26 +6,22 @@ One step is one pass of the whole path over one batch: for the default
 workload (ratio-4 prefill of 65536 tokens, hidden 4096) that is the 512-wide
 compressor (f32 projections, pooling + RMSNorm + fp4 cache codes) and the
 128-wide indexer compressor (projections, pooling + RMSNorm, bf16 latent),
-with the hidden states resident in HBM: x f32 [1, 65536, 4096] ~ N(0, 1).
-The projections are f32 products on the f16 matrix cores by default (each
-row of x and each weight row scaled by a power of two and split into two f16
-parts, three part products summed in f32; the step computes x's row
-exponents once for both compressors); --projection bf16-split (six bf16 part
-products) and f32-mfma (the f32 matrix cores) select the others. Beside the
-headline (`workloads`) the same step on the other projection paths, and from
-the model's bf16 hidden states (the bf16 rounding of the same draws as bf16
-rows: exact products from the weights' three parts; --x-format bf16 makes
-that the headline). Prints one JSON line.
+with the hidden states resident in HBM: x f32 [1, 65536, 4096] ~ N(0, 1). The
+projections run on the f32 matrix cores (the library's default for f32 x).
+Beside the headline (`workloads`): the same step on the library's opt-in
+emulations of the f32 products on 16-bit matrix cores (each with its own
+dtype label), from the model's bf16 hidden states, the other prefill
+workloads, the decode stream, the standalone quantisers and the ratio-1
+compressor. Prints one JSON line.
 
-Kernel durations are measured with HIP events on the launch stream around
-repeated launches of each kernel alone (the same library calls with the other
-stages switched off through their arguments: no outputs = projection only,
-which with a split projection is the weight split (under 1% of it) and the
-GEMM; projections given = pooling only). The roofline object reports the
-dominant kernel (the 512-wide projection GEMM, matrix-core bound: the f16 or
-bf16 part products against the 16-bit matrix-core peak, with the
-f32-equivalent rate beside it; the f32 matrix cores against the fp32 peak);
-`pool` reports the pooling kernel against HBM bandwidth.
+Timing: HIP events on the launch stream. Inside the timed steps the bench
+records an event before and after each compressor call, and the library
+records a pair right around its projection kernel (kvc_time_next_projection),
+so the dominant kernel's duration in the roofline is that of the kernel the
+step runs, measured live; the time before it (the split weights of an
+emulation) and after it (the pooling epilogue kernels and the state store)
+is reported per compressor. Reference launches of single stages (the plain
+projection, the pooling of given projections) are timed before the warmup.
 """
 from __future__ import annotations
 
@@ -33,6 +29,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -44,21 +41,34 @@ sys.path.insert(0, ROOT)
 METRIC = "compressed KV entries/sec + achieved HBM GB/s, ratio-4 prefill N=65536"
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
-PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix
+PEAK_16BIT_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 / f16 matrix
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_SOURCE = ("profiles/traffic.json: rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, of this benchmark's own "
+                  "command, each scaled by the same counter on a 1 GiB copy kernel; null once the kernel's "
+                  "sources differ from those the counters were taken on")
+CSRC = "kv_cache_compression_fp32_amd/csrc/"
 # the sources each counted kernel is built from (the traffic figures turn
 # null as soon as any of them changes)
 KERNEL_SOURCES = {
-    "gemm": ["kv_cache_compression_fp32_amd/csrc/gemm_common.h", "kv_cache_compression_fp32_amd/csrc/gemm_f32_kernel.h",
-             "kv_cache_compression_fp32_amd/csrc/gemm_f32.hip", "kv_cache_compression_fp32_amd/csrc/kvc_device.h",
-             "kv_cache_compression_fp32_amd/csrc/gemm_epilogue.h"],
-    "gemm_x6": ["kv_cache_compression_fp32_amd/csrc/gemm_common.h", "kv_cache_compression_fp32_amd/csrc/gemm_bf16.hip",
-                "kv_cache_compression_fp32_amd/csrc/kvc_device.h", "kv_cache_compression_fp32_amd/csrc/gemm_epilogue.h"],
-    "gemm_x3": ["kv_cache_compression_fp32_amd/csrc/gemm_common.h", "kv_cache_compression_fp32_amd/csrc/gemm_bf16.hip",
-                "kv_cache_compression_fp32_amd/csrc/kvc_device.h", "kv_cache_compression_fp32_amd/csrc/gemm_epilogue.h"],
-    "gemm_h3": ["kv_cache_compression_fp32_amd/csrc/gemm_common.h", "kv_cache_compression_fp32_amd/csrc/gemm_bf16.hip",
-                "kv_cache_compression_fp32_amd/csrc/kvc_device.h", "kv_cache_compression_fp32_amd/csrc/gemm_epilogue.h"],
-    "pool": ["kv_cache_compression_fp32_amd/csrc/pool.hip", "kv_cache_compression_fp32_amd/csrc/kvc_device.h"],
+    "gemm_f32": [CSRC + f for f in ("gemm_common.h", "gemm_f32_kernel.h", "gemm_f32.hip", "kvc_device.h",
+                                    "gemm_epilogue.h", "kvc_launch.h")],
+    "decode_f32": [CSRC + f for f in ("gemm_common.h", "decode_f32.hip", "kvc_launch.h")],
+    "pool": [CSRC + f for f in ("pool.hip", "kvc_device.h", "kvc_launch.h")],
+}
+
+# projection paths: (x format, projection, dtype label, description)
+PATHS = {
+    "f32-mfma": ("f32", "f32-mfma", "f32", "f32 rows, N(0,1); f32 matrix cores (the library's default)"),
+    "f16-split": ("f32", "f16-split", "f16x3-split",
+                  "f32 rows, N(0,1); opt-in emulation: rows of x and of the weights scaled by powers of two and "
+                  "split into two f16 parts, three part products on the f16 matrix cores, f32 accumulation"),
+    "bf16-split": ("f32", "bf16-split", "bf16x6-split",
+                   "f32 rows, N(0,1); opt-in emulation: x and the weights split into three bf16 parts, six part "
+                   "products on the bf16 matrix cores, f32 accumulation"),
+    "x-bf16": ("bf16", "auto", "bf16x3-split",
+               "bf16 rows (the bf16 rounding of the N(0,1) draws, the model's hidden-state type); the exact "
+               "three-part bf16 split of the f32 weights on the bf16 matrix cores (exact products), f32 "
+               "accumulation"),
 }
 
 
@@ -70,15 +80,15 @@ def source_sha(name: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(name: str):
+def measured_traffic(key: str, sources: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if there is none or the kernel source changed since it was taken."""
+    None if there is none or the kernel's sources changed since."""
     try:
         data = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    entry = data.get(name)
-    if not entry or entry.get("source_sha") != source_sha(name):
+    entry = data.get(key)
+    if not entry or entry.get("source_sha") != source_sha(sources):
         return None
     return entry.get("bytes_per_launch")
 
@@ -97,10 +107,35 @@ def pool_bytes(batch, seqlen, ratio, hd, quantize, latent, block=16):
     return read + write
 
 
+def post_projection_bytes(batch, seqlen, hd, quantize):
+    """Algorithmic bytes of the kernels after the fused ratio-4 projection:
+    the row tiles' first entries (8 candidate rows of both planes read, the
+    pooled entry written), the per-entry epilogue (pooled f32 entries read,
+    the outputs written) and the state store (the last block's rows of both
+    planes read and written)."""
+    proj, groups = 2 * hd, seqlen // 4
+    tiles = (batch * seqlen + 255) // 256
+    boundary = (tiles - 1) * (8 * hd * 2 * 4 + hd * 4)
+    out = batch * groups * ((hd // 2 + hd // 16) if quantize else hd * 2)
+    finish = batch * groups * hd * 4 + out
+    state = batch * 4 * proj * 2 * 4 * 2
+    return boundary + finish + state
+
+
 def bf16_hidden(torch, x: np.ndarray) -> np.ndarray:
     """The bf16 rounding of synthetic hidden states (torch's conversion), as
     float32 values."""
     return torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(wl, W, seconds=10.0, x_bf16=False):
@@ -108,11 +143,13 @@ def cpu_baseline(wl, W, seconds=10.0, x_bf16=False):
     the sample until it takes `seconds` or covers the whole sequence."""
     import torch
     import oracle
+    blas = []
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
     except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+        pass
+    threads = max([p.get("num_threads", 1) for p in blas] or [1])
     tokens = 512
     while True:
         x = np.stack([W.hidden_rows(wl, b, 0, tokens) for b in range(wl.batch)])
@@ -130,9 +167,13 @@ def cpu_baseline(wl, W, seconds=10.0, x_bf16=False):
         if dt >= seconds or tokens >= wl.seqlen:
             break
         tokens = min(2 * tokens, wl.seqlen)
-    return {"value": entries / dt, "unit": "entries/s", "cores": threads, "kind": "oracle",
+    return {"value": round(entries / dt, 1), "unit": "entries/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "blas_threads": threads,
+            "blas": ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in blas) or "none found",
+            "host_cpus": len(os.sched_getaffinity(0)),
             "sample": f"first {tokens} tokens of each of {wl.batch} batch rows through all "
-                      f"{len(wl.compressors)} compressor(s) of the workload ({entries} entries, {dt:.2f} s)"}
+                      f"{len(wl.compressors)} compressor(s) of the workload ({entries} entries, {dt:.2f} s; "
+                      f"float64 NumPy, the projection a BLAS matmul on {threads} threads, the rest one thread)"}
 
 
 def _timed(torch, stream, fn, reps):
@@ -148,44 +189,59 @@ def _timed(torch, stream, fn, reps):
     return a.elapsed_time(b) / reps
 
 
-def gemm_roofline(kvc, g, x_format, projection):
-    """Roofline object of the 512-wide projection launch `g`: on the bf16 or
-    f16 matrix cores its passes against that peak (with the f32-equivalent
-    rate beside it), on the f32 matrix cores its flops against the fp32 peak."""
-    passes = mfma_passes(kvc, x_format, projection)
-    if passes:
-        if resolved(kvc, x_format, projection) == kvc.KVC_PROJ_F16_SPLIT:
-            what = ("f32 x and f32 weights, rows scaled by powers of two and split into two f16 parts, three part "
-                    "products on the f16 matrix cores")
-            kernel, traffic = "gemm_x6_kernel<*, F16>", "gemm_h3"
-        elif passes == 3:
-            what = "bf16 x times the three bf16 parts of the f32 weights"
-            kernel, traffic = "gemm_mc_kernel", "gemm_x3"
-        else:
-            what = "f32 x split into three bf16 parts times the three parts of the f32 weights, six part products"
-            kernel, traffic = "gemm_x6_kernel", "gemm_x6"
-        return {"bound": "mfma", "achieved": round(g["mfma_tflops"], 2), "peak": PEAK_BF16_MFMA_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(g["mfma_tflops"] / PEAK_BF16_MFMA_TFLOPS, 4),
-                "traffic": measured_traffic(traffic),
-                "kernel": f"{kernel} (512-wide projection, {what}, f32 accumulation)",
-                "per_launch": g["mfma_flop"], "avg_ms": round(g["ms"], 4),
-                "f32_equivalent_tflops": round(g["tflops"], 2),
-                "f32_equivalent_frac_of_fp32_peak": round(g["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4)}
-    return {"bound": "mfma", "achieved": round(g["tflops"], 2), "peak": PEAK_FP32_MFMA_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(g["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4),
-            "traffic": measured_traffic("gemm"), "kernel": "gemm_f32_kernel (512-wide projection, f32 matrix cores)",
-            "per_launch": g["flop"], "avg_ms": round(g["ms"], 4)}
+def _events(torch, stream, n):
+    """n timing events that exist (recorded once), so that their handles can
+    be handed to the library."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in ev:
+        e.record(stream)
+    torch.cuda.synchronize()
+    return ev
 
 
-def _rounded(d):
-    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+def _kernel_ms(torch, kvc, stream, fn, reps):
+    """Average duration of the projection kernel of `fn` (one library call),
+    from the library's own events around it."""
+    fn()
+    ev = _events(torch, stream, 2 * reps)
+    for r in range(reps):
+        kvc.time_next_projection(ev[2 * r], ev[2 * r + 1])
+        fn()
+    torch.cuda.synchronize()
+    return sum(ev[2 * r].elapsed_time(ev[2 * r + 1]) for r in range(reps)) / reps
+
+
+def _cold_ms(torch, stream, fn, reps):
+    """Average duration of single launches of `fn`, each after 1 GiB of
+    writes that evict its inputs from the caches (a true HBM measurement
+    even where the inputs would fit in the 256 MB last-level cache)."""
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    fn()
+    ev = _events(torch, stream, 2 * reps)
+    for r in range(reps):
+        flush.fill_(float(r))
+        ev[2 * r].record(stream)
+        fn()
+        ev[2 * r + 1].record(stream)
+    torch.cuda.synchronize()
+    del flush
+    return sum(ev[2 * r].elapsed_time(ev[2 * r + 1]) for r in range(reps)) / reps
+
+
+def x_format_of(kvc, name):
+    return kvc.KVC_X_BF16 if name == "bf16" else kvc.KVC_X_F32
+
+
+def projection_of(kvc, name):
+    return {"auto": kvc.KVC_PROJ_AUTO, "f32-mfma": kvc.KVC_PROJ_F32_MFMA, "f16-split": kvc.KVC_PROJ_F16_SPLIT,
+            "bf16-split": kvc.KVC_PROJ_BF16_SPLIT}[name]
 
 
 def resolved(kvc, x_format, projection):
     """The projection the library runs for KVC_PROJ_AUTO."""
     if projection != kvc.KVC_PROJ_AUTO:
         return projection
-    return kvc.KVC_PROJ_F16_SPLIT if x_format == kvc.KVC_X_F32 else kvc.KVC_PROJ_BF16_SPLIT
+    return kvc.KVC_PROJ_F32_MFMA if x_format == kvc.KVC_X_F32 else kvc.KVC_PROJ_BF16_SPLIT
 
 
 def mfma_passes(kvc, x_format, projection):
@@ -199,11 +255,46 @@ def mfma_passes(kvc, x_format, projection):
     return 3 if x_format == kvc.KVC_X_BF16 else 6
 
 
-def run_prefill(wl, steps, warmup, reps, torch, kvc, W, x_format, projection):
-    """Time whole prefill steps of `wl`, then each kernel alone. x is the
-    workload's f32 draws, or (x_format bf16) their bf16 rounding as bf16 rows."""
+def gemm_kernel_name(kvc, x_format, projection, fused):
+    p = resolved(kvc, x_format, projection)
+    if p == kvc.KVC_PROJ_F32_MFMA:
+        return f"gemm_f32_kernel<256, 256, 64, 128, 8, 1, true, {'true' if fused else 'false'}>"
+    if p == kvc.KVC_PROJ_F16_SPLIT:
+        return f"gemm_x6_kernel<{'true' if fused else 'false'}, true, 256, 128>"
+    if x_format == kvc.KVC_X_BF16:
+        return f"gemm_mc_kernel<256, 256, 128, 64, 8, 1, {'true' if fused else 'false'}, true>"
+    return f"gemm_x6_kernel<{'true' if fused else 'false'}, false, 128, 64>"
+
+
+def gemm_roofline(kvc, ms, flop, x_format, projection, traffic):
+    """Roofline object of the 512-wide projection kernel: on the f32 matrix
+    cores its flops against the fp32 peak; an emulation's 16-bit part
+    products against the 16-bit peak, with the f32-equivalent rate beside it."""
+    passes = mfma_passes(kvc, x_format, projection)
+    tflops = flop / ms / 1e9
+    if passes:
+        work = passes * flop
+        return {"bound": "mfma", "achieved": round(work / ms / 1e9, 2), "peak": PEAK_16BIT_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(work / ms / 1e9 / PEAK_16BIT_MFMA_TFLOPS, 4),
+                "traffic": None, "per_launch": work, "avg_ms": round(ms, 4),
+                "work": f"{passes} 16-bit part products per f32 product",
+                "f32_equivalent_tflops": round(tflops, 2)}
+    return {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": traffic, "traffic_source": TRAFFIC_SOURCE,
+            "per_launch": flop, "avg_ms": round(ms, 4)}
+
+
+def _rounded(d):
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+
+
+def run_prefill(wl, steps, warmup, reps, torch, kvc, W, x_format, projection, cold_pool=False):
+    """Reference launches of single stages, then W warmup steps and K timed
+    steps of `wl` with the per-compressor breakdown. x is the workload's f32
+    draws, or (x_format bf16) their bf16 rounding as bf16 rows."""
     dev = "cuda"
-    print(f"[bench] {wl.name}: generating inputs (x_format {x_format})", file=sys.stderr, flush=True)
+    print(f"[bench] {wl.name}: generating inputs (x_format {x_format}, projection {projection})",
+          file=sys.stderr, flush=True)
     x = torch.from_numpy(W.hidden(wl)).to(dev)
     if x_format == kvc.KVC_X_BF16:
         x = x.to(torch.bfloat16)
@@ -220,48 +311,31 @@ def run_prefill(wl, steps, warmup, reps, torch, kvc, W, x_format, projection):
         out = kvc.new_outputs(cfg, wl.batch, groups, latent=not comp.quantize, fp4=comp.quantize)
         comps.append((comp, cfg, wts, ws, state, out, groups))
     stream = torch.cuda.current_stream()
-    m = wl.batch * wl.seqlen
-    # the f16 split scales each row of x by its own power of two: both
-    # compressors read the same hidden states, so the step computes the
-    # row exponents once and hands them to both
-    shared = resolved(kvc, x_format, projection) == kvc.KVC_PROJ_F16_SPLIT
-    exps = torch.empty(m, dtype=torch.int32, device=dev) if shared else None
 
-    def step():
-        if shared:
-            kvc.x_row_exponents(x, m, wl.dim, exps)
-        for comp, cfg, wts, ws, state, out, groups in comps:
-            kvc.compressor_prefill(cfg, wts, x, wl.batch, wl.seqlen, ws, state[0], state[1], out, x_exponents=exps)
+    def call(c):
+        comp, cfg, wts, ws, state, out, groups = c
+        kvc.compressor_prefill(cfg, wts, x, wl.batch, wl.seqlen, ws, state[0], state[1], out)
 
-    print(f"[bench] {wl.name}: warmup + {steps} timed steps", file=sys.stderr, flush=True)
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    ms_per_step = _timed(torch, stream, step, steps)
-    entries = comps[0][6] * wl.batch
-
+    # reference launches of single stages (also bring the clocks up)
+    print(f"[bench] {wl.name}: single-stage launches", file=sys.stderr, flush=True)
     kernels = {}
-    if shared:
-        xe_ms = _timed(torch, stream, lambda: kvc.x_row_exponents(x, m, wl.dim, exps), reps)
-        xe_bytes = m * wl.dim * 4 + m * 4
-        kernels["x_exponents"] = {"ms": xe_ms, "gbps": xe_bytes / xe_ms / 1e6, "bytes": xe_bytes}
     for comp, cfg, wts, ws, state, out, groups in comps:
         tag = f"hd{comp.head_dim}"
-        gemm_ms = _timed(torch, stream, lambda: kvc.compressor_prefill(cfg, wts, x, wl.batch, wl.seqlen, ws,
-                                                                       x_exponents=exps), reps)
-        # ws now holds this compressor's projections, the bias already in the
-        # score plane: pool them alone, exactly as the step's pooling launch
-        pool_ms = _timed(torch, stream, lambda: kvc.compressor_prefill(cfg, kvc.Weights(), None, wl.batch,
-                                                                       wl.seqlen, ws, None, None, out), reps)
-        proj = 2 * comp.head_dim if comp.ratio == 4 else comp.head_dim
+        proj = comp.proj
         flops = 2.0 * wl.batch * wl.seqlen * wl.dim * 2 * proj
+        plain = lambda: kvc.compressor_prefill(cfg, wts, x, wl.batch, wl.seqlen, ws)  # noqa: E731
+        plain_ms = _kernel_ms(torch, kvc, stream, plain, reps)
+        kernels[f"gemm_{tag}_plain"] = {"ms": plain_ms, "tflops": flops / plain_ms / 1e9, "flop": flops,
+                                        "note": "projection-only call: the GEMM without the pooling epilogue"}
+        # ws now holds this compressor's projections, the bias in the score
+        # plane: the separate pool kernel on them
+        given = lambda: kvc.compressor_prefill(cfg, kvc.Weights(), None, wl.batch, wl.seqlen, ws,  # noqa: E731
+                                               None, None, out)
+        pool_ms = (_cold_ms if cold_pool else _timed)(torch, stream, given, reps)
         pbytes = pool_bytes(wl.batch, wl.seqlen, comp.ratio, comp.head_dim, comp.quantize, not comp.quantize)
-        kernels[f"gemm_{tag}"] = {"ms": gemm_ms, "tflops": flops / gemm_ms / 1e9, "flop": flops}
-        passes = mfma_passes(kvc, x_format, projection)
-        if passes:
-            # the bf16 matrix-core work: one pass per part product
-            kernels[f"gemm_{tag}"].update({"mfma_flop": passes * flops, "mfma_tflops": passes * flops / gemm_ms / 1e9})
-        kernels[f"pool_{tag}"] = {"ms": pool_ms, "gbps": pbytes / pool_ms / 1e6, "bytes": pbytes}
+        kernels[f"pool_{tag}"] = {"ms": pool_ms, "gbps": pbytes / pool_ms / 1e6, "bytes": pbytes,
+                                  "note": "pooling of given projections (the separate pool kernel)"
+                                          + (", each launch after a cache flush" if cold_pool else "")}
         if comp.head_dim == 128 and not comp.quantize:
             # the same pooling with the index keys' fp4 form (power-of-two
             # scales, blocks of 32) fused in place of the bf16 latent
@@ -272,16 +346,50 @@ def run_prefill(wl, steps, warmup, reps, torch, kvc, W, x_format, projection):
             b8 = pool_bytes(wl.batch, wl.seqlen, comp.ratio, comp.head_dim, True, False, block=32)
             kernels[f"pool_{tag}_e8m0"] = {"ms": ms8, "gbps": b8 / ms8 / 1e6, "bytes": b8}
             del out8
+
+    print(f"[bench] {wl.name}: {warmup} warmup + {steps} timed steps", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        for c in comps:
+            call(c)
+    torch.cuda.synchronize()
+    nc = len(comps)
+    ev = _events(torch, stream, 4 * nc * steps + 2)
+    ev[-2].record(stream)
+    for i in range(steps):
+        for j, c in enumerate(comps):
+            e = ev[4 * (i * nc + j):4 * (i * nc + j) + 4]
+            e[0].record(stream)
+            kvc.time_next_projection(e[1], e[2])
+            call(c)
+            e[3].record(stream)
+    ev[-1].record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev[-2].elapsed_time(ev[-1]) / steps
+    for j, c in enumerate(comps):
+        tag = f"hd{c[0].head_dim}"
+        parts = [ev[4 * (i * nc + j):4 * (i * nc + j) + 4] for i in range(steps)]
+        gemm = sum(p[1].elapsed_time(p[2]) for p in parts) / steps
+        pre = sum(p[0].elapsed_time(p[1]) for p in parts) / steps
+        post = sum(p[2].elapsed_time(p[3]) for p in parts) / steps
+        flops = 2.0 * wl.batch * wl.seqlen * wl.dim * 2 * c[0].proj
+        kernels[f"gemm_{tag}"] = {"ms": gemm, "tflops": flops / gemm / 1e9, "flop": flops,
+                                  "note": "the projection kernel of the timed steps (HIP events the library "
+                                          "records around it)"}
+        kernels[f"step_{tag}"] = {"before_projection_ms": pre, "projection_ms": gemm, "after_projection_ms": post}
+    entries = comps[0][6] * wl.batch
+    fused = [c[0].ratio == 4 and c[6] > 0 for c in comps]
     del comps, x
     torch.cuda.empty_cache()
     return {"ms_per_step": ms_per_step, "entries_per_step": entries,
-            "entries_per_s": entries / (ms_per_step / 1e3), "kernels": kernels}
+            "entries_per_s": entries / (ms_per_step / 1e3), "kernels": kernels, "fused": fused}
 
 
 def run_decode(wl, passes, torch, kvc, W, x_format):
-    """Time whole decode passes (every row streams all its tokens from
-    start_pos 0, one decode step per token), captured once in a HIP graph so
-    that host launch overhead is not measured."""
+    """Whole decode passes (every row streams all its tokens from start_pos
+    0, one decode step per token), captured once in a HIP graph so that host
+    launch overhead is not measured; then one eager pass behind a long sleep
+    kernel (so the launches queue up) with the library's events around each
+    step's projection kernel."""
     dev = "cuda"
     comp = wl.compressors[0]
     cfg = kvc.Config(comp.ratio, comp.head_dim, wl.dim, wl.eps, x_format=x_format)
@@ -292,18 +400,23 @@ def run_decode(wl, passes, torch, kvc, W, x_format):
     x = x.transpose(0, 1).contiguous()  # [steps, batch, dim]
     w = {k: torch.from_numpy(v).to(dev) for k, v in W.weights(wl, comp).items()}
     wts = kvc.Weights(wkv=w["wkv"], wgate=w["wgate"], ape=w["ape"])
-    ws = torch.empty(kvc.kvc_decode_workspace_floats(cfg, wl.batch), dtype=torch.float32, device=dev)
+    ws = kvc.new_decode_workspace(cfg, wl.batch)
     state = kvc.new_state(cfg, wl.batch)
     groups = wl.seqlen // comp.ratio
     lat = torch.empty((groups, wl.batch, comp.head_dim), dtype=torch.bfloat16, device=dev)
     outs = [kvc.Outputs(latent=lat[e]) for e in range(groups)]
+    stream = torch.cuda.current_stream()
 
-    def one_pass():
+    def one_pass(ev=None):
         e = 0
         for p in range(wl.seqlen):
             emits = p > 0 and (p + 1) % comp.ratio == 0
+            if ev is not None:
+                kvc.time_next_projection(ev[3 * p], ev[3 * p + 1])
             kvc.compressor_decode_step(cfg, wts, x[p], wl.batch, p, ws, state[0], state[1],
                                        outs[e] if emits else None)
+            if ev is not None:
+                ev[3 * p + 2].record(stream)
             e += emits
 
     side = torch.cuda.Stream()
@@ -316,18 +429,32 @@ def run_decode(wl, passes, torch, kvc, W, x_format):
     with torch.cuda.graph(graph):
         one_pass()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
     print(f"[bench] {wl.name}: {passes} timed graph replays", file=sys.stderr, flush=True)
     ms = _timed(torch, stream, graph.replay, passes)
-    eager_ms = _timed(torch, stream, one_pass, 1)
-    proj = 2 * comp.head_dim if comp.ratio == 4 else comp.head_dim
+    ev = _events(torch, stream, 3 * wl.seqlen)
+    torch.cuda._sleep(int(3e8))  # the queue fills while the GPU sleeps
+    one_pass(ev)
+    torch.cuda.synchronize()
+    kern = [ev[3 * p].elapsed_time(ev[3 * p + 1]) for p in range(wl.seqlen)]
+    after = [ev[3 * p + 1].elapsed_time(ev[3 * p + 2]) for p in range(wl.seqlen)]
+    emit = [p for p in range(wl.seqlen) if p > 0 and (p + 1) % comp.ratio == 0]
+    proj = comp.proj
     flop_step = 2.0 * wl.batch * wl.dim * 2 * proj
     entries = wl.batch * groups
+    kern_us = 1e3 * sum(kern) / len(kern)
     del graph, x, outs, lat
     torch.cuda.empty_cache()
     return {"ms_per_pass": ms, "entries_per_pass": entries, "entries_per_s": entries / (ms / 1e3),
             "us_per_step": ms * 1e3 / wl.seqlen, "tflops": flop_step * wl.seqlen / ms / 1e9,
-            "eager_ms_per_pass": eager_ms}
+            "projection_kernel_us": kern_us,
+            "projection_kernel": "decode_f32_kernel<128, 4> (projection + state ingest)" if x_format == kvc.KVC_X_F32
+            else "decode_gemm_kernel<4, uint16_t> (projection)",
+            "projection_roofline": {"bound": "mfma", "achieved": round(flop_step / kern_us / 1e6, 2),
+                                    "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                                    "frac": round(flop_step / kern_us / 1e6 / PEAK_FP32_MFMA_TFLOPS, 4),
+                                    "per_launch": flop_step},
+            "emit_pool_us": 1e3 * sum(after[p] for p in emit) / max(1, len(emit)),
+            "note": "ms_per_pass from graph replays; the kernel times from one eager pass queued behind a sleep"}
 
 
 def run_ratio1(wl, steps, warmup, reps, torch, kvc, W):
@@ -352,15 +479,15 @@ def run_ratio1(wl, steps, warmup, reps, torch, kvc, W):
     ms = _timed(torch, stream, step, steps)
     gemm_ms = _timed(torch, stream, lambda: kvc.compressor_ratio1_forward(cfg, wkv, x, tokens, ws), reps)
     flop = 2.0 * tokens * wl.dim * comp.head_dim
-    # the epilogue kernel reads the f32 projections and writes the outputs
     hd = comp.head_dim
     fin_bytes = tokens * hd * 4 + (tokens * (hd // 2 + hd // 16) if comp.quantize else tokens * hd * 2)
     fin_ms = ms - gemm_ms
     del x, ws, out
     torch.cuda.empty_cache()
-    return {"ms_per_step": round(ms, 4), "entries_per_s": round(tokens / (ms / 1e3), 1),
+    return {"ms_per_step": round(ms, 4), "entries_per_s": round(tokens / (ms / 1e3), 1), "dtype": "bf16",
             "kernels": {"gemm_bf16": {"ms": round(gemm_ms, 4), "tflops": round(flop / gemm_ms / 1e9, 2),
-                                      "flop": flop, "frac_of_bf16_peak": round(flop / gemm_ms / 1e9 / PEAK_BF16_MFMA_TFLOPS, 4)},
+                                      "flop": flop,
+                                      "frac_of_bf16_peak": round(flop / gemm_ms / 1e9 / PEAK_16BIT_MFMA_TFLOPS, 4)},
                         "rows_finish": {"ms": round(fin_ms, 4), "gbps": round(fin_bytes / fin_ms / 1e6, 1),
                                         "bytes": fin_bytes, "note": "step minus projection"}}}
 
@@ -379,8 +506,13 @@ def run_fp4_quant(rows, width, reps, torch, kvc):
         ms = _timed(torch, torch.cuda.current_stream(), lambda: fn(inp, codes, scales, out), reps)
         nbytes = rows * width * (2 + 0.5 + 2) + rows * (width // blk)
         res[name] = {"rows": rows, "width": width, "ms": round(ms, 4), "gbps": round(nbytes / ms / 1e6, 1),
-                     "bytes": int(nbytes)}
-    del inp, out
+                     "frac_of_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBPS, 4), "bytes": int(nbytes)}
+    # the read + write ceiling on the same box: a plain 1 GiB copy
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    cms = _timed(torch, torch.cuda.current_stream(), lambda: dst.copy_(src), reps)
+    res["copy_1GiB"] = {"ms": round(cms, 4), "gbps": round(2 * (1 << 30) / cms / 1e6, 1)}
+    del inp, out, src, dst
     torch.cuda.empty_cache()
     return res
 
@@ -388,20 +520,18 @@ def run_fp4_quant(rows, width, reps, torch, kvc):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the clock climbs for about 100 ms of sustained matrix-core load: the
-    # default warmup (about 60 ms of steps) times the loaded state
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill_r4_n65536_fp4_idx128")
-    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--x-format", choices=("f32", "bf16"), default="f32",
                     help="hidden states handed to the library: the f32 draws, or their bf16 rounding as bf16 rows")
-    ap.add_argument("--projection", choices=("auto", "f16-split", "bf16-split", "f32-mfma"), default="auto",
-                    help="prefill projection: the library's default (f16 split for f32 x, bf16 split for bf16 x), "
-                         "the f16 matrix cores on scaled two-part f16 splits, the bf16 matrix cores on exact bf16 "
-                         "parts, or the f32 matrix cores")
+    ap.add_argument("--projection", choices=("auto", "f32-mfma", "f16-split", "bf16-split"), default="auto",
+                    help="prefill projection: the library's default (the f32 matrix cores for f32 x, the exact "
+                         "bf16 split for bf16 x), or one of the opt-in emulations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
+    ap.add_argument("--only-decode", action="store_true", help="run the decode stream only (for profiling)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain copy kernel (read + write) of this many MiB")
     args = ap.parse_args()
@@ -418,10 +548,6 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     kvc.lib()  # fails loudly if the HIP library is missing
-    wl = W.WORKLOADS[args.workload]
-    if wl.decode or wl.dim == 0:
-        print("bench.py's headline is a prefill workload with hidden states", file=sys.stderr)
-        sys.exit(2)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -430,65 +556,101 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
+    x_format = x_format_of(kvc, args.x_format)
+    projection = resolved(kvc, x_format, projection_of(kvc, args.projection))
+    if args.only_decode:
+        d = run_decode(W.WORKLOADS["decode_r4_b64_s512"], 5, torch, kvc, W, x_format)
+        print(json.dumps({"decode_r4_b64_s512": _rounded(d)}), flush=True)
+        return
+    wl = W.WORKLOADS[args.workload]
+    if wl.decode or wl.dim == 0:
+        print("bench.py's headline is a prefill workload with hidden states", file=sys.stderr)
+        sys.exit(2)
 
-    x_format = kvc.KVC_X_BF16 if args.x_format == "bf16" else kvc.KVC_X_F32
-    projection = {"auto": kvc.KVC_PROJ_AUTO, "bf16-split": kvc.KVC_PROJ_BF16_SPLIT, "f32-mfma": kvc.KVC_PROJ_F32_MFMA,
-                  "f16-split": kvc.KVC_PROJ_F16_SPLIT}[args.projection]
-    projection = resolved(kvc, x_format, projection)
     head = run_prefill(wl, args.steps, args.warmup, args.kernel_reps, torch, kvc, W, x_format, projection)
     kernels = head["kernels"]
-    main_tag = f"hd{wl.compressors[0].head_dim}"
-    g = kernels[f"gemm_{main_tag}"]
-    p = kernels[f"pool_{main_tag}"]
-    roofline = gemm_roofline(kvc, g, x_format, projection)
+    main = wl.compressors[0]
+    tag = f"hd{main.head_dim}"
+    g = kernels[f"gemm_{tag}"]
+    fused = head["fused"][0]
+    dtype = {(kvc.KVC_X_F32, kvc.KVC_PROJ_F32_MFMA): "f32", (kvc.KVC_X_F32, kvc.KVC_PROJ_F16_SPLIT): "f16x3-split",
+             (kvc.KVC_X_F32, kvc.KVC_PROJ_BF16_SPLIT): "bf16x6-split",
+             (kvc.KVC_X_BF16, kvc.KVC_PROJ_BF16_SPLIT): "bf16x3-split"}[(x_format, projection)]
+    traffic = measured_traffic("gemm_f32_pool" if fused else "gemm_f32", "gemm_f32")
+    roofline = gemm_roofline(kvc, g["ms"], g["flop"], x_format, projection, traffic)
+    roofline["kernel"] = (gemm_kernel_name(kvc, x_format, projection, fused) +
+                          f" ({main.head_dim}-wide projection" + (" with the pooling epilogue" if fused else "") + ")")
+    roofline["timing"] = ("HIP events the library records on the launch stream around this kernel in each timed "
+                          "step (kvc_time_next_projection), averaged over the timed steps")
+    p = kernels[f"pool_{tag}"]
     pool = {"bound": "hbm", "achieved": round(p["gbps"], 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": round(p["gbps"] / PEAK_HBM_GBPS, 4), "traffic": measured_traffic("pool"),
-            "kernel": "pool_small_kernel<512,4,true>", "per_launch": p["bytes"], "avg_ms": round(p["ms"], 4)}
+            "frac": round(p["gbps"] / PEAK_HBM_GBPS, 4), "traffic": measured_traffic("pool", "pool"),
+            "traffic_source": TRAFFIC_SOURCE,
+            "kernel": f"pool_small_kernel<{main.head_dim},4,true> (pooling + RMSNorm + fp4 of given projections)",
+            "workload": "the same step's projections handed over (x NULL): the library's separate pool path, "
+                        "which the fused step replaces by the GEMM epilogue",
+            "per_launch": p["bytes"], "avg_ms": round(p["ms"], 4)}
+    st = kernels[f"step_{tag}"]
+    post_b = post_projection_bytes(wl.batch, wl.seqlen, main.head_dim, main.quantize)
+    step_pooling = {
+        "fused_epilogue_ms": round(g["ms"] - kernels[f"gemm_{tag}_plain"]["ms"], 4),
+        "after_projection_ms": round(st["after_projection_ms"], 4),
+        "after_projection_kernels": f"pool_boundary_kernel<{main.head_dim}> + rows_finish_kernel<{main.head_dim}> "
+                                    "+ state_store_kernel",
+        "after_projection_bytes": post_b,
+        "after_projection_gbps": round(post_b / st["after_projection_ms"] / 1e6, 1),
+        "note": "the pooling the timed step runs: the pooling epilogue inside the projection kernel (its cost: "
+                "that kernel minus the plain projection) and the kernels after it"} if fused else None
     result = {
         "metric": METRIC, "value": round(head["entries_per_s"], 1), "unit": "entries/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "seqlen": wl.seqlen, "dim": wl.dim,
                    "x": ("bf16 rows: the bf16 rounding of the N(0,1) draws" if x_format == kvc.KVC_X_BF16
                          else "f32 rows, N(0,1)"),
-                   "projection": {kvc.KVC_PROJ_F32_MFMA: "f32 matrix cores",
-                                  kvc.KVC_PROJ_BF16_SPLIT: "bf16 matrix cores on exact bf16 parts, f32 accumulation",
-                                  kvc.KVC_PROJ_F16_SPLIT: "f16 matrix cores on row-scaled two-part f16 splits, "
-                                                          "f32 accumulation"}[projection],
+                   "projection": {"f32": "f32 matrix cores", "f16x3-split": PATHS["f16-split"][3],
+                                  "bf16x6-split": PATHS["bf16-split"][3], "bf16x3-split": PATHS["x-bf16"][3]}[dtype],
                    "weights": "f32",
                    "compressors": [{"ratio": c.ratio, "head_dim": c.head_dim, "fp4": c.quantize}
                                    for c in wl.compressors],
                    "entries_per_step": head["entries_per_step"]},
         "hbm_gbps": pool["achieved"],
+        "hbm_gbps_kernel": pool["kernel"] + "; " + pool["workload"],
         "roofline": roofline,
         "pool": pool,
+        "step_pooling": step_pooling,
         "kernels": {k: _rounded(v) for k, v in kernels.items()},
     }
     if not args.no_extras:
         extras = {}
-        # the same step by the other projection paths
-        for name, xf, pr, desc in (
-                ("f32_mfma", kvc.KVC_X_F32, kvc.KVC_PROJ_F32_MFMA, "f32 rows, N(0,1); f32 matrix cores"),
-                ("f16_split", kvc.KVC_X_F32, kvc.KVC_PROJ_F16_SPLIT,
-                 "f32 rows, N(0,1); f16 matrix cores on row-scaled two-part f16 splits (three part products)"),
-                ("bf16_split", kvc.KVC_X_F32, kvc.KVC_PROJ_BF16_SPLIT,
-                 "f32 rows, N(0,1); bf16 matrix cores on exact bf16 parts (six part products)"),
-                ("x_bf16", kvc.KVC_X_BF16, kvc.KVC_PROJ_BF16_SPLIT,
-                 "bf16 rows: the bf16 rounding of the N(0,1) draws, the model's hidden-state type; bf16 matrix "
-                 "cores on the exact bf16 parts of the weights")):
+        # the same step on the opt-in emulations and from bf16 rows
+        for name in ("f16-split", "bf16-split", "x-bf16"):
+            xf_name, pr_name, dt, desc = PATHS[name]
+            xf, pr = x_format_of(kvc, xf_name), resolved(kvc, x_format_of(kvc, xf_name), projection_of(kvc, pr_name))
             if (xf, pr) == (x_format, projection):
                 continue
             r = run_prefill(wl, 20, 20, args.kernel_reps, torch, kvc, W, xf, pr)
+            rg = r["kernels"][f"gemm_{tag}"]
+            roof = gemm_roofline(kvc, rg["ms"], rg["flop"], xf, pr, None)
+            roof["kernel"] = gemm_kernel_name(kvc, xf, pr, r["fused"][0])
             extras[f"{wl.name}_{name}"] = {
-                "x": desc, "ms_per_step": round(r["ms_per_step"], 4), "entries_per_s": round(r["entries_per_s"], 1),
-                "roofline": gemm_roofline(kvc, r["kernels"][f"gemm_{main_tag}"], xf, pr),
+                "dtype": dt, "x": desc, "ms_per_step": round(r["ms_per_step"], 4),
+                "entries_per_s": round(r["entries_per_s"], 1), "roofline": roof,
                 "kernels": {k: _rounded(v) for k, v in r["kernels"].items()}}
-        for name in ("prefill_r4_n4096", "prefill_r128_b2_n16384"):
-            r = run_prefill(W.WORKLOADS[name], 5, 2, 5, torch, kvc, W, x_format, projection)
-            extras[name] = {"ms_per_step": round(r["ms_per_step"], 4), "entries_per_s": round(r["entries_per_s"], 1),
+        for name, cold in (("prefill_r4_n4096", False), ("prefill_r128_b2_n16384", True)):
+            r = run_prefill(W.WORKLOADS[name], 5, 3, 5, torch, kvc, W, x_format, projection, cold_pool=cold)
+            extras[name] = {"dtype": dtype, "ms_per_step": round(r["ms_per_step"], 4),
+                            "entries_per_s": round(r["entries_per_s"], 1),
                             "kernels": {k: _rounded(v) for k, v in r["kernels"].items()}}
+            if cold:
+                pk = r["kernels"]["pool_hd512"]
+                extras[name]["pool"] = {"bound": "hbm", "achieved": round(pk["gbps"], 1), "peak": PEAK_HBM_GBPS,
+                                        "unit": "GB/s", "frac": round(pk["gbps"] / PEAK_HBM_GBPS, 4),
+                                        "kernel": "pool_long_kernel<512, 128>", "per_launch": pk["bytes"],
+                                        "avg_ms": round(pk["ms"], 4),
+                                        "note": "single launches, each after a 1 GiB cache flush"}
         d = run_decode(W.WORKLOADS["decode_r4_b64_s512"], 5, torch, kvc, W, x_format)
-        extras["decode_r4_b64_s512"] = _rounded(d)
+        extras["decode_r4_b64_s512"] = {"dtype": dtype, **_rounded(d)}
         extras["fp4_quant_262144x512"] = run_fp4_quant(262144, 512, 10, torch, kvc)
         extras["prefill_r1_n65536"] = run_ratio1(W.WORKLOADS["prefill_r1_n65536"], 10, 3, 10, torch, kvc, W)
         result["workloads"] = extras

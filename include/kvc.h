@@ -68,10 +68,10 @@ typedef struct ihipStream_t *kvc_stream; /* a hipStream_t */
 #define KVC_X_BF16 1 /* bf16 rows: the model's hidden state */
 
 /* matrix cores of the prefill projection (kvc_config.projection) */
-#define KVC_PROJ_AUTO 0       /* default: KVC_PROJ_F16_SPLIT for f32 x, KVC_PROJ_BF16_SPLIT for bf16 x */
+#define KVC_PROJ_AUTO 0       /* default: KVC_PROJ_F32_MFMA for f32 x, KVC_PROJ_BF16_SPLIT for bf16 x */
 #define KVC_PROJ_F32_MFMA 1   /* f32 matrix cores (x_format KVC_X_F32 only) */
-#define KVC_PROJ_F16_SPLIT 2  /* f16 matrix cores on scaled two-part f16 splits (x_format KVC_X_F32 only) */
-#define KVC_PROJ_BF16_SPLIT 3 /* bf16 matrix cores on exact three-part bf16 splits */
+#define KVC_PROJ_F16_SPLIT 2  /* opt-in emulation: f16 matrix cores on scaled two-part f16 splits (f32 x only) */
+#define KVC_PROJ_BF16_SPLIT 3 /* opt-in emulation for f32 x: bf16 matrix cores on three-part bf16 splits */
 
 /* fp4 forms of a compressed entry (kvc_config.fp4_format) */
 #define KVC_FP4_E4M3_B16 0 /* the KV latent's form: e4m3fn scale per block of 16 */
@@ -105,29 +105,37 @@ typedef struct ihipStream_t *kvc_stream; /* a hipStream_t */
  *                pairs", Compressor listing, forward); with KVC_X_BF16 the
  *                caller passes that bf16 state. Ignored by
  *                compressor_ratio1_forward, whose x is always bf16.
- *   projection : how compressor_prefill computes the f32 products x . w^T,
- *                all with f32 accumulation:
- *                KVC_PROJ_F16_SPLIT: on the f16 matrix cores. Every row of x
- *                and every weight row is scaled by the power of two that
- *                brings its largest magnitude into [2^14, 2^15); each scaled
- *                value y splits into h = f16(y) and l = f16(y - h) (y - h - l
- *                at most 2^-22 |y|, or 2^-40 of the row's largest magnitude
- *                where l falls below the f16 normal range); the three part
- *                products xh wh + xh wl + xl wh are summed (xl wl, left out,
- *                is at most 2^-22 |x w|) and the sum is scaled back exactly.
+ *   projection : how compressor_prefill computes the f32 products x . w^T:
+ *                KVC_PROJ_F32_MFMA (what KVC_PROJ_AUTO, 0, selects for f32
+ *                x): on the f32 matrix cores. Each output is the sum of two
+ *                halves of the hidden width, p0 over k in [0, ks) and p1 over
+ *                [ks, dim) with ks = 32 * floor(dim / 64), each accumulated
+ *                from zero in one fixed k order, then p0 + p1 in one f32
+ *                addition (p1 alone when ks is 0). A decode step with f32 x
+ *                computes its projections as the same two sums, so decode
+ *                and prefill give the same bits for the same tokens.
+ *                The other two are opt-in emulations of the f32 products on
+ *                16-bit matrix cores, with f32 accumulation:
+ *                KVC_PROJ_F16_SPLIT (f32 x only): every row of x and every
+ *                weight row is scaled by the power of two that brings its
+ *                largest magnitude into [2^14, 2^15); each scaled value y
+ *                splits into h = f16(y) and l = f16(y - h) (y - h - l at most
+ *                2^-22 |y|, or 2^-40 of the row's largest magnitude where l
+ *                falls below the f16 normal range); the three part products
+ *                xh wh + xh wl + xl wh are summed (xl wl, left out, is at most
+ *                2^-22 |x w|) and the sum is scaled back exactly.
  *                KVC_PROJ_BF16_SPLIT: on the bf16 matrix cores from the exact
  *                split of each f32 weight into three bf16 parts (hi, mid, lo:
  *                bits cleared, so w = hi + mid + lo); bf16 x then gives exact
  *                products (x . hi + x . mid + x . lo), and f32 x is split the
  *                same way and the six part products of size >= 2^-16 |x w|
  *                are summed (the three left out total below 2^-21 |x w|).
- *                KVC_PROJ_F32_MFMA: on the f32 matrix cores.
- *                KVC_PROJ_AUTO (0, the default): KVC_PROJ_F16_SPLIT for f32
- *                x, KVC_PROJ_BF16_SPLIT for bf16 x. KVC_PROJ_F16_SPLIT and
- *                KVC_PROJ_F32_MFMA need x_format KVC_X_F32 (KVC_EINVAL
- *                otherwise). Every error above lies far inside the f32
- *                summation's own bound (K 2^-24 sum |x w|). Decode steps
- *                always use the f32 matrix cores.
+ *                KVC_PROJ_AUTO selects it for bf16 x (whose products with
+ *                the three parts are exact).
+ *                KVC_PROJ_F16_SPLIT and KVC_PROJ_F32_MFMA need x_format
+ *                KVC_X_F32 (KVC_EINVAL otherwise). Every error above lies far
+ *                inside the f32 summation's own bound (K 2^-24 sum |x w|).
+ *                Decode steps always use the f32 matrix cores.
  * proj = 2 * head_dim at ratio 4, head_dim otherwise: the width of each
  * projection plane. */
 typedef struct kvc_config {
@@ -194,17 +202,24 @@ int64_t kvc_state_rows(const kvc_config *cfg);
 /* f32 elements of the workspace compressor_prefill needs: the projection
  * planes, 2 * batch * seqlen * proj; at ratio 4 the f32 pooled entries,
  * batch * (seqlen / 4) * head_dim (used when the projection and the pooling
- * run as one kernel: a smaller workspace runs them separately); the split
- * weights: with KVC_PROJ_F16_SPLIT (KVC_PROJ_AUTO with f32 x) two f16 parts
- * and the scale exponents of the weight rows and of x's rows,
+ * run as one kernel: a smaller workspace runs them separately); and for the
+ * opt-in split projections the split weights: KVC_PROJ_F16_SPLIT two f16
+ * parts and the scale exponents of the weight rows and of x's rows,
  * 2 * proj * dim + 2 * proj + batch * seqlen rounded up to a multiple of 4;
- * otherwise (KVC_PROJ_F32_MFMA does not read them) three bf16 parts,
- * 3 * proj * dim (bf16 [2 proj][3][dim]). Or a negative KVC_E* code. */
+ * KVC_PROJ_BF16_SPLIT (and KVC_PROJ_AUTO with bf16 x) three bf16 parts,
+ * 3 * proj * dim. Or a negative KVC_E* code. */
 int64_t kvc_prefill_workspace_floats(const kvc_config *cfg, int64_t batch, int64_t seqlen);
 
-/* f32 elements of the workspace compressor_decode_step needs (split
- * projection partial sums); at least 2 * batch * proj; or a negative code.
- * The same for either x_format. */
+/* f32 elements of the workspace compressor_decode_step needs, or a negative
+ * code. It holds the partial sums of the projection and, after them, the
+ * arrival counters of its two k halves (one per tile of 32 batch rows x 32
+ * columns). The workspace must be zero-filled before the first call that
+ * uses it; every completed call leaves the counters zero again, so the same
+ * workspace serves any number of steps, graph replays included. Where a
+ * call finds a counter that is not zero (a workspace that was not
+ * zero-filled), the state row it writes is NaN in that tile rather than
+ * silently wrong; zero-fill the workspace again before going on. The same
+ * size for either x_format. */
 int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch);
 
 /* Compressor forward at start_pos == 0 (prefill) over `seqlen` tokens of
@@ -217,13 +232,6 @@ int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch);
  *                  the kv plane [batch][seqlen][proj] followed by the score
  *                  plane [batch][seqlen][proj]; no weights are read then
  *                  except ape and norm_w.
- *   x_exponents  : [batch * seqlen] int32 scale exponents of x's rows as
- *                  kvc_x_row_exponents writes them for this x (so that
- *                  several compressors of the same hidden states compute
- *                  them once), or NULL: the call computes them into its
- *                  workspace. Read only by the KVC_PROJ_F16_SPLIT projection;
- *                  values that do not belong to x give wrong projections but
- *                  no invalid access.
  *   batch        : >= 1.   seqlen : >= 0.
  *   workspace    : f32, at least 2 * batch * seqlen * proj elements, and
  *                  with x all kvc_prefill_workspace_floats() elements
@@ -231,7 +239,8 @@ int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch);
  *                  when x is not NULL (the score plane then with the
  *                  positional bias added; at ratio 4 with the fused kernel,
  *                  only the rows the state and the row tiles' first entries
- *                  read).
+ *                  read hold projections, and the other rows intermediate
+ *                  values such as the first k half's partial sums).
  *   kv_state,
  *   score_state  : [state_batch][kvc_state_rows()][proj] f32 each, or both
  *                  NULL (nothing carried). Rows of batch row b are written as
@@ -245,19 +254,10 @@ int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch);
  *                  to compute only projections and state).
  *   n_groups     : host, optional; receives seqlen / ratio (0: no entry).
  * Errors: KVC_EINVAL, KVC_EUNSUPPORTED, KVC_ESPACE, KVC_EHIP. */
-int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *x, const int32_t *x_exponents,
-                       int64_t batch, int64_t seqlen, float *workspace, int64_t workspace_floats,
+int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *x, int64_t batch,
+                       int64_t seqlen, float *workspace, int64_t workspace_floats,
                        float *kv_state, float *score_state, int64_t state_batch, const kvc_outputs *out,
                        int64_t *n_groups, kvc_stream stream);
-
-/* The scale exponent of each of `rows` rows of f32 hidden states x ([rows][dim],
- * 16-byte aligned; dim a positive multiple of 32, at most 2^20): the e for
- * which 2^e brings the row's largest magnitude into [2^14, 2^15) (0 for a
- * row of zeros or one holding an infinity; NaN elements are passed over),
- * as the KVC_PROJ_F16_SPLIT projection scales the row before splitting it.
- * exponents: [rows] int32 (device). Errors: KVC_EINVAL, KVC_EUNSUPPORTED,
- * KVC_EHIP. */
-int kvc_x_row_exponents(const float *x, int64_t rows, int64_t dim, int32_t *exponents, kvc_stream stream);
 
 /* One decode step: one token per batch row at position start_pos
  * (Compressor listing, forward, decode branch). The token fills slot
@@ -265,13 +265,21 @@ int kvc_x_row_exponents(const float *x, int64_t rows, int64_t dim, int32_t *expo
  * group is pooled and one entry per batch row is written to `out` (G = 1);
  * at ratio 4 the current block then becomes the previous one. start_pos == 0
  * is a prefill of one token, which resets the carried block.
+ * Launches: from f32 x, one kernel computes the projections (summed exactly
+ * as compressor_prefill's f32 matrix cores sum them, so the entries equal a
+ * prefill's bit for bit) and writes the state row; a step that completes a
+ * group launches the pooling kernel after it. From bf16 x or given
+ * projections: the projection (bf16 x), then one kernel that ingests and,
+ * at ratios 2 and 4, pools.
  *   x            : [batch][dim] f32, or bf16 with KVC_X_BF16 (one token per
  *                  row), or NULL: then the
  *                  caller has put the token's projections (without bias) in
  *                  workspace[0 : 2 * batch * proj] as the kv rows
  *                  [batch][proj] followed by the score rows [batch][proj].
  *   start_pos    : >= 0, the token's position in its sequence.
- *   workspace    : f32, >= kvc_decode_workspace_floats() elements.
+ *   workspace    : f32, >= kvc_decode_workspace_floats() elements, its
+ *                  counters zero (see there). Two calls that share a
+ *                  workspace must not run concurrently.
  *   kv_state,
  *   score_state  : required, as for compressor_prefill, holding the carry
  *                  of the previous calls of this sequence.
@@ -352,6 +360,18 @@ int indexer_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *
  * Errors: KVC_EINVAL, KVC_EHIP. */
 int latent_rope(const uint16_t *in, int64_t rows, int64_t width, int32_t rope_dim, const float *rope_cs,
                 int64_t rope_rows, int64_t first_row, uint16_t *out, kvc_stream stream);
+
+/* Measurement hook (for benchmarks and profilers; no effect on results).
+ * start and stop are hipEvent_t handles the caller created. The next
+ * compressor_prefill or compressor_decode_step call made by the calling
+ * thread records start on its stream immediately before it launches its
+ * projection kernel (the GEMM, which at ratio 4 may also pool and, in a
+ * decode step from f32 x, also writes the state row) and stop immediately
+ * after, then forgets both; a call that launches no projection forgets them
+ * too. Both NULL clears a pending request. Errors: KVC_EINVAL (only one of
+ * the two NULL); a failed record makes the compressor call return
+ * KVC_EHIP. */
+int kvc_time_next_projection(void *start, void *stop);
 
 /* A static description of a KVC_* code. */
 const char *kvc_strerror(int code);

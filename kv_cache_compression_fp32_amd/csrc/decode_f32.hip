@@ -1,0 +1,257 @@
+// Decode step from f32 hidden states: the token's projections and their
+// ingest into the state, one launch per step (gfx950, wave64).
+//
+// One token per batch row: kv = x . wkv^T, score = x . wgate^T ("Module
+// compress", Functions, linear_f32; "DeepSeek V4.1 . Pool token pairs",
+// Compressor listing, forward, decode branch), summed exactly as the prefill
+// projection sums them (gemm_f32_kernel.h): two k halves [0, ks) and [ks, k),
+// each one chain of v_mfma_f32_16x16x4_f32 from zero over increasing 16-k
+// chunks, k-slot q of MFMA t holding k = chunk + 4 q + t, then p0 + p1. So a
+// decode step and a prefill over the same tokens write the same bits
+// ("Compressed Sparse Attention . ratio m = 4", Prefill and decode use the
+// same rule).
+//
+// Work split: a workgroup of four wavefronts computes a 32 x 32 tile (batch
+// rows x output columns) over one k half, wavefront w owning the 16 x 16
+// fragment (w / 2, w % 2). The two halves of a tile run in two workgroups,
+// so that the chip holds about one MFMA chain per SIMD (64 rows x 2048
+// columns: 256 workgroups). Each writes its half's partial sums to the
+// workspace; an arrival counter per tile (workspace, zero at rest) tells the
+// second one to arrive, which adds the halves in order, adds the bias row of
+// the token's slot to the score columns, writes the state row and resets the
+// counter, so the next step (or a graph replay) finds it zero. No workgroup
+// waits for another.
+//
+// Operands reach LDS through buffer loads that write it directly (no
+// registers): a stage is BK k of the tile's 32 x rows and 32 weight rows,
+// the 16-byte group q of row r at position q ^ (r & 7), so the fragment reads
+// of 8 neighbouring rows hit 8 distinct bank groups. NST stage buffers, the
+// loads NST - 1 stages ahead. The fragment reads of stage s + 1 are issued
+// before the MFMAs of stage s and land while the chain runs. LDS reads are
+// inline asm, which the compiler does not track: it would otherwise wait for
+// every load in flight into any stage buffer before each of them. One wait
+// tied to the values read precedes their MFMAs.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "gemm_common.h"
+#include "kvc_launch.h"
+
+namespace kvc {
+namespace {
+
+using gemm::buffer_load_lds;
+using gemm::f4;
+using gemm::i32x4;
+using gemm::lds_u32;
+using gemm::make_rsrc;
+using gemm::uniform_rsrc;
+using gemm::xcd_remap;
+
+constexpr int kTM = 32, kTN = 32;  // batch rows x output columns per workgroup
+
+typedef __attribute__((address_space(3))) float lds_f32;
+
+// s_waitcnt immediate waiting until at most n vector memory operations of
+// this wavefront are in flight (lgkmcnt and expcnt not waited on)
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+__device__ __forceinline__ void barrier_no_fence() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int BK, int NST>
+__global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs d) {
+  constexpr int P = BK / 4;            // 16-byte groups per row piece
+  constexpr int RPI = 64 / P;          // rows per load instruction
+  constexpr int INS = kTM / RPI / 4;   // load instructions per wavefront and operand per stage
+  constexpr int KK = BK / 16;          // 16-k chunks per stage
+  static_assert(INS >= 1 && kTM % (RPI * 4) == 0 && kTN == kTM, "stage / wavefront mismatch");
+  static_assert(NST >= 3, "the loads of a stage go to the buffer read two stages before");
+  __shared__ __attribute__((aligned(16))) float xs[NST][kTM * BK];
+  __shared__ __attribute__((aligned(16))) float ws[NST][kTN * BK];
+  __shared__ uint32_t s_arrival;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // tile order: batch row tile fastest, then k half, then column tile; each
+  // XCD walks a contiguous range, so the row tiles of a column tile read
+  // its weights through one L2
+  const int64_t m_tiles = (d.m + kTM - 1) / kTM;
+  const int halves = d.ks > 0 ? 2 : 1;
+  const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t mt = id % m_tiles;
+  const int half = (int)((id / m_tiles) % halves);
+  const int64_t nt = id / (m_tiles * halves);
+  const int64_t n_glob = nt * kTN;
+  const bool second = n_glob >= d.n_half;
+  const int64_t n0 = second ? n_glob - d.n_half : n_glob;
+  const float *W = second ? d.w1 : d.w0;
+  const int64_t m0 = mt * kTM;
+  const int64_t kbase = half == 0 ? 0 : d.ks;
+  const int64_t klen = halves == 1 ? d.k : (half == 0 ? d.ks : d.k - d.ks);
+  const int stages = (int)(klen / BK);
+  const int64_t a_rows = d.m - m0 < kTM ? d.m - m0 : kTM;
+
+  // buffer resources from the tile's first row at the half's first k
+  const i32x4 a_rsrc = uniform_rsrc(make_rsrc(d.x + m0 * d.k + kbase, (uint32_t)((a_rows * d.k - kbase) * 4)));
+  const i32x4 b_rsrc = uniform_rsrc(make_rsrc(W + n0 * d.k + kbase, (uint32_t)((kTN * d.k - kbase) * 4)));
+  // load u of wavefront w: rows RPI (INS w + u) + lane / P of both operands,
+  // LDS position lane % P holding the row's group (lane % P) ^ (row & 7);
+  // rows past the batch read its last row (computed, never stored)
+  const int rsub = lane / P, pos = lane % P;
+  uint32_t a_off[INS], b_off[INS];
+#pragma unroll
+  for (int u = 0; u < INS; ++u) {
+    const int r = RPI * (INS * wave + u) + rsub;
+    const int64_t rr = r < a_rows ? r : a_rows - 1;
+    a_off[u] = (uint32_t)((rr * d.k + 4 * (pos ^ (r & 7))) * 4);
+    b_off[u] = (uint32_t)(((int64_t)r * d.k + 4 * (pos ^ (r & 7))) * 4);
+  }
+  auto issue = [&](int s, int buf) {
+    const int32_t koff = s * BK * 4;
+#pragma unroll
+    for (int u = 0; u < INS; ++u)
+      buffer_load_lds(a_rsrc, (lds_u32 *)(&xs[buf][RPI * (INS * wave + u) * BK]), 16, (int32_t)a_off[u], koff, 0,
+                      0);
+#pragma unroll
+    for (int u = 0; u < INS; ++u)
+      buffer_load_lds(b_rsrc, (lds_u32 *)(&ws[buf][RPI * (INS * wave + u) * BK]), 16, (int32_t)b_off[u], koff, 0,
+                      0);
+  };
+
+  const int fi = wave >> 1, fj = wave & 1, row_in = lane & 15, slot = lane >> 4;
+  const int ra = 16 * fi + row_in, rb = 16 * fj + row_in;
+  // chunk kk of a stage: k = 16 kk + 4 slot .. + 3 of rows ra (x) and rb (w)
+  auto read = [&](int buf, f4(&af)[KK], f4(&bf)[KK]) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int q = 4 * kk + slot;
+      const uint32_t aa = (uint32_t)(uintptr_t)(const lds_f32 *)(&xs[buf][ra * BK + 4 * (q ^ (ra & 7))]);
+      const uint32_t ba = (uint32_t)(uintptr_t)(const lds_f32 *)(&ws[buf][rb * BK + 4 * (q ^ (rb & 7))]);
+      asm volatile("ds_read_b128 %0, %1" : "=v"(af[kk]) : "v"(aa));
+      asm volatile("ds_read_b128 %0, %1" : "=v"(bf[kk]) : "v"(ba));
+    }
+  };
+  // the reads above have landed; every value is tied to the wait
+  auto landed = [&](f4(&af)[KK], f4(&bf)[KK]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(af[0]), "+v"(bf[0]));
+#pragma unroll
+    for (int kk = 1; kk < KK; ++kk) asm volatile("" : "+v"(af[kk]), "+v"(bf[kk]));
+  };
+  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+  auto chain = [&](const f4(&af)[KK], const f4(&bf)[KK]) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kk][t], bf[kk][t], acc, 0, 0, 0);
+  };
+  // step s: stage s's fragments (read in the previous step) feed the chain;
+  // first the loads of stage s + NST - 1 go to the buffer of stage s - 1
+  // (every wavefront finished reading it before the previous step's
+  // barrier; past the last stage the last one is loaded again into a buffer
+  // nobody reads, which keeps the wait counts fixed), then the fragments of
+  // stage s + 1 are read once every wavefront's loads of it have landed
+  auto step = [&](int s, f4(&ca)[KK], f4(&cb)[KK], f4(&na)[KK], f4(&nb)[KK]) {
+    landed(ca, cb);
+    const int ahead = s + NST - 1;
+    issue(ahead < stages ? ahead : stages - 1, ahead % NST);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * 2 * INS));  // this wavefront's stage s + 1 landed
+    barrier_no_fence();                                          // every wavefront's
+    if (s + 1 < stages) read((s + 1) % NST, na, nb);
+    __builtin_amdgcn_sched_barrier(0);
+    chain(ca, cb);
+  };
+
+  f4 a0[KK], b0[KK], a1[KK], b1[KK];
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) issue(s < stages ? s : stages - 1, s);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * 2 * INS));  // stage 0
+  barrier_no_fence();
+  read(0, a0, b0);
+  for (int s = 0; s < stages; s += 2) {
+    step(s, a0, b0, a1, b1);
+    if (s + 1 < stages) step(s + 1, a1, b1, a0, b0);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load into LDS outlives the workgroup
+
+  // accumulator r of this lane: batch row m0 + 16 fi + 4 slot + r, column
+  // n_glob + 16 fj + row_in of the [2 n_half] output row (kv then score)
+  const int64_t ncols = 2 * d.n_half;
+  const int64_t col = n_glob + 16 * fj + row_in;
+  const int64_t row0 = m0 + 16 * fi + 4 * slot;
+  float tot[4] = {acc[0], acc[1], acc[2], acc[3]};
+  if (halves == 2) {
+    float *mine = d.part + (int64_t)half * d.m * ncols;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (row0 + r < d.m) mine[(row0 + r) * ncols + col] = acc[r];
+    __threadfence();  // release: this half's partial sums, before the arrival
+    __syncthreads();
+    uint32_t *counter = d.counters + nt * m_tiles + mt;
+    if (threadIdx.x == 0) s_arrival = atomicAdd(counter, 1u);
+    __syncthreads();
+    const uint32_t arrived = s_arrival;
+    if (arrived == 0) return;  // the other half finishes the tile
+    __threadfence();           // acquire: the other half's partial sums
+    const float *other = d.part + (int64_t)(1 - half) * d.m * ncols;
+    // a counter that was not zero at the call: the caller's workspace was not
+    // zero-filled; the state row turns NaN rather than silently wrong
+    const bool bad = arrived != 1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (row0 + r < d.m) {
+        // p0 + p1 (addition is commutative: the same bits from either half)
+        const float o = other[(row0 + r) * ncols + col];
+        tot[r] = bad ? __builtin_nanf("") : o + acc[r];
+      }
+    if (threadIdx.x == 0) *counter = 0u;  // at rest for the next step
+  }
+  // the ingest: the bias row of the token's slot joins the gate logits in
+  // one f32 addition, then the state row (and at ratio 4 from position 0 the
+  // previous block's padding)
+  const int64_t c = n0 + 16 * fj + row_in;
+  float *state = second ? d.sc_state : d.kv_state;
+  const float bias = (second && d.ape) ? d.ape[(int64_t)d.slot * d.n_half + c] : 0.0f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t row = row0 + r;
+    if (row >= d.m) continue;
+    float v = tot[r];
+    if (second && d.ape) v = v + bias;
+    float *srow = state + row * d.state_rows * d.n_half;
+    srow[(int64_t)d.state_row * d.n_half + c] = v;
+    for (int i = 0; i < d.reset_rows; ++i) srow[(int64_t)i * d.n_half + c] = second ? -INFINITY : 0.0f;
+  }
+}
+
+template <int BK, int NST>
+hipError_t launch(const DecodeArgs &d, int64_t tiles, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_f32_kernel<BK, NST>), dim3((uint32_t)tiles), dim3(256), 0, stream, d);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t decode_f32_tiles(int64_t m, int64_t n_half) { return ((m + kTM - 1) / kTM) * (2 * n_half / kTN); }
+
+int64_t decode_f32_split(int64_t k) { return 32 * (k / 64); }
+
+hipError_t launch_decode_f32(const DecodeArgs &d, hipStream_t stream) {
+  if (d.m <= 0) return hipSuccess;
+  // whole 32-column tiles, 32-k granules, and tile rows addressable with
+  // 32-bit buffer offsets
+  if (d.n_half % kTN != 0 || d.k % 32 != 0 || d.ks != decode_f32_split(d.k) || d.k <= 0 ||
+      (int64_t)kTM * d.k * 4 > INT32_MAX || (d.ks > 0 && !d.part) || !d.counters || d.slot < 0 ||
+      d.state_row < 0 || d.state_row >= d.state_rows || d.reset_rows < 0 || d.reset_rows > d.state_rows)
+    return hipErrorInvalidValue;
+  const int64_t tiles = decode_f32_tiles(d.m, d.n_half) * (d.ks > 0 ? 2 : 1);
+  // stages of 128 k when both halves are whole stages, else of 32 k
+  const bool wide = d.ks % 128 == 0 && (d.k - d.ks) % 128 == 0;
+  return wide ? launch<128, 4>(d, tiles, stream) : launch<32, 8>(d, tiles, stream);
+}
+
+}  // namespace kvc

@@ -11,9 +11,11 @@
 //   128 x 128 tiles (four 64 x 64 wavefronts, two workgroups per CU) below.
 // Tiles are remapped so each XCD walks a contiguous range of row tiles with
 // the column tiles fastest (an A row tile is then reused from that XCD's L2).
-// Decode (M = batch): decode_gemm_kernel, 32 columns per workgroup with the K
-// range split over workgroups (each split writes its own partial sums) and
-// over the wavefronts of a workgroup (summed in LDS).
+// Every instance sums each output as p0 + p1 over the two k halves
+// (gemm_f32_kernel.h), the order decode_f32.hip reproduces for one token.
+// Decode from bf16 rows (M = batch): decode_gemm_kernel, 32 columns per
+// workgroup with the K range split over workgroups (each split writes its
+// own partial sums) and over the wavefronts of a workgroup (summed in LDS).
 #include "gemm_f32_kernel.h"
 
 namespace kvc {

@@ -13,6 +13,14 @@
 // chunk takes element t, so k-slot q of MFMA t holds k = chunk_base + 4 q + t
 // for both operands and every k is covered once, in the same order for every
 // output element.
+//
+// Summation order: each output is p0 + p1, p0 the chain of MFMAs over the
+// k range [0, ks) and p1 over [ks, k), ks = 32 * floor(k / 64), each chain
+// starting from zero and taking the 16-k chunks in increasing k (p1 alone
+// when ks is 0). Between the halves the tile's p0 waits in its own output
+// positions of C. The decode projection (decode_f32.hip) computes the same
+// two chains for one token, so a token's projections have the same bits
+// whichever path computes them.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -78,10 +86,8 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
   const bool second = n_glob >= g.n_half;
   const int64_t n0 = second ? n_glob - g.n_half : n_glob;
   const float *__restrict__ B = second ? g.b1 : g.b0;
-  float *__restrict__ C = (second ? g.c1 : g.c0) + (int64_t)blockIdx.y * g.c_split_stride;
-  const int64_t k_len = g.k / g.splits;
-  const int64_t k_begin = (int64_t)blockIdx.y * k_len;
-  const int kt_count = (int)(k_len / BK);
+  float *__restrict__ C = second ? g.c1 : g.c0;
+  const int kt_count = (int)(g.k / BK);
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
   }
   const uint32_t b_voff = (uint32_t)(((POOL ? 0 : 8 * wave * B_INS) + lr) * g.ldb * 4 + 4 * lq * 4);
   auto issue = [&](int kt, int st) {
-    const uint32_t koff = (uint32_t)((k_begin + (int64_t)kt * BK) * 4);
+    const uint32_t koff = (uint32_t)(kt * BK * 4);
 #pragma unroll
     for (int u = 0; u < A_INS; ++u)
       buffer_load_lds(a_rsrc, (lds_u32 *)(&As[st][256 * (wave * A_INS + u)]), 16, (int32_t)a_voff[u],
@@ -152,9 +158,57 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[sl][i][s], fb[sl][j][s], acc[i][j], 0, 0, 0);
   };
 
+  // Accumulator element (i, j, r) of this lane belongs at row band0 + 16 i
+  // + 4 slot + r and a column of its fragment; its address is a
+  // wavefront-uniform row pointer (scalar registers) plus the lane's offset
+  // 4 slot ldc + lane % 16, so stash and readback need no address registers
+  // per element. Rows past the end of A are skipped.
+  // The lane's values are derived from a fresh lane id where they are used,
+  // so that nothing extra stays live through the k loops.
+  const int wm_u = wave_u / WAVES_N, wn_u = wave_u % WAVES_N;
+  const int64_t band0 = m0 + wm_u * WM;
+  auto lane_place = [&](int &rows_left, uint32_t &lane_off) {
+    const int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int64_t left = g.m - band0 - 4 * (l >> 4);
+    rows_left = left < WM ? (int)left : WM;  // rows of this lane's groups inside A (may be <= 0)
+    lane_off = (uint32_t)(4 * (l >> 4) * g.ldc + (l & 15));
+  };
+  auto row_ptr = [&](int i, int j, int r) -> float * {
+    const int64_t row = band0 + 16 * i + r;
+    if constexpr (POOL) {
+      constexpr int F = WN / 4, FJ = F / 16;  // pool_epilogue's column segments
+      const int seg = j / FJ, jj = j % FJ;
+      return (seg >= 2 ? g.c1 : g.c0) + row * g.ldc + (seg & 1) * g.pool_hd + f0 + F * wn_u + 16 * jj;
+    } else {
+      return C + row * g.ldc + n0 + wn_u * WN + 16 * j;
+    }
+  };
+
+  // p0 waits in the tile's own output positions (no other tile reads or
+  // writes them), the accumulators restart from zero for p1
+  auto stash = [&]() {
+    int rows_left;
+    uint32_t lane_off;
+    lane_place(rows_left, lane_off);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (16 * i + r < rows_left) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) row_ptr(i, j, r)[lane_off] = acc[i][j][r];
+        }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  const int kt_mid = kt_count / 2;  // ks / 32: the first stage of p1 (0: p1 alone)
   issue(0, 0);
   wait_vm0();
   __syncthreads();
+#pragma clang loop unroll(disable)
   for (int kt = 0; kt < kt_count; ++kt) {
     const int st = kt & 1;
     fload(st, 0, 0);
@@ -163,6 +217,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
       mfma_slice(LAST, 3);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (kt == kt_mid && kt_mid > 0) stash();
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       if (c + 1 < NCH) fload(st, c + 1, (c + 1) & 1);
@@ -178,6 +233,20 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
     __syncthreads();                    // everyone's landed; everyone is done reading this stage
   }
   if (DEFER) mfma_slice(LAST, 3);
+  if (kt_mid > 0) {
+    // p0 + p1 (the same lane wrote p0, so it reads its own stores back)
+    int rows_left;
+    uint32_t lane_off;
+    lane_place(rows_left, lane_off);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (16 * i + r < rows_left) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j][r] = row_ptr(i, j, r)[lane_off] + acc[i][j][r];
+        }
+  }
 
   if constexpr (POOL) {
     pool_epilogue<WM, WN>(g, acc, smem, m0, f0, wm, wn, lane);
@@ -201,8 +270,9 @@ __device__ __forceinline__ f4 load_a4(const uint16_t *p) {
 // memory (lane l reads 4 consecutive k of row l % 16 at k-slot l / 16, the
 // layout of v_mfma_f32_16x16x4_f32 with the same k permutation as the tiled
 // kernel); the loads of CPW chunks of 16 k are issued before their MFMAs. The
-// 8 partial 64 x 32 tiles are summed through LDS in a fixed order. x rows
-// are f32 (TA = float) or bf16 (TA = uint16_t, promoted on load).
+// 8 partial 64 x 32 tiles are summed through LDS in a fixed order. Used for
+// bf16 x rows (TA = uint16_t, promoted on load); f32 rows take the decode
+// kernel of decode_f32.hip, which sums as the prefill does.
 template <int CPW, typename TA>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_gemm_kernel(GemmArgs g) {
   constexpr int NWV = 8, FM = 4, FN = 2;
@@ -295,135 +365,12 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   if (m0 + row < g.m) *reinterpret_cast<float4 *>(C + (m0 + row) * g.ldc + n0 + col) = sum;
 }
 
-// Decode projection of f32 rows through LDS: a workgroup computes 64 rows x
-// 32 columns over one k split; wavefront w owns output fragment (w / 2,
-// w % 2) over that whole range (four accumulator chains, summed at the end),
-// so no cross-wavefront sum is needed. Stages of 128 k, x [64][128] and
-// weights [32][128] f32, 16-byte group q of row r at position q ^ (r & 7)
-// (the fragment reads of 8 neighbouring rows hit 8 distinct bank groups);
-// every load instruction brings two whole 512-byte row pieces straight to
-// LDS (lane l: row 2 u + l / 32, position l % 32). Three stage buffers, the
-// loads two stages ahead: a short kernel per token waits a memory round trip
-// per stage otherwise. The buffers are separate arrays and the stage loop is
-// unrolled by three, so each step names its buffers statically; the LDS
-// reads are opaque to the compiler (it would otherwise wait for every load
-// in flight into any LDS buffer before them) and one explicit wait, tied to
-// every value read, precedes the MFMAs; barriers carry no memory fence (which
-// would also drain the loads in flight), each wavefront having waited for
-// its own loads of the stage before it.
-constexpr int kDecBK = 128;
-
-__device__ __forceinline__ void barrier_no_fence() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-__global__ __launch_bounds__(512) void decode_lds_kernel(GemmArgs g) {
-  constexpr int BK = kDecBK;
-  __shared__ __attribute__((aligned(16))) float xa0[64 * BK], xa1[64 * BK], xa2[64 * BK];
-  __shared__ __attribute__((aligned(16))) float wb0[32 * BK], wb1[32 * BK], wb2[32 * BK];
-  typedef __attribute__((address_space(3))) float lds_f32;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t n_glob = (int64_t)blockIdx.x * 32;
-  const bool second = n_glob >= g.n_half;
-  const int64_t n0 = second ? n_glob - g.n_half : n_glob;
-  const float *B = second ? g.b1 : g.b0;
-  float *C = (second ? g.c1 : g.c0) + (int64_t)blockIdx.y * g.c_split_stride;
-  const int64_t m0 = (int64_t)blockIdx.z * 64;
-  const int64_t kper = g.k / g.splits, kbase = (int64_t)blockIdx.y * kper;
-  const int stages = (int)(kper / BK);
-  const int64_t a_rows = g.m - m0 < 64 ? g.m - m0 : 64;
-  const i32x4 a_rsrc = uniform_rsrc(make_rsrc(g.a + m0 * g.lda + kbase, (uint32_t)(a_rows * g.lda * 4)));
-  const i32x4 b_rsrc = uniform_rsrc(make_rsrc(B + n0 * g.ldb + kbase, (uint32_t)(32 * g.ldb * 4)));
-  // wavefront w loads x rows 8 w .. 8 w + 7 (4 instructions) and weight rows
-  // 4 w .. 4 w + 3 (2 instructions); rows past the batch read the last row
-  const int rsub = lane >> 5, pos = lane & 31;
-  uint32_t a_off[4], b_off[2];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = 8 * wave + 2 * u + rsub;
-    const int64_t rr = r < a_rows ? r : a_rows - 1;
-    a_off[u] = (uint32_t)((rr * g.lda + 4 * (pos ^ (r & 7))) * 4);
-  }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int r = 4 * wave + 2 * u + rsub;
-    b_off[u] = (uint32_t)((r * g.ldb + 4 * (pos ^ (r & 7))) * 4);
-  }
-  auto issue = [&](int s, float *xs, float *ws) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      buffer_load_lds(a_rsrc, (lds_u32 *)(xs + (8 * wave + 2 * u) * BK), 16, (int32_t)a_off[u],
-                      (int32_t)(s * BK * 4), 0, 0);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      buffer_load_lds(b_rsrc, (lds_u32 *)(ws + (4 * wave + 2 * u) * BK), 16, (int32_t)b_off[u],
-                      (int32_t)(s * BK * 4), 0, 0);
-  };
-  const int fi = wave >> 1, fj = wave & 1, row_in = lane & 15, slot = lane >> 4;
-  const int ra = 16 * fi + row_in, rb = 16 * fj + row_in;
-  f4 acc[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
-  // one stage: 8 groups of 16 k; MFMA t of a group takes k = 16 kk + 4 slot + t
-  // from both operands and accumulates into acc[t]
-  auto compute = [&](const float *xs, const float *ws) {
-    f4 af[8], bf[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int q = 4 * kk + slot;
-      const uint32_t aa = (uint32_t)(uintptr_t)(const lds_f32 *)(xs + ra * BK + 4 * (q ^ (ra & 7)));
-      const uint32_t ba = (uint32_t)(uintptr_t)(const lds_f32 *)(ws + rb * BK + 4 * (q ^ (rb & 7)));
-      asm volatile("ds_read_b128 %0, %1" : "=v"(af[kk]) : "v"(aa));
-      asm volatile("ds_read_b128 %0, %1" : "=v"(bf[kk]) : "v"(ba));
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(af[4]), "+v"(af[5]), "+v"(af[6]),
-                   "+v"(af[7]), "+v"(bf[0]), "+v"(bf[1]), "+v"(bf[2]), "+v"(bf[3]), "+v"(bf[4]), "+v"(bf[5]),
-                   "+v"(bf[6]), "+v"(bf[7]));
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kk][t], bf[kk][t], acc[t], 0, 0, 0);
-  };
-  // step s: stage s in (xc, wc); the loads of stage s + 2 go to (xn, wn),
-  // the buffers of stage s - 1, which every wavefront finished reading
-  // before this step's barrier
-  auto step = [&](int s, const float *xc, const float *wc, float *xn, float *wn) {
-    if (s + 1 < stages) __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6): this wavefront's stage s landed
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
-    barrier_no_fence();                                      // every wavefront's stage s landed
-    if (s + 2 < stages) issue(s + 2, xn, wn);
-    compute(xc, wc);
-  };
-  if (stages > 0) issue(0, xa0, wb0);
-  if (stages > 1) issue(1, xa1, wb1);
-  for (int s = 0; s < stages; s += 3) {
-    step(s, xa0, wb0, xa2, wb2);
-    if (s + 1 < stages) step(s + 1, xa1, wb1, xa0, wb0);
-    if (s + 2 < stages) step(s + 2, xa2, wb2, xa1, wb1);
-  }
-  const f4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t row = m0 + 16 * fi + 4 * slot + r;
-    if (row < g.m) C[row * g.ldc + n0 + 16 * fj + row_in] = sum[r];
-  }
-}
-
+// Decode projection of bf16 rows (the split-K partials of launch_gemm's
+// kDecode shape); f32 rows take decode_f32.hip's kernel instead.
 inline hipError_t launch_decode_gemm(const GemmArgs &g, hipStream_t stream) {
-  if (g.n_half % 32 != 0 || g.k % 16 != 0 || g.splits < 1 || g.bias1) return hipErrorInvalidValue;
+  if (!g.a16 || g.n_half % 32 != 0 || g.k % 16 != 0 || g.splits < 1 || g.bias1) return hipErrorInvalidValue;
   const dim3 grid((uint32_t)(2 * g.n_half / 32), (uint32_t)g.splits, (uint32_t)((g.m + 63) / 64));
-  // f32 rows whose split ranges are whole 128-k stages, tile rows addressable
-  // with 32-bit buffer offsets: through LDS; otherwise straight from memory
-  const bool staged = !g.a16 && g.k % g.splits == 0 && (g.k / g.splits) % kDecBK == 0 && g.lda >= g.k &&
-                      g.ldb >= g.k && (int64_t)64 * g.lda * 4 <= INT32_MAX && (int64_t)32 * g.ldb * 4 <= INT32_MAX;
-  if (staged) hipLaunchKernelGGL(decode_lds_kernel, grid, dim3(512), 0, stream, g);
-  else if (g.a16) hipLaunchKernelGGL((decode_gemm_kernel<4, uint16_t>), grid, dim3(512), 0, stream, g);
-  else hipLaunchKernelGGL((decode_gemm_kernel<4, float>), grid, dim3(512), 0, stream, g);
+  hipLaunchKernelGGL((decode_gemm_kernel<4, uint16_t>), grid, dim3(512), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -442,16 +389,16 @@ inline hipError_t launch_pooling(const GemmArgs &g, hipStream_t stream) {
 
 template <int BM, int BN, int WM, int WN, int NW, int MINW, bool DEFER>
 hipError_t launch_tiled(const GemmArgs &g, hipStream_t stream) {
-  // every column tile inside one half, every split whole k tiles, and a
-  // tile's rows addressable by a 32-bit buffer offset
-  if (g.n_half % BN != 0 || g.splits < 1 || g.k % (kBK * g.splits) != 0 || (g.bias1 && g.splits != 1) ||
+  // every column tile inside one half, whole k tiles, and a tile's rows
+  // addressable by a 32-bit buffer offset
+  if (g.n_half % BN != 0 || g.splits != 1 || g.k % kBK != 0 ||
       (g.bias1 && (g.bias_seqlen < 1 || g.bias_ratio < 1 || (g.bias_ratio & (g.bias_ratio - 1)) != 0)) || g.lda < g.k || g.ldb < g.k ||
       (int64_t)BM * g.lda * 4 > INT32_MAX || (int64_t)BN * g.ldb * 4 > INT32_MAX)
     return hipErrorInvalidValue;
   const int64_t m_tiles = (g.m + BM - 1) / BM;
   const int64_t n_tiles = 2 * g.n_half / BN;
   hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, WM, WN, NW, MINW, DEFER>),
-                     dim3((uint32_t)(m_tiles * n_tiles), (uint32_t)g.splits), dim3(NW * 64), 0, stream, g);
+                     dim3((uint32_t)(m_tiles * n_tiles)), dim3(NW * 64), 0, stream, g);
   return hipGetLastError();
 }
 

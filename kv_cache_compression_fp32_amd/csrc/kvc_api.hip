@@ -50,11 +50,12 @@ int check_ratio1(const kvc_config *cfg) {
 }
 
 bool overlapped(const kvc_config *cfg) { return cfg->ratio == 4; }
-// the projection KVC_PROJ_AUTO stands for: the f16 split for f32 rows, the
-// exact bf16 split for bf16 rows
+// the projection KVC_PROJ_AUTO stands for: the f32 matrix cores for f32
+// rows, the exact bf16 split for bf16 rows (whose products with the three
+// bf16 parts of the weights are exact)
 int32_t projection_of(const kvc_config *cfg) {
   if (cfg->projection != KVC_PROJ_AUTO) return cfg->projection;
-  return cfg->x_format == KVC_X_F32 ? KVC_PROJ_F16_SPLIT : KVC_PROJ_BF16_SPLIT;
+  return cfg->x_format == KVC_X_F32 ? KVC_PROJ_F32_MFMA : KVC_PROJ_BF16_SPLIT;
 }
 int64_t proj_of(const kvc_config *cfg) { return overlapped(cfg) ? 2 * (int64_t)cfg->head_dim : cfg->head_dim; }
 int64_t rows_of(const kvc_config *cfg) { return overlapped(cfg) ? 2 * (int64_t)cfg->ratio : cfg->ratio; }
@@ -103,6 +104,30 @@ int32_t decode_splits(const kvc_config *cfg, int64_t batch) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_EHIP; }
 
+// Decode workspace: the partial sums (f32 x: the two k halves, [2][batch]
+// [2 proj]; bf16 x: the split-K parts, [splits][2][batch][proj]; given
+// projections: [2][batch][proj] at the start), then the f32 path's arrival
+// counters, one per tile, rounded up to 64.
+int64_t decode_partial_floats(const kvc_config *cfg, int64_t batch) {
+  const int64_t halves = 2 * 2 * batch * proj_of(cfg);
+  const int32_t splits = cfg->dim > 0 && cfg->dim % 32 == 0 ? decode_splits(cfg, batch) : 1;
+  const int64_t parts = (int64_t)splits * 2 * batch * proj_of(cfg);
+  return halves > parts ? halves : parts;
+}
+int64_t decode_counter_floats(const kvc_config *cfg, int64_t batch) {
+  return (kvc::decode_f32_tiles(batch, proj_of(cfg)) + 63) / 64 * 64;
+}
+
+// The measurement hook of kvc_time_next_projection: events pending for this
+// thread's next compressor call, taken (and cleared) at its start.
+thread_local hipEvent_t g_time_start = nullptr, g_time_stop = nullptr;
+struct ProjectionTimer {
+  hipEvent_t start, stop;
+  ProjectionTimer() : start(g_time_start), stop(g_time_stop) { g_time_start = g_time_stop = nullptr; }
+  int before(hipStream_t s) const { return start ? hip_status(hipEventRecord(start, s)) : KVC_OK; }
+  int after(hipStream_t s) const { return stop ? hip_status(hipEventRecord(stop, s)) : KVC_OK; }
+};
+
 // Prefill workspace: the kv and score planes, then (ratio 4) the f32 pooled
 // entries of the fused projection + pooling path, then the split weights:
 // bf16 [2 proj][3][dim] (KVC_PROJ_BF16_SPLIT), or f16 [2 proj][2][dim]
@@ -117,8 +142,11 @@ int64_t split_offset(const kvc_config *cfg, int64_t batch, int64_t seqlen) {
 int64_t round4(int64_t v) { return (v + 3) / 4 * 4; }
 int64_t split_floats(const kvc_config *cfg, int64_t m) {
   if (cfg->dim <= 0) return 0;
-  if (projection_of(cfg) == KVC_PROJ_F16_SPLIT) return 2 * proj_of(cfg) * cfg->dim + 2 * proj_of(cfg) + round4(m);
-  return 3 * proj_of(cfg) * cfg->dim;
+  switch (projection_of(cfg)) {
+    case KVC_PROJ_F16_SPLIT: return 2 * proj_of(cfg) * cfg->dim + 2 * proj_of(cfg) + round4(m);
+    case KVC_PROJ_BF16_SPLIT: return 3 * proj_of(cfg) * cfg->dim;
+    default: return 0;  // the f32 matrix cores read the weights as they are
+  }
 }
 
 // The fused path (projection GEMM with pooling in its epilogue) needs 4-token
@@ -186,14 +214,20 @@ int64_t kvc_decode_workspace_floats(const kvc_config *cfg, int64_t batch) {
   const int rc = check_config(cfg);
   if (rc) return rc;
   if (batch < 1) return KVC_EINVAL;
-  const int32_t splits = cfg->dim > 0 && cfg->dim % 32 == 0 ? decode_splits(cfg, batch) : 1;
-  return (int64_t)splits * 2 * batch * proj_of(cfg);
+  return decode_partial_floats(cfg, batch) + decode_counter_floats(cfg, batch);
 }
 
-int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *x, const int32_t *x_exponents,
-                       int64_t batch, int64_t seqlen, float *workspace, int64_t workspace_floats,
-                       float *kv_state, float *score_state, int64_t state_batch, const kvc_outputs *out,
-                       int64_t *n_groups, kvc_stream stream) {
+int kvc_time_next_projection(void *start, void *stop) {
+  if ((start == nullptr) != (stop == nullptr)) return KVC_EINVAL;
+  g_time_start = static_cast<hipEvent_t>(start);
+  g_time_stop = static_cast<hipEvent_t>(stop);
+  return KVC_OK;
+}
+
+int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *x, int64_t batch, int64_t seqlen,
+                       float *workspace, int64_t workspace_floats, float *kv_state, float *score_state,
+                       int64_t state_batch, const kvc_outputs *out, int64_t *n_groups, kvc_stream stream) {
+  const ProjectionTimer timer;
   int rc = check_config(cfg);
   if (rc) return rc;
   if (batch < 1 || seqlen < 0) return KVC_EINVAL;
@@ -252,7 +286,9 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *
       g.pool_hd = cfg->head_dim;
     }
     if (projection == KVC_PROJ_F32_MFMA) {
+      if ((rc = timer.before(s))) return rc;
       rc = hip_status(fused ? kvc::launch_gemm_pool(g, s) : kvc::launch_gemm(g, kvc::GemmShape::kPrefill, s));
+      if (!rc) rc = timer.after(s);
     } else {
       // the weights' parts, in the row order the kernel reads
       const bool f16 = projection == KVC_PROJ_F16_SPLIT;
@@ -277,15 +313,14 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *
       g.bsplit = split;
       if (f16) {
         g.wexp = wexp;
-        if (x_exponents) {
-          g.xexp = x_exponents;
-        } else {
-          g.xexp = xexp;
-          if ((rc = hip_status(kvc::launch_row_exponents(g.a, m, cfg->dim, cfg->dim, xexp, s)))) return rc;
-        }
-        rc = hip_status(fused ? kvc::launch_gemm_h3_pool(g, s) : kvc::launch_gemm_h3(g, s));
-      } else if (x_bf16) rc = hip_status(fused ? kvc::launch_gemm_x3_pool(g, s) : kvc::launch_gemm_x3(g, s));
+        g.xexp = xexp;
+        if ((rc = hip_status(kvc::launch_row_exponents(g.a, m, cfg->dim, cfg->dim, xexp, s)))) return rc;
+      }
+      if ((rc = timer.before(s))) return rc;
+      if (f16) rc = hip_status(fused ? kvc::launch_gemm_h3_pool(g, s) : kvc::launch_gemm_h3(g, s));
+      else if (x_bf16) rc = hip_status(fused ? kvc::launch_gemm_x3_pool(g, s) : kvc::launch_gemm_x3(g, s));
       else rc = hip_status(fused ? kvc::launch_gemm_x6_pool(g, s) : kvc::launch_gemm_x6(g, s));
+      if (!rc) rc = timer.after(s);
     }
     if (rc) return rc;
   }
@@ -346,18 +381,11 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *
   return KVC_OK;
 }
 
-int kvc_x_row_exponents(const float *x, int64_t rows, int64_t dim, int32_t *exponents, kvc_stream stream) {
-  if (rows < 0 || dim <= 0) return KVC_EINVAL;
-  if (dim % 32 != 0 || dim > kMaxDim) return KVC_EUNSUPPORTED;
-  if (rows == 0) return KVC_OK;
-  if (!x || !exponents || !aligned(x)) return KVC_EINVAL;
-  return hip_status(kvc::launch_row_exponents(x, rows, dim, dim, exponents, reinterpret_cast<hipStream_t>(stream)));
-}
-
 int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const void *x, int64_t batch,
                            int64_t start_pos, float *workspace, int64_t workspace_floats, float *kv_state,
                            float *score_state, int64_t state_batch, const kvc_outputs *out, int32_t *emitted,
                            kvc_stream stream) {
+  const ProjectionTimer timer;
   int rc = check_config(cfg);
   if (rc) return rc;
   if (batch < 1 || start_pos < 0) return KVC_EINVAL;
@@ -367,9 +395,7 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const vo
   }
   if (w && (!aligned(w->ape) || !aligned(w->norm_w))) return KVC_EINVAL;
   if (!workspace || !aligned(workspace)) return KVC_EINVAL;
-  const int64_t proj = proj_of(cfg);
-  const int32_t splits = x ? decode_splits(cfg, batch) : 1;
-  if (workspace_floats < (int64_t)splits * 2 * batch * proj) return KVC_ESPACE;
+  if (workspace_floats < decode_partial_floats(cfg, batch) + decode_counter_floats(cfg, batch)) return KVC_ESPACE;
   if (!kv_state || !score_state || state_batch < batch || !aligned(kv_state) || !aligned(score_state))
     return KVC_EINVAL;
   if ((rc = check_outputs(cfg, out))) return rc;
@@ -381,40 +407,10 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const vo
   if (emit && wants_entries(out) && (rc = check_rope(cfg, w, entry, 1))) return rc;
   if (emitted) *emitted = emit ? 1 : 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-
-  if (x) {
-    const bool x_bf16 = cfg->x_format == KVC_X_BF16;
-    kvc::GemmArgs g{};
-    g.a = x_bf16 ? nullptr : static_cast<const float *>(x);
-    g.a16 = x_bf16 ? static_cast<const uint16_t *>(x) : nullptr;
-    g.b0 = w->wkv;
-    g.b1 = w->wgate;
-    g.c0 = workspace;
-    g.c1 = workspace + batch * proj;
-    g.lda = cfg->dim;
-    g.ldb = cfg->dim;
-    g.ldc = proj;
-    g.m = batch;
-    g.n_half = proj;
-    g.k = cfg->dim;
-    g.splits = splits;
-    g.c_split_stride = 2 * batch * proj;
-    if ((rc = hip_status(kvc::launch_gemm(g, kvc::GemmShape::kDecode, s)))) return rc;
-  }
+  const int64_t proj = proj_of(cfg);
   const int slot = (int)(start_pos % r);
-  kvc::IngestArgs in{};
-  in.part = workspace;
-  in.splits = splits;
-  in.ape = w ? w->ape : nullptr;
-  in.kv_state = kv_state;
-  in.sc_state = score_state;
-  in.batch = batch;
-  in.proj = proj;
-  in.state_rows = rows_of(cfg);
-  in.slot = slot;
-  in.state_row = overlapped(cfg) ? r + slot : slot;
-  in.ratio = r;
-  in.reset_prev = (start_pos == 0 && overlapped(cfg)) ? 1 : 0;
+  const int state_row = overlapped(cfg) ? r + slot : slot;
+  const bool reset_prev = start_pos == 0 && overlapped(cfg);
 
   // the pooled entry of a completed group, over the state planes (whose
   // scores already hold the bias); at ratio 4 the block then shifts even
@@ -438,6 +434,69 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const vo
     p.shift_kv = kv_state;
     p.shift_sc = score_state;
   }
+
+  if (x && cfg->x_format == KVC_X_F32) {
+    // one launch: the projection (the prefill's two k halves) and the ingest
+    kvc::DecodeArgs d{};
+    d.x = static_cast<const float *>(x);
+    d.w0 = w->wkv;
+    d.w1 = w->wgate;
+    d.m = batch;
+    d.k = cfg->dim;
+    d.n_half = proj;
+    d.ks = kvc::decode_f32_split(cfg->dim);
+    d.part = workspace;
+    d.counters = reinterpret_cast<uint32_t *>(workspace + decode_partial_floats(cfg, batch));
+    d.ape = w->ape;
+    d.kv_state = kv_state;
+    d.sc_state = score_state;
+    d.state_rows = rows_of(cfg);
+    d.slot = slot;
+    d.state_row = state_row;
+    d.reset_rows = reset_prev ? r : 0;
+    if ((rc = timer.before(s))) return rc;
+    if ((rc = hip_status(kvc::launch_decode_f32(d, s)))) return rc;
+    if ((rc = timer.after(s))) return rc;
+    // a group completed: pool it (the only other launch of the step)
+    if (pool_now) return hip_status(kvc::launch_pool(p, r, cfg->head_dim, s));
+    return KVC_OK;
+  }
+
+  // bf16 rows (split-K partials) or given projections: the projection, then
+  // one launch that sums the parts, ingests and (groups of 2 and 4) pools
+  const int32_t splits = x ? decode_splits(cfg, batch) : 1;
+  if (x) {
+    kvc::GemmArgs g{};
+    g.a16 = static_cast<const uint16_t *>(x);
+    g.b0 = w->wkv;
+    g.b1 = w->wgate;
+    g.c0 = workspace;
+    g.c1 = workspace + batch * proj;
+    g.lda = cfg->dim;
+    g.ldb = cfg->dim;
+    g.ldc = proj;
+    g.m = batch;
+    g.n_half = proj;
+    g.k = cfg->dim;
+    g.splits = splits;
+    g.c_split_stride = 2 * batch * proj;
+    if ((rc = timer.before(s))) return rc;
+    if ((rc = hip_status(kvc::launch_gemm(g, kvc::GemmShape::kDecode, s)))) return rc;
+    if ((rc = timer.after(s))) return rc;
+  }
+  kvc::IngestArgs in{};
+  in.part = workspace;
+  in.splits = splits;
+  in.ape = w ? w->ape : nullptr;
+  in.kv_state = kv_state;
+  in.sc_state = score_state;
+  in.batch = batch;
+  in.proj = proj;
+  in.state_rows = rows_of(cfg);
+  in.slot = slot;
+  in.state_row = state_row;
+  in.ratio = r;
+  in.reset_prev = reset_prev ? 1 : 0;
   if (pool_now && r != 128) {
     // ingest and pool in one launch
     return hip_status(kvc::launch_decode_finish(in, &p, cfg->head_dim, s));

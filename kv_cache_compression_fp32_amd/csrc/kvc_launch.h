@@ -47,8 +47,10 @@ struct GemmArgs {
   const int32_t *xexp, *wexp;
 };
 
-// Prefill tiles need n_half % 128 == 0 and k % 32 == 0; decode needs
-// n_half % 32 == 0 and k % 16 == 0 (any split count; no bias).
+// Prefill tiles need n_half % 128 == 0, k % 32 == 0 and splits == 1 (each
+// output the sum p0 + p1 of two k halves split at 32 * floor(k / 64)); the
+// decode shape (bf16 a16 only, the split-K partials of `splits` parts) needs
+// n_half % 32 == 0 and k % 16 == 0, no bias.
 enum class GemmShape { kPrefill, kDecode };
 hipError_t launch_gemm(const GemmArgs &g, GemmShape shape, hipStream_t stream);
 
@@ -174,6 +176,31 @@ struct IngestArgs {
   int32_t slot, state_row, ratio, reset_prev;
 };
 hipError_t launch_decode_finish(const IngestArgs &g, const PoolArgs *pool, int head_dim, hipStream_t stream);
+
+// Decode step from f32 x (decode_f32.hip): the projections of one token per
+// batch row, summed as the prefill sums them (two k halves split at
+// ks = decode_f32_split(k), p0 + p1), and their ingest into the state: the
+// slot's bias row added to the score columns, the state row written, and
+// rows [0, reset_rows) reset to (0, -inf). The halves run in different
+// workgroups; the second to finish a tile (arrival counter in `counters`,
+// zero at rest and left zero) combines them.
+struct DecodeArgs {
+  const float *x;             // [m][k] f32
+  const float *w0, *w1;       // wkv, wgate [n_half][k]
+  int64_t m, k, n_half;       // batch, dim, proj
+  int64_t ks;                 // decode_f32_split(k)
+  float *part;                // [2][m][2 n_half] partial sums of the two halves
+  uint32_t *counters;         // [decode_f32_tiles(m, n_half)]
+  const float *ape;           // [ratio][n_half] or null
+  float *kv_state, *sc_state; // [m][state_rows][n_half] each
+  int64_t state_rows;
+  int32_t slot, state_row, reset_rows;
+};
+hipError_t launch_decode_f32(const DecodeArgs &d, hipStream_t stream);
+// tiles (= arrival counters) of a decode step over m rows, 2 n_half columns
+int64_t decode_f32_tiles(int64_t m, int64_t n_half);
+// the k split point of the projection's two halves: 32 * floor(k / 64)
+int64_t decode_f32_split(int64_t k);
 
 // Standalone RoPE of bf16 rows: row r turns its last rope_dim features by
 // table row first_row + r. in may equal out.

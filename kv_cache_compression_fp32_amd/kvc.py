@@ -59,10 +59,10 @@ _SIGNATURES = {
     "kvc_state_rows": (_I64, [ctypes.POINTER(_Config)]),
     "kvc_prefill_workspace_floats": (_I64, [ctypes.POINTER(_Config), _I64, _I64]),
     "kvc_decode_workspace_floats": (_I64, [ctypes.POINTER(_Config), _I64]),
-    "compressor_prefill": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), _P, _P, _I64, _I64,
+    "compressor_prefill": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), _P, _I64, _I64,
                                           _P, _I64, _P, _P, _I64, ctypes.POINTER(_Outputs),
                                           ctypes.POINTER(_I64), _P]),
-    "kvc_x_row_exponents": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
+    "kvc_time_next_projection": (ctypes.c_int, [_P, _P]),
     "compressor_decode_step": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), _P, _I64, _I64,
                                               _P, _I64, _P, _P, _I64, ctypes.POINTER(_Outputs),
                                               ctypes.POINTER(ctypes.c_int32), _P]),
@@ -110,7 +110,15 @@ class Config:
     fp4_format: int = KVC_FP4_E4M3_B16
     rope_dim: int = 0
     x_format: int = KVC_X_F32  # KVC_X_BF16: x is the bf16 hidden state
-    projection: int = KVC_PROJ_AUTO  # f16 split for f32 x, exact bf16 split for bf16 x
+    projection: int = KVC_PROJ_AUTO  # f32 matrix cores for f32 x, exact bf16 split for bf16 x
+
+    @property
+    def proj(self) -> int:
+        return 2 * self.head_dim if self.ratio == 4 else self.head_dim
+
+    @property
+    def state_rows(self) -> int:
+        return 2 * self.ratio if self.ratio == 4 else self.ratio
 
     @property
     def fp4_block(self) -> int:
@@ -165,6 +173,52 @@ def _ptr(t, dtype=None, name="tensor") -> int | None:
     return t.data_ptr()
 
 
+def _need(t, n: int, name: str) -> None:
+    """The C ABI takes bare pointers: a tensor of the wrong size would be read
+    or written out of bounds on the GPU, so every size is checked here."""
+    if t is not None and t.numel() != n:
+        raise ValueError(f"{name} holds {t.numel()} elements, expected {n}")
+
+
+def _check_state(cfg: "Config", kv_state, score_state, batch: int) -> int:
+    """Both state planes [state_batch, state_rows, proj], state_batch >= batch;
+    returns state_batch (0 without a state)."""
+    if (kv_state is None) != (score_state is None):
+        raise ValueError("kv_state and score_state go together")
+    if kv_state is None:
+        return 0
+    for t, name in ((kv_state, "kv_state"), (score_state, "score_state")):
+        if t.dim() != 3 or tuple(t.shape[1:]) != (cfg.state_rows, cfg.proj):
+            raise ValueError(f"{name} must be [state_batch, {cfg.state_rows}, {cfg.proj}], got {tuple(t.shape)}")
+    if kv_state.shape[0] != score_state.shape[0] or kv_state.shape[0] < batch:
+        raise ValueError("state planes must share a batch capacity of at least batch rows")
+    return kv_state.shape[0]
+
+
+def _check_weights(cfg: "Config", w: "Weights", projection: bool) -> None:
+    if projection:
+        if w.wkv is None or w.wgate is None:
+            raise ValueError("wkv and wgate are required with x")
+        _need(w.wkv, cfg.proj * cfg.dim, "wkv")
+        _need(w.wgate, cfg.proj * cfg.dim, "wgate")
+    _need(w.ape, cfg.ratio * cfg.proj, "ape")
+    _need(w.norm_w, cfg.head_dim, "norm_w")
+    if w.rope_cs is not None:
+        if w.rope_cs.dim() != 3 or tuple(w.rope_cs.shape[1:]) != (cfg.rope_dim // 2, 2):
+            raise ValueError(f"rope_cs must be [rows, {cfg.rope_dim // 2}, 2]")
+
+
+def _check_outputs(cfg: "Config", out: "Outputs | None", batch: int, groups: int) -> None:
+    if out is None:
+        return
+    hd, n = cfg.head_dim, batch * groups
+    for t, name in ((out.latent, "latent"), (out.pooled, "pooled"), (out.dequant, "dequant"),
+                    (out.rotated, "rotated")):
+        _need(t, n * hd, name)
+    _need(out.codes, n * hd // 2, "codes")
+    _need(out.scales, n * hd // cfg.fp4_block, "scales")
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -214,17 +268,17 @@ def _x_ptr(cfg: Config, x):
 def compressor_prefill(cfg: Config, w: Weights, x: torch.Tensor | None, batch: int, seqlen: int,
                        workspace: torch.Tensor, kv_state: torch.Tensor | None = None,
                        score_state: torch.Tensor | None = None, out: Outputs | None = None,
-                       stream=None, x_exponents: torch.Tensor | None = None) -> int:
-    """Enqueue a prefill; returns the number of groups (seqlen // ratio).
-    x_exponents: int32 [batch * seqlen] from x_row_exponents of the same x,
-    or None (the call computes them)."""
+                       stream=None) -> int:
+    """Enqueue a prefill; returns the number of groups (seqlen // ratio)."""
     n = ctypes.c_int64(0)
-    state_batch = kv_state.shape[0] if kv_state is not None else 0
-    if x_exponents is not None and x_exponents.numel() < batch * seqlen:
-        raise ValueError("x_exponents holds fewer than batch * seqlen values")
+    if batch < 1 or seqlen < 0:
+        raise ValueError("batch must be >= 1 and seqlen >= 0")
+    _need(x, batch * seqlen * cfg.dim, "x")
+    _check_weights(cfg, w, x is not None)
+    state_batch = _check_state(cfg, kv_state, score_state, batch)
+    _check_outputs(cfg, out, batch, seqlen // cfg.ratio)
     rc = lib().compressor_prefill(
-        ctypes.byref(cfg.c()), ctypes.byref(w.c()), _x_ptr(cfg, x), _ptr(x_exponents, torch.int32, "x_exponents"),
-        batch, seqlen,
+        ctypes.byref(cfg.c()), ctypes.byref(w.c()), _x_ptr(cfg, x), batch, seqlen,
         _ptr(workspace, torch.float32, "workspace"), workspace.numel(),
         _ptr(kv_state, torch.float32, "kv_state"), _ptr(score_state, torch.float32, "score_state"),
         state_batch, ctypes.byref(out.c()) if out is not None else None, ctypes.byref(n), _stream(stream))
@@ -232,24 +286,26 @@ def compressor_prefill(cfg: Config, w: Weights, x: torch.Tensor | None, batch: i
     return n.value
 
 
-def x_row_exponents(x: torch.Tensor, rows: int, dim: int, exponents: torch.Tensor, stream=None) -> None:
-    """Enqueue the scale exponents of `rows` f32 rows of x into int32 `exponents`."""
-    if exponents.numel() < rows or x.numel() < rows * dim:
-        raise ValueError("x or exponents smaller than rows x dim / rows")
-    _check(lib().kvc_x_row_exponents(_ptr(x, torch.float32, "x"), rows, dim, _ptr(exponents, torch.int32, "exponents"),
-                                     _stream(stream)), "kvc_x_row_exponents")
-
-
 def compressor_decode_step(cfg: Config, w: Weights, x: torch.Tensor | None, batch: int, start_pos: int,
                            workspace: torch.Tensor, kv_state: torch.Tensor, score_state: torch.Tensor,
                            out: Outputs | None = None, stream=None) -> bool:
-    """Enqueue one decode step; returns True if entries were written."""
+    """Enqueue one decode step; returns True if entries were written. The
+    workspace must be zero-filled before its first use (new_decode_workspace);
+    steps leave its arrival counters zero."""
     e = ctypes.c_int32(0)
+    if batch < 1 or start_pos < 0:
+        raise ValueError("batch must be >= 1 and start_pos >= 0")
+    _need(x, batch * cfg.dim, "x")
+    _check_weights(cfg, w, x is not None)
+    if kv_state is None or score_state is None:
+        raise ValueError("decode needs both state planes")
+    state_batch = _check_state(cfg, kv_state, score_state, batch)
+    _check_outputs(cfg, out, batch, 1)
     rc = lib().compressor_decode_step(
         ctypes.byref(cfg.c()), ctypes.byref(w.c()), _x_ptr(cfg, x), batch, start_pos,
         _ptr(workspace, torch.float32, "workspace"), workspace.numel(),
         _ptr(kv_state, torch.float32, "kv_state"), _ptr(score_state, torch.float32, "score_state"),
-        kv_state.shape[0], ctypes.byref(out.c()) if out is not None else None, ctypes.byref(e),
+        state_batch, ctypes.byref(out.c()) if out is not None else None, ctypes.byref(e),
         _stream(stream))
     _check(rc, "compressor_decode_step")
     return bool(e.value)
@@ -266,6 +322,12 @@ def compressor_ratio1_forward(cfg: Config, wkv: torch.Tensor, x: torch.Tensor, t
                               norm_w: torch.Tensor | None = None, stream=None) -> None:
     """Enqueue the ratio-1 compressor over `tokens` rows of bf16 x [tokens,
     dim] with bf16 wkv [head_dim, dim]; every token is one entry."""
+    if tokens < 0:
+        raise ValueError("tokens must be >= 0")
+    _need(x, tokens * cfg.dim, "x")
+    _need(wkv, cfg.head_dim * cfg.dim, "wkv")
+    _need(norm_w, cfg.head_dim, "norm_w")
+    _check_outputs(cfg, out, 1, tokens)
     rc = lib().compressor_ratio1_forward(
         ctypes.byref(cfg.c()), _bf16_ptr(wkv, "wkv"), _ptr(norm_w, torch.float32, "norm_w"), _bf16_ptr(x, "x"),
         tokens, _ptr(workspace, torch.float32, "workspace"), workspace.numel(),
@@ -281,12 +343,15 @@ def latent_rope(inp: torch.Tensor, rope_dim: int, rope_cs: torch.Tensor, first_r
         raise ValueError("inp must be [rows, width]")
     rows, width = inp.shape
     dst = inp if out is None else out
+    _need(dst, rows * width, "out")
+    if rope_cs.dim() != 3 or tuple(rope_cs.shape[1:]) != (rope_dim // 2, 2):
+        raise ValueError(f"rope_cs must be [rows, {rope_dim // 2}, 2]")
     rc = lib().latent_rope(_bf16_ptr(inp, "inp"), rows, width, rope_dim, _ptr(rope_cs, torch.float32, "rope_cs"),
                            rope_cs.shape[0], first_row, _bf16_ptr(dst, "out"), _stream(stream))
     _check(rc, "latent_rope")
 
 
-def _fp4_quant(fn, name, inp, codes, scales, out, stream):
+def _fp4_quant(fn, name, block, inp, codes, scales, out, stream):
     if inp.dim() != 2:
         raise ValueError("inp must be [rows, width]")
     if inp.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
@@ -294,6 +359,11 @@ def _fp4_quant(fn, name, inp, codes, scales, out, stream):
     if out is not None and out.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
         raise TypeError("out must be bf16")
     rows, width = inp.shape
+    if width % block:
+        raise ValueError(f"width must be a multiple of {block}")
+    _need(codes, rows * width // 2, "codes")
+    _need(scales, rows * width // block, "scales")
+    _need(out, rows * width, "out")
     rc = fn(_ptr(inp, None, "inp"), rows, width, _ptr(codes, torch.uint8, "codes"),
             _ptr(scales, torch.uint8, "scales"), _ptr(out, None, "out"), _stream(stream))
     _check(rc, name)
@@ -303,17 +373,32 @@ def latent_fp4_quant(inp: torch.Tensor, codes: torch.Tensor | None = None, scale
                      out: torch.Tensor | None = None, stream=None) -> None:
     """Enqueue the latent's fp4 round trip (e4m3 scales, blocks of 16) of
     [rows, width] bf16 values."""
-    _fp4_quant(lib().latent_fp4_quant, "latent_fp4_quant", inp, codes, scales, out, stream)
+    _fp4_quant(lib().latent_fp4_quant, "latent_fp4_quant", 16, inp, codes, scales, out, stream)
 
 
 def indexer_fp4_quant(inp: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
                       out: torch.Tensor | None = None, stream=None) -> None:
     """Enqueue the indexer's fp4 round trip (power-of-two scales, blocks of
     32) of [rows, width] bf16 values."""
-    _fp4_quant(lib().indexer_fp4_quant, "indexer_fp4_quant", inp, codes, scales, out, stream)
+    _fp4_quant(lib().indexer_fp4_quant, "indexer_fp4_quant", 32, inp, codes, scales, out, stream)
+
+
+def time_next_projection(start: "torch.cuda.Event | None", stop: "torch.cuda.Event | None") -> None:
+    """Measurement hook: the next compressor call of this thread records
+    `start` / `stop` (torch.cuda.Event with enable_timing, already recorded
+    once so that they exist) right before and after its projection kernel on
+    its stream. None, None clears a pending request."""
+    a = start.cuda_event if start is not None else None
+    b = stop.cuda_event if stop is not None else None
+    _check(lib().kvc_time_next_projection(a or None, b or None), "kvc_time_next_projection")
 
 
 # ----------------------------------------------------------------- convenience
+def new_decode_workspace(cfg: Config, batch: int, device="cuda") -> torch.Tensor:
+    """A zero-filled decode workspace (its arrival counters must start at 0)."""
+    return torch.zeros(kvc_decode_workspace_floats(cfg, batch), dtype=torch.float32, device=device)
+
+
 def new_state(cfg: Config, batch: int, device="cuda") -> tuple[torch.Tensor, torch.Tensor]:
     """kv_state / score_state planes initialised as the model does (kv 0,
     score -inf)."""

@@ -7,6 +7,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import kv_cache_compression_fp32_amd.kvc as kvc
 
@@ -47,19 +48,21 @@ def test_version_and_strerror():
                                                 (128, 512, 512, 128), (128, 128, 128, 128)])
 def test_sizes(ratio, hd, proj, rows):
     cfg = kvc.Config(ratio, hd, 4096)
-    assert kvc.kvc_proj_width(cfg) == proj
-    assert kvc.kvc_state_rows(cfg) == rows
-    # the two projection planes, at ratio 4 the pooled entries of the fused
-    # path, then the split weights: by default (f32 x: the f16 split) two f16
-    # parts [2 proj][2][dim], the exponents of the 2 proj weight rows and of
-    # the 300 x rows
+    assert kvc.kvc_proj_width(cfg) == proj == cfg.proj
+    assert kvc.kvc_state_rows(cfg) == rows == cfg.state_rows
+    # the two projection planes and, at ratio 4, the pooled entries of the
+    # fused path; by default (f32 x: the f32 matrix cores) nothing else
     pooled = 3 * (100 // ratio) * hd if ratio == 4 else 0
+    assert kvc.kvc_prefill_workspace_floats(cfg, 3, 100) == 2 * 3 * 100 * proj + pooled
+    assert kvc.kvc_prefill_workspace_floats(kvc.Config(ratio, hd, 4096, projection=kvc.KVC_PROJ_F32_MFMA), 3,
+                                            100) == 2 * 3 * 100 * proj + pooled
+    # the f16 split: two f16 parts [2 proj][2][dim], the exponents of the
+    # 2 proj weight rows and of the 300 x rows
     f16_parts = 2 * proj * 4096 + 2 * proj + 300
-    assert kvc.kvc_prefill_workspace_floats(cfg, 3, 100) == 2 * 3 * 100 * proj + pooled + f16_parts
     cfgh = kvc.Config(ratio, hd, 4096, projection=kvc.KVC_PROJ_F16_SPLIT)
     assert kvc.kvc_prefill_workspace_floats(cfgh, 3, 100) == 2 * 3 * 100 * proj + pooled + f16_parts
     ws = kvc.kvc_decode_workspace_floats(cfg, 64)
-    assert ws >= 2 * 64 * proj and ws % (2 * 64 * proj) == 0
+    assert ws >= 2 * 2 * 64 * proj and ws % 64 == 0
     # bf16 hidden states (and the bf16 split of f32 x): the weights' three
     # bf16 parts, [2 proj][3][dim]
     parts = 2 * proj * 3 * 4096 // 2
@@ -71,12 +74,16 @@ def test_sizes(ratio, hd, proj, rows):
 
 
 def test_decode_workspace_of_the_b64_ratio4_step():
-    # 64 rows, 2 x 1024 columns: 64 column tiles of 32, k split in 4 so that
-    # 256 workgroups (one per CU) share the step
+    # partial sums: from f32 x the two k halves, [2][64][2 x 1024]; from
+    # bf16 x the split-K parts (64 column tiles of 32, k split in 4 so that
+    # 256 workgroups share the step), [4][2][64][1024], the larger; then one
+    # arrival counter per 32 x 32 tile (2 x 64), rounded up to 64
     cfg = kvc.Config(4, 512, 4096)
-    assert kvc.kvc_decode_workspace_floats(cfg, 64) == 4 * 2 * 64 * 1024
-    # a narrower projection splits k further, at most 16 ways
-    assert kvc.kvc_decode_workspace_floats(kvc.Config(4, 128, 4096), 64) == 16 * 2 * 64 * 256
+    assert kvc.kvc_decode_workspace_floats(cfg, 64) == max(2 * 64 * 2048, 4 * 2 * 64 * 1024) + 128
+    # a narrower projection splits bf16 k further, at most 16 ways
+    assert kvc.kvc_decode_workspace_floats(kvc.Config(4, 128, 4096), 64) == 16 * 2 * 64 * 256 + 64
+    # a ragged batch: 70 rows are 3 tiles of 32
+    assert kvc.kvc_decode_workspace_floats(cfg, 70) % 64 == 0
 
 
 @pytest.mark.parametrize("cfg,code", [
@@ -104,7 +111,7 @@ def _prefill_raw(cfg, **kw):
     n = ctypes.c_int64(-7)
     w = args["w"]
     rc = lib.compressor_prefill(ctypes.byref(cfg.c()), ctypes.byref(w) if w is not None else None,
-                                args["x"], None, args["batch"], args["seqlen"], args["ws"], args["ws_n"],
+                                args["x"], args["batch"], args["seqlen"], args["ws"], args["ws_n"],
                                 args["kv"], args["sc"], args["sb"], args["out"], ctypes.byref(n), None)
     return rc, n.value
 
@@ -162,18 +169,6 @@ def test_f16_split_projection_needs_room_for_parts_and_exponents():
     assert _prefill_raw(cfg, x=fake, w=w, ws=fake, ws_n=planes + 2 * 1024 * 4096)[0] == kvc.KVC_ESPACE
 
 
-def test_x_row_exponents_argument_errors_return_before_enqueueing():
-    lib = kvc.lib()
-    fake = 0x100000  # never dereferenced: every case below fails its host checks, or has no rows
-    assert lib.kvc_x_row_exponents(fake, -1, 4096, fake, None) == kvc.KVC_EINVAL
-    assert lib.kvc_x_row_exponents(fake, 8, 0, fake, None) == kvc.KVC_EINVAL
-    assert lib.kvc_x_row_exponents(fake, 8, 100, fake, None) == kvc.KVC_EUNSUPPORTED
-    assert lib.kvc_x_row_exponents(None, 8, 4096, fake, None) == kvc.KVC_EINVAL
-    assert lib.kvc_x_row_exponents(fake, 8, 4096, None, None) == kvc.KVC_EINVAL
-    assert lib.kvc_x_row_exponents(fake + 4, 8, 4096, fake, None) == kvc.KVC_EINVAL
-    assert lib.kvc_x_row_exponents(None, 0, 4096, None, None) == kvc.KVC_OK
-
-
 def test_f32_matrix_core_projection_needs_only_the_planes():
     fake = 0x100000
     w = kvc._Weights(fake, fake, None, None)
@@ -197,6 +192,8 @@ def test_decode_argument_errors_return_before_enqueueing():
     assert call(kv=None) == kvc.KVC_EINVAL
     assert call(ws=None) == kvc.KVC_EINVAL
     assert call(ws_n=2 * 1024 - 1) == kvc.KVC_ESPACE
+    # the partial sums fit but the arrival counters after them do not
+    assert call(ws_n=kvc.kvc_decode_workspace_floats(cfg, 1) - 1) == kvc.KVC_ESPACE
     assert call(batch=2, sb=1) == kvc.KVC_EINVAL
 
 
@@ -276,3 +273,97 @@ def test_rope_arguments_are_checked():
     assert lib.latent_rope(fake, 4, 512, 64, fake + 4, 8, 0, fake, None) == kvc.KVC_EINVAL  # misaligned table
     assert lib.latent_rope(fake, 4, 512, 64, fake, 8, 0, fake + 64, None) == kvc.KVC_EINVAL  # partial overlap
     assert lib.latent_rope(None, 0, 512, 64, None, 0, 0, None, None) == kvc.KVC_OK         # nothing to do
+
+
+def test_time_hook_arguments():
+    lib = kvc.lib()
+    fake = 0x100000  # never recorded: the pending request is cleared below
+    assert lib.kvc_time_next_projection(fake, None) == kvc.KVC_EINVAL
+    assert lib.kvc_time_next_projection(None, fake) == kvc.KVC_EINVAL
+    assert lib.kvc_time_next_projection(None, None) == kvc.KVC_OK
+
+
+# ---------------------------------------------------------------- binding size checks
+def _t(shape, dtype=torch.float32):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _prefill_tensors():
+    # ratio 4, head_dim 128 (proj 256, 8 state rows), dim 64, batch 2, 12 tokens (3 entries)
+    cfg = kvc.Config(4, 128, 64)
+    w = kvc.Weights(_t((256, 64)), _t((256, 64)), _t((4, 256)), _t(128))
+    t = dict(x=_t((2, 12, 64)), kv=_t((2, 8, 256)), sc=_t((2, 8, 256)),
+             out=kvc.Outputs(latent=_t((2, 3, 128), torch.bfloat16), pooled=_t((2, 3, 128)),
+                             codes=_t((2, 3, 64), torch.uint8), scales=_t((2, 3, 8), torch.uint8)))
+    return cfg, w, t
+
+
+@pytest.mark.parametrize("bad,name", [
+    ("x", "x"), ("wkv", "wkv"), ("wgate", "wgate"), ("ape", "ape"), ("norm_w", "norm_w"),
+    ("kv", "kv_state"), ("sc", "score_state"), ("latent", "latent"), ("pooled", "pooled"),
+    ("codes", "codes"), ("scales", "scales"),
+])
+def test_prefill_binding_rejects_wrong_sizes(bad, name):
+    """The C ABI gets bare pointers, so the binding checks every tensor's size
+    against the config, batch and seqlen before calling it (no GPU needed:
+    the checks come before any device or pointer is looked at)."""
+    cfg, w, t = _prefill_tensors()
+    if bad in ("wkv", "wgate", "ape", "norm_w"):
+        setattr(w, bad, _t(getattr(w, bad).numel() + 4))
+    elif bad in ("latent", "pooled", "codes", "scales"):
+        o = getattr(t["out"], bad)
+        setattr(t["out"], bad, _t((o.shape[0], o.shape[1] + 1, o.shape[2]), o.dtype))
+    else:
+        o = t[bad]
+        t[bad] = _t((o.shape[0], o.shape[1] + 1, o.shape[2]))
+    with pytest.raises(ValueError, match=name):
+        kvc.compressor_prefill(cfg, w, t["x"], 2, 12, _t(10), t["kv"], t["sc"], t["out"])
+    # with every size right, the next check is the device
+    cfg, w, t = _prefill_tensors()
+    with pytest.raises(ValueError, match="GPU"):
+        kvc.compressor_prefill(cfg, w, t["x"], 2, 12, _t(10), t["kv"], t["sc"], t["out"])
+
+
+def test_state_planes_must_hold_the_batch():
+    cfg, w, t = _prefill_tensors()
+    with pytest.raises(ValueError, match="batch"):
+        kvc.compressor_prefill(cfg, w, t["x"], 3, 8, _t(10), t["kv"], t["sc"])
+    with pytest.raises(ValueError, match="together"):
+        kvc.compressor_prefill(cfg, w, t["x"], 2, 12, _t(10), t["kv"], None)
+
+
+def test_decode_binding_rejects_wrong_sizes():
+    cfg, w, t = _prefill_tensors()
+    one = kvc.Outputs(latent=_t((2, 1, 128), torch.bfloat16))
+    with pytest.raises(ValueError, match="x"):
+        kvc.compressor_decode_step(cfg, w, _t((2, 65)), 2, 3, _t(10), t["kv"], t["sc"], one)
+    with pytest.raises(ValueError, match="latent"):
+        kvc.compressor_decode_step(cfg, w, _t((2, 64)), 2, 3, _t(10), t["kv"], t["sc"],
+                                   kvc.Outputs(latent=_t((2, 2, 128), torch.bfloat16)))
+    with pytest.raises(ValueError, match="state"):
+        kvc.compressor_decode_step(cfg, w, _t((2, 64)), 2, 3, _t(10), None, None, one)
+    with pytest.raises(ValueError, match="GPU"):
+        kvc.compressor_decode_step(cfg, w, _t((2, 64)), 2, 3, _t(10), t["kv"], t["sc"], one)
+
+
+def test_ratio1_and_quantiser_bindings_reject_wrong_sizes():
+    cfg = kvc.Config(1, 128, 64)
+    x, wkv = _t((10, 64), torch.bfloat16), _t((128, 64), torch.bfloat16)
+    with pytest.raises(ValueError, match="wkv"):
+        kvc.compressor_ratio1_forward(cfg, _t((128, 32), torch.bfloat16), x, 10, _t(1280))
+    with pytest.raises(ValueError, match="x"):
+        kvc.compressor_ratio1_forward(cfg, wkv, x, 11, _t(1280))
+    with pytest.raises(ValueError, match="latent"):
+        kvc.compressor_ratio1_forward(cfg, wkv, x, 10, _t(1280),
+                                      kvc.Outputs(latent=_t((1, 9, 128), torch.bfloat16)))
+    inp = _t((4, 64), torch.bfloat16)
+    with pytest.raises(ValueError, match="codes"):
+        kvc.latent_fp4_quant(inp, codes=_t((4, 31), torch.uint8))
+    with pytest.raises(ValueError, match="scales"):
+        kvc.latent_fp4_quant(inp, scales=_t((4, 2), torch.uint8))
+    with pytest.raises(ValueError, match="scales"):
+        kvc.indexer_fp4_quant(inp, scales=_t((4, 4), torch.uint8))   # blocks of 32: 2 per row
+    with pytest.raises(ValueError, match="out"):
+        kvc.latent_fp4_quant(inp, out=_t((4, 48), torch.bfloat16))
+    with pytest.raises(ValueError, match="rope_cs"):
+        kvc.latent_rope(inp, 16, _t((4, 16, 2)))

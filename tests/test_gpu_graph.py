@@ -29,7 +29,7 @@ def test_decode_graph_replays_match_eager():
     w = kvc.Weights(d(rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.05)),
                     d(rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.05)),
                     d(rng.standard_normal((ratio, proj), dtype=np.float32) * np.float32(0.1)))
-    ws = torch.empty(kvc.kvc_decode_workspace_floats(cfg, batch), dtype=torch.float32, device="cuda")
+    ws = kvc.new_decode_workspace(cfg, batch)
     state = kvc.new_state(cfg, batch)
     groups = steps // ratio
     lat = torch.zeros((groups, batch, hd), dtype=torch.bfloat16, device="cuda")

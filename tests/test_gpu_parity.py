@@ -233,7 +233,7 @@ def _decode_gpu(cfg, w, batch, xs=None, kvs=None, scs=None, start=0, state=None,
     concatenated along the entry axis, and the final state."""
     proj = kvc.kvc_proj_width(cfg)
     steps = (xs if xs is not None else kvs).shape[1]
-    ws = torch.empty(kvc.kvc_decode_workspace_floats(cfg, batch), dtype=torch.float32, device="cuda")
+    ws = kvc.new_decode_workspace(cfg, batch)
     if state is None:
         state = kvc.new_state(cfg, batch)
     xd = dev_x(cfg, xs) if xs is not None else None
@@ -339,9 +339,18 @@ def test_decode_with_projection_matches_oracle(x_format):
     check_pooled(dec["pooled"], ref["pooled"])
     check_latent(dec["latent"], dec["pooled"], ref["latent"], ref["pooled"])
     check_fp4(dec["codes"], dec["scales"], dec["latent"], ref["codes"], ref["scales"], ref["latent"], dec["dequant"])
-    # and the GPU prefill over the same tokens
+    # and the GPU prefill over the same tokens: from f32 x both sum each
+    # projection in the same order, so every output is bit for bit the
+    # prefill's; from bf16 x the prefill projects on the bf16 matrix cores
     full = prefill(cfg, w, batch, steps, x=x)
-    check_pooled(dec["pooled"], full["pooled"], "decode vs prefill")
+    if x_format == kvc.KVC_X_F32:
+        for k in ("pooled", "latent", "codes", "scales", "dequant"):
+            assert np.array_equal(dec[k].view(np.uint8), full[k].view(np.uint8)), k
+        live = _live_rows(4, steps)
+        assert np.array_equal(dec["state_kv"][:, live].view(np.uint32), full["state_kv"][:, live].view(np.uint32))
+        assert np.array_equal(dec["state_sc"][:, live].view(np.uint32), full["state_sc"][:, live].view(np.uint32))
+    else:
+        check_pooled(dec["pooled"], full["pooled"], "decode vs prefill")
 
 
 @pytest.mark.parametrize("ratio,batch,dim,steps", [(2, 8, 256, 21), (128, 4, 128, 2 * 128 + 3)])
@@ -558,9 +567,13 @@ def test_fused_pooling_equals_separate_kernels_bitwise(hd, batch, seqlen, dim, o
     kvc.compressor_prefill(cfg, kvc.Weights(norm_w=W.norm_w, rope_cs=W.rope_cs), None, batch, seqlen, ws2,
                            st_u[0], st_u[1], sep)
     torch.cuda.synchronize()
-    # the fused path ran: interior plane rows were never written
-    planes = ws[:2 * batch * seqlen * proj].view(2, batch * seqlen, proj)
-    assert torch.isnan(planes[0, 100, 0]).item() and torch.isnan(planes[1, 1000, hd]).item()
+    # the fused path ran: it alone writes the pooled rows after the planes
+    # (NaN sentinel everywhere else it leaves alone)
+    pooled_rows = ws[2 * batch * seqlen * proj:2 * batch * seqlen * proj + batch * groups * hd]
+    assert not torch.isnan(pooled_rows).any().item()
+    if projection != kvc.KVC_PROJ_F32_MFMA:  # (there interior rows hold the first k half's sums)
+        planes = ws[:2 * batch * seqlen * proj].view(2, batch * seqlen, proj)
+        assert torch.isnan(planes[0, 100, 0]).item() and torch.isnan(planes[1, 1000, hd]).item()
     a, b = outputs_to_host(fused), outputs_to_host(sep)
     for k in a:
         assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
@@ -810,51 +823,12 @@ def test_f16_split_of_f32_rows_is_the_two_part_sum(ratio, hd, dim, batch, seqlen
         assert not bad.any(), f"{name}: {bad.sum()} differ, e.g. {want[bad][:4]} -> {got[bad][:4]}"
 
 
-@pytest.mark.parametrize("hd,seqlen,dim", [(128, 300, 256), (512, 16384 + 7, 64)])
-def test_shared_x_exponents_give_the_same_outputs(hd, seqlen, dim):
-    """kvc_x_row_exponents gives 15 - E for a row whose largest magnitude is
-    in [2^(E-1), 2^E) (0 for a zero row), and a prefill handed those
-    exponents writes the same bits as one that computes its own (the plain
-    kernel at 300 tokens, the pooling kernel at 16391)."""
-    note(f"shared x exponents hd={hd} seqlen={seqlen} dim={dim}")
-    from gpu_util import weights
-    rng = np.random.default_rng(hd + seqlen)
-    cfg = kvc.Config(4, hd, dim, projection=kvc.KVC_PROJ_F16_SPLIT)
-    proj = kvc.kvc_proj_width(cfg)
-    x = (rng.standard_normal((seqlen, dim)) * np.exp2(rng.integers(-20, 20, (seqlen, 1)))).astype(np.float32)
-    x[1] = 0.0
-    x[2] = (rng.standard_normal(dim) * 2.0 ** -140).astype(np.float32)   # f32 subnormals
-    w = {"wkv": (rng.standard_normal((proj, dim)) * 0.05).astype(np.float32),
-         "wgate": (rng.standard_normal((proj, dim)) * 0.05).astype(np.float32),
-         "ape": (rng.standard_normal((4, proj)) * 0.1).astype(np.float32)}
-    xd = dev(x[None])
-    exps = torch.empty(seqlen, dtype=torch.int32, device="cuda")
-    kvc.x_row_exponents(xd, seqlen, dim, exps)
-    torch.cuda.synchronize()
-    amax = np.abs(x).max(axis=1).astype(np.float64)
-    want = np.where(amax > 0, 15 - np.frexp(np.where(amax > 0, amax, 1.0))[1], 0)
-    assert np.array_equal(exps.cpu().numpy(), want)
-    groups = seqlen // 4
-    res = []
-    for given in (None, exps):
-        ws = torch.empty(kvc.kvc_prefill_workspace_floats(cfg, 1, seqlen), dtype=torch.float32, device="cuda")
-        st = kvc.new_state(cfg, 1)
-        out = kvc.new_outputs(cfg, 1, groups, latent=True, pooled=True, fp4=True)
-        kvc.compressor_prefill(cfg, weights(w), xd, 1, seqlen, ws, st[0], st[1], out, x_exponents=given)
-        torch.cuda.synchronize()
-        res.append((outputs_to_host(out), st[0].cpu().numpy(), st[1].cpu().numpy()))
-    (a, ka, sa), (b, kb, sb) = res
-    for k in a:
-        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
-    assert np.array_equal(ka.view(np.uint32), kb.view(np.uint32)) and np.array_equal(sa.view(np.uint32), sb.view(np.uint32))
-
-
 @pytest.mark.parametrize("batch,dim,hd", [(70, 2048, 128), (5, 4096, 512), (33, 1536, 512)])
 def test_decode_projection_tiles(batch, dim, hd):
-    """Decode from f32 rows through the staged projection kernel: batches that
-    are not a multiple of its 64-row tile (70: two row tiles; 5; 33), split
-    ranges of 2, 8 and 3 stages of 128 k; the emitted entries and the carried
-    state against the oracle over the same tokens."""
+    """Decode from f32 rows: batches that are not a multiple of the 32-row
+    tile (70: three row tiles; 5; 33), k halves of 8, 16 and 6 stages of 128
+    k; the emitted entries and the carried state against the oracle over the
+    same tokens, and bit for bit against the GPU prefill."""
     note(f"decode projection tiles batch={batch} dim={dim} hd={hd}")
     from gpu_util import weights
     rng = np.random.default_rng(batch + dim + hd)
@@ -876,3 +850,91 @@ def test_decode_projection_tiles(batch, dim, hd):
     assert np.array_equal(np.isfinite(dec["state_sc"][:, live]), fin)
     check_pooled(dec["state_kv"][:, live], st.kv[:, live], "state kv")
     check_pooled(np.where(fin, dec["state_sc"][:, live], 0), np.where(fin, st.score[:, live], 0), "state score")
+    full = prefill(cfg, w, batch, steps, x=x)
+    for k in ("pooled", "latent", "codes", "scales"):
+        assert np.array_equal(dec[k].view(np.uint8), full[k].view(np.uint8)), k
+    assert np.array_equal(dec["state_kv"][:, live].view(np.uint32), full["state_kv"][:, live].view(np.uint32))
+    assert np.array_equal(dec["state_sc"][:, live].view(np.uint32), full["state_sc"][:, live].view(np.uint32))
+
+
+# ratio, head_dim, dim, batch, steps: stages of 128 k (dim % 256 == 0), of 32 k
+# (k halves of 32 and 64 at dim 96; 224 and 256 at dim 480), one half (dim
+# 32), ragged batches, every ratio
+DECODE_BITWISE_CASES = [
+    (4, 512, 4096, 64, 12),
+    (4, 128, 96, 5, 9),
+    (2, 512, 32, 3, 6),
+    (128, 128, 256, 2, 130),
+    (4, 512, 480, 33, 8),
+    (2, 128, 1024, 97, 5),
+]
+
+
+@pytest.mark.parametrize("ratio,hd,dim,batch,steps", DECODE_BITWISE_CASES)
+def test_decode_equals_prefill_bitwise_from_x(ratio, hd, dim, batch, steps):
+    """From f32 hidden states a decode step sums each projection exactly as
+    the prefill's f32 matrix cores do (two k halves, the same MFMA order,
+    p0 + p1), so a decode stream and a prefill over the same tokens write the
+    same bits: entries, fp4 codes and the carried state. Also a continuation:
+    prefill of the first tokens, decode of the rest."""
+    note(f"decode == prefill bitwise from x ratio={ratio} hd={hd} dim={dim} batch={batch} steps={steps}")
+    from gpu_util import weights
+    rng = np.random.default_rng(ratio * 7 + hd + dim + batch)
+    cfg = kvc.Config(ratio, hd, dim)
+    proj = kvc.kvc_proj_width(cfg)
+    x = rng.standard_normal((batch, steps, dim), dtype=np.float32)
+    w = {"wkv": rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.05),
+         "wgate": rng.standard_normal((proj, dim), dtype=np.float32) * np.float32(0.05),
+         "ape": rng.standard_normal((ratio, proj), dtype=np.float32) * np.float32(0.1)}
+    dec = _decode_gpu(cfg, weights(w), batch, xs=x)
+    full = prefill(cfg, w, batch, steps, x=x)
+    live = _live_rows(ratio, steps)
+    if steps >= ratio:
+        for k in ("pooled", "latent", "codes", "scales", "dequant"):
+            assert np.array_equal(dec[k].view(np.uint8), full[k].view(np.uint8)), k
+    assert np.array_equal(dec["state_kv"][:, live].view(np.uint32), full["state_kv"][:, live].view(np.uint32))
+    assert np.array_equal(dec["state_sc"][:, live].view(np.uint32), full["state_sc"][:, live].view(np.uint32))
+    # prefill of n0 tokens, then decode: the same entries as the full prefill
+    n0 = steps // 2 + 1
+    state = kvc.new_state(cfg, batch)
+    first = prefill(cfg, w, batch, n0, x=x[:, :n0], state=state)
+    rest = _decode_gpu(cfg, weights(w), batch, xs=x[:, n0:], start=n0, state=state)
+    parts = [p for p in (first.get("latent"), rest.get("latent")) if p is not None]
+    if parts:
+        got = np.concatenate(parts, axis=1)
+        assert np.array_equal(got.view(np.uint16), full["latent"].view(np.uint16))
+    assert np.array_equal(rest["state_kv"][:, live].view(np.uint32), full["state_kv"][:, live].view(np.uint32))
+
+
+def test_decode_workspace_counters_rest_at_zero_and_a_dirty_one_poisons():
+    """The decode workspace's arrival counters are zero after every step (so
+    any number of steps and graph replays can share it); a workspace that was
+    not zero-filled makes the affected state rows NaN instead of silently
+    wrong values, and once it is zero-filled again the steps are correct."""
+    note("decode arrival counters")
+    from gpu_util import weights
+    rng = np.random.default_rng(17)
+    cfg = kvc.Config(4, 128, 256)
+    batch, proj = 40, 256
+    w = {"wkv": rng.standard_normal((proj, 256), dtype=np.float32) * np.float32(0.05),
+         "wgate": rng.standard_normal((proj, 256), dtype=np.float32) * np.float32(0.05)}
+    x = dev(rng.standard_normal((3, batch, 256), dtype=np.float32))
+    ws = kvc.new_decode_workspace(cfg, batch)
+    tiles = ((batch + 31) // 32) * (2 * proj // 32)
+    counters = ws[-((tiles + 63) // 64 * 64):]
+    st = kvc.new_state(cfg, batch)
+    kvc.compressor_decode_step(cfg, weights(w), x[0], batch, 0, ws, st[0], st[1])
+    torch.cuda.synchronize()
+    assert torch.all(counters.view(torch.int32) == 0).item()
+    good = st[0][:, 4].clone()
+    assert torch.isfinite(good).all().item()
+    # a dirty counter (tile 0: batch rows 0..31, kv columns 0..31)
+    counters.view(torch.int32)[0] = 5
+    kvc.compressor_decode_step(cfg, weights(w), x[0], batch, 0, ws, st[0], st[1])
+    torch.cuda.synchronize()
+    assert torch.isnan(st[0][:32, 4, :32]).all().item()
+    assert torch.equal(st[0][:, 4, 32:], good[:, 32:]) and torch.equal(st[0][32:, 4], good[32:])
+    ws.zero_()
+    kvc.compressor_decode_step(cfg, weights(w), x[0], batch, 0, ws, st[0], st[1])
+    torch.cuda.synchronize()
+    assert torch.equal(st[0][:, 4], good)
