@@ -4,26 +4,29 @@
 // One token per batch row: kv = x . wkv^T, score = x . wgate^T ("Module
 // compress", Functions, linear_f32; "DeepSeek V4.1 . Pool token pairs",
 // Compressor listing, forward, decode branch), summed exactly as the prefill
-// projection sums them (gemm_f32_kernel.h): two k halves [0, ks) and [ks, k),
-// each one chain of v_mfma_f32_16x16x4_f32 from zero over increasing 16-k
-// chunks, k-slot q of MFMA t holding k = chunk + 4 q + t, then p0 + p1. So a
-// decode step and a prefill over the same tokens write the same bits
-// ("Compressed Sparse Attention . ratio m = 4", Prefill and decode use the
-// same rule).
+// projection sums them (gemm_f32_kernel.h): the kKSegments k segments of
+// kvc_launch.h, each one chain of v_mfma_f32_16x16x4_f32 from zero over
+// increasing 16-k chunks, k-slot q of MFMA t holding k = chunk + 4 q + t,
+// then (p0 + p1) + .. in segment order. So a decode step and a prefill over
+// the same tokens write the same bits ("Compressed Sparse Attention . ratio
+// m = 4", Prefill and decode use the same rule).
 //
-// Work split: a workgroup of four wavefronts computes a 32 x 32 tile (batch
-// rows x output columns) over one k half, wavefront w owning the 16 x 16
-// fragment (w / 2, w % 2). The two halves of a tile run in two workgroups,
-// so that the chip holds about one MFMA chain per SIMD (64 rows x 2048
-// columns: 256 workgroups). Each writes its half's partial sums to the
-// workspace; an arrival counter per tile (workspace, zero at rest) tells the
-// second one to arrive, which adds the halves in order, adds the bias row of
-// the token's slot to the score columns, writes the state row and resets the
-// counter, so the next step (or a graph replay) finds it zero. No workgroup
-// waits for another.
+// Work split: a workgroup of TM / 8 wavefronts computes a TM x 32 tile (batch
+// rows x output columns) over one k segment, wavefront w owning the 16 x 16
+// fragment (w / 2, w % 2). The segments of a tile run in different
+// workgroups (64 rows x 2048 columns in two segments make 256 workgroups of
+// 32 x 32). Each writes its segment's partial sums to the workspace with
+// device-coherent stores; an arrival counter per tile (workspace, zero at
+// rest) tells the last one to arrive, which reads the other partials with
+// device-coherent loads, adds them in segment order, adds the bias row of
+// the token's slot to the score columns, writes the state row and resets
+// the counter, so the next step (or a graph replay) finds it zero. No
+// workgroup waits for another, and no cache-wide fence is needed: every
+// value that crosses workgroups is written and read coherently, and a
+// wavefront's stores have completed before its workgroup's arrival.
 //
 // Operands reach LDS through buffer loads that write it directly (no
-// registers): a stage is BK k of the tile's 32 x rows and 32 weight rows,
+// registers): a stage is BK k of the tile's TM x rows and 32 weight rows,
 // the 16-byte group q of row r at position q ^ (r & 7), so the fragment reads
 // of 8 neighbouring rows hit 8 distinct bank groups. NST stage buffers, the
 // loads NST - 1 stages ahead. The fragment reads of stage s + 1 are issued
@@ -49,7 +52,7 @@ using gemm::make_rsrc;
 using gemm::uniform_rsrc;
 using gemm::xcd_remap;
 
-constexpr int kTM = 32, kTN = 32;  // batch rows x output columns per workgroup
+constexpr int kTN = 32;  // output columns per workgroup
 
 typedef __attribute__((address_space(3))) float lds_f32;
 
@@ -63,13 +66,17 @@ __device__ __forceinline__ void barrier_no_fence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int BK, int NST>
-__global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs d) {
-  constexpr int P = BK / 4;            // 16-byte groups per row piece
-  constexpr int RPI = 64 / P;          // rows per load instruction
-  constexpr int INS = kTM / RPI / 4;   // load instructions per wavefront and operand per stage
-  constexpr int KK = BK / 16;          // 16-k chunks per stage
-  static_assert(INS >= 1 && kTM % (RPI * 4) == 0 && kTN == kTM, "stage / wavefront mismatch");
+template <int TM, int BK, int NST>
+__global__ __launch_bounds__(TM / 8 * 64) void decode_f32_kernel(DecodeArgs d) {
+  constexpr int kTM = TM, kWaves = TM / 8;  // one 16 x 16 fragment per wavefront
+  constexpr int P = BK / 4;              // 16-byte groups per row piece
+  constexpr int RPI = 64 / P;            // rows per load instruction
+  constexpr int XI = kTM / RPI;          // load instructions per stage: x
+  constexpr int WI = kTN / RPI;          //                              weights
+  constexpr int XPW = (XI + kWaves - 1) / kWaves, WPW = (WI + kWaves - 1) / kWaves;  // per wavefront
+  constexpr int KK = BK / 16;            // 16-k chunks per stage
+  static_assert(XI * RPI == kTM && WI * RPI == kTN && XI % kWaves == 0 && (WI % kWaves == 0 || WI < kWaves),
+                "stage / wavefront mismatch");
   static_assert(NST >= 3, "the loads of a stage go to the buffer read two stages before");
   __shared__ __attribute__((aligned(16))) float xs[NST][kTM * BK];
   __shared__ __attribute__((aligned(16))) float ws[NST][kTN * BK];
@@ -77,51 +84,60 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs d) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // tile order: batch row tile fastest, then k half, then column tile; each
-  // XCD walks a contiguous range, so the row tiles of a column tile read
-  // its weights through one L2
+  // tile order: batch row tile fastest, then k segment, then column tile;
+  // each XCD walks a contiguous range, so the segments of a tile meet in
+  // one L2 and share the tile's x rows there
   const int64_t m_tiles = (d.m + kTM - 1) / kTM;
-  const int halves = d.ks > 0 ? 2 : 1;
+  const int segs = d.seg > 0 ? kKSegments : 1;
   const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t mt = id % m_tiles;
-  const int half = (int)((id / m_tiles) % halves);
-  const int64_t nt = id / (m_tiles * halves);
+  const int seg = (int)((id / m_tiles) % segs);
+  const int64_t nt = id / (m_tiles * segs);
   const int64_t n_glob = nt * kTN;
   const bool second = n_glob >= d.n_half;
   const int64_t n0 = second ? n_glob - d.n_half : n_glob;
   const float *W = second ? d.w1 : d.w0;
   const int64_t m0 = mt * kTM;
-  const int64_t kbase = half == 0 ? 0 : d.ks;
-  const int64_t klen = halves == 1 ? d.k : (half == 0 ? d.ks : d.k - d.ks);
+  const int64_t kbase = segs == 1 ? 0 : seg * d.seg;
+  const int64_t klen = segs == 1 ? d.k : (seg < kKSegments - 1 ? d.seg : d.k - (kKSegments - 1) * d.seg);
   const int stages = (int)(klen / BK);
   const int64_t a_rows = d.m - m0 < kTM ? d.m - m0 : kTM;
 
-  // buffer resources from the tile's first row at the half's first k
+  // buffer resources from the tile's first row at the segment's first k
   const i32x4 a_rsrc = uniform_rsrc(make_rsrc(d.x + m0 * d.k + kbase, (uint32_t)((a_rows * d.k - kbase) * 4)));
   const i32x4 b_rsrc = uniform_rsrc(make_rsrc(W + n0 * d.k + kbase, (uint32_t)((kTN * d.k - kbase) * 4)));
-  // load u of wavefront w: rows RPI (INS w + u) + lane / P of both operands,
-  // LDS position lane % P holding the row's group (lane % P) ^ (row & 7);
-  // rows past the batch read its last row (computed, never stored)
+  // x load u of wavefront w fills rows RPI (XPW w + u) + lane / P, weight
+  // load u rows RPI (WPW w + u) + lane / P (with fewer weight loads than
+  // wavefronts, wavefront w repeats load w mod WI: same bytes to the same
+  // place, so every wavefront has the same count in flight); LDS position
+  // lane % P holds the row's group (lane % P) ^ (row & 7); rows past the
+  // batch read its last row (computed, never stored)
   const int rsub = lane / P, pos = lane % P;
-  uint32_t a_off[INS], b_off[INS];
+  uint32_t a_off[XPW], b_off[WPW];
+  int a_row0[XPW], b_row0[WPW];
 #pragma unroll
-  for (int u = 0; u < INS; ++u) {
-    const int r = RPI * (INS * wave + u) + rsub;
+  for (int u = 0; u < XPW; ++u) {
+    a_row0[u] = RPI * (XPW * wave + u);
+    const int r = a_row0[u] + rsub;
     const int64_t rr = r < a_rows ? r : a_rows - 1;
     a_off[u] = (uint32_t)((rr * d.k + 4 * (pos ^ (r & 7))) * 4);
+  }
+#pragma unroll
+  for (int u = 0; u < WPW; ++u) {
+    b_row0[u] = RPI * (WI < kWaves ? wave % WI : WPW * wave + u);
+    const int r = b_row0[u] + rsub;
     b_off[u] = (uint32_t)(((int64_t)r * d.k + 4 * (pos ^ (r & 7))) * 4);
   }
   auto issue = [&](int s, int buf) {
     const int32_t koff = s * BK * 4;
 #pragma unroll
-    for (int u = 0; u < INS; ++u)
-      buffer_load_lds(a_rsrc, (lds_u32 *)(&xs[buf][RPI * (INS * wave + u) * BK]), 16, (int32_t)a_off[u], koff, 0,
-                      0);
+    for (int u = 0; u < XPW; ++u)
+      buffer_load_lds(a_rsrc, (lds_u32 *)(&xs[buf][a_row0[u] * BK]), 16, (int32_t)a_off[u], koff, 0, 0);
 #pragma unroll
-    for (int u = 0; u < INS; ++u)
-      buffer_load_lds(b_rsrc, (lds_u32 *)(&ws[buf][RPI * (INS * wave + u) * BK]), 16, (int32_t)b_off[u], koff, 0,
-                      0);
+    for (int u = 0; u < WPW; ++u)
+      buffer_load_lds(b_rsrc, (lds_u32 *)(&ws[buf][b_row0[u] * BK]), 16, (int32_t)b_off[u], koff, 0, 0);
   };
+  constexpr int PER_STAGE = XPW + WPW;  // loads in flight per stage and wavefront
 
   const int fi = wave >> 1, fj = wave & 1, row_in = lane & 15, slot = lane >> 4;
   const int ra = 16 * fi + row_in, rb = 16 * fj + row_in;
@@ -159,8 +175,8 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs d) {
     landed(ca, cb);
     const int ahead = s + NST - 1;
     issue(ahead < stages ? ahead : stages - 1, ahead % NST);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * 2 * INS));  // this wavefront's stage s + 1 landed
-    barrier_no_fence();                                          // every wavefront's
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * PER_STAGE));  // this wavefront's stage s + 1 landed
+    barrier_no_fence();                                           // every wavefront's
     if (s + 1 < stages) read((s + 1) % NST, na, nb);
     __builtin_amdgcn_sched_barrier(0);
     chain(ca, cb);
@@ -169,7 +185,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs d) {
   f4 a0[KK], b0[KK], a1[KK], b1[KK];
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s) issue(s < stages ? s : stages - 1, s);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * 2 * INS));  // stage 0
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * PER_STAGE));  // stage 0
   barrier_no_fence();
   read(0, a0, b0);
   for (int s = 0; s < stages; s += 2) {
@@ -184,31 +200,37 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs d) {
   const int64_t col = n_glob + 16 * fj + row_in;
   const int64_t row0 = m0 + 16 * fi + 4 * slot;
   float tot[4] = {acc[0], acc[1], acc[2], acc[3]};
-  if (halves == 2) {
-    float *mine = d.part + (int64_t)half * d.m * ncols;
+  if (segs > 1) {
+    const int64_t plane = d.m * ncols;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (row0 + r < d.m) mine[(row0 + r) * ncols + col] = acc[r];
-    __threadfence();  // release: this half's partial sums, before the arrival
-    __syncthreads();
+      if (row0 + r < d.m)
+        __hip_atomic_store(d.part + seg * plane + (row0 + r) * ncols + col, acc[r], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wavefront's partial sums are stored
+    __syncthreads();                           // and every wavefront's
     uint32_t *counter = d.counters + nt * m_tiles + mt;
-    if (threadIdx.x == 0) s_arrival = atomicAdd(counter, 1u);
+    if (threadIdx.x == 0) s_arrival = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     const uint32_t arrived = s_arrival;
-    if (arrived == 0) return;  // the other half finishes the tile
-    __threadfence();           // acquire: the other half's partial sums
-    const float *other = d.part + (int64_t)(1 - half) * d.m * ncols;
+    if (arrived + 1 < (uint32_t)segs) return;  // another segment finishes the tile
     // a counter that was not zero at the call: the caller's workspace was not
     // zero-filled; the state row turns NaN rather than silently wrong
-    const bool bad = arrived != 1;
+    const bool bad = arrived + 1 != (uint32_t)segs;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (row0 + r < d.m) {
-        // p0 + p1 (addition is commutative: the same bits from either half)
-        const float o = other[(row0 + r) * ncols + col];
-        tot[r] = bad ? __builtin_nanf("") : o + acc[r];
+        float t = 0.0f;
+#pragma unroll
+        for (int sg = 0; sg < kKSegments; ++sg) {
+          const float p = sg == seg ? acc[r]
+                                    : __hip_atomic_load(d.part + sg * plane + (row0 + r) * ncols + col,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          t = sg == 0 ? p : t + p;  // (p0 + p1) + ..
+        }
+        tot[r] = bad ? __builtin_nanf("") : t;
       }
-    if (threadIdx.x == 0) *counter = 0u;  // at rest for the next step
+    if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // the ingest: the bias row of the token's slot joins the gate logits in
   // one f32 addition, then the state row (and at ratio 4 from position 0 the
@@ -228,30 +250,31 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs d) {
   }
 }
 
-template <int BK, int NST>
-hipError_t launch(const DecodeArgs &d, int64_t tiles, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_f32_kernel<BK, NST>), dim3((uint32_t)tiles), dim3(256), 0, stream, d);
+template <int TM, int BK, int NST>
+hipError_t launch(const DecodeArgs &d, hipStream_t stream) {
+  const int64_t tiles = ((d.m + TM - 1) / TM) * (2 * d.n_half / kTN) * (d.seg > 0 ? kKSegments : 1);
+  hipLaunchKernelGGL((decode_f32_kernel<TM, BK, NST>), dim3((uint32_t)tiles), dim3(TM / 8 * 64), 0, stream, d);
   return hipGetLastError();
 }
 
+constexpr int kDecTM = 32;  // batch rows per workgroup
+
 }  // namespace
 
-int64_t decode_f32_tiles(int64_t m, int64_t n_half) { return ((m + kTM - 1) / kTM) * (2 * n_half / kTN); }
-
-int64_t decode_f32_split(int64_t k) { return 32 * (k / 64); }
+int64_t decode_f32_tiles(int64_t m, int64_t n_half) { return ((m + kDecTM - 1) / kDecTM) * (2 * n_half / kTN); }
 
 hipError_t launch_decode_f32(const DecodeArgs &d, hipStream_t stream) {
   if (d.m <= 0) return hipSuccess;
   // whole 32-column tiles, 32-k granules, and tile rows addressable with
   // 32-bit buffer offsets
-  if (d.n_half % kTN != 0 || d.k % 32 != 0 || d.ks != decode_f32_split(d.k) || d.k <= 0 ||
-      (int64_t)kTM * d.k * 4 > INT32_MAX || (d.ks > 0 && !d.part) || !d.counters || d.slot < 0 ||
+  if (d.n_half % kTN != 0 || d.k % 32 != 0 || d.seg != kseg_length(d.k) || d.k <= 0 ||
+      (int64_t)kDecTM * d.k * 4 > INT32_MAX || (d.seg > 0 && !d.part) || !d.counters || d.slot < 0 ||
       d.state_row < 0 || d.state_row >= d.state_rows || d.reset_rows < 0 || d.reset_rows > d.state_rows)
     return hipErrorInvalidValue;
-  const int64_t tiles = decode_f32_tiles(d.m, d.n_half) * (d.ks > 0 ? 2 : 1);
-  // stages of 128 k when both halves are whole stages, else of 32 k
-  const bool wide = d.ks % 128 == 0 && (d.k - d.ks) % 128 == 0;
-  return wide ? launch<128, 4>(d, tiles, stream) : launch<32, 8>(d, tiles, stream);
+  // stages of 128 k when every segment is whole stages, else of 32 k
+  const int64_t last = d.k - (kKSegments - 1) * d.seg;
+  const bool wide = d.seg > 0 && d.seg % 128 == 0 && last % 128 == 0;
+  return wide ? launch<kDecTM, 128, 4>(d, stream) : launch<kDecTM, 32, 8>(d, stream);
 }
 
 }  // namespace kvc

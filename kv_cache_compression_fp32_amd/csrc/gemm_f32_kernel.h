@@ -14,17 +14,19 @@
 // for both operands and every k is covered once, in the same order for every
 // output element.
 //
-// Summation order: each output is p0 + p1, p0 the chain of MFMAs over the
-// k range [0, ks) and p1 over [ks, k), ks = 32 * floor(k / 64), each chain
-// starting from zero and taking the 16-k chunks in increasing k (p1 alone
-// when ks is 0). Between the halves the tile's p0 waits in its own output
-// positions of C. The decode projection (decode_f32.hip) computes the same
-// two chains for one token, so a token's projections have the same bits
-// whichever path computes them.
+// Summation order: each output is (p0 + p1) + ..., p_s the chain of MFMAs
+// over the k segment [s L, (s + 1) L) of the kKSegments segments
+// (kvc_launch.h; the last one to k), L = 32 * floor(k / (32 kKSegments)),
+// each chain starting from zero and taking the 16-k chunks in increasing k
+// (one chain over all of k when L is 0). The decode projection
+// (decode_f32.hip) computes the same chains for one token, so a token's
+// projections have the same bits whichever path computes them.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "gemm_common.h"
 #include "gemm_epilogue.h"
@@ -158,53 +160,79 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[sl][i][s], fb[sl][j][s], acc[i][j], 0, 0, 0);
   };
 
-  // Accumulator element (i, j, r) of this lane belongs at row band0 + 16 i
-  // + 4 slot + r and a column of its fragment; its address is a
-  // wavefront-uniform row pointer (scalar registers) plus the lane's offset
-  // 4 slot ldc + lane % 16, so stash and readback need no address registers
-  // per element. Rows past the end of A are skipped.
-  // The lane's values are derived from a fresh lane id where they are used,
-  // so that nothing extra stays live through the k loops.
-  const int wm_u = wave_u / WAVES_N, wn_u = wave_u % WAVES_N;
-  const int64_t band0 = m0 + wm_u * WM;
-  auto lane_place = [&](int &rows_left, uint32_t &lane_off) {
+  // The k segments (see the header): stages [0, L), [L, 2 L), .. of 32 k, L
+  // = floor(k / (32 kKSegments)), the last segment to k / 32; each segment's
+  // chain starts from zero, and the running sum p0, then p0 + p1, ..
+  // waits between segments in the tile's own output positions of C, which no
+  // other tile reads or writes (a ragged last row tile, whose rows past the
+  // end of A do not exist in C, uses g.rag instead: BM rows of its column
+  // tile's BN columns). The sum is kept lane-major, each store or load
+  // instruction of a wavefront covering one contiguous KiB: wavefront w owns
+  // rows 32 w .. 32 w + 31 of the tile, and its accumulator fragment q (of
+  // FM x FN) goes to row 32 w + q (BN = 256; with BN = 128, rows 32 w + 2 q
+  // and 32 w + 2 q + 1), lane l at 16-byte position l of that KiB (with POOL
+  // the four 256-byte pieces of the row's kv branch A, kv branch B, score
+  // branch A and score branch B columns of the tile's 64 features). The
+  // lane's pointer is derived from a fresh lane id where it is used, so that
+  // nothing extra stays live through the k loop.
+  const int kt_seg = (int)(g.k / (32 * kKSegments));
+  constexpr int NQ = FM * FN;  // accumulator fragments per lane
+  static_assert(BM / NW == 32 && (BN == 256 || BN == 128) && NQ * 64 * 16 == 32 * BN * 4,
+                "the lane-major layout covers the wavefront's 32 rows of the tile");
+  constexpr int QROWS = BN == 256 ? 1 : 2;  // tile rows between fragment slots q and q + 1
+  auto sum_ptr = [&](int64_t &stride) -> float * {
     const int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    const int64_t left = g.m - band0 - 4 * (l >> 4);
-    rows_left = left < WM ? (int)left : WM;  // rows of this lane's groups inside A (may be <= 0)
-    lane_off = (uint32_t)(4 * (l >> 4) * g.ldc + (l & 15));
-  };
-  auto row_ptr = [&](int i, int j, int r) -> float * {
-    const int64_t row = band0 + 16 * i + r;
+    const int64_t r0 = 32 * wave_u + (BN == 256 ? 0 : (l >> 5));  // the lane's row for q = 0
+    const int c4 = BN == 256 ? 4 * l : 4 * (l & 31);                // the lane's column offset in a row
+    if (m0 + BM > g.m) {
+      stride = BN;
+      return g.rag + nt * BM * BN + r0 * BN + c4;
+    }
+    stride = g.ldc;
     if constexpr (POOL) {
-      constexpr int F = WN / 4, FJ = F / 16;  // pool_epilogue's column segments
-      const int seg = j / FJ, jj = j % FJ;
-      return (seg >= 2 ? g.c1 : g.c0) + row * g.ldc + (seg & 1) * g.pool_hd + f0 + F * wn_u + 16 * jj;
+      const int piece = l >> 4;
+      return (piece >= 2 ? g.c1 : g.c0) + (m0 + r0) * g.ldc + (piece & 1) * g.pool_hd + f0 + 4 * (l & 15);
     } else {
-      return C + row * g.ldc + n0 + wn_u * WN + 16 * j;
+      return C + (m0 + r0) * g.ldc + n0 + c4;
+    }
+  };
+  // mode 0: store the accumulators; 1: add them to the stored sum and store
+  // that; 2: add them to the stored sum (the final sum). The accumulators
+  // restart from zero after modes 0 and 1. Loads go in chunks (8 fragments
+  // inside the k loop, 16 after it), each drained before the next, so that
+  // few registers are held.
+  auto spill = [&](auto mode_tag) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    int64_t stride;
+    float *p = sum_ptr(stride);
+    if constexpr (MODE == 0) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) *reinterpret_cast<f4 *>(p + QROWS * q * stride) = acc[q / FN][q % FN];
+    } else {
+      constexpr int CH = MODE == 2 ? (NQ < 16 ? NQ : 16) : (NQ < 8 ? NQ : 8);
+#pragma unroll
+      for (int q0 = 0; q0 < NQ; q0 += CH) {
+        f4 t[CH];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) t[u] = *reinterpret_cast<const f4 *>(p + QROWS * (q0 + u) * stride);
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+          f4 &a = acc[(q0 + u) / FN][(q0 + u) % FN];
+          const f4 sum = f4{t[u][0] + a[0], t[u][1] + a[1], t[u][2] + a[2], t[u][3] + a[3]};
+          if constexpr (MODE == 1) *reinterpret_cast<f4 *>(p + QROWS * (q0 + u) * stride) = sum;
+          else a = sum;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if constexpr (MODE != 2) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
     }
   };
 
-  // p0 waits in the tile's own output positions (no other tile reads or
-  // writes them), the accumulators restart from zero for p1
-  auto stash = [&]() {
-    int rows_left;
-    uint32_t lane_off;
-    lane_place(rows_left, lane_off);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (16 * i + r < rows_left) {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) row_ptr(i, j, r)[lane_off] = acc[i][j][r];
-        }
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
-  };
-
-  const int kt_mid = kt_count / 2;  // ks / 32: the first stage of p1 (0: p1 alone)
   issue(0, 0);
   wait_vm0();
   __syncthreads();
@@ -217,7 +245,12 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
       mfma_slice(LAST, 3);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt == kt_mid && kt_mid > 0) stash();
+    // a segment ended with the previous stage: p0 is stored, later ones join
+    // the stored sum (the previous stage's fragment registers are free here)
+    if (kKSegments > 1 && kt_seg > 0 && kt <= (kKSegments - 1) * kt_seg && kt % kt_seg == 0 && kt > 0) {
+      if (kKSegments == 2 || kt == kt_seg) spill(std::integral_constant<int, 0>{});
+      else spill(std::integral_constant<int, 1>{});
+    }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       if (c + 1 < NCH) fload(st, c + 1, (c + 1) & 1);
@@ -233,19 +266,12 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_f32_kernel(GemmArgs g) {
     __syncthreads();                    // everyone's landed; everyone is done reading this stage
   }
   if (DEFER) mfma_slice(LAST, 3);
-  if (kt_mid > 0) {
-    // p0 + p1 (the same lane wrote p0, so it reads its own stores back)
-    int rows_left;
-    uint32_t lane_off;
-    lane_place(rows_left, lane_off);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (16 * i + r < rows_left) {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j][r] = row_ptr(i, j, r)[lane_off] + acc[i][j][r];
-        }
+  // (p0 + p1) + .. (each lane reads back what it stored); the outputs then
+  // go to positions whose stored sums other lanes read, so every wavefront
+  // first finishes its reads
+  if (kKSegments > 1 && kt_seg > 0) {
+    spill(std::integral_constant<int, 2>{});
+    __syncthreads();
   }
 
   if constexpr (POOL) {
@@ -379,6 +405,7 @@ inline hipError_t launch_pooling(const GemmArgs &g, hipStream_t stream) {
   // the flattened rows, tile rows addressable with 32-bit buffer offsets
   if (g.k % kBK != 0 || g.pool_hd % 64 != 0 || g.ldc != 2 * g.pool_hd || g.lda < g.k || g.ldb < g.k ||
       g.m != g.pool_batch * g.pool_seqlen || (g.pool_batch > 1 && g.pool_seqlen % 4 != 0) || !g.pooled ||
+      (g.m % 256 != 0 && !g.rag) ||
       (int64_t)256 * g.lda * 4 > INT32_MAX || (int64_t)32 * g.ldb * 4 > INT32_MAX)
     return hipErrorInvalidValue;
   const int64_t m_tiles = (g.m + 255) / 256;
@@ -391,7 +418,7 @@ template <int BM, int BN, int WM, int WN, int NW, int MINW, bool DEFER>
 hipError_t launch_tiled(const GemmArgs &g, hipStream_t stream) {
   // every column tile inside one half, whole k tiles, and a tile's rows
   // addressable by a 32-bit buffer offset
-  if (g.n_half % BN != 0 || g.splits != 1 || g.k % kBK != 0 ||
+  if (g.n_half % BN != 0 || g.splits != 1 || g.k % kBK != 0 || (g.m % BM != 0 && !g.rag) ||
       (g.bias1 && (g.bias_seqlen < 1 || g.bias_ratio < 1 || (g.bias_ratio & (g.bias_ratio - 1)) != 0)) || g.lda < g.k || g.ldb < g.k ||
       (int64_t)BM * g.lda * 4 > INT32_MAX || (int64_t)BN * g.ldb * 4 > INT32_MAX)
     return hipErrorInvalidValue;

@@ -104,12 +104,12 @@ int32_t decode_splits(const kvc_config *cfg, int64_t batch) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_EHIP; }
 
-// Decode workspace: the partial sums (f32 x: the two k halves, [2][batch]
-// [2 proj]; bf16 x: the split-K parts, [splits][2][batch][proj]; given
+// Decode workspace: the partial sums (f32 x: the k segments, [kKSegments]
+// [batch][2 proj]; bf16 x: the split-K parts, [splits][2][batch][proj]; given
 // projections: [2][batch][proj] at the start), then the f32 path's arrival
 // counters, one per tile, rounded up to 64.
 int64_t decode_partial_floats(const kvc_config *cfg, int64_t batch) {
-  const int64_t halves = 2 * 2 * batch * proj_of(cfg);
+  const int64_t halves = kvc::kKSegments * 2 * batch * proj_of(cfg);
   const int32_t splits = cfg->dim > 0 && cfg->dim % 32 == 0 ? decode_splits(cfg, batch) : 1;
   const int64_t parts = (int64_t)splits * 2 * batch * proj_of(cfg);
   return halves > parts ? halves : parts;
@@ -129,10 +129,12 @@ struct ProjectionTimer {
 };
 
 // Prefill workspace: the kv and score planes, then (ratio 4) the f32 pooled
-// entries of the fused projection + pooling path, then the split weights:
-// bf16 [2 proj][3][dim] (KVC_PROJ_BF16_SPLIT), or f16 [2 proj][2][dim]
-// followed by the int32 scale exponents of the 2 proj weight rows and of the
-// batch * seqlen rows of x (KVC_PROJ_F16_SPLIT; each part 16-byte aligned).
+// entries of the fused projection + pooling path, then for the f32 matrix
+// cores the running sums of a ragged last row tile (256 rows of both
+// planes' columns), or the split weights: bf16 [2 proj][3][dim]
+// (KVC_PROJ_BF16_SPLIT), or f16 [2 proj][2][dim] followed by the int32 scale
+// exponents of the 2 proj weight rows and of the batch * seqlen rows of x
+// (KVC_PROJ_F16_SPLIT; each part 16-byte aligned).
 int64_t pooled_floats(const kvc_config *cfg, int64_t batch, int64_t seqlen) {
   return overlapped(cfg) ? batch * (seqlen / cfg->ratio) * cfg->head_dim : 0;
 }
@@ -145,7 +147,7 @@ int64_t split_floats(const kvc_config *cfg, int64_t m) {
   switch (projection_of(cfg)) {
     case KVC_PROJ_F16_SPLIT: return 2 * proj_of(cfg) * cfg->dim + 2 * proj_of(cfg) + round4(m);
     case KVC_PROJ_BF16_SPLIT: return 3 * proj_of(cfg) * cfg->dim;
-    default: return 0;  // the f32 matrix cores read the weights as they are
+    default: return kvc::gemm_rag_floats(proj_of(cfg));  // the f32 matrix cores
   }
 }
 
@@ -241,8 +243,8 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *
   const bool x_bf16 = cfg->x_format == KVC_X_BF16;
   // with x the split weights sit after the planes and pooled rows
   const int32_t projection = projection_of(cfg);
-  const bool split_proj = x && m > 0 && projection != KVC_PROJ_F32_MFMA;
-  const int64_t need = split_proj ? split_offset(cfg, batch, seqlen) + split_floats(cfg, m) : 2 * m * proj;
+  const bool with_x = x && m > 0;
+  const int64_t need = with_x ? split_offset(cfg, batch, seqlen) + split_floats(cfg, m) : 2 * m * proj;
   if (need > 0 && !workspace) return KVC_EINVAL;
   if (workspace_floats < need) return KVC_ESPACE;
   if (!aligned(workspace)) return KVC_EINVAL;
@@ -286,6 +288,7 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *
       g.pool_hd = cfg->head_dim;
     }
     if (projection == KVC_PROJ_F32_MFMA) {
+      g.rag = workspace + split_offset(cfg, batch, seqlen);
       if ((rc = timer.before(s))) return rc;
       rc = hip_status(fused ? kvc::launch_gemm_pool(g, s) : kvc::launch_gemm(g, kvc::GemmShape::kPrefill, s));
       if (!rc) rc = timer.after(s);
@@ -444,7 +447,7 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const vo
     d.m = batch;
     d.k = cfg->dim;
     d.n_half = proj;
-    d.ks = kvc::decode_f32_split(cfg->dim);
+    d.seg = kvc::kseg_length(cfg->dim);
     d.part = workspace;
     d.counters = reinterpret_cast<uint32_t *>(workspace + decode_partial_floats(cfg, batch));
     d.ape = w->ape;

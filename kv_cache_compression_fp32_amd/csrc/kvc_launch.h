@@ -45,14 +45,21 @@ struct GemmArgs {
   // the row exponents of the scaled split (x rows: launch_row_exponents,
   // weight rows: launch_split_weights with f16 set)
   const int32_t *xexp, *wexp;
+  // f32 matrix cores (launch_gemm, launch_gemm_pool): gemm_rag_floats(m,
+  // n_half) f32 where a ragged last row tile keeps its running sum between
+  // k segments (tiles with every row inside m keep it in C)
+  float *rag;
 };
 
 // Prefill tiles need n_half % 128 == 0, k % 32 == 0 and splits == 1 (each
-// output the sum p0 + p1 of two k halves split at 32 * floor(k / 64)); the
+// output summed over the kKSegments k segments defined below); the
 // decode shape (bf16 a16 only, the split-K partials of `splits` parts) needs
 // n_half % 32 == 0 and k % 16 == 0, no bias.
 enum class GemmShape { kPrefill, kDecode };
 hipError_t launch_gemm(const GemmArgs &g, GemmShape shape, hipStream_t stream);
+
+// Floats of GemmArgs.rag: 256 rows of every column of both halves.
+inline int64_t gemm_rag_floats(int64_t n_half) { return 256 * 2 * n_half; }
 
 // The ratio-4 projection with pooling in the epilogue (fields above):
 // b0 = wkv, b1 = wgate ([2 * pool_hd][k] each), m = pool_batch * pool_seqlen,
@@ -177,19 +184,28 @@ struct IngestArgs {
 };
 hipError_t launch_decode_finish(const IngestArgs &g, const PoolArgs *pool, int head_dim, hipStream_t stream);
 
+// The f32 matrix-core projections sum every output over kKSegments k
+// segments, the first kKSegments - 1 of 32 * floor(k / (32 kKSegments)) k
+// and the last one to k, each one chain of MFMAs from zero, then the chains'
+// results in segment order ((p0 + p1) + ...). Prefill (gemm_f32_kernel.h)
+// and decode (decode_f32.hip) share it, so they give the same bits.
+constexpr int kKSegments = 2;
+inline int64_t kseg_length(int64_t k) { return 32 * (k / (32 * kKSegments)); }
+
 // Decode step from f32 x (decode_f32.hip): the projections of one token per
-// batch row, summed as the prefill sums them (two k halves split at
-// ks = decode_f32_split(k), p0 + p1), and their ingest into the state: the
-// slot's bias row added to the score columns, the state row written, and
-// rows [0, reset_rows) reset to (0, -inf). The halves run in different
-// workgroups; the second to finish a tile (arrival counter in `counters`,
-// zero at rest and left zero) combines them.
+// batch row, summed as the prefill sums them (kKSegments k segments of seg =
+// kseg_length(k); one chain when seg is 0),
+// and their ingest into the state: the slot's bias row added to the score
+// columns, the state row written, and rows [0, reset_rows) reset to (0,
+// -inf). The segments run in different workgroups; the last to finish a
+// tile (arrival counter in `counters`, zero at rest and left zero) combines
+// them.
 struct DecodeArgs {
   const float *x;             // [m][k] f32
   const float *w0, *w1;       // wkv, wgate [n_half][k]
   int64_t m, k, n_half;       // batch, dim, proj
-  int64_t ks;                 // decode_f32_split(k)
-  float *part;                // [2][m][2 n_half] partial sums of the two halves
+  int64_t seg;                // kseg_length(k)
+  float *part;                // [kKSegments][m][2 n_half] partial sums of the segments
   uint32_t *counters;         // [decode_f32_tiles(m, n_half)]
   const float *ape;           // [ratio][n_half] or null
   float *kv_state, *sc_state; // [m][state_rows][n_half] each
@@ -199,8 +215,6 @@ struct DecodeArgs {
 hipError_t launch_decode_f32(const DecodeArgs &d, hipStream_t stream);
 // tiles (= arrival counters) of a decode step over m rows, 2 n_half columns
 int64_t decode_f32_tiles(int64_t m, int64_t n_half);
-// the k split point of the projection's two halves: 32 * floor(k / 64)
-int64_t decode_f32_split(int64_t k);
 
 // Standalone RoPE of bf16 rows: row r turns its last rope_dim features by
 // table row first_row + r. in may equal out.

@@ -51,11 +51,13 @@ def test_sizes(ratio, hd, proj, rows):
     assert kvc.kvc_proj_width(cfg) == proj == cfg.proj
     assert kvc.kvc_state_rows(cfg) == rows == cfg.state_rows
     # the two projection planes and, at ratio 4, the pooled entries of the
-    # fused path; by default (f32 x: the f32 matrix cores) nothing else
+    # fused path; by default (f32 x: the f32 matrix cores) then the running
+    # sums of a ragged last row tile, 256 rows of both planes' columns
     pooled = 3 * (100 // ratio) * hd if ratio == 4 else 0
-    assert kvc.kvc_prefill_workspace_floats(cfg, 3, 100) == 2 * 3 * 100 * proj + pooled
+    rag = 256 * 2 * proj
+    assert kvc.kvc_prefill_workspace_floats(cfg, 3, 100) == 2 * 3 * 100 * proj + pooled + rag
     assert kvc.kvc_prefill_workspace_floats(kvc.Config(ratio, hd, 4096, projection=kvc.KVC_PROJ_F32_MFMA), 3,
-                                            100) == 2 * 3 * 100 * proj + pooled
+                                            100) == 2 * 3 * 100 * proj + pooled + rag
     # the f16 split: two f16 parts [2 proj][2][dim], the exponents of the
     # 2 proj weight rows and of the 300 x rows
     f16_parts = 2 * proj * 4096 + 2 * proj + 300
@@ -74,16 +76,16 @@ def test_sizes(ratio, hd, proj, rows):
 
 
 def test_decode_workspace_of_the_b64_ratio4_step():
-    # partial sums: from f32 x the two k halves, [2][64][2 x 1024]; from
+    # partial sums: from f32 x the two k segments, [2][64][2 x 1024]; from
     # bf16 x the split-K parts (64 column tiles of 32, k split in 4 so that
-    # 256 workgroups share the step), [4][2][64][1024], the larger; then one
-    # arrival counter per 32 x 32 tile (2 x 64), rounded up to 64
+    # 256 workgroups share the step), [4][2][64][1024]; the larger of the two;
+    # then one arrival counter per 32 x 32 tile (2 x 64), rounded up to 64
     cfg = kvc.Config(4, 512, 4096)
     assert kvc.kvc_decode_workspace_floats(cfg, 64) == max(2 * 64 * 2048, 4 * 2 * 64 * 1024) + 128
     # a narrower projection splits bf16 k further, at most 16 ways
     assert kvc.kvc_decode_workspace_floats(kvc.Config(4, 128, 4096), 64) == 16 * 2 * 64 * 256 + 64
-    # a ragged batch: 70 rows are 3 tiles of 32
-    assert kvc.kvc_decode_workspace_floats(cfg, 70) % 64 == 0
+    # a ragged batch: 70 rows are 3 tiles of 32 (192 counters); bf16 splits k in 2
+    assert kvc.kvc_decode_workspace_floats(cfg, 70) == 2 * 70 * 2048 + 192
 
 
 @pytest.mark.parametrize("cfg,code", [
@@ -169,12 +171,15 @@ def test_f16_split_projection_needs_room_for_parts_and_exponents():
     assert _prefill_raw(cfg, x=fake, w=w, ws=fake, ws_n=planes + 2 * 1024 * 4096)[0] == kvc.KVC_ESPACE
 
 
-def test_f32_matrix_core_projection_needs_only_the_planes():
+def test_f32_matrix_core_projection_needs_the_planes_and_the_ragged_tile_sums():
     fake = 0x100000
     w = kvc._Weights(fake, fake, None, None)
     cfg = kvc.Config(4, 512, 4096, projection=kvc.KVC_PROJ_F32_MFMA)
-    planes = 2 * 8 * 1024
-    assert _prefill_raw(cfg, x=fake, w=w, ws=fake, ws_n=planes - 1)[0] == kvc.KVC_ESPACE
+    full = kvc.kvc_prefill_workspace_floats(cfg, 1, 8)
+    assert full == 2 * 8 * 1024 + 2 * 512 + 256 * 2048
+    assert _prefill_raw(cfg, x=fake, w=w, ws=fake, ws_n=full - 1)[0] == kvc.KVC_ESPACE
+    # without x only the planes are read
+    assert _prefill_raw(cfg, ws=fake, ws_n=2 * 8 * 1024 - 1)[0] == kvc.KVC_ESPACE
 
 
 def test_decode_argument_errors_return_before_enqueueing():

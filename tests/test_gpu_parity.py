@@ -826,9 +826,9 @@ def test_f16_split_of_f32_rows_is_the_two_part_sum(ratio, hd, dim, batch, seqlen
 @pytest.mark.parametrize("batch,dim,hd", [(70, 2048, 128), (5, 4096, 512), (33, 1536, 512)])
 def test_decode_projection_tiles(batch, dim, hd):
     """Decode from f32 rows: batches that are not a multiple of the 32-row
-    tile (70: three row tiles; 5; 33), k halves of 8, 16 and 6 stages of 128
-    k; the emitted entries and the carried state against the oracle over the
-    same tokens, and bit for bit against the GPU prefill."""
+    tile (70: three row tiles; 5; 33), k segments of 8, 16 and 6 stages of
+    128 k; the emitted entries and the carried state against the oracle over
+    the same tokens, and bit for bit against the GPU prefill."""
     note(f"decode projection tiles batch={batch} dim={dim} hd={hd}")
     from gpu_util import weights
     rng = np.random.default_rng(batch + dim + hd)
@@ -857,26 +857,28 @@ def test_decode_projection_tiles(batch, dim, hd):
     assert np.array_equal(dec["state_sc"][:, live].view(np.uint32), full["state_sc"][:, live].view(np.uint32))
 
 
-# ratio, head_dim, dim, batch, steps: stages of 128 k (dim % 256 == 0), of 32 k
-# (k halves of 32 and 64 at dim 96; 224 and 256 at dim 480), one half (dim
-# 32), ragged batches, every ratio
+# ratio, head_dim, dim, batch, steps: k segments of whole 128-k stages (dim %
+# 256 == 0), of 32-k stages (segments 64 and 96 at dim 160, 224 and 256 at
+# dim 480, 32 and 64 at dim 96), one segment (dim 32), ragged batches, every
+# ratio
 DECODE_BITWISE_CASES = [
     (4, 512, 4096, 64, 12),
-    (4, 128, 96, 5, 9),
+    (4, 128, 160, 5, 9),
     (2, 512, 32, 3, 6),
     (128, 128, 256, 2, 130),
     (4, 512, 480, 33, 8),
     (2, 128, 1024, 97, 5),
+    (4, 128, 96, 70, 6),
 ]
 
 
 @pytest.mark.parametrize("ratio,hd,dim,batch,steps", DECODE_BITWISE_CASES)
 def test_decode_equals_prefill_bitwise_from_x(ratio, hd, dim, batch, steps):
     """From f32 hidden states a decode step sums each projection exactly as
-    the prefill's f32 matrix cores do (two k halves, the same MFMA order,
+    the prefill's f32 matrix cores do (two k segments, the same MFMA order,
     p0 + p1), so a decode stream and a prefill over the same tokens write the
-    same bits: entries, fp4 codes and the carried state. Also a continuation:
-    prefill of the first tokens, decode of the rest."""
+    same bits: entries, fp4 codes and the carried state. Also a
+    continuation: prefill of the first tokens, decode of the rest."""
     note(f"decode == prefill bitwise from x ratio={ratio} hd={hd} dim={dim} batch={batch} steps={steps}")
     from gpu_util import weights
     rng = np.random.default_rng(ratio * 7 + hd + dim + batch)
@@ -929,7 +931,7 @@ def test_decode_workspace_counters_rest_at_zero_and_a_dirty_one_poisons():
     good = st[0][:, 4].clone()
     assert torch.isfinite(good).all().item()
     # a dirty counter (tile 0: batch rows 0..31, kv columns 0..31)
-    counters.view(torch.int32)[0] = 5
+    counters.view(torch.int32)[0] = 9
     kvc.compressor_decode_step(cfg, weights(w), x[0], batch, 0, ws, st[0], st[1])
     torch.cuda.synchronize()
     assert torch.isnan(st[0][:32, 4, :32]).all().item()
