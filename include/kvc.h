@@ -290,6 +290,28 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const vo
                            float *kv_state, float *score_state, int64_t state_batch,
                            const kvc_outputs *out, int32_t *emitted, kvc_stream stream);
 
+/* compressor_decode_step for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same step, with the same kernels and results, but no
+ * workspace argument. Its partial sums and arrival counters live in a
+ * scratch array inside the library, 4 MiB + 16 KiB of device memory that
+ * each GPU the library runs on holds until the process ends (the counters
+ * start at zero and every completed step leaves them zero). Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (different
+ * streams, or different threads without ordering) race and give undefined
+ * results; serialise them.
+ *   Arguments as compressor_decode_step, except that x is required (given
+ *   projections need the caller's workspace: KVC_EINVAL).
+ *   Limits: the step's partial sums (kvc_decode_workspace_floats() less
+ *   its counters) must fit in 2^20 floats and its counters in 4096: batch
+ *   <= 256 at proj 1024, 512 at proj 512, 1024 at proj 256; KVC_ESPACE
+ *   beyond. KVC_EHIP if the scratch address cannot be resolved.
+ * Nothing is allocated by the call (no hipMalloc or allocating library
+ * routine). */
+int compressor_decode_step_noalloc(const kvc_config *cfg, const kvc_weights *w, const void *x, int64_t batch,
+                                   int64_t start_pos, float *kv_state, float *score_state, int64_t state_batch,
+                                   const kvc_outputs *out, int32_t *emitted, kvc_stream stream);
+
 /* f32 elements of the workspace compressor_ratio1_forward needs:
  * tokens * head_dim; or a negative KVC_E* code (cfg->ratio must be 1). */
 int64_t kvc_ratio1_workspace_floats(const kvc_config *cfg, int64_t tokens);

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kvc.h"
 #include "kvc_launch.h"
 
@@ -127,6 +129,10 @@ struct ProjectionTimer {
   int before(hipStream_t s) const { return start ? hip_status(hipEventRecord(start, s)) : KVC_OK; }
   int after(hipStream_t s) const { return stop ? hip_status(hipEventRecord(stop, s)) : KVC_OK; }
 };
+
+int decode_step(const kvc_config *cfg, const kvc_weights *w, const void *x, int64_t batch, int64_t start_pos,
+                float *part, uint32_t *counters, float *kv_state, float *score_state, int64_t state_batch,
+                const kvc_outputs *out, int32_t *emitted, const ProjectionTimer &timer, hipStream_t s);
 
 // Prefill workspace: the kv and score planes, then (ratio 4) the f32 pooled
 // entries of the fused projection + pooling path, then for the f32 matrix
@@ -391,14 +397,31 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const vo
   const ProjectionTimer timer;
   int rc = check_config(cfg);
   if (rc) return rc;
+  if (batch < 1) return KVC_EINVAL;
+  if (!workspace || !aligned(workspace)) return KVC_EINVAL;
+  const int64_t part_floats = decode_partial_floats(cfg, batch);
+  if (workspace_floats < part_floats + decode_counter_floats(cfg, batch)) return KVC_ESPACE;
+  return decode_step(cfg, w, x, batch, start_pos, workspace, reinterpret_cast<uint32_t *>(workspace + part_floats),
+                     kv_state, score_state, state_batch, out, emitted, timer, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// One decode step with the partial sums in `part` (decode_partial_floats()
+// floats; given projections at its start when x is NULL) and the f32 path's
+// arrival counters in `counters` (decode_counter_floats(), zero at rest).
+int decode_step(const kvc_config *cfg, const kvc_weights *w, const void *x, int64_t batch, int64_t start_pos,
+                float *part, uint32_t *counters, float *kv_state, float *score_state, int64_t state_batch,
+                const kvc_outputs *out, int32_t *emitted, const ProjectionTimer &timer, hipStream_t s) {
+  int rc;
   if (batch < 1 || start_pos < 0) return KVC_EINVAL;
   if (x) {
     if ((rc = check_projection_inputs(cfg, w))) return rc;
     if (!aligned(x)) return KVC_EINVAL;
   }
   if (w && (!aligned(w->ape) || !aligned(w->norm_w))) return KVC_EINVAL;
-  if (!workspace || !aligned(workspace)) return KVC_EINVAL;
-  if (workspace_floats < decode_partial_floats(cfg, batch) + decode_counter_floats(cfg, batch)) return KVC_ESPACE;
   if (!kv_state || !score_state || state_batch < batch || !aligned(kv_state) || !aligned(score_state))
     return KVC_EINVAL;
   if ((rc = check_outputs(cfg, out))) return rc;
@@ -409,7 +432,6 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const vo
   const int64_t entry = (start_pos + 1) / r - 1;
   if (emit && wants_entries(out) && (rc = check_rope(cfg, w, entry, 1))) return rc;
   if (emitted) *emitted = emit ? 1 : 0;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t proj = proj_of(cfg);
   const int slot = (int)(start_pos % r);
   const int state_row = overlapped(cfg) ? r + slot : slot;
@@ -448,8 +470,8 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const vo
     d.k = cfg->dim;
     d.n_half = proj;
     d.seg = kvc::kseg_length(cfg->dim);
-    d.part = workspace;
-    d.counters = reinterpret_cast<uint32_t *>(workspace + decode_partial_floats(cfg, batch));
+    d.part = part;
+    d.counters = counters;
     d.ape = w->ape;
     d.kv_state = kv_state;
     d.sc_state = score_state;
@@ -473,8 +495,8 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const vo
     g.a16 = static_cast<const uint16_t *>(x);
     g.b0 = w->wkv;
     g.b1 = w->wgate;
-    g.c0 = workspace;
-    g.c1 = workspace + batch * proj;
+    g.c0 = part;
+    g.c1 = part + batch * proj;
     g.lda = cfg->dim;
     g.ldb = cfg->dim;
     g.ldc = proj;
@@ -488,7 +510,7 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const vo
     if ((rc = timer.after(s))) return rc;
   }
   kvc::IngestArgs in{};
-  in.part = workspace;
+  in.part = part;
   in.splits = splits;
   in.ape = w ? w->ape : nullptr;
   in.kv_state = kv_state;
@@ -509,6 +531,55 @@ int compressor_decode_step(const kvc_config *cfg, const kvc_weights *w, const vo
     if ((rc = hip_status(kvc::launch_pool(p, r, cfg->head_dim, s)))) return rc;
   }
   return KVC_OK;
+}
+
+// The scratch of compressor_decode_step_noalloc: a file-scope device array
+// (each GPU holds its own copy until the process ends), the partial sums
+// first, then the arrival counters at a fixed place, so that they are zero
+// at rest whatever the size of the previous call (device arrays start
+// zeroed, and every completed step leaves the counters zero).
+constexpr int64_t kScratchPartFloats = int64_t(1) << 20;  // 4 MiB of partial sums
+constexpr int64_t kScratchCounterFloats = 4096;          // arrival counters
+__device__ __align__(256) float scratch[kScratchPartFloats + kScratchCounterFloats];
+
+// The device address of `scratch` on the current device, resolved once per
+// device (host code must not pass the array's name to a kernel: in host
+// code it stands for a host-side handle, not a device address).
+constexpr int kMaxDevices = 64;
+float *g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mutex;
+
+int scratch_ptr(float **ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVC_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVC_EHIP;
+    g_scratch_ptr[dev] = static_cast<float *>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int compressor_decode_step_noalloc(const kvc_config *cfg, const kvc_weights *w, const void *x, int64_t batch,
+                                   int64_t start_pos, float *kv_state, float *score_state, int64_t state_batch,
+                                   const kvc_outputs *out, int32_t *emitted, kvc_stream stream) {
+  const ProjectionTimer timer;
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (batch < 1 || !x) return KVC_EINVAL;
+  if (decode_partial_floats(cfg, batch) > kScratchPartFloats ||
+      decode_counter_floats(cfg, batch) > kScratchCounterFloats)
+    return KVC_ESPACE;
+  float *base = nullptr;
+  if ((rc = scratch_ptr(&base))) return rc;
+  return decode_step(cfg, w, x, batch, start_pos, base, reinterpret_cast<uint32_t *>(base + kScratchPartFloats),
+                     kv_state, score_state, state_batch, out, emitted, timer, reinterpret_cast<hipStream_t>(stream));
 }
 
 int64_t kvc_ratio1_workspace_floats(const kvc_config *cfg, int64_t tokens) {

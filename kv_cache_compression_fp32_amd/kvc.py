@@ -66,6 +66,9 @@ _SIGNATURES = {
     "compressor_decode_step": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), _P, _I64, _I64,
                                               _P, _I64, _P, _P, _I64, ctypes.POINTER(_Outputs),
                                               ctypes.POINTER(ctypes.c_int32), _P]),
+    "compressor_decode_step_noalloc": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), _P, _I64,
+                                                      _I64, _P, _P, _I64, ctypes.POINTER(_Outputs),
+                                                      ctypes.POINTER(ctypes.c_int32), _P]),
     "kvc_ratio1_workspace_floats": (_I64, [ctypes.POINTER(_Config), _I64]),
     "compressor_ratio1_forward": (ctypes.c_int, [ctypes.POINTER(_Config), _P, _P, _P, _I64, _P, _I64,
                                                  ctypes.POINTER(_Outputs), _P]),
@@ -308,6 +311,31 @@ def compressor_decode_step(cfg: Config, w: Weights, x: torch.Tensor | None, batc
         state_batch, ctypes.byref(out.c()) if out is not None else None, ctypes.byref(e),
         _stream(stream))
     _check(rc, "compressor_decode_step")
+    return bool(e.value)
+
+
+def compressor_decode_step_noalloc(cfg: Config, w: Weights, x: torch.Tensor, batch: int, start_pos: int,
+                                   kv_state: torch.Tensor, score_state: torch.Tensor, out: Outputs | None = None,
+                                   stream=None) -> bool:
+    """compressor_decode_step without a workspace: the library's own scratch
+    array on the current GPU holds the partial sums (calls that overlap on
+    one GPU race). Returns True if entries were written."""
+    e = ctypes.c_int32(0)
+    if batch < 1 or start_pos < 0:
+        raise ValueError("batch must be >= 1 and start_pos >= 0")
+    if x is None:
+        raise ValueError("the step without a workspace needs x")
+    _need(x, batch * cfg.dim, "x")
+    _check_weights(cfg, w, True)
+    if kv_state is None or score_state is None:
+        raise ValueError("decode needs both state planes")
+    state_batch = _check_state(cfg, kv_state, score_state, batch)
+    _check_outputs(cfg, out, batch, 1)
+    rc = lib().compressor_decode_step_noalloc(
+        ctypes.byref(cfg.c()), ctypes.byref(w.c()), _x_ptr(cfg, x), batch, start_pos,
+        _ptr(kv_state, torch.float32, "kv_state"), _ptr(score_state, torch.float32, "score_state"),
+        state_batch, ctypes.byref(out.c()) if out is not None else None, ctypes.byref(e), _stream(stream))
+    _check(rc, "compressor_decode_step_noalloc")
     return bool(e.value)
 
 

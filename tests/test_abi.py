@@ -372,3 +372,22 @@ def test_ratio1_and_quantiser_bindings_reject_wrong_sizes():
         kvc.latent_fp4_quant(inp, out=_t((4, 48), torch.bfloat16))
     with pytest.raises(ValueError, match="rope_cs"):
         kvc.latent_rope(inp, 16, _t((4, 16, 2)))
+
+
+def test_noalloc_decode_limits_are_checked_before_the_gpu():
+    """The step without a workspace rejects a missing x and batches whose
+    partial sums exceed its 2^20-float scratch before touching a GPU."""
+    lib = kvc.lib()
+    fake = 0x100000  # never dereferenced: every case below fails its host checks
+    e = ctypes.c_int32(-1)
+
+    def call(cfg, x, batch):
+        w = kvc._Weights(fake, fake, None, None)
+        return lib.compressor_decode_step_noalloc(ctypes.byref(cfg.c()), ctypes.byref(w), x, batch, 3, fake, fake,
+                                                  batch, None, ctypes.byref(e), None)
+    cfg = kvc.Config(4, 512, 4096)   # proj 1024: 4 * batch * 1024 floats of partial sums
+    assert call(cfg, None, 8) == kvc.KVC_EINVAL
+    assert call(cfg, fake, 0) == kvc.KVC_EINVAL
+    assert call(cfg, fake, 257) == kvc.KVC_ESPACE
+    assert call(kvc.Config(4, 128, 4096), fake, 1025) == kvc.KVC_ESPACE   # proj 256
+    assert call(kvc.Config(128, 512, 4096), fake, 513) == kvc.KVC_ESPACE  # proj 512
