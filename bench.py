@@ -212,14 +212,15 @@ def _kernel_ms(torch, kvc, stream, fn, reps):
 
 
 def _cold_ms(torch, stream, fn, reps):
-    """Average duration of single launches of `fn`, each after 1 GiB of
-    writes that evict its inputs from the caches (a true HBM measurement
-    even where the inputs would fit in the 256 MB last-level cache)."""
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    """Average duration of single launches of `fn`, each after a 1 GiB read
+    that evicts its inputs from the caches (a true HBM measurement even
+    where the inputs would fit in the 256 MB last-level cache; a read leaves
+    no dirty lines whose write-back the launch would pay for)."""
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     fn()
     ev = _events(torch, stream, 2 * reps)
     for r in range(reps):
-        flush.fill_(float(r))
+        flush.sum()
         ev[2 * r].record(stream)
         fn()
         ev[2 * r + 1].record(stream)
