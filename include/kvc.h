@@ -339,11 +339,13 @@ int compressor_ratio1_forward(const kvc_config *cfg, const uint16_t *wkv, const 
 
 /* The latent's fp4 round trip ("Module compress", Functions,
  * fp4_quant_e4m3_inplace; to_e2m1_rne; Constants, LATENT_BLOCK) on
- * [rows][width] bf16 values, per block of 16 consecutive values of a row:
- * amax floored at 6 * 2^-9; scale = e4m3fn(amax / 6), round to nearest even,
- * the division an IEEE f32 one; codes = e2m1(value / scale), nearest, ties to
- * the even code, saturating at 6, sign kept (also for values rounding to 0);
- * dequant = e2m1 value * scale (exact in bf16).
+ * [rows][width] bf16 values. Each run of 16 consecutive values of a row
+ * shares one scale: the largest magnitude M of the run, raised to 6 * 2^-9
+ * when smaller, is divided by 6 (IEEE f32 division) and rounded to the
+ * nearest e4m3fn value (ties to even). Each value divided by that scale maps
+ * to the nearest e2m1 code (ties to the even code, saturating at 6, the sign
+ * bit kept even for a zero code); the dequantised value is the code's value
+ * times the scale, which bf16 holds exactly.
  *   in     : [rows][width] bf16.   rows >= 0, width > 0 and width % 16 == 0.
  *   codes  : [rows][width / 2] bytes (layout as kvc_outputs.codes), or NULL.
  *   scales : [rows][width / 16] e4m3fn bytes, or NULL.
@@ -356,10 +358,11 @@ int latent_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uint8_t *c
 /* The indexer's fp4 round trip ("Module compress", Functions,
  * fp4_quant_e8m0_inplace; Constants, FP4_BLOCK; Precision paragraph: the
  * indexer's q and k use power-of-two scales in blocks of 32) on [rows][width]
- * bf16 values, per block of 32 consecutive values of a row: amax floored at
- * 6 * 2^-126; scale = 2^e with e the smallest integer such that 2^e >= amax / 6
- * (an IEEE f32 division); codes = e2m1(value / scale), nearest, ties to the
- * even code, sign kept; dequant = e2m1 value * scale (exact in bf16).
+ * bf16 values. Each run of 32 consecutive values of a row shares one scale
+ * 2^e: e is the least integer with 2^e >= M / 6 (IEEE f32 division), M the
+ * run's largest magnitude raised to 6 * 2^-126 when smaller (so M / 6 is a
+ * normal f32). Codes, their sign and the dequantised values follow the rule
+ * of latent_fp4_quant with this scale.
  *   in     : [rows][width] bf16.   rows >= 0, width > 0 and width % 32 == 0.
  *   codes  : [rows][width / 2] bytes (layout as kvc_outputs.codes), or NULL.
  *   scales : [rows][width / 32] e8m0 bytes (e + 127), or NULL.

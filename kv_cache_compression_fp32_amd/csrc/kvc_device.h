@@ -137,10 +137,11 @@ __device__ __forceinline__ uint32_t e2m1_code_scaled(float t, uint32_t sign) {
 
 // fp4 round trip with power-of-two scales (the indexer's form, "Module
 // compress", Functions, fp4_quant_e8m0_inplace) of VEC consecutive bf16
-// values per lane, 32 / VEC neighbouring lanes forming one block of 32:
-// amax floored at 6 * 2^-126, scale = 2^e with e the power-of-two ceiling
-// exponent of amax / 6 (an IEEE f32 division), codes of y / scale, dequant =
-// code value * scale. Scaling by 2^e is done with ldexp, which is exact here.
+// values per lane, 32 / VEC neighbouring lanes forming one block of 32. The
+// block's scale is 2^e, e the least integer with 2^e >= M / 6 (IEEE f32
+// division), M its largest magnitude but at least 6 * 2^-126; the codes are
+// those of y / 2^e and the dequantised values code * 2^e. Both scalings are
+// ldexp by e, exact here.
 // Returns the packed codes (element 2k in the low nibble), the e8m0 scale byte
 // (e + 127) and the bf16 bits of the dequantised values.
 template <int VEC>

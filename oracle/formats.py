@@ -10,16 +10,17 @@ reader can check each function against the format's definition by eye.
 
 Sources:
   * "Module compress" (DeepSeek-V4.1 reference docs), Precision paragraph: the
-    ratio > 1 compressor stays in f32 until its pooled result is rounded to bf16
-    for the RMSNorm; the compressed KV latent goes through e2m1 with e4m3 scales
-    in blocks of 16.
-  * "Module compress", Functions, fp4_quant_e4m3_inplace: amax floored at
-    6 * 2^-9, scale = amax / 6 rounded through e4m3, values to e2m1, then
-    dequantised and rounded to bf16, in place.
-  * "Module compress", Functions, to_e2m1_rne: round onto the e2m1 grid, ties to
-    the even code, sign kept.
-  * "Module compress", Constants, LATENT_BLOCK: the number of values per e4m3
-    scale (16).
+    number types along the compressor. Arithmetic is f32 through pooling, a
+    bf16 rounding sits in front of the RMSNorm, and the cached latent is kept
+    in an fp4 form (e2m1 elements, one e4m3 scale per 16 values).
+  * "Module compress", Functions, fp4_quant_e4m3_inplace: the latent's fp4
+    round trip. Per block the scale comes from the block's largest magnitude
+    (bounded below by 6 * 2^-9) over 6, rounded to e4m3; each value over the
+    scale becomes an e2m1 code; code times scale, as bf16, overwrites the
+    input.
+  * "Module compress", Functions, to_e2m1_rne: the e2m1 rounding (nearest grid
+    point, exact ties to the even code, the sign carried over).
+  * "Module compress", Constants, LATENT_BLOCK: 16 values per e4m3 scale.
   * Format definitions (not on the pages): bf16 = the upper half of an IEEE
     binary32; e4m3fn and e2m1 = the OCP 8-bit floating point and OCP
     Microscaling (MX) v1.0 element formats.
@@ -38,8 +39,9 @@ import numpy as np
 # Constants, LATENT_BLOCK).
 LATENT_BLOCK = 16
 
-# Values per power-of-two scale in the indexer's fp4 round trip ("Module
-# compress", Constants, FP4_BLOCK; Precision paragraph: block 32).
+# Block length of the indexer's fp4 form, which shares one power-of-two
+# scale among 32 values ("Module compress", Constants, FP4_BLOCK, and the
+# Precision paragraph).
 FP4_BLOCK = 32
 
 # The amax floor of fp4_quant_e8m0_inplace: 6 * 2^-126, so that amax / 6 is
