@@ -202,12 +202,14 @@ int64_t kvc_state_rows(const kvc_config *cfg);
 /* f32 elements of the workspace compressor_prefill needs: the projection
  * planes, 2 * batch * seqlen * proj; at ratio 4 the f32 pooled entries,
  * batch * (seqlen / 4) * head_dim (used when the projection and the pooling
- * run as one kernel: a smaller workspace runs them separately); and for the
- * opt-in split projections the split weights: KVC_PROJ_F16_SPLIT two f16
- * parts and the scale exponents of the weight rows and of x's rows,
- * 2 * proj * dim + 2 * proj + batch * seqlen rounded up to a multiple of 4;
- * KVC_PROJ_BF16_SPLIT (and KVC_PROJ_AUTO with bf16 x) three bf16 parts,
- * 3 * proj * dim. Or a negative KVC_E* code. */
+ * run as one kernel: a smaller workspace runs them separately); then, by
+ * projection: on the f32 matrix cores (KVC_PROJ_F32_MFMA, the default for
+ * f32 x) the running sums of a ragged last row tile, 256 * 2 * proj; for the
+ * opt-in KVC_PROJ_F16_SPLIT two f16 weight parts and the scale exponents of
+ * the weight rows and of x's rows, 2 * proj * dim + 2 * proj + batch * seqlen
+ * rounded up to a multiple of 4; for KVC_PROJ_BF16_SPLIT (and KVC_PROJ_AUTO
+ * with bf16 x) three bf16 weight parts, 3 * proj * dim. Or a negative KVC_E*
+ * code. */
 int64_t kvc_prefill_workspace_floats(const kvc_config *cfg, int64_t batch, int64_t seqlen);
 
 /* f32 elements of the workspace compressor_decode_step needs, or a negative

@@ -79,8 +79,9 @@ def test_pair_pool_r2_full():
     ref = oracle.prefill(oracle_cfg(cfg), oracle.Weights(), oracle.State(oracle_cfg(cfg), wl.batch), kv=kc,
                          score=gc)
     assert g["latent"].shape == (1, 32, 512)
-    check_pooled(g["pooled"], ref["pooled"])
-    check_latent(g["latent"], g["pooled"], ref["latent"], ref["pooled"], eps=wl.eps)
+    worst = check_pooled(g["pooled"], ref["pooled"])
+    flips, total = check_latent(g["latent"], g["pooled"], ref["latent"], ref["pooled"], eps=wl.eps)
+    note(f"    every entry: pooled worst {worst:.2e} of the entry's scale; latent bf16 flips {flips} of {total}")
 
 
 @functools.lru_cache(maxsize=1)
