@@ -485,7 +485,9 @@ int decode_step(const kvc_config *cfg, const kvc_weights *w, const void *x, int6
     if ((rc = hip_status(kvc::launch_decode_f32(d, s)))) return rc;
     if ((rc = timer.after(s))) return rc;
     // a group completed: pool it (the only other launch of the step)
-    if (pool_now) return hip_status(kvc::launch_pool(p, r, cfg->head_dim, s));
+    if (pool_now)
+      return hip_status(overlapped(cfg) ? kvc::launch_decode_emit(p, cfg->head_dim, s)
+                                        : kvc::launch_pool(p, r, cfg->head_dim, s));
     return KVC_OK;
   }
 

@@ -146,6 +146,13 @@ struct PoolArgs {
 };
 hipError_t launch_pool(const PoolArgs &p, int ratio, int head_dim, hipStream_t stream);
 
+// Decode at ratio 4 when a group completes: the entry of every batch row
+// from the state window and the move of the block into the previous-block
+// rows, one two-wavefront workgroup per batch row (the move overlapping the
+// pooling). p as for launch_pool over the state (groups 1, first_entry 1,
+// shift_kv / shift_sc the state planes, no bias).
+hipError_t launch_decode_emit(const PoolArgs &p, int head_dim, hipStream_t stream);
+
 // Ratio 1: the per-entry epilogue (bf16 round, RMSNorm, outputs, fp4) of
 // `groups` rows of f32 projections, row e at kv + e * row_stride; one entry
 // per row (batch 1 in the PoolArgs; sc, ape and the shift are unused).

@@ -187,43 +187,45 @@ __device__ __forceinline__ void finish_entry(const float (&p)[HD / kWave], const
   }
 }
 
-// One entry of a small group (ratio 2, ratio 4 overlapped) by one wavefront
-// (features laid out as Lanes<HD>), from kv/score planes holding the token
-// rows of batch row b. Ratio 4: entry j pools rows 4(j-1)..4j-1 of branch B
-// (columns [HD, 2HD)) then rows 4j..4j+3 of branch A (columns [0, HD));
-// entry 0's previous branch is kv 0 / score -inf. The entry loads exactly its
-// own candidates. With shift_kv set (decode), the block just pooled is then
-// copied to the previous-block rows; the lane only touches features it alone
-// reads.
+// The candidates of one entry of a small group (ratio 2, ratio 4
+// overlapped) in this lane's features (layout Lanes<HD>), from kv/score
+// planes holding the token rows of batch row b. Ratio 4: entry j pools rows
+// 4(j-1)..4j-1 of branch B (columns [HD, 2HD)) then rows 4j..4j+3 of branch
+// A (columns [0, HD)); entry 0's previous branch is kv 0 / score -inf. The
+// entry loads exactly its own candidates.
 template <int HD, int R, bool OV>
-__device__ __forceinline__ void small_entry(const PoolArgs &a, int64_t b, int64_t e, int lane) {
-  constexpr int VEC = HD / kWave;
-  constexpr int NC = OV ? 2 * R : R;
-  constexpr int C0 = OV ? R : 0;
+struct Candidates {
+  static constexpr int VEC = HD / kWave;
+  static constexpr int NC = OV ? 2 * R : R;
+  static constexpr int C0 = OV ? R : 0;  // the current block's first candidate
+  float k[NC][VEC], s[NC][VEC];          // in pooling order: [previous B,] current rows
+};
+
+template <int HD, int R, bool OV>
+__device__ __forceinline__ void load_candidates(const PoolArgs &a, int64_t b, int64_t j, int lane,
+                                                Candidates<HD, R, OV> &c) {
+  constexpr int VEC = HD / kWave, C0 = Candidates<HD, R, OV>::C0;
   const float *KV = a.kv + b * a.batch_stride;
   const float *SC = a.sc + b * a.batch_stride;
-  const int64_t j = a.first_entry + e;
-  // candidates in pooling order: [previous block's branch B,] current rows
-  float ck[NC][VEC], cs[NC][VEC];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int64_t row = (int64_t)R * j + i;
-    load_row_stream<HD>(KV + row * a.row_stride, lane, ck[C0 + i]);
-    load_row_stream<HD>(SC + row * a.row_stride, lane, cs[C0 + i]);
+    load_row_stream<HD>(KV + row * a.row_stride, lane, c.k[C0 + i]);
+    load_row_stream<HD>(SC + row * a.row_stride, lane, c.s[C0 + i]);
   }
   if constexpr (OV) {
     if (j > 0) {
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int64_t row = (int64_t)R * (j - 1) + i;
-        load_row_stream<HD>(KV + row * a.row_stride + HD, lane, ck[i]);
-        load_row_stream<HD>(SC + row * a.row_stride + HD, lane, cs[i]);
+        load_row_stream<HD>(KV + row * a.row_stride + HD, lane, c.k[i]);
+        load_row_stream<HD>(SC + row * a.row_stride + HD, lane, c.s[i]);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < R; ++i)
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) { ck[i][v] = 0.0f; cs[i][v] = -INFINITY; }
+        for (int v = 0; v < VEC; ++v) { c.k[i][v] = 0.0f; c.s[i][v] = -INFINITY; }
     }
   }
   if (a.ape) {
@@ -232,20 +234,43 @@ __device__ __forceinline__ void small_entry(const PoolArgs &a, int64_t b, int64_
       float bias[VEC];
       load_row<HD>(a.ape + (int64_t)i * a.row_stride, lane, bias);
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) cs[C0 + i][v] += bias[v];
+      for (int v = 0; v < VEC; ++v) c.s[C0 + i][v] += bias[v];
       if constexpr (OV) {
         load_row<HD>(a.ape + (int64_t)i * a.row_stride + HD, lane, bias);
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) cs[i][v] += bias[v];  // -inf padding stays -inf
+        for (int v = 0; v < VEC; ++v) c.s[i][v] += bias[v];  // -inf padding stays -inf
       }
     }
   }
+}
+
+// The pooled entry (output e of batch row b) from its candidates: softmax
+// pooling, then the per-entry epilogue.
+template <int HD, int R, bool OV>
+__device__ __forceinline__ void pool_candidates(const PoolArgs &a, int64_t b, int64_t e, int lane,
+                                                const Candidates<HD, R, OV> &c) {
+  constexpr int VEC = HD / kWave;
   float p[VEC];
-  softmax_pool<NC, VEC>(ck, cs, p);
+  softmax_pool<Candidates<HD, R, OV>::NC, VEC>(c.k, c.s, p);
   finish_entry<HD>(p, a, b * a.out_batch_stride + e, a.rope_row0 + e, lane);
+}
+
+// One entry of a small group by one wavefront (features laid out as
+// Lanes<HD>). With shift_kv set (decode), the block just pooled is then
+// copied to the previous-block rows; the lane only touches features it
+// alone reads.
+template <int HD, int R, bool OV>
+__device__ __forceinline__ void small_entry(const PoolArgs &a, int64_t b, int64_t e, int lane) {
+  constexpr int VEC = HD / kWave, C0 = Candidates<HD, R, OV>::C0;
+  const int64_t j = a.first_entry + e;
+  Candidates<HD, R, OV> c;
+  load_candidates<HD, R, OV>(a, b, j, lane, c);
+  pool_candidates<HD, R, OV>(a, b, e, lane, c);
 
   if constexpr (OV) {
     if (a.shift_kv) {
+      const float *KV = a.kv + b * a.batch_stride;
+      const float *SC = a.sc + b * a.batch_stride;
       float *SK = a.shift_kv + b * a.batch_stride;
       float *SS = a.shift_sc + b * a.batch_stride;
 #pragma unroll
@@ -255,8 +280,8 @@ __device__ __forceinline__ void small_entry(const PoolArgs &a, int64_t b, int64_
         load_row<HD>(KV + row * a.row_stride + HD, lane, bk);
         load_row<HD>(SC + row * a.row_stride + HD, lane, bs);
         const int64_t dst = (int64_t)R * (j - 1) + i;
-        store_row<HD>(SK + dst * a.row_stride, lane, ck[C0 + i]);
-        store_row<HD>(SS + dst * a.row_stride, lane, cs[C0 + i]);
+        store_row<HD>(SK + dst * a.row_stride, lane, c.k[C0 + i]);
+        store_row<HD>(SS + dst * a.row_stride, lane, c.s[C0 + i]);
         store_row<HD>(SK + dst * a.row_stride + HD, lane, bk);
         store_row<HD>(SS + dst * a.row_stride + HD, lane, bs);
       }
@@ -278,6 +303,56 @@ __global__ __launch_bounds__(256) void pool_small_kernel(PoolArgs a) {
   const int64_t e_begin = run * a.entries_per_wave;
   const int64_t e_end = min(e_begin + (int64_t)a.entries_per_wave, a.groups);
   for (int64_t e = e_begin; e < e_end; ++e) small_entry<HD, R, OV>(a, b, e, lane);
+}
+
+// Decode at ratio 4, a group just completed: the entry of each batch row
+// (workgroup b) from the state window, and the move of the block into the
+// previous-block rows (rows R..2R-1 to 0..R-1, both halves, both planes).
+// Wavefront 0 loads the candidates, wavefront 1 the rows to move; once both
+// have their data (the barrier), wavefront 0 pools and wavefront 1 stores,
+// so the move's round trip overlaps the pooling instead of following it.
+// The state's scores already hold the bias (a.ape is null). Same bits as
+// small_entry with shift_kv.
+template <int HD, int R>
+__global__ __launch_bounds__(128) void decode_emit_kernel(PoolArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t b = blockIdx.x;
+  const int64_t j = a.first_entry;
+  // wavefront 0: the candidates; wavefront 1: the 2 R half rows to move, in
+  // the same registers (slot 2 i + h: row R j + i, half h)
+  Candidates<HD, R, true> c;
+  static_assert(Candidates<HD, R, true>::NC == 2 * R, "one slot per half row");
+  if (wave == 0) {
+    load_candidates<HD, R, true>(a, b, j, lane, c);
+  } else {
+    const float *KV = a.kv + b * a.batch_stride;
+    const float *SC = a.sc + b * a.batch_stride;
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t off = ((int64_t)R * j + i) * a.row_stride + h * HD;
+        load_row<HD>(KV + off, lane, c.k[2 * i + h]);
+        load_row<HD>(SC + off, lane, c.s[2 * i + h]);
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // every load of this wavefront has returned
+  __syncthreads();                // and the other wavefront's
+  if (wave == 0) {
+    pool_candidates<HD, R, true>(a, b, 0, lane, c);
+  } else {
+    float *SK = a.shift_kv + b * a.batch_stride;
+    float *SS = a.shift_sc + b * a.batch_stride;
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t off = ((int64_t)R * (j - 1) + i) * a.row_stride + h * HD;
+        store_row<HD>(SK + off, lane, c.k[2 * i + h]);
+        store_row<HD>(SS + off, lane, c.s[2 * i + h]);
+      }
+  }
 }
 
 // Ratio 1: every row of f32 projections is one entry; one wavefront runs the
@@ -559,6 +634,18 @@ hipError_t launch_pool(const PoolArgs &p, int ratio, int head_dim, hipStream_t s
     case 128 * 10000 + 128: return launch_long<128>(p, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_decode_emit(const PoolArgs &p, int head_dim, hipStream_t stream) {
+  if (p.batch <= 0) return hipSuccess;
+  if (p.groups != 1 || p.first_entry < 1 || !p.shift_kv || !p.shift_sc || p.ape) return hipErrorInvalidValue;
+  const dim3 grid((uint32_t)p.batch), block(128);
+  switch (head_dim) {
+    case 512: hipLaunchKernelGGL((decode_emit_kernel<512, 4>), grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((decode_emit_kernel<128, 4>), grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_rows_finish(const PoolArgs &p, int head_dim, hipStream_t stream) {
