@@ -270,7 +270,8 @@ int compressor_prefill(const kvc_config *cfg, const kvc_weights *w, const void *
  * Launches: from f32 x, one kernel computes the projections (summed exactly
  * as compressor_prefill's f32 matrix cores sum them, so the entries equal a
  * prefill's bit for bit) and writes the state row; a step that completes a
- * group launches the pooling kernel after it. From bf16 x or given
+ * group launches the pooling kernel after it (at ratio 4 the same kernel
+ * moves the block, while it pools). From bf16 x or given
  * projections: the projection (bf16 x), then one kernel that ingests and,
  * at ratios 2 and 4, pools.
  *   x            : [batch][dim] f32, or bf16 with KVC_X_BF16 (one token per
