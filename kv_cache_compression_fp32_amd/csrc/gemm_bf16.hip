@@ -26,12 +26,14 @@
 // 2. The ratio-1 projection (bf16 x times bf16 wkv, f32 accumulation; the
 //    Compressor listing's __init__ and ratio-1 branch of forward; "Module
 //    compress", CompressorWeights): the same kernel with plain bf16 weights.
-// 3. Prefill projection for f32 hidden states: gemm_x6_kernel, with x split
-//    in registers, either like the weights into three bf16 parts (six part
-//    products) or, by default, into two f16 parts of the row scaled by a
-//    power of two, against the weights' two f16 parts
-//    (split_weights_f16_kernel, row_exponents_kernel; three part products,
-//    the sums scaled back exactly).
+// 3. Opt-in emulations of the prefill projection for f32 hidden states (the
+//    default for them is the f32 matrix cores, gemm_f32_kernel.h):
+//    gemm_x6_kernel, with x split in registers, either like the weights into
+//    three bf16 parts (six part products, KVC_PROJ_BF16_SPLIT) or into two
+//    f16 parts of the row scaled by a power of two, against the weights' two
+//    f16 parts (KVC_PROJ_F16_SPLIT: split_weights_f16_kernel,
+//    row_exponents_kernel; three part products, the sums scaled back
+//    exactly).
 //
 // gemm_mc_kernel: BM x BN workgroup tile, WM x WN per wavefront, two LDS
 // stages of 64 KiB: with the split weights, one 32-k slice of the x tile
