@@ -98,7 +98,7 @@ def test_e4m3fn_every_code_is_a_fixed_point():
 
 
 def test_e4m3fn_matches_torch_on_every_latent_scale_quotient():
-    # every positive finite bf16 amax, floored at 6 * 2^-9, divided by 6 in f32:
+    # every positive finite bf16 amax, raised to at least 6 * 2^-9, divided by 6 in f32:
     # exactly the quotients fp4_quant_e4m3 can hand to the scale rounding
     pats = np.arange(0x0001, 0x7F80, dtype=np.uint32) << 16
     amax = pats.view(np.float32)
