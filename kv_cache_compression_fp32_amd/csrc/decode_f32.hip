@@ -29,8 +29,8 @@
 // registers): a stage is BK k of the tile's TM x rows and 32 weight rows,
 // the 16-byte group q of row r at position q ^ (r & 15) (stages of 128 k;
 // q ^ (r & 7) with 32 k), so the fragment reads of 16 neighbouring rows hit
-// 16 distinct bank groups. NST stage buffers, the
-// loads NST - 1 stages ahead. The fragment reads of stage s + 1 are issued
+// 16 distinct bank groups. NST stage buffers, the loads NST - 1 stages
+// ahead. The fragment reads of stage s + 1 are issued
 // before the MFMAs of stage s and land while the chain runs. LDS reads are
 // inline asm, which the compiler does not track: it would otherwise wait for
 // every load in flight into any stage buffer before each of them. One wait
