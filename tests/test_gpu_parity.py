@@ -869,6 +869,7 @@ DECODE_BITWISE_CASES = [
     (4, 512, 480, 33, 8),
     (2, 128, 1024, 97, 5),
     (4, 128, 96, 70, 6),
+    (4, 512, 256, 256, 6),   # eight 32-row tiles
 ]
 
 

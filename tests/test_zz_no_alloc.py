@@ -1,8 +1,9 @@
 """compressor_decode_step_noalloc (no workspace: the library's own scratch
-array) against compressor_decode_step on the same inputs, bit for bit: a
-stream of steps at one batch size, then another at a smaller one (the
-scratch's arrival counters must be back at zero and its partial sums are
-laid out anew), from f32 and from bf16 hidden states."""
+array) against compressor_decode_step on the same inputs, bit for bit:
+streams of steps at batch 64, at 256 (the largest batch the scratch holds at
+this width) and at 17 (the scratch's arrival counters must be back at zero
+and its partial sums are laid out anew), from f32 and from bf16 hidden
+states."""
 import numpy as np
 import pytest
 import torch
@@ -34,7 +35,8 @@ def test_noalloc_decode_matches_the_workspace_decode(x_format):
     w = kvc.Weights(d(rng.standard_normal((proj, 1024), dtype=np.float32) * np.float32(0.03)),
                     d(rng.standard_normal((proj, 1024), dtype=np.float32) * np.float32(0.03)),
                     d(rng.standard_normal((4, proj), dtype=np.float32) * np.float32(0.1)))
-    for batch, steps in ((64, 9), (17, 6)):
+    # 256 rows at proj 1024 fill the scratch's 2^20 floats of partial sums
+    for batch, steps in ((64, 9), (256, 5), (17, 6)):
         note(f"no-alloc decode x_format={x_format} batch={batch} steps={steps}")
         x = d(rng.standard_normal((steps, batch, 1024), dtype=np.float32))
         if x_format == kvc.KVC_X_BF16:
