@@ -103,9 +103,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 // fp4 round trip of VEC consecutive bf16 values held by each lane, 16 / VEC
 // neighbouring lanes forming one block of 16. `y` holds the bf16 values as
 // f32. Returns through references: the packed codes of this lane (VEC / 2
-// bytes, element 2k in the low nibble), the block's scale byte, and the bf16
-// bits of the dequantised values.
-template <int VEC>
+// bytes, element 2k in the low nibble), the block's scale byte, and (DEQ)
+// the bf16 bits of the dequantised values.
+template <int VEC, bool DEQ = true>
 __device__ __forceinline__ void fp4_block(const float (&y)[VEC], uint32_t &packed, uint32_t &scale_code,
                                           uint32_t (&deq)[VEC]) {
   static_assert(VEC >= 2 && VEC <= 8 && 16 % VEC == 0, "VEC must divide 16 and fit 32 code bits");
@@ -123,7 +123,7 @@ __device__ __forceinline__ void fp4_block(const float (&y)[VEC], uint32_t &packe
   for (int v = 0; v < VEC; ++v) {
     const uint32_t c = e2m1_rne(y[v], s);
     packed |= c << (4 * v);
-    deq[v] = as_u32(e2m1_val(c) * s) >> 16;  // exact: at most 6 significant bits
+    if constexpr (DEQ) deq[v] = as_u32(e2m1_val(c) * s) >> 16;  // exact: at most 6 significant bits
   }
 }
 
@@ -144,7 +144,7 @@ __device__ __forceinline__ uint32_t e2m1_code_scaled(float t, uint32_t sign) {
 // ldexp by e, exact here.
 // Returns the packed codes (element 2k in the low nibble), the e8m0 scale byte
 // (e + 127) and the bf16 bits of the dequantised values.
-template <int VEC>
+template <int VEC, bool DEQ = true>
 __device__ __forceinline__ void fp4_block_e8m0(const float (&y)[VEC], uint32_t &packed, uint32_t &scale_code,
                                                uint32_t (&deq)[VEC]) {
   static_assert(VEC >= 2 && VEC <= 8 && 32 % VEC == 0, "VEC must divide 32 and fit 32 code bits");
@@ -163,7 +163,7 @@ __device__ __forceinline__ void fp4_block_e8m0(const float (&y)[VEC], uint32_t &
     const float t = __builtin_ldexpf(__builtin_fabsf(y[v]), -e);
     const uint32_t c = e2m1_code_scaled(t, as_u32(y[v]) >> 31);
     packed |= c << (4 * v);
-    deq[v] = as_u32(__builtin_ldexpf(e2m1_val(c), e)) >> 16;
+    if constexpr (DEQ) deq[v] = as_u32(__builtin_ldexpf(e2m1_val(c), e)) >> 16;
   }
 }
 

@@ -16,6 +16,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kvc_device.h"
 #include "kvc_launch.h"
 
@@ -165,7 +167,11 @@ __device__ __forceinline__ void finish_entry(const float (&p)[HD / kWave], const
       for (int h = 0; h < L::H; ++h) store_bf16_q<QV>(a.rotated + out_row * HD + L::feature(lane, h), yb + h * QV);
     }
   }
-  if (a.codes || a.scales || a.deq) {
+  // the fp4 forms, each instance computing the dequantised values only when
+  // they are stored (the flags are uniform across the launch)
+  auto fp4_out = [&](auto e8m0_tag, auto deq_tag) {
+    constexpr bool E8 = decltype(e8m0_tag)::value, DQ = decltype(deq_tag)::value;
+    constexpr int blk = E8 ? 32 : 16;
 #pragma unroll
     for (int h = 0; h < L::H; ++h) {
       const int f = L::feature(lane, h);
@@ -173,17 +179,25 @@ __device__ __forceinline__ void finish_entry(const float (&p)[HD / kWave], const
 #pragma unroll
       for (int q = 0; q < QV; ++q) yq[q] = y[h * QV + q];
       uint32_t packed, scode, deq[QV];
-      const int blk = a.e8m0 ? 32 : 16;
-      if (a.e8m0) fp4_block_e8m0<QV>(yq, packed, scode, deq);
-      else fp4_block<QV>(yq, packed, scode, deq);
+      if constexpr (E8) fp4_block_e8m0<QV, DQ>(yq, packed, scode, deq);
+      else fp4_block<QV, DQ>(yq, packed, scode, deq);
       if (a.codes) {
         uint8_t *c = a.codes + out_row * (HD / 2) + f / 2;
         if constexpr (QV == 4) *reinterpret_cast<uint16_t *>(c) = (uint16_t)packed;
         else *c = (uint8_t)packed;
       }
       if (a.scales && (f % blk) == 0) a.scales[out_row * (HD / blk) + f / blk] = (uint8_t)scode;
-      if (a.deq) store_bf16_q<QV>(a.deq + out_row * HD + f, deq);
+      if constexpr (DQ) store_bf16_q<QV>(a.deq + out_row * HD + f, deq);
     }
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
+  if (a.deq) {
+    if (a.e8m0) fp4_out(yes{}, yes{});
+    else fp4_out(no{}, yes{});
+  } else if (a.codes || a.scales) {
+    if (a.e8m0) fp4_out(yes{}, no{});
+    else fp4_out(no{}, no{});
   }
 }
 
@@ -567,7 +581,7 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(IngestArgs g, PoolAr
 // in) is allowed: a thread reads its chunks before it writes them.
 constexpr int kQuantChunks = 2;
 
-template <bool E8M0>
+template <bool E8M0, bool OUT>
 __global__ __launch_bounds__(256) void fp4_quant_kernel(const uint16_t *in, int64_t n8, uint8_t *codes,
                                                         uint8_t *scales, uint16_t *out) {
   typedef uint32_t u4 __attribute__((ext_vector_type(4)));
@@ -589,12 +603,12 @@ __global__ __launch_bounds__(256) void fp4_quant_kernel(const uint16_t *in, int6
       y[2 * q + 1] = bf16_val(raw[u][q] >> 16);
     }
     uint32_t packed, scode, deq[8];
-    if constexpr (E8M0) fp4_block_e8m0<8>(y, packed, scode, deq);
-    else fp4_block<8>(y, packed, scode, deq);
+    if constexpr (E8M0) fp4_block_e8m0<8, OUT>(y, packed, scode, deq);
+    else fp4_block<8, OUT>(y, packed, scode, deq);
     if (codes) *reinterpret_cast<uint32_t *>(codes + 4 * i) = packed;
     constexpr int per = E8M0 ? 4 : 2;  // threads per block
     if (scales && (i % per) == 0) scales[i / per] = (uint8_t)scode;
-    if (out) {
+    if constexpr (OUT) {
       u4 t;
       t.x = deq[0] | (deq[1] << 16);
       t.y = deq[2] | (deq[3] << 16);
@@ -704,8 +718,10 @@ hipError_t launch_fp4_quant(const uint16_t *in, int64_t rows, int64_t width, uin
   const int64_t n8 = rows * width / 8;
   if (n8 == 0) return hipSuccess;
   const dim3 grid((uint32_t)((n8 + 256 * kQuantChunks - 1) / (256 * kQuantChunks))), block(256);
-  if (e8m0) hipLaunchKernelGGL(fp4_quant_kernel<true>, grid, block, 0, stream, in, n8, codes, scales, out);
-  else hipLaunchKernelGGL(fp4_quant_kernel<false>, grid, block, 0, stream, in, n8, codes, scales, out);
+  if (e8m0 && out) hipLaunchKernelGGL((fp4_quant_kernel<true, true>), grid, block, 0, stream, in, n8, codes, scales, out);
+  else if (e8m0) hipLaunchKernelGGL((fp4_quant_kernel<true, false>), grid, block, 0, stream, in, n8, codes, scales, out);
+  else if (out) hipLaunchKernelGGL((fp4_quant_kernel<false, true>), grid, block, 0, stream, in, n8, codes, scales, out);
+  else hipLaunchKernelGGL((fp4_quant_kernel<false, false>), grid, block, 0, stream, in, n8, codes, scales, out);
   return hipGetLastError();
 }
 
