@@ -184,7 +184,7 @@ def _timed(torch, stream, fn, reps):
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(2e7))
+    torch.cuda._sleep(int(2e8))
     a.record(stream)
     for _ in range(reps):
         fn()
@@ -464,7 +464,7 @@ def run_decode(wl, passes, torch, kvc, W, x_format):
     return {"ms_per_pass": ms, "entries_per_pass": entries, "entries_per_s": entries / (ms / 1e3),
             "us_per_step": ms * 1e3 / wl.seqlen, "tflops": flop_step * wl.seqlen / ms / 1e9,
             "projection_kernel_us": kern_us,
-            "projection_kernel": "decode_f32_kernel<32, 128, 4> (projection + state ingest)"
+            "projection_kernel": "decode_f32_kernel<32, 64, 4> (projection + state ingest)"
             if x_format == kvc.KVC_X_F32 else "decode_gemm_kernel<4, uint16_t> (projection)",
             "projection_kernel_timing": "a step that completes no group, repeated back to back (its one launch)",
             "projection_kernel_us_hook": 1e3 * sum(kern) / len(kern),

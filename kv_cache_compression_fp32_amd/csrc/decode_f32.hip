@@ -27,14 +27,17 @@
 //
 // Operands reach LDS through buffer loads that write it directly (no
 // registers): a stage is BK k of the tile's TM x rows and 32 weight rows,
-// the 16-byte group q of row r at position q ^ (r & 15) (stages of 128 k;
+// the 16-byte group q of row r at position q ^ (r & 15) (stages of 64 k;
 // q ^ (r & 7) with 32 k), so the fragment reads of 16 neighbouring rows hit
 // 16 distinct bank groups. NST stage buffers, the loads NST - 1 stages
-// ahead. The fragment reads of stage s + 1 are issued
-// before the MFMAs of stage s and land while the chain runs. LDS reads are
-// inline asm, which the compiler does not track: it would otherwise wait for
-// every load in flight into any stage buffer before each of them. One wait
-// tied to the values read precedes their MFMAs.
+// ahead. One wavefront per SIMD runs one dependent chain, so whatever the
+// wavefront issues between two chunks of MFMAs delays the chain: the loads
+// go out one per chunk, between the MFMAs; the fragment reads of stage s + 1
+// go out after the barrier that ends step s and drain while the chain of
+// step s + 1 runs, each chunk waiting only for its own two reads. LDS reads
+// are inline asm, which the compiler does not track: it would otherwise
+// wait for every load in flight into any stage buffer before each of them.
+// Each wait is tied to the values it covers.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -108,6 +111,11 @@ __global__ __launch_bounds__(TM / 8 * 64) void decode_f32_kernel(DecodeArgs d) {
   const int64_t klen = segs == 1 ? d.k : (seg < kKSegments - 1 ? d.seg : d.k - (kKSegments - 1) * d.seg);
   const int stages = (int)(klen / BK);
   const int64_t a_rows = d.m - m0 < kTM ? d.m - m0 : kTM;
+  // the bias of this lane's output column for the ingest, loaded ahead of
+  // the operands so that it has landed by the end
+  const int64_t c = n0 + 16 * (wave & 1) + (lane & 15);
+  const bool has_bias = second && d.ape;
+  float bias = has_bias ? d.ape[(int64_t)d.slot * d.n_half + c] : 0.0f;
 
   // buffer resources from the tile's first row at the segment's first k
   const i32x4 a_rsrc = uniform_rsrc(make_rsrc(d.x + m0 * d.k + kbase, (uint32_t)((a_rows * d.k - kbase) * 4)));
@@ -134,14 +142,14 @@ __global__ __launch_bounds__(TM / 8 * 64) void decode_f32_kernel(DecodeArgs d) {
     const int r = b_row0[u] + rsub;
     b_off[u] = (uint32_t)(((int64_t)r * d.k + 4 * (pos ^ (r & SWM))) * 4);
   }
-  auto issue = [&](int s, int buf) {
+  // load u of stage s into stage buffer buf: the x loads, then the weight loads
+  auto issue_one = [&](int s, int buf, int u) {
     const int32_t koff = s * BK * 4;
-#pragma unroll
-    for (int u = 0; u < XPW; ++u)
+    if (u < XPW)
       buffer_load_lds(a_rsrc, (lds_u32 *)(&xs[buf][a_row0[u] * BK]), 16, (int32_t)a_off[u], koff, 0, 0);
-#pragma unroll
-    for (int u = 0; u < WPW; ++u)
-      buffer_load_lds(b_rsrc, (lds_u32 *)(&ws[buf][b_row0[u] * BK]), 16, (int32_t)b_off[u], koff, 0, 0);
+    else
+      buffer_load_lds(b_rsrc, (lds_u32 *)(&ws[buf][b_row0[u - XPW] * BK]), 16, (int32_t)b_off[u - XPW], koff, 0,
+                      0);
   };
   constexpr int PER_STAGE = XPW + WPW;  // loads in flight per stage and wavefront
 
@@ -158,40 +166,43 @@ __global__ __launch_bounds__(TM / 8 * 64) void decode_f32_kernel(DecodeArgs d) {
       asm volatile("ds_read_b128 %0, %1" : "=v"(bf[kk]) : "v"(ba));
     }
   };
-  // the reads above have landed; every value is tied to the wait
-  auto landed = [&](f4(&af)[KK], f4(&bf)[KK]) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(af[0]), "+v"(bf[0]));
-#pragma unroll
-    for (int kk = 1; kk < KK; ++kk) asm volatile("" : "+v"(af[kk]), "+v"(bf[kk]));
-  };
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-  auto chain = [&](const f4(&af)[KK], const f4(&bf)[KK]) {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kk][t], bf[kk][t], acc, 0, 0, 0);
-  };
-  // step s: stage s's fragments (read in the previous step) feed the chain;
-  // first the loads of stage s + NST - 1 go to the buffer of stage s - 1
-  // (every wavefront finished reading it before the previous step's
-  // barrier; past the last stage the last one is loaded again into a buffer
-  // nobody reads, which keeps the wait counts fixed), then the fragments of
-  // stage s + 1 are read once every wavefront's loads of it have landed
+  // step s: the chain over stage s, whose fragments were read at the end of
+  // the previous step. One load of stage s + NST - 1 goes out before each
+  // chunk's MFMAs (into the buffer of stage s - 1: every wavefront finished
+  // reading it before the previous step's barrier; past the last stage the
+  // last one is loaded again into a buffer nobody reads, which keeps the wait
+  // counts fixed), and each chunk waits only for its own two fragment reads
+  // (a wavefront's LDS reads complete in order), so the reads of a stage
+  // drain while the chain runs. Then, once every wavefront's loads of stage
+  // s + 1 have landed, its fragments are read.
   auto step = [&](int s, f4(&ca)[KK], f4(&cb)[KK], f4(&na)[KK], f4(&nb)[KK]) {
-    landed(ca, cb);
     const int ahead = s + NST - 1;
-    issue(ahead < stages ? ahead : stages - 1, ahead % NST);
+    const int sa = ahead < stages ? ahead : stages - 1, ba = ahead % NST;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int u = kk * PER_STAGE / KK; u < (kk + 1) * PER_STAGE / KK; ++u) issue_one(sa, ba, u);
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(ca[kk]), "+v"(cb[kk]) : "n"(2 * (KK - 1 - kk)));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ca[kk][t], cb[kk][t], acc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * PER_STAGE));  // this wavefront's stage s + 1 landed
     barrier_no_fence();                                           // every wavefront's
     if (s + 1 < stages) read((s + 1) % NST, na, nb);
     __builtin_amdgcn_sched_barrier(0);
-    chain(ca, cb);
   };
 
   f4 a0[KK], b0[KK], a1[KK], b1[KK];
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s) issue(s < stages ? s : stages - 1, s);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * PER_STAGE));  // stage 0
+  for (int s = 0; s < NST - 1; ++s)
+#pragma unroll
+    for (int u = 0; u < PER_STAGE; ++u) issue_one(s < stages ? s : stages - 1, s, u);
+  // the bias is needed only at the end; it was loaded before the operands
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * PER_STAGE));  // stage 0 (and the bias)
+  asm volatile("" : "+v"(bias));
   barrier_no_fence();
   read(0, a0, b0);
   for (int s = 0; s < stages; s += 2) {
@@ -223,36 +234,39 @@ __global__ __launch_bounds__(TM / 8 * 64) void decode_f32_kernel(DecodeArgs d) {
     // a counter that was not zero at the call: the caller's workspace was not
     // zero-filled; the state row turns NaN rather than silently wrong
     const bool bad = arrived + 1 != (uint32_t)segs;
+    // every segment's partial sums (the own ones too, as stored above), all
+    // loads in flight at once; rows past the batch read the last row
+    float p[kKSegments][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (row0 + r < d.m) {
-        float t = 0.0f;
+    for (int sg = 0; sg < kKSegments; ++sg)
 #pragma unroll
-        for (int sg = 0; sg < kKSegments; ++sg) {
-          const float p = sg == seg ? acc[r]
-                                    : __hip_atomic_load(d.part + sg * plane + (row0 + r) * ncols + col,
-                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          t = sg == 0 ? p : t + p;  // (p0 + p1) + ..
-        }
-        tot[r] = bad ? __builtin_nanf("") : t;
+      for (int r = 0; r < 4; ++r) {
+        const int64_t rr = row0 + r < d.m ? row0 + r : d.m - 1;
+        p[sg][r] = __hip_atomic_load(d.part + sg * plane + rr * ncols + col, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
       }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float t = p[0][r];
+#pragma unroll
+      for (int sg = 1; sg < kKSegments; ++sg) t = t + p[sg][r];  // (p0 + p1) + ..
+      tot[r] = bad ? __builtin_nanf("") : t;
+    }
     if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // the ingest: the bias row of the token's slot joins the gate logits in
   // one f32 addition, then the state row (and at ratio 4 from position 0 the
   // previous block's padding)
-  const int64_t c = n0 + 16 * fj + row_in;
   float *state = second ? d.sc_state : d.kv_state;
-  const float bias = (second && d.ape) ? d.ape[(int64_t)d.slot * d.n_half + c] : 0.0f;
+  const float fill = second ? -INFINITY : 0.0f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t row = row0 + r;
     if (row >= d.m) continue;
-    float v = tot[r];
-    if (second && d.ape) v = v + bias;
+    const float v = has_bias ? tot[r] + bias : tot[r];
     float *srow = state + row * d.state_rows * d.n_half;
     srow[(int64_t)d.state_row * d.n_half + c] = v;
-    for (int i = 0; i < d.reset_rows; ++i) srow[(int64_t)i * d.n_half + c] = second ? -INFINITY : 0.0f;
+    for (int i = 0; i < d.reset_rows; ++i) srow[(int64_t)i * d.n_half + c] = fill;
   }
 }
 
@@ -277,10 +291,12 @@ hipError_t launch_decode_f32(const DecodeArgs &d, hipStream_t stream) {
       (int64_t)kDecTM * d.k * 4 > INT32_MAX || (d.seg > 0 && !d.part) || !d.counters || d.slot < 0 ||
       d.state_row < 0 || d.state_row >= d.state_rows || d.reset_rows < 0 || d.reset_rows > d.state_rows)
     return hipErrorInvalidValue;
-  // stages of 128 k when every segment is whole stages, else of 32 k
+  // stages of 64 k when every segment is whole stages, else of 32 k (both
+  // 64 KiB of LDS, so two workgroups share a CU once the tiles outnumber
+  // the CUs)
   const int64_t last = d.k - (kKSegments - 1) * d.seg;
-  const bool wide = d.seg > 0 && d.seg % 128 == 0 && last % 128 == 0;
-  return wide ? launch<kDecTM, 128, 4>(d, stream) : launch<kDecTM, 32, 8>(d, stream);
+  const bool wide = d.seg > 0 && d.seg % 64 == 0 && last % 64 == 0;
+  return wide ? launch<kDecTM, 64, 4>(d, stream) : launch<kDecTM, 32, 8>(d, stream);
 }
 
 }  // namespace kvc
