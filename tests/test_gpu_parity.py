@@ -826,8 +826,8 @@ def test_f16_split_of_f32_rows_is_the_two_part_sum(ratio, hd, dim, batch, seqlen
 @pytest.mark.parametrize("batch,dim,hd", [(70, 2048, 128), (5, 4096, 512), (33, 1536, 512)])
 def test_decode_projection_tiles(batch, dim, hd):
     """Decode from f32 rows: batches that are not a multiple of the 32-row
-    tile (70: three row tiles; 5; 33), k segments of 8, 16 and 6 stages of
-    128 k; the emitted entries and the carried state against the oracle over
+    tile (70: three row tiles; 5; 33), k segments of 16, 32 and 12 stages of
+    64 k; the emitted entries and the carried state against the oracle over
     the same tokens, and bit for bit against the GPU prefill."""
     note(f"decode projection tiles batch={batch} dim={dim} hd={hd}")
     from gpu_util import weights
@@ -857,8 +857,8 @@ def test_decode_projection_tiles(batch, dim, hd):
     assert np.array_equal(dec["state_sc"][:, live].view(np.uint32), full["state_sc"][:, live].view(np.uint32))
 
 
-# ratio, head_dim, dim, batch, steps: k segments of whole 128-k stages (dim %
-# 256 == 0), of 32-k stages (segments 64 and 96 at dim 160, 224 and 256 at
+# ratio, head_dim, dim, batch, steps: k segments of whole 64-k stages (dim %
+# 128 == 0), of 32-k stages (segments 64 and 96 at dim 160, 224 and 256 at
 # dim 480, 32 and 64 at dim 96), one segment (dim 32), ragged batches, every
 # ratio
 DECODE_BITWISE_CASES = [
