@@ -75,10 +75,10 @@ __global__ __launch_bounds__(TM / 8 * 64) void decode_f32_kernel(DecodeArgs d) {
   constexpr int kTM = TM, kWaves = TM / 8;  // one 16 x 16 fragment per wavefront
   constexpr int P = BK / 4;              // 16-byte groups per row piece
   constexpr int RPI = 64 / P;            // rows per load instruction
-  // row r's 16-byte group q sits at position q ^ (r & SWM): with 32 groups
-  // per row (BK = 128) the 16 rows of a fragment read land on 16 distinct
-  // 16-byte bank groups (measured on gfx950: 1 us per 64-row step faster than
-  // spreading 8 rows, whose pairs r, r + 8 then share banks)
+  // row r's 16-byte group q sits at position q ^ (r & SWM): with 16 or more
+  // groups per row (stages of 64 k or more) the 16 rows of a fragment read
+  // land on 16 distinct 16-byte bank groups (measured on gfx950: 1 us per
+  // step faster than spreading 8 rows, whose pairs r, r + 8 then share banks)
   constexpr int SWM = P >= 16 ? 15 : 7;
   constexpr int XI = kTM / RPI;          // load instructions per stage: x
   constexpr int WI = kTN / RPI;          //                              weights
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(TM / 8 * 64) void decode_f32_kernel(DecodeArgs d) {
   constexpr int KK = BK / 16;            // 16-k chunks per stage
   static_assert(XI * RPI == kTM && WI * RPI == kTN && XI % kWaves == 0 && (WI % kWaves == 0 || WI < kWaves),
                 "stage / wavefront mismatch");
-  static_assert(NST >= 3, "the loads of a stage go to the buffer read two stages before");
+  static_assert(NST >= 3, "a step loads into the buffer of the stage before it, read one step earlier");
   __shared__ __attribute__((aligned(16))) float xs[NST][kTM * BK];
   __shared__ __attribute__((aligned(16))) float ws[NST][kTN * BK];
   __shared__ uint32_t s_arrival;
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(TM / 8 * 64) void decode_f32_kernel(DecodeArgs d) {
   // load u rows RPI (WPW w + u) + lane / P (with fewer weight loads than
   // wavefronts, wavefront w repeats load w mod WI: same bytes to the same
   // place, so every wavefront has the same count in flight); LDS position
-  // lane % P holds the row's group (lane % P) ^ (row & 7); rows past the
+  // lane % P holds the row's group (lane % P) ^ (row & SWM); rows past the
   // batch read its last row (computed, never stored)
   const int rsub = lane / P, pos = lane % P;
   uint32_t a_off[XPW], b_off[WPW];
